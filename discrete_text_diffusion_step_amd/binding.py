@@ -1,0 +1,380 @@
+"""Thin Python binding over libdgstep's C ABI (argument marshalling only).
+
+Every computation runs in the HIP kernels of libdgstep.so; PyTorch provides
+device memory and the current stream.  Functions carry the C entry points'
+names.  Loading fails loudly when the library has not been built.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdgstep.so")
+
+DG_F32, DG_BF16 = 0, 1
+_DT = {"f32": DG_F32, "bf16": DG_BF16}
+STATUS = {0: "DG_OK", -1: "DG_ERR_NULL", -2: "DG_ERR_SHAPE", -3: "DG_ERR_UNSUPPORTED",
+          -4: "DG_ERR_WORKSPACE", -5: "DG_ERR_DTYPE", -6: "DG_ERR_HIP", -7: "DG_ERR_CAPACITY"}
+
+c_int, c_float, c_size, c_void = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+
+class DGError(RuntimeError):
+    def __init__(self, status, where):
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+class AttnCfg(ctypes.Structure):
+    _fields_ = [("hidden", c_int), ("n_q_heads", c_int), ("n_kv_heads", c_int), ("head_dim", c_int),
+                ("layer_type", c_int), ("window", c_int), ("shared_kv", c_int), ("v_unit_rms", c_int),
+                ("rope_base", c_float), ("rotary_factor", c_float), ("rms_eps", c_float), ("dtype", c_int)]
+
+
+class AttnW(ctypes.Structure):
+    _fields_ = [(n, c_void) for n in ("w_in_norm", "w_q", "w_k", "w_v", "w_o", "q_norm", "k_norm")]
+
+
+class KVLayer(ctypes.Structure):
+    _fields_ = [("k", c_void), ("v", c_void), ("capacity", c_int), ("kv_len", c_int)]
+
+
+class MoeCfg(ctypes.Structure):
+    _fields_ = [("hidden", c_int), ("n_experts", c_int), ("top_k", c_int), ("ffn", c_int),
+                ("shared_ffn", c_int), ("route_scale", c_float), ("rms_eps", c_float),
+                ("layer_scalar", c_float), ("dtype", c_int)]
+
+
+class MoeW(ctypes.Structure):
+    _fields_ = [(n, c_void) for n in ("w_in_norm", "w_router", "w_gate", "w_up", "w_down",
+                                      "ws_gate", "ws_up", "ws_down")]
+
+
+class SamplerCfg(ctypes.Structure):
+    _fields_ = [("vocab", c_int), ("tau", c_float), ("t_max", c_float), ("t_min", c_float),
+                ("n_steps", c_int), ("step", c_int), ("canvas_idx", ctypes.c_uint32),
+                ("seed", ctypes.c_uint64), ("final_step", c_int)]
+
+
+class ModelCfg(ctypes.Structure):
+    _fields_ = [("sliding", AttnCfg), ("global_", AttnCfg), ("moe", MoeCfg), ("n_layers", c_int),
+                ("global_every", c_int), ("vocab", c_int), ("sc_ffn", c_int), ("rms_eps", c_float),
+                ("dtype", c_int)]
+
+
+class ModelW(ctypes.Structure):
+    _fields_ = [("embed", c_void), ("embed_t", c_void), ("w_final_norm", c_void), ("sc_gate", c_void),
+                ("sc_up", c_void), ("sc_down", c_void), ("attn", ctypes.POINTER(AttnW)),
+                ("moe", ctypes.POINTER(MoeW)), ("layer_scalar", ctypes.POINTER(c_float))]
+
+
+class KVCache(ctypes.Structure):
+    _fields_ = [("layer", ctypes.POINTER(KVLayer)), ("n_layers", c_int)]
+
+
+class CanvasState(ctypes.Structure):
+    _fields_ = [("tokens", c_void), ("u", c_void), ("use_u", c_int), ("commit", c_void),
+                ("entropy", c_void), ("n_renoised", c_void), ("logits", c_void), ("canvas_len", c_int)]
+
+
+_LIB = None
+
+
+def lib():
+    """Load libdgstep.so (built in-tree by build.py); raise if it is missing."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run discrete_text_diffusion_step_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        sig = {
+            "dg_status_string": (ctypes.c_char_p, [c_int]),
+            "dg_attn_workspace_bytes": (c_size, [P(AttnCfg), c_int]),
+            "dg_attn_layer": (c_int, [P(AttnCfg), P(AttnW), P(KVLayer), c_int, c_int, c_void, c_void, c_size,
+                                      c_void]),
+            "dg_moe_workspace_bytes": (c_size, [P(MoeCfg), c_int]),
+            "dg_moe_block": (c_int, [P(MoeCfg), P(MoeW), c_int, c_void, c_void, c_void, c_void, c_void, c_size,
+                                     c_void]),
+            "dg_sample_workspace_bytes": (c_size, [c_int, c_int]),
+            "dg_sample_renoise": (c_int, [P(SamplerCfg), c_int, c_void, c_int, c_void, c_void, c_void, c_void,
+                                          c_void, c_void, c_size, c_void]),
+            "dg_canvas_noise": (c_int, [c_int, c_int, ctypes.c_uint64, ctypes.c_uint32, c_void, c_void]),
+            "dg_lm_head_workspace_bytes": (c_size, [c_int, c_int, c_int]),
+            "dg_lm_head": (c_int, [c_int, c_int, c_int, c_float, c_int, c_void, c_void, c_void, c_void, c_void,
+                                   c_size, c_void]),
+            "dg_soft_embed_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int]),
+            "dg_soft_embed": (c_int, [P(SamplerCfg), c_int, c_int, c_int, c_void, c_void, c_void, c_void, c_void,
+                                      c_size, c_void]),
+            "dg_embed_transpose": (c_int, [c_int, c_int, c_int, c_void, c_void, c_void]),
+            "dg_workspace_bytes": (c_size, [P(ModelCfg), c_int, c_int]),
+            "dg_canvas_step": (c_int, [P(ModelCfg), P(ModelW), P(KVCache), P(CanvasState), P(SamplerCfg),
+                                       c_void, c_size, c_void]),
+            "dg_commit_canvas": (c_int, [P(ModelCfg), P(ModelW), P(KVCache), c_void, c_int, c_void, c_size,
+                                         c_void]),
+            "dg_rmsnorm": (c_int, [c_int, c_int, c_float, c_int, c_void, c_void, c_void, c_void]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+# ----------------------------------------------------------------- helpers
+
+
+def ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def stream_handle(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def check(status, where):
+    if status != 0:
+        raise DGError(status, where)
+
+
+_WS = {}
+
+
+def workspace(nbytes, device=None):
+    """A cached device workspace of at least nbytes (256-byte aligned by torch)."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    cur = _WS.get(dev)
+    if cur is None or cur.numel() < nbytes:
+        cur = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+        _WS[dev] = cur
+    return cur
+
+
+def attn_cfg_c(c):
+    return AttnCfg(c["hidden"], c["n_q_heads"], c["n_kv_heads"], c["head_dim"], c["layer_type"],
+                   c.get("window", 0), c["shared_kv"], c["v_unit_rms"], c["rope_base"],
+                   c["rotary_factor"], c["rms_eps"], _DT[c["dtype"]])
+
+
+def attn_w_c(w):
+    return AttnW(*(ptr(w.get(n)) for n in ("w_in_norm", "w_q", "w_k", "w_v", "w_o", "q_norm", "k_norm")))
+
+
+def moe_cfg_c(c, layer_scalar=None):
+    return MoeCfg(c["hidden"], c["n_experts"], c["top_k"], c["ffn"], c["shared_ffn"], c["route_scale"],
+                  c["rms_eps"], c["layer_scalar"] if layer_scalar is None else layer_scalar, _DT[c["dtype"]])
+
+
+def moe_w_c(w):
+    return MoeW(*(ptr(w.get(n)) for n in ("w_in_norm", "w_router", "w_gate", "w_up", "w_down",
+                                          "ws_gate", "ws_up", "ws_down")))
+
+
+def sampler_cfg_c(c):
+    return SamplerCfg(c["vocab"], c["tau"], c["t_max"], c["t_min"], c["n_steps"], c["step"],
+                      c["canvas_idx"] & 0xFFFFFFFF, c["seed"], 1 if c.get("final_step") else 0)
+
+
+def model_cfg_c(m):
+    return ModelCfg(attn_cfg_c(m["sliding"]), attn_cfg_c(m["global"]), moe_cfg_c(m["moe"]), m["n_layers"],
+                    m["global_every"], m["vocab"], m["sc_ffn"], m["rms_eps"], _DT[m["dtype"]])
+
+
+# ------------------------------------------------------------ entry points
+
+
+def dg_status_string(status):
+    return lib().dg_status_string(status).decode()
+
+
+def dg_attn_layer(cfg, w, k_cache, v_cache, kv_len, x, causal, stream=None):
+    """x <- x + Attention(x) in place; returns the new committed length."""
+    L = lib()
+    c = attn_cfg_c(cfg)
+    n = x.shape[0]
+    kv = KVLayer(ptr(k_cache), ptr(v_cache), k_cache.shape[1] if k_cache is not None else 0, kv_len)
+    nb = L.dg_attn_workspace_bytes(ctypes.byref(c), n)
+    ws = workspace(nb, x.device)
+    check(L.dg_attn_layer(ctypes.byref(c), ctypes.byref(attn_w_c(w)), ctypes.byref(kv), n, int(causal), ptr(x),
+                          ptr(ws), ws.numel(), stream_handle(stream)), "dg_attn_layer")
+    return kv.kv_len
+
+
+def dg_moe_block(cfg, w, x, router_logits=None, want_topk=False, stream=None):
+    """x <- layer_scalar * (x + MoE(x)) in place; optionally returns (idx, weights)."""
+    L = lib()
+    c = moe_cfg_c(cfg)
+    n = x.shape[0]
+    idx = wts = None
+    if want_topk:
+        idx = torch.empty(n, cfg["top_k"], dtype=torch.int32, device=x.device)
+        wts = torch.empty(n, cfg["top_k"], dtype=torch.float32, device=x.device)
+    nb = L.dg_moe_workspace_bytes(ctypes.byref(c), n)
+    ws = workspace(nb, x.device)
+    rl = None if router_logits is None else router_logits.contiguous()
+    check(L.dg_moe_block(ctypes.byref(c), ctypes.byref(moe_w_c(w)), n, ptr(x), ptr(rl), ptr(idx), ptr(wts),
+                         ptr(ws), ws.numel(), stream_handle(stream)), "dg_moe_block")
+    return idx, wts
+
+
+def dg_sample_renoise(scfg, logits, want_rowstats=True, stream=None):
+    L = lib()
+    n, V = logits.shape
+    dev = logits.device
+    out = dict(tokens=torch.empty(n, dtype=torch.int32, device=dev),
+               commit=torch.empty(n, dtype=torch.uint8, device=dev),
+               entropy=torch.empty(n, dtype=torch.float32, device=dev),
+               n_renoised=torch.empty(1, dtype=torch.int32, device=dev),
+               rowstats=torch.empty(n, 2, dtype=torch.float32, device=dev) if want_rowstats else None)
+    c = sampler_cfg_c(scfg)
+    ws = workspace(L.dg_sample_workspace_bytes(n, V), dev)
+    ldt = DG_BF16 if logits.dtype == torch.bfloat16 else DG_F32
+    check(L.dg_sample_renoise(ctypes.byref(c), n, ptr(logits), ldt, ptr(out["tokens"]), ptr(out["commit"]),
+                              ptr(out["entropy"]), ptr(out["rowstats"]), ptr(out["n_renoised"]), ptr(ws),
+                              ws.numel(), stream_handle(stream)), "dg_sample_renoise")
+    return out
+
+
+def dg_canvas_noise(n, vocab, seed, canvas_idx, device="cuda", stream=None):
+    t = torch.empty(n, dtype=torch.int32, device=device)
+    check(lib().dg_canvas_noise(n, vocab, seed, canvas_idx & 0xFFFFFFFF, ptr(t), stream_handle(stream)),
+          "dg_canvas_noise")
+    return t
+
+
+def dg_lm_head(x, w_final_norm, embed, eps, stream=None):
+    L = lib()
+    n, D = x.shape
+    V = embed.shape[0]
+    dt = DG_BF16 if x.dtype == torch.bfloat16 else DG_F32
+    logits = torch.empty(n, V, dtype=torch.float32, device=x.device)
+    ws = workspace(L.dg_lm_head_workspace_bytes(n, D, dt), x.device)
+    check(L.dg_lm_head(n, D, V, eps, dt, ptr(x), ptr(w_final_norm), ptr(embed), ptr(logits), ptr(ws), ws.numel(),
+                       stream_handle(stream)), "dg_lm_head")
+    return logits
+
+
+def dg_soft_embed(scfg, logits, rowstats, embed_t, dtype, stream=None):
+    L = lib()
+    n = logits.shape[0]
+    D = embed_t.shape[0]
+    dt = _DT[dtype]
+    u = torch.empty(n, D, dtype=torch.bfloat16 if dt == DG_BF16 else torch.float32, device=logits.device)
+    c = sampler_cfg_c(scfg)
+    ws = workspace(L.dg_soft_embed_workspace_bytes(n, D, scfg["vocab"], dt), logits.device)
+    check(L.dg_soft_embed(ctypes.byref(c), n, D, dt, ptr(logits), ptr(rowstats), ptr(embed_t), ptr(u), ptr(ws),
+                          ws.numel(), stream_handle(stream)), "dg_soft_embed")
+    return u
+
+
+def dg_embed_transpose(embed, stream=None):
+    V, D = embed.shape
+    et = torch.empty(D, V, dtype=embed.dtype, device=embed.device)
+    dt = DG_BF16 if embed.dtype == torch.bfloat16 else DG_F32
+    check(lib().dg_embed_transpose(V, D, dt, ptr(embed), ptr(et), stream_handle(stream)), "dg_embed_transpose")
+    return et
+
+
+def dg_rmsnorm(x, w, eps, out=None, stream=None):
+    n, D = x.shape
+    y = torch.empty_like(x) if out is None else out
+    dt = DG_BF16 if x.dtype == torch.bfloat16 else DG_F32
+    check(lib().dg_rmsnorm(n, D, eps, dt, ptr(x), ptr(w), ptr(y), stream_handle(stream)), "dg_rmsnorm")
+    return y
+
+
+class Model:
+    """Device weights of a whole stack plus the C records that point at them."""
+
+    def __init__(self, mcfg, weights):
+        self.cfg = mcfg
+        self.w = weights
+        self.c_cfg = model_cfg_c(mcfg)
+        L = mcfg["n_layers"]
+        self._attn = (AttnW * L)(*[attn_w_c(a) for a in weights["attn"]])
+        self._moe = (MoeW * L)(*[moe_w_c(m) for m in weights["moe"]])
+        self._ls = (c_float * L)(*weights["layer_scalar"])
+        if weights.get("embed_t") is None:
+            weights["embed_t"] = dg_embed_transpose(weights["embed"])
+        sc = weights.get("sc") or {}
+        self.c_w = ModelW(ptr(weights["embed"]), ptr(weights["embed_t"]), ptr(weights["w_final_norm"]),
+                          ptr(sc.get("sc_gate")), ptr(sc.get("sc_up")), ptr(sc.get("sc_down")),
+                          self._attn, self._moe, self._ls)
+
+
+class KV:
+    """Per-layer K/V caches [Hkv][capacity][d_h] and the C record over them."""
+
+    def __init__(self, mcfg, capacity, device="cuda", tensors=None):
+        L = mcfg["n_layers"]
+        dt = torch.bfloat16 if mcfg["dtype"] == "bf16" else torch.float32
+        self.k, self.v = [], []
+        for l in range(L):
+            glob = (l % mcfg["global_every"]) == mcfg["global_every"] - 1
+            c = mcfg["global"] if glob else mcfg["sliding"]
+            shape = (c["n_kv_heads"], capacity, c["head_dim"])
+            if tensors is not None:
+                self.k.append(tensors[0][l])
+                self.v.append(tensors[1][l])
+            else:
+                self.k.append(torch.zeros(shape, dtype=dt, device=device))
+                self.v.append(torch.zeros(shape, dtype=dt, device=device))
+        self._layers = (KVLayer * L)(*[KVLayer(ptr(self.k[l]), ptr(self.v[l]), capacity, 0) for l in range(L)])
+        self.c = KVCache(self._layers, L)
+
+    @property
+    def kv_len(self):
+        return self._layers[0].kv_len
+
+    def set_len(self, n):
+        for l in range(self.c.n_layers):
+            self._layers[l].kv_len = n
+
+
+def dg_workspace_bytes(mcfg_c, max_canvas, max_commit):
+    return lib().dg_workspace_bytes(ctypes.byref(mcfg_c), max_canvas, max_commit)
+
+
+class Canvas:
+    """Device state of one canvas carried across denoising steps."""
+
+    def __init__(self, n, hidden, dtype, device="cuda", keep_logits_vocab=0):
+        dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.tokens = torch.zeros(n, dtype=torch.int32, device=device)
+        self.u = torch.zeros(n, hidden, dtype=dt, device=device)
+        self.commit = torch.zeros(n, dtype=torch.uint8, device=device)
+        self.entropy = torch.zeros(n, dtype=torch.float32, device=device)
+        self.n_renoised = torch.zeros(1, dtype=torch.int32, device=device)
+        self.logits = (torch.empty(n, keep_logits_vocab, dtype=torch.float32, device=device)
+                       if keep_logits_vocab else None)
+        self.use_u = 0
+        self.n = n
+
+    def c_state(self):
+        return CanvasState(ptr(self.tokens), ptr(self.u), self.use_u, ptr(self.commit), ptr(self.entropy),
+                           ptr(self.n_renoised), ptr(self.logits), self.n)
+
+
+def dg_canvas_step(model, kv, canvas, scfg, ws=None, stream=None):
+    L = lib()
+    st = canvas.c_state()
+    c = sampler_cfg_c(scfg)
+    if ws is None:
+        ws = workspace(L.dg_workspace_bytes(ctypes.byref(model.c_cfg), canvas.n, 0), canvas.tokens.device)
+    check(L.dg_canvas_step(ctypes.byref(model.c_cfg), ctypes.byref(model.c_w), ctypes.byref(kv.c),
+                           ctypes.byref(st), ctypes.byref(c), ptr(ws), ws.numel(), stream_handle(stream)),
+          "dg_canvas_step")
+    canvas.use_u = 1 if model.cfg["sc_ffn"] > 0 else 0
+
+
+def dg_commit_canvas(model, kv, tokens, ws=None, stream=None):
+    L = lib()
+    n = tokens.shape[0]
+    if ws is None:
+        ws = workspace(L.dg_workspace_bytes(ctypes.byref(model.c_cfg), 0, n), tokens.device)
+    check(L.dg_commit_canvas(ctypes.byref(model.c_cfg), ctypes.byref(model.c_w), ctypes.byref(kv.c), ptr(tokens), n,
+                             ptr(ws), ws.numel(), stream_handle(stream)), "dg_commit_canvas")

@@ -1,0 +1,854 @@
+// C ABI of libdgstep: argument validation, workspace layout and the order of
+// kernel launches for one canvas denoising step and for a commit (encode).
+// Every entry point validates on the host, then only enqueues work on the
+// caller's stream.  No allocation, no host synchronisation.
+#include <math.h>
+#include <string.h>
+
+#include "dg_launch.h"
+
+
+using namespace dg;
+
+namespace {
+
+#define DG_TRY(expr)                         \
+  do {                                       \
+    const int st__ = (expr);                 \
+    if (st__ != DG_OK) return st__;          \
+  } while (0)
+#define DG_HIP(expr)                                  \
+  do {                                                \
+    if ((expr) != hipSuccess) return DG_ERR_HIP;      \
+  } while (0)
+
+size_t esize(int dtype) { return dtype == DG_BF16 ? 2 : 4; }
+bool dtype_ok(int dtype) { return dtype == DG_BF16 || dtype == DG_F32; }
+
+// Bump allocator over the caller's workspace; with base == nullptr it only
+// measures.  Every block is 256-byte aligned.
+struct Carve {
+  char *base;
+  size_t off = 0;
+  explicit Carve(void *b) : base(static_cast<char *>(b)) {}
+  template <typename T>
+  T *take(size_t count) {
+    off = (off + 255) & ~static_cast<size_t>(255);
+    T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+  void *bytes(size_t n) { return take<char>(n); }
+};
+
+hipError_t gemm(int dtype, const GemmArgs &a, int mode, int bm, int bn, hipStream_t s) {
+  return dtype == DG_BF16 ? launch_gemm<bf16_t>(a, mode, bm, bn, s) : launch_gemm<float>(a, mode, bm, bn, s);
+}
+
+GemmArgs dense_args(const void *A, long long lda, int M, int N, int K, void *C, long long ldc) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.A = A;
+  g.lda = lda;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.ldb = K;
+  g.nseg = 1;
+  g.seg_start[0] = 0;
+  g.seg_start[1] = N;
+  g.k_splits = 1;
+  g.C = C;
+  g.ldc = ldc;
+  return g;
+}
+
+// split count for a dense product so that the grid covers the chip
+int choose_ksplit(int M, int N, int K, int bm, int bn, int target, int max_split) {
+  const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  int ks = 1;
+  while (tiles * ks < target && ks * 2 <= max_split && K % (64 * ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
+// ------------------------------------------------------------ attention
+
+struct AttnPlan {
+  int n, Ntot, Nq, Nk, Nv, R, n_split_max, oproj_ks;
+};
+
+AttnPlan attn_plan(const dg_attn_cfg *c, int n) {
+  AttnPlan p;
+  p.n = n;
+  p.Nq = c->n_q_heads * c->head_dim;
+  p.Nk = c->n_kv_heads * c->head_dim;
+  p.Nv = c->shared_kv ? 0 : p.Nk;
+  p.Ntot = p.Nq + p.Nk + p.Nv;
+  p.R = (c->n_q_heads / c->n_kv_heads) * n;
+  const int bq = attn_block_rows(c->dtype, c->head_dim);
+  const int blocks = c->n_kv_heads * ((p.R + bq - 1) / (bq > 0 ? bq : 1));
+  int ns = (512 + blocks - 1) / (blocks > 0 ? blocks : 1);
+  p.n_split_max = ns < 1 ? 1 : (ns > 16 ? 16 : ns);
+  p.oproj_ks = choose_ksplit(n, c->hidden, p.Nq, 64, 128, 256, 8);
+  return p;
+}
+
+struct AttnWs {
+  void *h, *qkv, *k_new, *v_new, *o;
+  float *o_part, *ml_part, *oproj_part;
+};
+
+AttnWs attn_carve(const dg_attn_cfg *c, const AttnPlan &p, Carve &cv) {
+  const size_t es = esize(c->dtype);
+  AttnWs w;
+  const size_t n = static_cast<size_t>(p.n);
+  w.h = cv.bytes(n * c->hidden * es);
+  w.qkv = cv.bytes(n * p.Ntot * es);
+  w.k_new = cv.bytes(n * p.Nk * es);
+  w.v_new = cv.bytes(n * p.Nk * es);
+  w.o = cv.bytes(n * p.Nq * es);
+  const size_t rows = static_cast<size_t>(c->n_kv_heads) * p.R;
+  if (p.n_split_max > 1) {
+    w.o_part = cv.take<float>(p.n_split_max * rows * c->head_dim);
+    w.ml_part = cv.take<float>(p.n_split_max * rows * 2);
+  } else {
+    w.o_part = w.ml_part = nullptr;
+  }
+  w.oproj_part = p.oproj_ks > 1 ? cv.take<float>(p.oproj_ks * n * c->hidden) : nullptr;
+  return w;
+}
+
+int check_attn_cfg(const dg_attn_cfg *c) {
+  if (!c) return DG_ERR_NULL;
+  if (!dtype_ok(c->dtype)) return DG_ERR_DTYPE;
+  if (c->hidden <= 0 || c->hidden % 64 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->n_q_heads % c->n_kv_heads || c->head_dim <= 0)
+    return DG_ERR_SHAPE;
+  if ((c->n_q_heads * c->head_dim) % 64) return DG_ERR_SHAPE;
+  // the fused Q|K|V product tiles columns by 128: every segment must fill whole tiles
+  if ((c->n_q_heads * c->head_dim) % 128 || (c->n_kv_heads * c->head_dim) % 128) return DG_ERR_UNSUPPORTED;
+  if (attn_block_rows(c->dtype, c->head_dim) == 0) return DG_ERR_UNSUPPORTED;
+  if (c->layer_type != 0 && c->layer_type != 1) return DG_ERR_SHAPE;
+  if (c->layer_type == 0 && c->window <= 0) return DG_ERR_SHAPE;
+  if (!(c->rope_base > 0.f) || !(c->rotary_factor >= 0.f && c->rotary_factor <= 1.f)) return DG_ERR_SHAPE;
+  if (!(c->rms_eps >= 0.f)) return DG_ERR_SHAPE;
+  return DG_OK;
+}
+
+int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, int causal, void *x,
+              Carve &cv, hipStream_t s) {
+  const AttnPlan p = attn_plan(c, n);
+  const AttnWs ws = attn_carve(c, p, cv);
+  const int dt = c->dtype;
+  const int D = c->hidden, dh = c->head_dim, Hq = c->n_q_heads, Hkv = c->n_kv_heads;
+  const int P = kv->kv_len;
+
+  DG_HIP(launch_rmsnorm(dt, n, D, c->rms_eps, x, w->w_in_norm, ws.h, s));
+
+  GemmArgs g = dense_args(ws.h, D, n, p.Ntot, D, ws.qkv, p.Ntot);
+  g.nseg = c->shared_kv ? 2 : 3;
+  g.seg_start[0] = 0;
+  g.seg_start[1] = p.Nq;
+  g.seg_start[2] = p.Nq + p.Nk;
+  g.seg_start[3] = p.Ntot;
+  g.seg_B0[0] = w->w_q;
+  g.seg_B0[1] = w->w_k;
+  g.seg_B0[2] = w->w_v;
+  g.seg_start[g.nseg] = p.Ntot;
+  DG_HIP(gemm(dt, g, EPI_STORE, 64, 128, s));
+
+  NormRopeArgs nr;
+  nr.qkv = ws.qkv;
+  nr.ld = p.Ntot;
+  nr.n_tok = n;
+  nr.Hq = Hq;
+  nr.Hkv = Hkv;
+  nr.dh = dh;
+  nr.q_off = 0;
+  nr.k_off = p.Nq;
+  nr.v_off = c->shared_kv ? p.Nq : p.Nq + p.Nk;
+  nr.q_norm = w->q_norm;
+  nr.k_norm = w->k_norm;
+  if (causal) {
+    nr.k_dst = kv->k;
+    nr.v_dst = kv->v;
+    nr.dst_head_stride = static_cast<long long>(kv->capacity) * dh;
+    nr.dst_row0 = P;
+  } else {
+    nr.k_dst = ws.k_new;
+    nr.v_dst = ws.v_new;
+    nr.dst_head_stride = static_cast<long long>(n) * dh;
+    nr.dst_row0 = 0;
+  }
+  nr.pos0 = P;
+  nr.rope_base = c->rope_base;
+  const double rf = c->layer_type == 1 ? c->rotary_factor : 1.0;
+  nr.n_rot = static_cast<int>(floor(rf * (dh / 2) + 0.5));
+  nr.eps = c->rms_eps;
+  nr.sqrt_dh = static_cast<float>(sqrt(static_cast<double>(dh)));
+  nr.v_unit_rms = c->v_unit_rms;
+  DG_HIP(launch_norm_rope(nr, dt, s));
+
+  AttnArgs at;
+  at.q = ws.qkv;
+  at.q_ld = p.Ntot;
+  at.k_cache = kv->k;
+  at.v_cache = kv->v;
+  at.cache_hs = static_cast<long long>(kv->capacity) * dh;
+  if (causal) {
+    const size_t es = esize(dt);
+    at.k_new = static_cast<const char *>(kv->k) + static_cast<size_t>(P) * dh * es;
+    at.v_new = static_cast<const char *>(kv->v) + static_cast<size_t>(P) * dh * es;
+    at.new_hs = at.cache_hs;
+  } else {
+    at.k_new = ws.k_new;
+    at.v_new = ws.v_new;
+    at.new_hs = static_cast<long long>(n) * dh;
+  }
+  at.n_tok = n;
+  at.Hq = Hq;
+  at.Hkv = Hkv;
+  at.n_rep = Hq / Hkv;
+  at.kv_len = P;
+  at.sliding = c->layer_type == 0;
+  at.window = c->window;
+  at.key_lo = (at.sliding && !causal) ? (P > c->window ? P - c->window : 0) : 0;
+  at.causal = causal;
+  // split the keys so the grid covers the chip, at least 64 keys per slice
+  const int n_keys = P + n - at.key_lo;
+  int ns = p.n_split_max;
+  const int max_by_keys = (n_keys + 63) / 64;
+  if (ns > max_by_keys) ns = max_by_keys;
+  if (ns < 1) ns = 1;
+  at.n_split = ns;
+  at.o_part = ws.o_part;
+  at.ml_part = ws.ml_part;
+  at.out = ws.o;
+  at.out_ld = p.Nq;
+  DG_HIP(launch_attention(at, dt, dh, s));
+
+  // x += o W_o^T
+  if (p.oproj_ks > 1) {
+    GemmArgs o = dense_args(ws.o, p.Nq, n, D, p.Nq, ws.oproj_part, D);
+    o.seg_B0[0] = w->w_o;
+    o.k_splits = p.oproj_ks;
+    DG_HIP(gemm(dt, o, EPI_PARTIAL_F32, 64, 128, s));
+    DG_HIP(dt == DG_BF16 ? launch_splitk_reduce<bf16_t>(ws.oproj_part, p.oproj_ks, n, D, D, x, EPI_ADD, s)
+                         : launch_splitk_reduce<float>(ws.oproj_part, p.oproj_ks, n, D, D, x, EPI_ADD, s));
+  } else {
+    GemmArgs o = dense_args(ws.o, p.Nq, n, D, p.Nq, x, D);
+    o.seg_B0[0] = w->w_o;
+    DG_HIP(gemm(dt, o, EPI_ADD, 64, 128, s));
+  }
+  if (causal) kv->kv_len = P + n;
+  return DG_OK;
+}
+
+int check_attn_call(const dg_attn_cfg *c, const dg_attn_w *w, const dg_kv_layer *kv, int n, int causal,
+                    const void *x) {
+  DG_TRY(check_attn_cfg(c));
+  if (!w || !kv || !x) return DG_ERR_NULL;
+  if (!w->w_in_norm || !w->w_q || !w->w_k || !w->w_o || !w->q_norm || !w->k_norm) return DG_ERR_NULL;
+  if (!c->shared_kv && !w->w_v) return DG_ERR_NULL;
+  if (n < 0 || kv->kv_len < 0 || kv->capacity < 0 || kv->kv_len > kv->capacity) return DG_ERR_SHAPE;
+  if (n > 0 && (!kv->k || !kv->v) && (causal || kv->kv_len > 0)) return DG_ERR_NULL;
+  if (causal != 0 && causal != 1) return DG_ERR_SHAPE;
+  if (causal && kv->kv_len + n > kv->capacity) return DG_ERR_CAPACITY;
+  return DG_OK;
+}
+
+size_t attn_ws_bytes(const dg_attn_cfg *c, int n) {
+  Carve cv(nullptr);
+  attn_carve(c, attn_plan(c, n), cv);
+  return cv.off + 256;
+}
+
+// ------------------------------------------------------------------ MoE
+
+struct MoeWs {
+  void *h;
+  float *rl, *tw;
+  int32_t *idx;
+  int *g_off, *row_token, *pair_row;
+  float *row_weight, *Y;
+  void *H;
+};
+
+MoeWs moe_carve(const dg_moe_cfg *c, int n, Carve &cv) {
+  const size_t es = esize(c->dtype);
+  const size_t rows = static_cast<size_t>(n) * (c->top_k + 1);
+  const int fmax = c->ffn > c->shared_ffn ? c->ffn : c->shared_ffn;
+  MoeWs w;
+  w.h = cv.bytes(static_cast<size_t>(n) * c->hidden * es);
+  w.rl = cv.take<float>(static_cast<size_t>(n) * c->n_experts);
+  w.idx = cv.take<int32_t>(static_cast<size_t>(n) * c->top_k);
+  w.tw = cv.take<float>(static_cast<size_t>(n) * c->top_k);
+  w.g_off = cv.take<int>(c->n_experts + 2);
+  w.row_token = cv.take<int>(rows);
+  w.row_weight = cv.take<float>(rows);
+  w.pair_row = cv.take<int>(static_cast<size_t>(n) * c->top_k);
+  w.H = cv.bytes(rows * fmax * es);
+  w.Y = cv.take<float>(rows * c->hidden);
+  return w;
+}
+
+int check_moe_cfg(const dg_moe_cfg *c) {
+  if (!c) return DG_ERR_NULL;
+  if (!dtype_ok(c->dtype)) return DG_ERR_DTYPE;
+  if (c->hidden <= 0 || c->hidden % 64 || c->ffn <= 0 || c->ffn % 64 || c->shared_ffn <= 0 ||
+      c->shared_ffn % 64)
+    return DG_ERR_SHAPE;
+  if (c->n_experts <= 0 || c->n_experts > 256 || c->top_k <= 0 || c->top_k > 8 || c->top_k > c->n_experts)
+    return DG_ERR_SHAPE;
+  return DG_OK;
+}
+
+int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float *rl_in, int32_t *idx_out,
+             float *w_out, Carve &cv, hipStream_t s) {
+  const MoeWs ws = moe_carve(c, n, cv);
+  if (n == 0) return DG_OK;
+  const int dt = c->dtype, D = c->hidden, E = c->n_experts, k = c->top_k, F = c->ffn, Fs = c->shared_ffn;
+  const int fmax = F > Fs ? F : Fs;
+  DG_HIP(launch_rmsnorm(dt, n, D, c->rms_eps, x, w->w_in_norm, ws.h, s));
+  const float *rl = rl_in;
+  if (!rl) {
+    GemmArgs g = dense_args(ws.h, D, n, E, D, ws.rl, E);
+    g.seg_B0[0] = w->w_router;
+    DG_HIP(gemm(dt, g, EPI_STORE_F32, 64, 128, s));
+    rl = ws.rl;
+  }
+  int32_t *idx = idx_out ? idx_out : ws.idx;
+  float *tw = w_out ? w_out : ws.tw;
+  DG_HIP(launch_router_topk(rl, n, E, k, c->route_scale, idx, tw, s));
+  DG_HIP(launch_moe_permute(idx, tw, n, k, E, ws.g_off, ws.row_token, ws.row_weight, ws.pair_row, s));
+
+  const int rows_per_expert = (n * k + E - 1) / E;
+  const int bm = (dt == DG_BF16 && rows_per_expert > 48) ? 128 : 32;
+
+  // gate/up of every expert (group 0 = shared) with the SwiGLU epilogue
+  GemmArgs gu;
+  memset(&gu, 0, sizeof(gu));
+  gu.A = ws.h;
+  gu.lda = D;
+  gu.a_rows = ws.row_token;
+  gu.seg_B0[0] = w->w_gate;
+  gu.seg_B1[0] = w->w_up;
+  gu.ldb = D;
+  gu.b_gstride = static_cast<long long>(F) * D;
+  gu.g_off = ws.g_off;
+  gu.n_groups = E + 1;
+  gu.Bx0 = w->ws_gate;
+  gu.Bx1 = w->ws_up;
+  gu.N_x = Fs;
+  gu.K_x = D;
+  gu.ldb_x = D;
+  gu.M = n * (k + 1);
+  gu.N = F;
+  gu.K = D;
+  gu.k_splits = 1;
+  gu.C = ws.H;
+  gu.ldc = fmax;
+  DG_HIP(gemm(dt, gu, EPI_SWIGLU, bm, 64, s));
+
+  // down projection, scaled by the routing weight of each row
+  GemmArgs dn;
+  memset(&dn, 0, sizeof(dn));
+  dn.A = ws.H;
+  dn.lda = fmax;
+  dn.seg_B0[0] = w->w_down;
+  dn.ldb = F;
+  dn.b_gstride = static_cast<long long>(D) * F;
+  dn.g_off = ws.g_off;
+  dn.n_groups = E + 1;
+  dn.Bx0 = w->ws_down;
+  dn.N_x = D;
+  dn.K_x = Fs;
+  dn.ldb_x = Fs;
+  dn.M = n * (k + 1);
+  dn.N = D;
+  dn.K = F;
+  dn.k_splits = 1;
+  dn.C = ws.Y;
+  dn.ldc = D;
+  dn.rowscale = ws.row_weight;
+  DG_HIP(gemm(dt, dn, EPI_ROWSCALE_F32, bm, 64, s));
+
+  DG_HIP(launch_moe_combine(dt, x, ws.Y, ws.pair_row, n, k, D, c->layer_scalar, s));
+  return DG_OK;
+}
+
+int check_moe_call(const dg_moe_cfg *c, const dg_moe_w *w, int n, const void *x, const float *rl_in) {
+  DG_TRY(check_moe_cfg(c));
+  if (!w || !x) return DG_ERR_NULL;
+  if (!w->w_in_norm || !w->w_gate || !w->w_up || !w->w_down || !w->ws_gate || !w->ws_up || !w->ws_down)
+    return DG_ERR_NULL;
+  if (!rl_in && !w->w_router) return DG_ERR_NULL;
+  if (n < 0) return DG_ERR_SHAPE;
+  return DG_OK;
+}
+
+size_t moe_ws_bytes(const dg_moe_cfg *c, int n) {
+  Carve cv(nullptr);
+  moe_carve(c, n, cv);
+  return cv.off + 256;
+}
+
+// -------------------------------------------------------------- sampler
+
+int sample_chunks(int vocab) {
+  int nc = 1;
+  while (nc < 16 && vocab % (nc * 2 * 2048) == 0) nc *= 2;
+  return nc;
+}
+
+struct SampleWs {
+  float *part;
+  int *part_idx;
+};
+
+SampleWs sample_carve(int n, int vocab, Carve &cv) {
+  const int nc = sample_chunks(vocab);
+  SampleWs w;
+  w.part = cv.take<float>(static_cast<size_t>(n) * nc * 4);
+  w.part_idx = cv.take<int>(static_cast<size_t>(n) * nc);
+  return w;
+}
+
+double temperature(const dg_sampler_cfg *c) {
+  if (c->n_steps <= 1) return c->t_max;
+  return static_cast<double>(c->t_max) +
+         (static_cast<double>(c->t_min) - static_cast<double>(c->t_max)) * c->step / (c->n_steps - 1);
+}
+
+int check_sampler_cfg(const dg_sampler_cfg *c) {
+  if (!c) return DG_ERR_NULL;
+  if (c->vocab <= 0 || c->vocab % 8) return DG_ERR_SHAPE;
+  if (!(c->t_max > 0.f) || !(c->t_min > 0.f) || c->n_steps < 1 || c->step < 0) return DG_ERR_SHAPE;
+  if (!(temperature(c) > 0.0)) return DG_ERR_SHAPE;
+  return DG_OK;
+}
+
+int sample_impl(const dg_sampler_cfg *c, int n, const void *logits, int ldt, int32_t *tok, uint8_t *commit,
+                float *ent, float *rowstats, int32_t *nre, Carve &cv, hipStream_t s) {
+  const SampleWs ws = sample_carve(n, c->vocab, cv);
+  SampleArgs a;
+  a.logits = logits;
+  a.logits_bf16 = ldt == DG_BF16;
+  a.n_pos = n;
+  a.vocab = c->vocab;
+  a.n_chunks = sample_chunks(c->vocab);
+  a.inv_t = static_cast<float>(1.0 / temperature(c));
+  a.tau = c->tau;
+  a.final_step = c->final_step;
+  a.step = static_cast<uint32_t>(c->step);
+  a.canvas_idx = c->canvas_idx;
+  a.key0 = static_cast<uint32_t>(c->seed & 0xffffffffull);
+  a.key1 = static_cast<uint32_t>(c->seed >> 32);
+  a.part = ws.part;
+  a.part_idx = ws.part_idx;
+  a.tokens = tok;
+  a.commit = commit;
+  a.entropy = ent;
+  a.rowstats = rowstats;
+  a.n_renoised = nre;
+  DG_HIP(launch_sampler(a, s));
+  return DG_OK;
+}
+
+// ----------------------------------------------------- head, soft embedding
+
+int softembed_ksplit(int n, int D, int V) { return choose_ksplit(n, D, V, 64, 128, 512, 32); }
+
+struct SoftWs {
+  void *P;
+  float *part;
+};
+
+SoftWs soft_carve(int n, int D, int V, int dtype, Carve &cv) {
+  SoftWs w;
+  w.P = cv.bytes(static_cast<size_t>(n) * V * esize(dtype));
+  const int ks = softembed_ksplit(n, D, V);
+  w.part = ks > 1 ? cv.take<float>(static_cast<size_t>(ks) * n * D) : nullptr;
+  return w;
+}
+
+int soft_embed_impl(const dg_sampler_cfg *sc, int n, int D, int dt, const float *logits, const float *rowstats,
+                    const void *embed_t, void *u, Carve &cv, hipStream_t s) {
+  const int V = sc->vocab;
+  const SoftWs ws = soft_carve(n, D, V, dt, cv);
+  if (n == 0) return DG_OK;
+  DG_HIP(launch_probs(dt, logits, rowstats, n, V, static_cast<float>(1.0 / temperature(sc)), ws.P, s));
+  const int ks = softembed_ksplit(n, D, V);
+  if (ks > 1) {
+    GemmArgs g = dense_args(ws.P, V, n, D, V, ws.part, D);
+    g.seg_B0[0] = embed_t;
+    g.k_splits = ks;
+    g.tile_order = 1;
+    DG_HIP(gemm(dt, g, EPI_PARTIAL_F32, 64, 128, s));
+    DG_HIP(dt == DG_BF16 ? launch_splitk_reduce<bf16_t>(ws.part, ks, n, D, D, u, EPI_STORE, s)
+                         : launch_splitk_reduce<float>(ws.part, ks, n, D, D, u, EPI_STORE, s));
+  } else {
+    GemmArgs g = dense_args(ws.P, V, n, D, V, u, D);
+    g.seg_B0[0] = embed_t;
+    g.tile_order = 1;
+    DG_HIP(gemm(dt, g, EPI_STORE, 64, 128, s));
+  }
+  return DG_OK;
+}
+
+int lm_head_impl(int n, int D, int V, float eps, int dt, const void *x, const void *wn, const void *E, float *logits,
+                 Carve &cv, hipStream_t s) {
+  void *h = cv.bytes(static_cast<size_t>(n) * D * esize(dt));
+  if (n == 0) return DG_OK;
+  DG_HIP(launch_rmsnorm(dt, n, D, eps, x, wn, h, s));
+  GemmArgs g = dense_args(h, D, n, V, D, logits, V);
+  g.seg_B0[0] = E;
+  g.tile_order = 0;
+  DG_HIP(gemm(dt, g, EPI_STORE_F32, 64, 128, s));
+  return DG_OK;
+}
+
+// ---------------------------------------------------------- whole model
+
+int check_model(const dg_model_cfg *c) {
+  if (!c) return DG_ERR_NULL;
+  if (!dtype_ok(c->dtype)) return DG_ERR_DTYPE;
+  DG_TRY(check_attn_cfg(&c->sliding));
+  DG_TRY(check_attn_cfg(&c->global));
+  DG_TRY(check_moe_cfg(&c->moe));
+  if (c->sliding.dtype != c->dtype || c->global.dtype != c->dtype || c->moe.dtype != c->dtype) return DG_ERR_DTYPE;
+  const int D = c->sliding.hidden;
+  if (c->global.hidden != D || c->moe.hidden != D) return DG_ERR_SHAPE;
+  if (c->n_layers <= 0 || c->global_every <= 0 || c->vocab <= 0 || c->vocab % 64 || c->sc_ffn < 0 ||
+      c->sc_ffn % 64)
+    return DG_ERR_SHAPE;
+  return DG_OK;
+}
+
+const dg_attn_cfg *layer_cfg(const dg_model_cfg *c, int l) {
+  return (l % c->global_every) == c->global_every - 1 ? &c->global : &c->sliding;
+}
+
+size_t layer_ws_bytes(const dg_model_cfg *c, int n) {
+  size_t m = moe_ws_bytes(&c->moe, n);
+  const size_t a0 = attn_ws_bytes(&c->sliding, n), a1 = attn_ws_bytes(&c->global, n);
+  if (a0 > m) m = a0;
+  if (a1 > m) m = a1;
+  return m;
+}
+
+struct StepWs {
+  void *x, *g_sc;
+  float *logits, *rowstats;
+  void *rest;
+};
+
+StepWs step_carve(const dg_model_cfg *c, int n, bool need_logits, Carve &cv) {
+  const size_t es = esize(c->dtype);
+  const int D = c->sliding.hidden;
+  StepWs w;
+  w.x = cv.bytes(static_cast<size_t>(n) * D * es);
+  w.g_sc = cv.bytes(static_cast<size_t>(n) * (c->sc_ffn > 0 ? c->sc_ffn : 1) * es);
+  w.logits = need_logits ? cv.take<float>(static_cast<size_t>(n) * c->vocab) : nullptr;
+  w.rowstats = cv.take<float>(static_cast<size_t>(n) * 2);
+  size_t tail = layer_ws_bytes(c, n);
+  {
+    Carve t(nullptr);
+    t.bytes(static_cast<size_t>(n) * D * es);
+    sample_carve(n, c->vocab, t);
+    if (t.off > tail) tail = t.off;
+  }
+  {
+    Carve t(nullptr);
+    soft_carve(n, D, c->vocab, c->dtype, t);
+    if (t.off > tail) tail = t.off;
+  }
+  w.rest = cv.bytes(tail + 256);
+  return w;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+
+extern "C" {
+
+const char *dg_status_string(int st) {
+  switch (st) {
+    case DG_OK: return "ok";
+    case DG_ERR_NULL: return "required pointer is NULL";
+    case DG_ERR_SHAPE: return "invalid or inconsistent size";
+    case DG_ERR_UNSUPPORTED: return "configuration not supported by the built kernels";
+    case DG_ERR_WORKSPACE: return "workspace too small";
+    case DG_ERR_DTYPE: return "invalid or mismatched dtype";
+    case DG_ERR_HIP: return "HIP launch failed";
+    case DG_ERR_CAPACITY: return "KV cache capacity exceeded";
+  }
+  return "unknown status";
+}
+
+size_t dg_attn_workspace_bytes(const dg_attn_cfg *cfg, int n_tok) {
+  if (check_attn_cfg(cfg) != DG_OK || n_tok < 0) return 0;
+  return attn_ws_bytes(cfg, n_tok);
+}
+
+int dg_attn_layer(const dg_attn_cfg *cfg, const dg_attn_w *w, dg_kv_layer *kv, int n_tok, int causal, void *x,
+                  void *ws, size_t ws_bytes, void *stream) {
+  DG_TRY(check_attn_call(cfg, w, kv, n_tok, causal, x));
+  if (n_tok == 0) return DG_OK;
+  if (!ws) return DG_ERR_NULL;
+  if (ws_bytes < attn_ws_bytes(cfg, n_tok)) return DG_ERR_WORKSPACE;
+  Carve cv(ws);
+  return attn_impl(cfg, w, kv, n_tok, causal, x, cv, static_cast<hipStream_t>(stream));
+}
+
+size_t dg_moe_workspace_bytes(const dg_moe_cfg *cfg, int n_tok) {
+  if (check_moe_cfg(cfg) != DG_OK || n_tok < 0) return 0;
+  return moe_ws_bytes(cfg, n_tok);
+}
+
+int dg_moe_block(const dg_moe_cfg *cfg, const dg_moe_w *w, int n_tok, void *x, const float *rl_in,
+                 int32_t *idx_out, float *w_out, void *ws, size_t ws_bytes, void *stream) {
+  DG_TRY(check_moe_call(cfg, w, n_tok, x, rl_in));
+  if (n_tok == 0) return DG_OK;
+  if (!ws) return DG_ERR_NULL;
+  if (ws_bytes < moe_ws_bytes(cfg, n_tok)) return DG_ERR_WORKSPACE;
+  Carve cv(ws);
+  return moe_impl(cfg, w, n_tok, x, rl_in, idx_out, w_out, cv, static_cast<hipStream_t>(stream));
+}
+
+size_t dg_sample_workspace_bytes(int n_pos, int vocab) {
+  if (n_pos < 0 || vocab <= 0) return 0;
+  Carve cv(nullptr);
+  sample_carve(n_pos, vocab, cv);
+  return cv.off + 256;
+}
+
+int dg_sample_renoise(const dg_sampler_cfg *cfg, int n_pos, const void *logits, int logits_dtype, int32_t *tok,
+                      uint8_t *commit, float *ent, float *rowstats, int32_t *nre, void *ws, size_t ws_bytes,
+                      void *stream) {
+  DG_TRY(check_sampler_cfg(cfg));
+  if (!dtype_ok(logits_dtype)) return DG_ERR_DTYPE;
+  if (n_pos < 0) return DG_ERR_SHAPE;
+  if (!logits || !tok || !commit || !ent || !nre || !ws) return DG_ERR_NULL;
+  if (ws_bytes < dg_sample_workspace_bytes(n_pos, cfg->vocab)) return DG_ERR_WORKSPACE;
+  Carve cv(ws);
+  return sample_impl(cfg, n_pos, logits, logits_dtype, tok, commit, ent, rowstats, nre, cv,
+                     static_cast<hipStream_t>(stream));
+}
+
+int dg_canvas_noise(int n_pos, int vocab, uint64_t seed, uint32_t canvas_idx, int32_t *tokens, void *stream) {
+  if (!tokens) return DG_ERR_NULL;
+  if (n_pos < 0 || vocab <= 0) return DG_ERR_SHAPE;
+  if (launch_canvas_noise(n_pos, vocab, static_cast<uint32_t>(seed & 0xffffffffull), static_cast<uint32_t>(seed >> 32),
+                          canvas_idx, tokens, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DG_ERR_HIP;
+  return DG_OK;
+}
+
+size_t dg_lm_head_workspace_bytes(int n_pos, int hidden, int dtype) {
+  if (n_pos < 0 || hidden <= 0 || !dtype_ok(dtype)) return 0;
+  return static_cast<size_t>(n_pos) * hidden * esize(dtype) + 512;
+}
+
+int dg_lm_head(int n_pos, int hidden, int vocab, float eps, int dtype, const void *x, const void *wn, const void *E,
+               float *logits, void *ws, size_t ws_bytes, void *stream) {
+  if (!dtype_ok(dtype)) return DG_ERR_DTYPE;
+  if (n_pos < 0 || hidden <= 0 || hidden % 64 || vocab <= 0 || vocab % 8) return DG_ERR_SHAPE;
+  if (!x || !wn || !E || !logits || !ws) return DG_ERR_NULL;
+  if (ws_bytes < dg_lm_head_workspace_bytes(n_pos, hidden, dtype)) return DG_ERR_WORKSPACE;
+  Carve cv(ws);
+  return lm_head_impl(n_pos, hidden, vocab, eps, dtype, x, wn, E, logits, cv, static_cast<hipStream_t>(stream));
+}
+
+size_t dg_soft_embed_workspace_bytes(int n_pos, int hidden, int vocab, int dtype) {
+  if (n_pos < 0 || hidden <= 0 || vocab <= 0 || !dtype_ok(dtype)) return 0;
+  Carve cv(nullptr);
+  soft_carve(n_pos, hidden, vocab, dtype, cv);
+  return cv.off + 256;
+}
+
+int dg_soft_embed(const dg_sampler_cfg *scfg, int n_pos, int hidden, int dtype, const float *logits,
+                  const float *rowstats, const void *embed_t, void *u, void *ws, size_t ws_bytes, void *stream) {
+  DG_TRY(check_sampler_cfg(scfg));
+  if (!dtype_ok(dtype)) return DG_ERR_DTYPE;
+  if (n_pos < 0 || hidden <= 0 || hidden % 64 || scfg->vocab % 64) return DG_ERR_SHAPE;
+  if (!logits || !rowstats || !embed_t || !u || !ws) return DG_ERR_NULL;
+  if (ws_bytes < dg_soft_embed_workspace_bytes(n_pos, hidden, scfg->vocab, dtype)) return DG_ERR_WORKSPACE;
+  Carve cv(ws);
+  return soft_embed_impl(scfg, n_pos, hidden, dtype, logits, rowstats, embed_t, u, cv,
+                         static_cast<hipStream_t>(stream));
+}
+
+int dg_embed_transpose(int vocab, int hidden, int dtype, const void *E, void *Et, void *stream) {
+  if (!dtype_ok(dtype)) return DG_ERR_DTYPE;
+  if (vocab <= 0 || hidden <= 0) return DG_ERR_SHAPE;
+  if (!E || !Et) return DG_ERR_NULL;
+  if (launch_transpose(dtype, vocab, hidden, E, Et, static_cast<hipStream_t>(stream)) != hipSuccess) return DG_ERR_HIP;
+  return DG_OK;
+}
+
+int dg_rmsnorm(int n, int hidden, float eps, int dtype, const void *x, const void *w, void *y, void *stream) {
+  if (!dtype_ok(dtype)) return DG_ERR_DTYPE;
+  if (n < 0 || hidden <= 0 || hidden % 8) return DG_ERR_SHAPE;
+  if (!x || !w || !y) return DG_ERR_NULL;
+  if (launch_rmsnorm(dtype, n, hidden, eps, x, w, y, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DG_ERR_HIP;
+  return DG_OK;
+}
+
+size_t dg_workspace_bytes(const dg_model_cfg *cfg, int max_canvas_tokens, int max_commit_tokens) {
+  if (check_model(cfg) != DG_OK || max_canvas_tokens < 0 || max_commit_tokens < 0) return 0;
+  Carve a(nullptr), b(nullptr);
+  step_carve(cfg, max_canvas_tokens, true, a);
+  step_carve(cfg, max_commit_tokens, false, b);
+  return (a.off > b.off ? a.off : b.off) + 256;
+}
+
+static int check_model_w(const dg_model_cfg *c, const dg_model_w *w, bool need_head) {
+  if (!w || !w->embed || !w->attn || !w->moe || !w->layer_scalar) return DG_ERR_NULL;
+  if (need_head && (!w->w_final_norm || !w->embed_t)) return DG_ERR_NULL;
+  if (c->sc_ffn > 0 && need_head && (!w->sc_gate || !w->sc_up || !w->sc_down)) return DG_ERR_NULL;
+  return DG_OK;
+}
+
+static int check_kv(const dg_model_cfg *c, const dg_kv_cache *kv) {
+  if (!kv || !kv->layer) return DG_ERR_NULL;
+  if (kv->n_layers != c->n_layers) return DG_ERR_SHAPE;
+  const int P = kv->layer[0].kv_len;
+  for (int l = 0; l < c->n_layers; ++l) {
+    const dg_kv_layer &L = kv->layer[l];
+    if (L.kv_len != P || L.kv_len < 0 || L.kv_len > L.capacity) return DG_ERR_SHAPE;
+    if ((!L.k || !L.v) && L.capacity > 0) return DG_ERR_NULL;
+  }
+  return DG_OK;
+}
+
+int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cache *kv, dg_canvas_state *st,
+                   const dg_sampler_cfg *scfg, void *ws, size_t ws_bytes, void *stream) {
+  DG_TRY(check_model(cfg));
+  DG_TRY(check_sampler_cfg(scfg));
+  DG_TRY(check_model_w(cfg, w, true));
+  DG_TRY(check_kv(cfg, kv));
+  if (!st || !st->tokens || !st->u || !st->commit || !st->entropy || !st->n_renoised) return DG_ERR_NULL;
+  if (scfg->vocab != cfg->vocab) return DG_ERR_SHAPE;
+  const int n = st->canvas_len;
+  if (n <= 0) return DG_ERR_SHAPE;
+  if (!ws) return DG_ERR_NULL;
+  Carve cv(ws);
+  const StepWs sw = step_carve(cfg, n, st->logits == nullptr, cv);
+  if (ws_bytes < cv.off) return DG_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int dt = cfg->dtype, D = cfg->sliding.hidden;
+
+  DG_HIP(launch_embed(dt, st->tokens, n, D, cfg->vocab, w->embed, sw.x, s));
+  if (st->use_u && cfg->sc_ffn > 0) {
+    GemmArgs g = dense_args(st->u, D, n, cfg->sc_ffn, D, sw.g_sc, cfg->sc_ffn);
+    g.seg_B0[0] = w->sc_gate;
+    g.seg_B1[0] = w->sc_up;
+    DG_HIP(gemm(dt, g, EPI_SWIGLU, 64, 64, s));
+    GemmArgs d = dense_args(sw.g_sc, cfg->sc_ffn, n, D, cfg->sc_ffn, sw.x, D);
+    d.seg_B0[0] = w->sc_down;
+    DG_HIP(gemm(dt, d, EPI_ADD, 64, 128, s));
+  }
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    Carve c1(sw.rest);
+    dg_kv_layer L = kv->layer[l];
+    DG_TRY(attn_impl(layer_cfg(cfg, l), &w->attn[l], &L, n, 0, sw.x, c1, s));
+    dg_moe_cfg mc = cfg->moe;
+    mc.layer_scalar = w->layer_scalar[l];
+    Carve c2(sw.rest);
+    DG_TRY(moe_impl(&mc, &w->moe[l], n, sw.x, nullptr, nullptr, nullptr, c2, s));
+  }
+  float *logits = st->logits ? st->logits : sw.logits;
+  {
+    Carve c(sw.rest);
+    DG_TRY(lm_head_impl(n, D, cfg->vocab, cfg->rms_eps, dt, sw.x, w->w_final_norm, w->embed, logits, c, s));
+  }
+  {
+    Carve c(sw.rest);
+    DG_TRY(sample_impl(scfg, n, logits, DG_F32, st->tokens, st->commit, st->entropy, sw.rowstats, st->n_renoised,
+                       c, s));
+  }
+  if (cfg->sc_ffn > 0) {
+    Carve c(sw.rest);
+    DG_TRY(soft_embed_impl(scfg, n, D, dt, logits, sw.rowstats, w->embed_t, st->u, c, s));
+  }
+  return DG_OK;
+}
+
+int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *kv, const int32_t *tokens, int n,
+                     void *ws, size_t ws_bytes, void *stream) {
+  DG_TRY(check_model(cfg));
+  DG_TRY(check_model_w(cfg, w, false));
+  DG_TRY(check_kv(cfg, kv));
+  if (!tokens) return DG_ERR_NULL;
+  if (n < 0) return DG_ERR_SHAPE;
+  if (n == 0) return DG_OK;
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if (kv->layer[l].kv_len + n > kv->layer[l].capacity) return DG_ERR_CAPACITY;
+  if (!ws) return DG_ERR_NULL;
+  Carve cv(ws);
+  const StepWs sw = step_carve(cfg, n, false, cv);
+  if (ws_bytes < cv.off) return DG_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int dt = cfg->dtype, D = cfg->sliding.hidden;
+  DG_HIP(launch_embed(dt, tokens, n, D, cfg->vocab, w->embed, sw.x, s));
+  const int L = cfg->n_layers;
+  for (int l = 0; l < L; ++l) {
+    const dg_attn_cfg *ac = layer_cfg(cfg, l);
+    dg_kv_layer &KL = kv->layer[l];
+    if (l == L - 1) {
+      // last layer: only its K/V are needed (pre-norm, projections, norm/RoPE, append)
+      Carve c1(sw.rest);
+      const AttnPlan p = attn_plan(ac, n);
+      const AttnWs aw = attn_carve(ac, p, c1);
+      DG_HIP(launch_rmsnorm(dt, n, D, ac->rms_eps, sw.x, w->attn[l].w_in_norm, aw.h, s));
+      GemmArgs g = dense_args(aw.h, D, n, p.Nk + p.Nv, D, aw.qkv, p.Ntot);
+      // write k|v at column Nq of the qkv rows so the norm/RoPE pass reads the usual layout
+      g.C = static_cast<char *>(aw.qkv) + static_cast<size_t>(p.Nq) * esize(dt);
+      g.nseg = ac->shared_kv ? 1 : 2;
+      g.seg_start[0] = 0;
+      g.seg_start[1] = p.Nk;
+      g.seg_start[2] = p.Nk + p.Nv;
+      g.seg_B0[0] = w->attn[l].w_k;
+      g.seg_B0[1] = w->attn[l].w_v;
+      DG_HIP(gemm(dt, g, EPI_STORE, 64, 128, s));
+      NormRopeArgs nr;
+      nr.qkv = aw.qkv;
+      nr.ld = p.Ntot;
+      nr.n_tok = n;
+      nr.Hq = 0;
+      nr.Hkv = ac->n_kv_heads;
+      nr.dh = ac->head_dim;
+      nr.q_off = 0;
+      nr.k_off = p.Nq;
+      nr.v_off = ac->shared_kv ? p.Nq : p.Nq + p.Nk;
+      nr.q_norm = w->attn[l].q_norm;
+      nr.k_norm = w->attn[l].k_norm;
+      nr.k_dst = KL.k;
+      nr.v_dst = KL.v;
+      nr.dst_head_stride = static_cast<long long>(KL.capacity) * ac->head_dim;
+      nr.dst_row0 = KL.kv_len;
+      nr.pos0 = KL.kv_len;
+      nr.rope_base = ac->rope_base;
+      const double rf = ac->layer_type == 1 ? ac->rotary_factor : 1.0;
+      nr.n_rot = static_cast<int>(floor(rf * (ac->head_dim / 2) + 0.5));
+      nr.eps = ac->rms_eps;
+      nr.sqrt_dh = static_cast<float>(sqrt(static_cast<double>(ac->head_dim)));
+      nr.v_unit_rms = ac->v_unit_rms;
+      DG_HIP(launch_norm_rope(nr, dt, s));
+      KL.kv_len += n;
+      break;
+    }
+    Carve c1(sw.rest);
+    DG_TRY(attn_impl(ac, &w->attn[l], &KL, n, 1, sw.x, c1, s));
+    dg_moe_cfg mc = cfg->moe;
+    mc.layer_scalar = w->layer_scalar[l];
+    Carve c2(sw.rest);
+    DG_TRY(moe_impl(&mc, &w->moe[l], n, sw.x, nullptr, nullptr, nullptr, c2, s));
+  }
+  return DG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,194 @@
+// Common device helpers for libdgstep (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dgstep.h"
+
+namespace dg {
+
+typedef uint16_t bf16_t;  // bfloat16 storage
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even, as the storage rounding of a bf16 tensor.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+// ------------------------------------------------------------ MFMA fragments
+//
+// One 16x16x32 step.  Lane l supplies row (A) / column (B) l % 16 and eight
+// consecutive k values [8*(l/16), 8*(l/16)+8) of the 32-wide k slice.  A and B
+// use the same k assignment, so the product is the plain sum over k.  The
+// fp32 accumulator of lane l holds C[4*(l/16) + i][l % 16], i = 0..3.
+
+template <typename T> struct Frag;
+
+template <> struct Frag<bf16_t> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const bf16_t *p) { v = *reinterpret_cast<const bf16x8 *>(p); }
+  __device__ __forceinline__ void zero() {
+    uint4 z = make_uint4(0, 0, 0, 0);
+    v = *reinterpret_cast<bf16x8 *>(&z);
+  }
+  __device__ __forceinline__ void from_floats(const float *f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = static_cast<uint32_t>(f32_to_bf16(f[2 * j])) | (static_cast<uint32_t>(f32_to_bf16(f[2 * j + 1])) << 16);
+    v = *reinterpret_cast<bf16x8 *>(w);
+  }
+};
+
+template <> struct Frag<float> {
+  float v[8];
+  __device__ __forceinline__ void load(const float *p) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0];
+    const float4 b = reinterpret_cast<const float4 *>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0.f;
+  }
+  __device__ __forceinline__ void from_floats(const float *f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = f[j];
+  }
+};
+
+__device__ __forceinline__ void mma(f32x4 &acc, const Frag<bf16_t> &a, const Frag<bf16_t> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+
+// fp32 path: eight 16x16x4 steps, step j taking element j of every lane, so the
+// k assignment matches the bf16 path.
+__device__ __forceinline__ void mma(f32x4 &acc, const Frag<float> &a, const Frag<float> &b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+// ---------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// 16-byte vector of T elements.
+template <typename T> struct Vec16 { static constexpr int n = 16 / sizeof(T); };
+
+__device__ __forceinline__ void load8(const bf16_t *p, float *f) {
+  const uint4 u = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = __uint_as_float(w[j] << 16);
+    f[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float *p, float *f) {
+  const float4 a = reinterpret_cast<const float4 *>(p)[0];
+  const float4 b = reinterpret_cast<const float4 *>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+__device__ __forceinline__ void store8(bf16_t *p, const float *f) {
+  uint4 u;
+  u.x = static_cast<uint32_t>(f32_to_bf16(f[0])) | (static_cast<uint32_t>(f32_to_bf16(f[1])) << 16);
+  u.y = static_cast<uint32_t>(f32_to_bf16(f[2])) | (static_cast<uint32_t>(f32_to_bf16(f[3])) << 16);
+  u.z = static_cast<uint32_t>(f32_to_bf16(f[4])) | (static_cast<uint32_t>(f32_to_bf16(f[5])) << 16);
+  u.w = static_cast<uint32_t>(f32_to_bf16(f[6])) | (static_cast<uint32_t>(f32_to_bf16(f[7])) << 16);
+  *reinterpret_cast<uint4 *>(p) = u;
+}
+__device__ __forceinline__ void store8(float *p, const float *f) {
+  reinterpret_cast<float4 *>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
+  reinterpret_cast<float4 *>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+}  // namespace dg
+
+// ------------------------------------------------------------ host launchers
+// Implemented in the kernel translation units; all return hipError_t.
+namespace dg {
+
+enum EpiMode {
+  EPI_STORE = 0,       // C (T)   = acc
+  EPI_STORE_F32 = 1,   // C (f32) = acc
+  EPI_ADD = 2,         // C (T)   = T(C + acc)          (residual add)
+  EPI_SWIGLU = 3,      // C (T)   = T(silu(acc0) * acc1) (dual B)
+  EPI_ROWSCALE_F32 = 4,// C (f32) = acc * rowscale[row]
+  EPI_PARTIAL_F32 = 5  // C (f32)[split][row][col] = acc  (split-K partials)
+};
+
+struct GemmArgs {
+  // A operand: logical row r reads physical row a_rows ? a_rows[r] : r.
+  const void *A;
+  long long lda;
+  const int *a_rows;
+  // B operand ([N][K] rows, i.e. y = x B^T).  Dense: up to 4 column segments
+  // (seg_start ascending, seg_start[nseg] = N), each with its own matrix.
+  int nseg;
+  int seg_start[5];
+  const void *seg_B0[4];
+  const void *seg_B1[4];  // second matrix for the dual (SwiGLU) mode
+  long long ldb;
+  // Grouped mode (g_off != nullptr): group 0 uses (Bx0, Bx1, N_x); groups
+  // 1..n_groups-1 use B0 + (g-1)*b_gstride (and B1) with N columns.  Rows of
+  // group g are logical rows [g_off[g], g_off[g+1]).
+  const int *g_off;
+  int n_groups;
+  const void *Bx0, *Bx1;
+  int N_x, K_x;           // group 0 columns and depth
+  long long ldb_x;        // group 0 weight row stride
+  long long b_gstride;
+  // sizes
+  int M, N, K;
+  int k_splits;     // split-K count (dense only); K % (64 * k_splits) == 0
+  // output
+  void *C;
+  long long ldc;
+  const float *rowscale;
+  int tile_order;   // 0: consecutive tiles share B columns (m fastest), 1: share A rows (n fastest)
+};
+
+template <typename T>
+hipError_t launch_gemm(const GemmArgs &a, int mode, int bm, int bn, hipStream_t s);
+template <typename T>
+hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, long long ldc,
+                                void *C, int mode, hipStream_t s);
+
+}  // namespace dg

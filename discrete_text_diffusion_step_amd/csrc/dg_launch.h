@@ -1,0 +1,76 @@
+// Host-side launcher interface between the C ABI layer and the kernels.
+#pragma once
+#include "dg_common.h"
+
+namespace dg {
+
+struct NormRopeArgs {
+  void *qkv;                 // [n_tok][ld] raw projections (q | k | v)
+  long long ld;
+  int n_tok, Hq, Hkv, dh;
+  int q_off, k_off, v_off;   // column offsets of q, k, v (v_off = k_off when K/V are shared)
+  const void *q_norm, *k_norm;
+  void *k_dst, *v_dst;       // [Hkv][..][dh], row dst_row0 + j
+  long long dst_head_stride; // elements between heads
+  int dst_row0;
+  int pos0;
+  double rope_base;
+  int n_rot;                 // frequencies kept (the rest are zero)
+  float eps, sqrt_dh;
+  int v_unit_rms;
+};
+
+struct AttnArgs {
+  const void *q;             // row (token j, head h) at q + j*q_ld + h*dh
+  long long q_ld;
+  const void *k_cache, *v_cache;  // [Hkv][cap][dh]: committed rows (position m at row m)
+  long long cache_hs;
+  const void *k_new, *v_new; // rows of positions >= kv_len: row m - kv_len
+  long long new_hs;
+  int n_tok, Hq, Hkv, n_rep;
+  int kv_len, key_lo;
+  int causal, sliding, window;
+  int n_split;
+  float *o_part;             // [n_split][Hkv*R][dh]
+  float *ml_part;            // [n_split][Hkv*R][2]
+  void *out;                 // row (token j, head h) at out + j*out_ld + h*dh
+  long long out_ld;
+};
+
+struct SampleArgs {
+  const void *logits;
+  int logits_bf16;
+  int n_pos, vocab, n_chunks;
+  float inv_t, tau;
+  int final_step;
+  uint32_t step, canvas_idx, key0, key1;
+  float *part;          // [n_pos][n_chunks][4]: m, Z, S, best value
+  int *part_idx;        // [n_pos][n_chunks]: argmax index
+  int32_t *tokens;
+  uint8_t *commit;
+  float *entropy;
+  float *rowstats;      // optional [n_pos][2]
+  int32_t *n_renoised;
+};
+
+hipError_t launch_norm_rope(const NormRopeArgs &a, int dtype, hipStream_t s);
+hipError_t launch_attention(const AttnArgs &a, int dtype, int dh, hipStream_t s);
+int attn_block_rows(int dtype, int dh);
+hipError_t launch_router_topk(const float *logits, int n_tok, int E, int k, float scale, int32_t *idx, float *w,
+                              hipStream_t s);
+hipError_t launch_moe_permute(const int32_t *idx, const float *w, int n_tok, int k, int E, int *g_off,
+                              int *row_token, float *row_weight, int *pair_row, hipStream_t s);
+hipError_t launch_moe_combine(int dtype, void *x, const float *Y, const int *pair_row, int n_tok, int k, int D,
+                              float layer_scalar, hipStream_t s);
+hipError_t launch_sampler(const SampleArgs &a, hipStream_t s);
+hipError_t launch_canvas_noise(int n_pos, int vocab, uint32_t key0, uint32_t key1, uint32_t canvas_idx,
+                               int32_t *tokens, hipStream_t s);
+hipError_t launch_probs(int dtype, const float *logits, const float *rowstats, int n_pos, int vocab, float inv_t,
+                        void *P, hipStream_t s);
+hipError_t launch_rmsnorm(int dtype, int n, int D, float eps, const void *x, const void *w, void *y,
+                          hipStream_t s);
+hipError_t launch_embed(int dtype, const int32_t *tokens, int n, int D, int vocab, const void *E, void *x,
+                        hipStream_t s);
+hipError_t launch_transpose(int dtype, int rows, int cols, const void *in, void *out, hipStream_t s);
+
+}  // namespace dg

@@ -1,0 +1,322 @@
+// Matrix products y = x W^T on bf16/fp32 MFMA (gfx950).
+//
+// Every product of the step has a weight operand W [N][K] that is streamed
+// from HBM exactly once per output tile, and a narrow activation operand
+// (256 canvas rows, or the few rows routed to one expert).  The kernel stages
+// the activation tile (A) through LDS, where the four waves of a workgroup
+// share it, and streams each wave's own weight columns (B) from global memory
+// straight into MFMA fragment registers, one 64-wide k stage ahead of use.
+//
+// Modes: dense (tiles over M x N, optional split-K, up to four weight
+// segments side by side, e.g. the Q|K|V projections) and grouped (one group
+// per expert: rows gathered by token index, one weight matrix per group,
+// workgroup loops over the group's row tiles).  Epilogues: store, residual
+// add, SwiGLU of two products (expert gate/up), per-row scale (routing
+// weight) and split-K partials.
+#include "dg_common.h"
+
+namespace dg {
+
+namespace {
+
+constexpr int kBK = 64;  // k elements per LDS stage (two 32-wide MFMA steps)
+
+template <typename T, int BM, int BN, int NB, int MODE>
+struct GemmTile {
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int LDS_ROW = kBK + PAD;  // elements per LDS row (16 B pad vs bank conflicts)
+  static constexpr int MT = BM / 16;
+  static constexpr int WN = BN / 4;          // columns per wave
+  static constexpr int NT = WN / 16;
+  static constexpr int VEC = 16 / sizeof(T); // elements per 16-byte chunk
+  static constexpr int CPR = kBK / VEC;      // chunks per A row per stage
+  static constexpr int A_CHUNKS = BM * CPR;
+  static constexpr int A_ITERS = (A_CHUNKS + 255) / 256;
+  static_assert(BN % 64 == 0, "BN must give each of the four waves a multiple of 16 columns");
+  static_assert(BM % 16 == 0, "BM must be a multiple of 16");
+};
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+
+// One BM x BN output tile over k in [kb, ke).
+//   row_begin/rows: logical rows of the tile (rows <= BM valid)
+//   Bp[nb]: pointer to row n0 of weight nb; ncols: valid columns from n0
+template <typename T, int BM, int BN, int NB, int MODE>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &a, T *sA0, T *sA1, int row_begin, int rows,
+                                          const T *const *Bp, int n0, int ncols, int kb, int ke,
+                                          int split) {
+  using G = GemmTile<T, BM, BN, NB, MODE>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const T *A = static_cast<const T *>(a.A);
+
+  // physical A rows of the chunks this thread stages (fixed over k)
+  long long arow[G::A_ITERS];
+  int acol[G::A_ITERS];
+  bool aval[G::A_ITERS];
+#pragma unroll
+  for (int it = 0; it < G::A_ITERS; ++it) {
+    const int c = tid + it * 256;
+    const int r = c / G::CPR;
+    acol[it] = (c % G::CPR) * G::VEC;
+    aval[it] = (c < G::A_CHUNKS) && (r < rows);
+    int pr = row_begin + r;
+    if (aval[it] && a.a_rows) pr = a.a_rows[pr];
+    arow[it] = aval[it] ? static_cast<long long>(pr) * a.lda : 0;
+  }
+  // per-lane column validity (N need not be a multiple of 16)
+  bool bval[G::NT];
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) bval[nt] = (wave * G::WN + nt * 16 + l16) < ncols;
+
+  f32x4 acc[NB][G::MT][G::NT];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < G::NT; ++nt) acc[nb][mt][nt] = zero4();
+
+  uint4 ra[G::A_ITERS];
+  auto loadA = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < G::A_ITERS; ++it) {
+      if (aval[it]) ra[it] = *reinterpret_cast<const uint4 *>(A + arow[it] + k0 + acol[it]);
+      else ra[it] = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto storeA = [&](T *s) {
+#pragma unroll
+    for (int it = 0; it < G::A_ITERS; ++it) {
+      const int c = tid + it * 256;
+      if (c < G::A_CHUNKS)
+        *reinterpret_cast<uint4 *>(s + (c / G::CPR) * G::LDS_ROW + acol[it]) = ra[it];
+    }
+  };
+  auto loadB = [&](Frag<T>(&fb)[NB][G::NT][2], int k0) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int nt = 0; nt < G::NT; ++nt) {
+        const T *p = Bp[nb] + static_cast<long long>(wave * G::WN + nt * 16 + l16) * a.ldb + k0 + lg * 8;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          if (bval[nt]) fb[nb][nt][s].load(p + s * 32);
+          else fb[nb][nt][s].zero();
+        }
+      }
+  };
+  auto compute = [&](const T *s, const Frag<T>(&fb)[NB][G::NT][2]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt) {
+        Frag<T> fa;
+        fa.load(s + (mt * 16 + l16) * G::LDS_ROW + ks * 32 + lg * 8);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int nt = 0; nt < G::NT; ++nt) mma(acc[nb][mt][nt], fa, fb[nb][nt][ks]);
+      }
+    }
+  };
+
+  Frag<T> fb0[NB][G::NT][2], fb1[NB][G::NT][2];
+  const int nst = (ke - kb) / kBK;
+  loadA(kb);
+  loadB(fb0, kb);
+  storeA(sA0);
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    const bool more1 = st + 1 < nst;
+    if (more1) {
+      loadA(kb + (st + 1) * kBK);
+      loadB(fb1, kb + (st + 1) * kBK);
+    }
+    compute(sA0, fb0);
+    if (more1) storeA(sA1);
+    __syncthreads();
+    if (!more1) break;
+    const bool more2 = st + 2 < nst;
+    if (more2) {
+      loadA(kb + (st + 2) * kBK);
+      loadB(fb0, kb + (st + 2) * kBK);
+    }
+    compute(sA1, fb1);
+    if (more2) storeA(sA0);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows 4*lg + i, column l16 of each 16x16 sub-tile
+#pragma unroll
+  for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt) {
+      if (!bval[nt]) continue;
+      const int col = n0 + wave * G::WN + nt * 16 + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mt * 16 + lg * 4 + i;
+        if (r >= rows) continue;
+        const long long row = row_begin + r;
+        const float v = acc[0][mt][nt][i];
+        if constexpr (MODE == EPI_STORE) {
+          static_cast<T *>(a.C)[row * a.ldc + col] = from_f32<T>(v);
+        } else if constexpr (MODE == EPI_STORE_F32) {
+          static_cast<float *>(a.C)[row * a.ldc + col] = v;
+        } else if constexpr (MODE == EPI_ADD) {
+          T *c = static_cast<T *>(a.C) + row * a.ldc + col;
+          *c = from_f32<T>(to_f32<T>(*c) + v);
+        } else if constexpr (MODE == EPI_SWIGLU) {
+          const float u = acc[NB - 1][mt][nt][i];
+          static_cast<T *>(a.C)[row * a.ldc + col] = from_f32<T>(silu_f(v) * u);
+        } else if constexpr (MODE == EPI_ROWSCALE_F32) {
+          static_cast<float *>(a.C)[row * a.ldc + col] = v * a.rowscale[row];
+        } else if constexpr (MODE == EPI_PARTIAL_F32) {
+          static_cast<float *>(a.C)[(static_cast<long long>(split) * a.M + row) * a.ldc + col] = v;
+        }
+      }
+    }
+}
+
+template <typename T, int BM, int BN, int NB, int MODE>
+__global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmArgs a) {
+  using G = GemmTile<T, BM, BN, NB, MODE>;
+  __shared__ __attribute__((aligned(16))) T sA0[BM * G::LDS_ROW];
+  __shared__ __attribute__((aligned(16))) T sA1[BM * G::LDS_ROW];
+
+  if (a.g_off == nullptr) {
+    // dense: one tile per workgroup; consecutive workgroup ids are spread
+    // over the 8 XCDs, so renumber tiles to keep neighbours on one XCD (L2)
+    int L = blockIdx.x;
+    const int total = gridDim.x;
+    if ((total & 7) == 0) {
+      const int per = total >> 3;
+      L = (L & 7) * per + (L >> 3);
+    }
+    const int m_tiles = (a.M + BM - 1) / BM;
+    const int n_tiles = (a.N + BN - 1) / BN;
+    int m_tile, n_tile, split;
+    if (a.tile_order == 0) {
+      m_tile = L % m_tiles;
+      const int r = L / m_tiles;
+      n_tile = r % n_tiles;
+      split = r / n_tiles;
+    } else {
+      n_tile = L % n_tiles;
+      const int r = L / n_tiles;
+      m_tile = r % m_tiles;
+      split = r / m_tiles;
+    }
+    const int n0 = n_tile * BN;
+    int s = 0;
+    while (s + 1 < a.nseg && n0 >= a.seg_start[s + 1]) ++s;
+    const T *Bp[NB];
+    Bp[0] = static_cast<const T *>(a.seg_B0[s]) + static_cast<long long>(n0 - a.seg_start[s]) * a.ldb;
+    if (NB > 1) Bp[NB - 1] = static_cast<const T *>(a.seg_B1[s]) + static_cast<long long>(n0 - a.seg_start[s]) * a.ldb;
+    const int kper = a.K / a.k_splits;
+    const int row0 = m_tile * BM;
+    gemm_tile<T, BM, BN, NB, MODE>(a, sA0, sA1, row0, min(BM, a.M - row0), Bp, n0,
+                                   a.seg_start[s + 1] - n0, split * kper, (split + 1) * kper, split);
+  } else {
+    const int g = blockIdx.y;
+    const int n0 = blockIdx.x * BN;
+    const int Ng = (g == 0) ? a.N_x : a.N;
+    if (n0 >= Ng) return;
+    const T *Bp[NB];
+    GemmArgs ga = a;   // group 0 (shared expert) may have its own depth and row stride
+    if (g == 0) {
+      ga.K = a.K_x;
+      ga.ldb = a.ldb_x;
+      Bp[0] = static_cast<const T *>(a.Bx0) + static_cast<long long>(n0) * a.ldb_x;
+      if (NB > 1) Bp[NB - 1] = static_cast<const T *>(a.Bx1) + static_cast<long long>(n0) * a.ldb_x;
+    } else {
+      const long long off = static_cast<long long>(g - 1) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
+      Bp[0] = static_cast<const T *>(a.seg_B0[0]) + off;
+      if (NB > 1) Bp[NB - 1] = static_cast<const T *>(a.seg_B1[0]) + off;
+    }
+    const int r0 = a.g_off[g], r1 = a.g_off[g + 1];
+    for (int rb = r0; rb < r1; rb += BM)
+      gemm_tile<T, BM, BN, NB, MODE>(ga, sA0, sA1, rb, min(BM, r1 - rb), Bp, n0, Ng - n0, 0, ga.K, 0);
+  }
+}
+
+template <typename T, int BM, int BN, int NB, int MODE>
+hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
+  dim3 grid;
+  if (a.g_off) {
+    const int nmax = a.N > a.N_x ? a.N : a.N_x;
+    grid = dim3((nmax + BN - 1) / BN, a.n_groups);
+  } else {
+    const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
+    grid = dim3(mt * nt * a.k_splits, 1);
+  }
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, NB, MODE>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *part, int splits, int M, int N,
+                                                            long long ldc, void *C, int mode) {
+  const long long i8 = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i8 >= static_cast<long long>(M) * N) return;
+  const int row = static_cast<int>(i8 / N), col = static_cast<int>(i8 % N);
+  float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int z = 0; z < splits; ++z) {
+    float v[8];
+    load8(part + (static_cast<long long>(z) * M + row) * N + col, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] += v[j];
+  }
+  if (mode == EPI_STORE_F32) {
+    store8(static_cast<float *>(C) + row * ldc + col, s);
+  } else {
+    T *c = static_cast<T *>(C) + row * ldc + col;
+    if (mode == EPI_ADD) {
+      float o[8];
+      load8(c, o);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s[j] += o[j];
+    }
+    store8(c, s);
+  }
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_gemm(const GemmArgs &a, int mode, int bm, int bn, hipStream_t s) {
+#define DG_GEMM_CASE(BM_, BN_, NB_, MODE_) \
+  if (bm == BM_ && bn == BN_ && mode == MODE_) return launch_one<T, BM_, BN_, NB_, MODE_>(a, s);
+  DG_GEMM_CASE(64, 128, 1, EPI_STORE)
+  DG_GEMM_CASE(64, 128, 1, EPI_STORE_F32)
+  DG_GEMM_CASE(64, 128, 1, EPI_ADD)
+  DG_GEMM_CASE(64, 128, 1, EPI_PARTIAL_F32)
+  DG_GEMM_CASE(64, 64, 2, EPI_SWIGLU)
+  DG_GEMM_CASE(32, 64, 2, EPI_SWIGLU)
+  DG_GEMM_CASE(32, 64, 1, EPI_ROWSCALE_F32)
+  if constexpr (sizeof(T) == 2) {
+    DG_GEMM_CASE(128, 64, 2, EPI_SWIGLU)
+    DG_GEMM_CASE(128, 64, 1, EPI_ROWSCALE_F32)
+  }
+#undef DG_GEMM_CASE
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, long long ldc, void *C,
+                                int mode, hipStream_t s) {
+  const long long n8 = static_cast<long long>(M) * N / 8;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, s,
+                     part, splits, M, N, ldc, C, mode);
+  return hipGetLastError();
+}
+
+template hipError_t launch_gemm<bf16_t>(const GemmArgs &, int, int, int, hipStream_t);
+template hipError_t launch_gemm<float>(const GemmArgs &, int, int, int, hipStream_t);
+template hipError_t launch_splitk_reduce<bf16_t>(const float *, int, int, int, long long, void *, int, hipStream_t);
+template hipError_t launch_splitk_reduce<float>(const float *, int, int, int, long long, void *, int, hipStream_t);
+
+}  // namespace dg

@@ -1,0 +1,107 @@
+// Row kernels (gfx950): RMSNorm, embedding gather, embedding transpose.
+#include "dg_launch.h"
+
+namespace dg {
+
+namespace {
+
+// aitrends notebook summary, rms code: y = w * x * sqrt(D) / (||x||_2 + eps)
+// with the norm reduced in fp32.  One wave per row, 16-byte vector accesses.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(int n, int D, float eps, float sqrt_d, const T *x,
+                                                      const T *w, T *y) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const T *xr = x + static_cast<long long>(row) * D;
+  float ss = 0.f;
+  for (int c = lane * 8; c < D; c += 64 * 8) {
+    float v[8];
+    load8(xr + c, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
+  }
+  ss = wave_sum(ss);
+  const float scale = sqrt_d / (sqrtf(ss) + eps);
+  T *yr = y + static_cast<long long>(row) * D;
+  for (int c = lane * 8; c < D; c += 64 * 8) {
+    float v[8], g[8];
+    load8(xr + c, v);
+    load8(w + c, g);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = g[j] * v[j] * scale;
+    store8(yr + c, v);
+  }
+}
+
+// x[j] = E[tokens[j]]; ids outside [0, vocab) are clamped into range.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t *tokens, int n, int D, int vocab, const T *E,
+                                                    T *x) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  int t = tokens[row];
+  t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
+  const uint4 *src = reinterpret_cast<const uint4 *>(E + static_cast<long long>(t) * D);
+  uint4 *dst = reinterpret_cast<uint4 *>(x + static_cast<long long>(row) * D);
+  const int nv = D * static_cast<int>(sizeof(T)) / 16;
+  for (int c = lane; c < nv; c += 64) dst[c] = src[c];
+}
+
+// out[c][r] = in[r][c] through a 64x64 LDS tile.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(int rows, int cols, const T *in, T *out) {
+  __shared__ T tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) tile[i][tx] = in[static_cast<long long>(r) * cols + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (r < rows && c < cols) out[static_cast<long long>(c) * rows + r] = tile[tx][i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(int dtype, int n, int D, float eps, const void *x, const void *w, void *y,
+                          hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const float sqrt_d = static_cast<float>(__builtin_sqrt(static_cast<double>(D)));
+  if (dtype == DG_BF16)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3((n + 3) / 4), dim3(256), 0, s, n, D, eps, sqrt_d,
+                       static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(w), static_cast<bf16_t *>(y));
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3((n + 3) / 4), dim3(256), 0, s, n, D, eps, sqrt_d,
+                       static_cast<const float *>(x), static_cast<const float *>(w), static_cast<float *>(y));
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(int dtype, const int32_t *tokens, int n, int D, int vocab, const void *E, void *x,
+                        hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (dtype == DG_BF16)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3((n + 3) / 4), dim3(256), 0, s, tokens, n, D, vocab,
+                       static_cast<const bf16_t *>(E), static_cast<bf16_t *>(x));
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3((n + 3) / 4), dim3(256), 0, s, tokens, n, D, vocab,
+                       static_cast<const float *>(E), static_cast<float *>(x));
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(int dtype, int rows, int cols, const void *in, void *out, hipStream_t s) {
+  dim3 grid((cols + 63) / 64, (rows + 63) / 64);
+  if (dtype == DG_BF16)
+    hipLaunchKernelGGL(transpose_kernel<bf16_t>, grid, dim3(256), 0, s, rows, cols, static_cast<const bf16_t *>(in),
+                       static_cast<bf16_t *>(out));
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, rows, cols, static_cast<const float *>(in),
+                       static_cast<float *>(out));
+  return hipGetLastError();
+}
+
+}  // namespace dg

@@ -1,0 +1,298 @@
+/*
+ * dgstep.h -- C ABI of libdgstep: one denoising step of a DiffusionGemma-style
+ * discrete text diffusion model over a canvas of tokens, on one MI355X (gfx950).
+ *
+ * Sources (five web pages on DiffusionGemma, cited by page and section):
+ *   aitrends.kr notebook summary  -- QK-norm paragraph + rms code, RoPE
+ *       paragraph + rotate code, attention paragraph + projection code,
+ *       sampler paragraph, glossary (Scalar QK Norm, Partial RoPE, Layer
+ *       Scalar, Self-conditioning, MoE, Sliding-window Attention);
+ *   thakicloud "DiffusionGemma 26B-A4B" post -- Architecture;
+ *   velog "DiffusionGemma Self-conditioning" post -- Self-conditioning,
+ *       DiffusionGemma structure;
+ *   DiffusionGemma Technical Report review -- section 1 (Canvas, Adaptive
+ *       Stopping);
+ *   aibars.net news -- block-autoregressive denoising and self-correction.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers inside weight, cache and state records, and every tensor
+ *     argument, are DEVICE pointers owned by the caller.  Config records and
+ *     the arrays of per-layer records are HOST memory.  The library never
+ *     allocates or frees device memory and keeps no mutable global state;
+ *     scratch memory is the caller's workspace `ws` of `ws_bytes` bytes,
+ *     256-byte aligned, sized by the matching *_workspace_bytes query.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  All device work is
+ *     enqueued asynchronously on it; nothing synchronises with the host.
+ *   - Arguments are validated on the host before any HIP call; a failed
+ *     check returns a negative dg_status and enqueues nothing.  A launch
+ *     failure returns DG_ERR_HIP.  Faults inside kernels surface at the
+ *     caller's next synchronisation of the stream.
+ *   - Layout is row-major.  Weight matrices are [out, in] (y = x W^T, as in
+ *     the projection code on the aitrends page).  A head-major activation
+ *     row [n_heads * head_dim] holds head n at columns [n*d, (n+1)*d).
+ *   - dtype selects the element type of activations, weights and KV cache:
+ *     DG_BF16 (bfloat16, fp32 accumulation) or DG_F32.  Router logits, LM
+ *     logits, entropies and partial sums are always fp32.
+ *   - Canvas positions are contiguous: token j of a call sits at absolute
+ *     position kv_len + j (rotate(x, layer_type, start_idx) on the aitrends
+ *     page).
+ */
+#ifndef DGSTEP_H
+#define DGSTEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_NULL = -1,        /* a required pointer is NULL */
+  DG_ERR_SHAPE = -2,       /* a size is non-positive, inconsistent or misaligned */
+  DG_ERR_UNSUPPORTED = -3, /* valid but not built (e.g. a head_dim without a kernel) */
+  DG_ERR_WORKSPACE = -4,   /* ws_bytes smaller than the workspace query returns */
+  DG_ERR_DTYPE = -5,       /* unknown dtype, or dtypes that must agree do not */
+  DG_ERR_HIP = -6,         /* a HIP launch failed */
+  DG_ERR_CAPACITY = -7     /* the KV cache cannot hold the rows to append */
+} dg_status;
+
+typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+
+/* ---------------------------------------------------------------- attention */
+
+/* One attention layer (aitrends page: attention paragraph and projection code;
+ * glossary "Sliding-window Attention").  layer_type 0 = sliding window: the
+ * canvas sees itself plus the last `window` committed rows; 1 = global: the
+ * canvas sees every committed row.  Global layers share the K/V projection
+ * (shared_kv = 1, W_v = W_k) and normalise V to unit RMS (v_unit_rms = 1);
+ * their RoPE keeps only the first rotary_factor of the frequencies. */
+typedef struct {
+  int hidden;          /* D, multiple of 64 */
+  int n_q_heads;       /* Hq, multiple of n_kv_heads */
+  int n_kv_heads;      /* Hkv */
+  int head_dim;        /* d_h: 64, 128, 256 or 512 */
+  int layer_type;      /* 0 sliding window, 1 global */
+  int window;          /* W, committed rows visible in front of the canvas (sliding) */
+  int shared_kv;       /* 1: the value projection is the key projection */
+  int v_unit_rms;      /* 1: v <- rms(v, 1) per head */
+  float rope_base;     /* f_t = rope_base^(-2t/d_h) */
+  float rotary_factor; /* fraction of the d_h/2 frequencies kept (global layers) */
+  float rms_eps;       /* added to the L2 norm */
+  int dtype;           /* dg_dtype */
+} dg_attn_cfg;
+
+typedef struct {
+  const void *w_in_norm; /* [D]              pre-attention RMSNorm weight */
+  const void *w_q;       /* [Hq*d_h, D] */
+  const void *w_k;       /* [Hkv*d_h, D] */
+  const void *w_v;       /* [Hkv*d_h, D], ignored (may be NULL) when shared_kv */
+  const void *w_o;       /* [D, Hq*d_h] */
+  const void *q_norm;    /* [d_h] QK-norm weights (constant vectors in the trained model) */
+  const void *k_norm;    /* [d_h] */
+} dg_attn_w;
+
+/* Committed keys/values of one layer, stored after QK-norm and RoPE at their
+ * own positions: k, v are [Hkv][capacity][d_h] in the layer dtype.  Rows
+ * [0, kv_len) are valid. */
+typedef struct {
+  void *k;
+  void *v;
+  int capacity;
+  int kv_len;
+} dg_kv_layer;
+
+/* Workspace bytes for dg_attn_layer with at most n_tok tokens per call. */
+size_t dg_attn_workspace_bytes(const dg_attn_cfg *cfg, int n_tok);
+
+/* x <- x + Attention(rms(x)) for n_tok tokens at positions kv_len.. .
+ * causal = 0 (decode): the canvas attends bidirectionally to the visible
+ *   committed rows and to itself; the cache is read only.
+ * causal = 1 (encode/commit): key m is visible to the query at position p iff
+ *   m <= p (and m > p - window in sliding layers); this call's post-norm/RoPE
+ *   K/V rows are written to the cache at [kv_len, kv_len + n_tok) and
+ *   kv->kv_len is advanced on the host when the work is enqueued.
+ * x_inout: [n_tok, D] device, layer dtype.  Softmax scale is 1 (scalar
+ * QK-norm fixes the temperature; aitrends QK-norm paragraph). */
+int dg_attn_layer(const dg_attn_cfg *cfg, const dg_attn_w *w, dg_kv_layer *kv, int n_tok,
+                  int causal, void *x_inout, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------- MoE */
+
+/* MoE block (aitrends glossary "MoE"; thakicloud Architecture: 128 experts,
+ * 8 active + 1 shared).  Experts are bias-free SwiGLU FFNs.  The router takes
+ * softmax over the experts, keeps the top_k (ties to the lower id),
+ * renormalises over them and multiplies by route_scale; the shared expert is
+ * always added.  The layer scalar rescales the layer output (glossary
+ * "Layer Scalar"): x <- layer_scalar * (x + y). */
+typedef struct {
+  int hidden;          /* D, multiple of 64 */
+  int n_experts;       /* E <= 256 */
+  int top_k;           /* <= 8, <= E */
+  int ffn;             /* F, multiple of 64 */
+  int shared_ffn;      /* F_s, multiple of 64 */
+  float route_scale;
+  float rms_eps;
+  float layer_scalar;
+  int dtype;
+} dg_moe_cfg;
+
+typedef struct {
+  const void *w_in_norm; /* [D] pre-MoE RMSNorm weight */
+  const void *w_router;  /* [E, D]; may be NULL when router logits are injected */
+  const void *w_gate;    /* [E, F, D] */
+  const void *w_up;      /* [E, F, D] */
+  const void *w_down;    /* [E, D, F] */
+  const void *ws_gate;   /* [F_s, D] shared expert */
+  const void *ws_up;     /* [F_s, D] */
+  const void *ws_down;   /* [D, F_s] */
+} dg_moe_w;
+
+size_t dg_moe_workspace_bytes(const dg_moe_cfg *cfg, int n_tok);
+
+/* x <- layer_scalar * (x + MoE(rms(x))) for n_tok tokens.
+ * router_logits_in: optional [n_tok, E] fp32 device logits used instead of
+ *   rms(x) W_router^T (lets callers feed both sides identical logits).
+ * topk_idx_out [n_tok, top_k] int32 and topk_w_out [n_tok, top_k] fp32 are
+ *   optional device outputs, in descending-score order. */
+int dg_moe_block(const dg_moe_cfg *cfg, const dg_moe_w *w, int n_tok, void *x_inout,
+                 const float *router_logits_in, int32_t *topk_idx_out, float *topk_w_out,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ sampler */
+
+/* Entropy-bound sampler (aitrends sampler paragraph; aibars self-correction):
+ * temperature t_i falls linearly from t_max (step 0) to t_min (step
+ * n_steps-1); for every position the entropy H of softmax(l/t_i) (nats) is
+ * computed; positions with H < tau commit their argmax token (lowest id on
+ * ties), the others are re-noised with a uniform random token.  Tokens come
+ * from Philox4x32-10 (Salmon et al., SC'11) with key = (seed lo, seed hi) and
+ * counter = (position, step, canvas_idx, 0): token = (X0 * vocab) >> 32.
+ * final_step != 0 commits every position. */
+typedef struct {
+  int vocab;
+  float tau;           /* entropy bound, nats */
+  float t_max, t_min;  /* temperature schedule */
+  int n_steps;         /* schedule length (max denoising steps) */
+  int step;            /* this step, 0-based */
+  uint32_t canvas_idx;
+  uint64_t seed;
+  int final_step;
+} dg_sampler_cfg;
+
+size_t dg_sample_workspace_bytes(int n_pos, int vocab);
+
+/* logits: [n_pos, vocab] device, fp32 (logits_dtype DG_F32) or bf16.
+ * Outputs (device): tokens_out [n_pos] int32, commit_out [n_pos] uint8 (1 =
+ * committed), entropy_out [n_pos] fp32, n_renoised_out [1] int32.
+ * rowstats_out: optional [n_pos, 2] fp32 = (max of l/t, sum of exp(l/t - max)),
+ * the statistics dg_soft_embed needs. */
+int dg_sample_renoise(const dg_sampler_cfg *cfg, int n_pos, const void *logits, int logits_dtype,
+                      int32_t *tokens_out, uint8_t *commit_out, float *entropy_out,
+                      float *rowstats_out, int32_t *n_renoised_out, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/* Initial canvas: n_pos uniform random tokens (counter step word 0xFFFFFFFF;
+ * aibars text-diffusion paragraph: generation starts from a noise block). */
+int dg_canvas_noise(int n_pos, int vocab, uint64_t seed, uint32_t canvas_idx, int32_t *tokens_out,
+                    void *stream);
+
+/* ------------------------------------------------- tied head, self-condition */
+
+/* logits = rms(x, w_final_norm) E^T with the head tied to the embedding table.
+ * x [n_pos, D] and embed [vocab, D] in `dtype`; logits_out [n_pos, vocab] fp32. */
+size_t dg_lm_head_workspace_bytes(int n_pos, int hidden, int dtype);
+int dg_lm_head(int n_pos, int hidden, int vocab, float rms_eps, int dtype, const void *x,
+               const void *w_final_norm, const void *embed, float *logits_out, void *ws,
+               size_t ws_bytes, void *stream);
+
+/* Self-conditioning soft embedding (aitrends glossary "Self-conditioning";
+ * velog Self-conditioning): u = P E with P = softmax(l / t_i) from fp32 logits
+ * and the (max, sum) row statistics dg_sample_renoise wrote; t_i comes from
+ * the sampler record.  embed_t is the [D, vocab] transposed copy of the
+ * embedding table made once by dg_embed_transpose.  u_out [n_pos, D] dtype. */
+size_t dg_soft_embed_workspace_bytes(int n_pos, int hidden, int vocab, int dtype);
+int dg_soft_embed(const dg_sampler_cfg *scfg, int n_pos, int hidden, int dtype, const float *logits,
+                  const float *rowstats, const void *embed_t, void *u_out, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/* embed_t[d][v] = embed[v][d]: the layout copy dg_soft_embed streams. */
+int dg_embed_transpose(int vocab, int hidden, int dtype, const void *embed, void *embed_t,
+                       void *stream);
+
+/* -------------------------------------------------------------- whole model */
+
+typedef struct {
+  dg_attn_cfg sliding;  /* config of the sliding-window layers */
+  dg_attn_cfg global;   /* config of the global layers */
+  dg_moe_cfg moe;       /* shared by every layer (layer_scalar taken per layer) */
+  int n_layers;
+  int global_every;     /* layer l is global iff l % global_every == global_every - 1 */
+  int vocab;
+  int sc_ffn;           /* self-conditioning MLP width, 0 = no self-conditioning */
+  float rms_eps;        /* final norm */
+  int dtype;
+} dg_model_cfg;
+
+typedef struct {
+  const void *embed;         /* [vocab, D] embedding table, also the tied LM head */
+  const void *embed_t;       /* [D, vocab] transposed copy (dg_embed_transpose) */
+  const void *w_final_norm;  /* [D] */
+  const void *sc_gate;       /* [sc_ffn, D] self-conditioning MLP (SwiGLU, no bias) */
+  const void *sc_up;         /* [sc_ffn, D] */
+  const void *sc_down;       /* [D, sc_ffn] */
+  const dg_attn_w *attn;     /* host array [n_layers] */
+  const dg_moe_w *moe;       /* host array [n_layers] */
+  const float *layer_scalar; /* host array [n_layers] */
+} dg_model_w;
+
+typedef struct {
+  dg_kv_layer *layer;  /* host array [n_layers] */
+  int n_layers;
+} dg_kv_cache;
+
+/* Per-canvas state carried between steps (all device buffers). */
+typedef struct {
+  int32_t *tokens;     /* [canvas_len] in: current canvas, out: next canvas */
+  void *u;             /* [canvas_len, D] dtype: in: P.E of the previous step, out: this step's */
+  int use_u;           /* 0 on the first step: u is not read (self-conditioning input 0) */
+  uint8_t *commit;     /* [canvas_len] out */
+  float *entropy;      /* [canvas_len] out */
+  int32_t *n_renoised; /* [1] out: positions re-noised this step (adaptive stop when 0) */
+  float *logits;       /* [canvas_len, vocab] fp32 out (optional: NULL keeps them in ws) */
+  int canvas_len;
+} dg_canvas_state;
+
+/* Workspace bytes for dg_canvas_step with canvases of up to max_canvas_tokens
+ * positions (logits kept in the workspace) and dg_commit_canvas with up to
+ * max_commit_tokens tokens per call (e.g. a prompt). */
+size_t dg_workspace_bytes(const dg_model_cfg *cfg, int max_canvas_tokens, int max_commit_tokens);
+
+/* One denoising step: x = E[tokens] + MLP_sc(u); every layer in decode mode
+ * (attention then MoE); final norm + tied head; sampler; u <- P.E for the next
+ * step.  The KV cache is read only.  No device-to-host transfer. */
+int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cache *kv,
+                   dg_canvas_state *state, const dg_sampler_cfg *scfg, void *ws, size_t ws_bytes,
+                   void *stream);
+
+/* Commit (encode): run the n_tok final tokens causally through the stack and
+ * append every layer's K/V at [kv_len, kv_len + n_tok); the last layer stops
+ * after its K/V (aitrends attention paragraph: work after the last layer is
+ * skipped).  Every layer's kv_len is advanced by n_tok on the host. */
+int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *kv,
+                     const int32_t *tokens, int n_tok, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ misc */
+
+/* RMSNorm rows (aitrends rms code): y = w * x * sqrt(D) / (||x|| + eps).
+ * x, y [n, D] dtype, w [D] dtype.  y may alias x. */
+int dg_rmsnorm(int n, int hidden, float eps, int dtype, const void *x, const void *w, void *y,
+               void *stream);
+
+const char *dg_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DGSTEP_H */

@@ -1,0 +1,120 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+entry point, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from discrete_text_diffusion_step_amd import binding as B
+from discrete_text_diffusion_step_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dgstep.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    L = B.lib()
+    names = declared_functions()
+    assert len(names) >= 17
+    for n in ("dg_canvas_step", "dg_attn_layer", "dg_moe_block", "dg_sample_renoise", "dg_commit_canvas"):
+        assert n in names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in range(-7, 1):
+        assert B.dg_status_string(s) != "unknown status"
+    assert B.dg_status_string(-99) == "unknown status"
+
+
+def _attn_c(**over):
+    cfg = synth.sliding_cfg()
+    cfg.update(over)
+    return B.attn_cfg_c(cfg)
+
+
+def test_attn_validation_codes():
+    L = B.lib()
+    w = B.AttnW(*(ctypes.c_void_p(256) for _ in range(7)))
+    kv = B.KVLayer(ctypes.c_void_p(256), ctypes.c_void_p(256), 4096, 2048)
+    x = ctypes.c_void_p(256)
+    ws = ctypes.c_void_p(256)
+    call = lambda c, n=256, causal=0, kvv=kv, wsb=1 << 40, xx=x, ww=w: L.dg_attn_layer(
+        ctypes.byref(c), ctypes.byref(ww), ctypes.byref(kvv), n, causal, xx, ws, wsb, None)
+    assert call(_attn_c(), xx=None) == -1
+    assert call(_attn_c(), ww=B.AttnW()) == -1
+    assert call(_attn_c(head_dim=96)) == -3
+    assert call(_attn_c(hidden=100)) == -2
+    assert call(_attn_c(n_q_heads=12, n_kv_heads=8)) == -2
+    assert call(_attn_c(), n=-1) == -2
+    assert call(_attn_c(), causal=2) == -2
+    assert call(_attn_c(), wsb=1024) == -4
+    full = B.KVLayer(ctypes.c_void_p(256), ctypes.c_void_p(256), 2100, 2048)
+    assert call(_attn_c(), causal=1, kvv=full) == -7
+    c = _attn_c()
+    c.dtype = 7
+    assert call(c) == -5
+    # zero tokens is a no-op
+    assert call(_attn_c(), n=0) == 0
+
+
+def test_moe_validation_codes():
+    L = B.lib()
+    m = synth.moe_cfg(2816, 128, 8, 704, 704)
+    w = B.MoeW(*(ctypes.c_void_p(256) for _ in range(8)))
+    call = lambda c, n=256, ww=w, rl=None, wsb=1 << 40: L.dg_moe_block(
+        ctypes.byref(c), ctypes.byref(ww), n, ctypes.c_void_p(256), rl, None, None, ctypes.c_void_p(256), wsb, None)
+    assert call(B.moe_cfg_c(dict(m, top_k=9))) == -2
+    assert call(B.moe_cfg_c(dict(m, n_experts=300))) == -2
+    assert call(B.moe_cfg_c(dict(m, ffn=700))) == -2
+    wr = B.MoeW(*(ctypes.c_void_p(256) for _ in range(8)))
+    wr.w_router = None
+    assert call(B.moe_cfg_c(m), ww=wr) == -1
+    assert call(B.moe_cfg_c(m), wsb=16) == -4
+    assert call(B.moe_cfg_c(m), n=0) == 0
+
+
+def test_sampler_validation_codes():
+    L = B.lib()
+    p = ctypes.c_void_p(256)
+    call = lambda s, n=256, ldt=0, wsb=1 << 30: L.dg_sample_renoise(
+        ctypes.byref(s), n, p, ldt, p, p, p, None, p, p, wsb, None)
+    assert call(B.sampler_cfg_c(synth.sampler_cfg(262144, t_max=0.0))) == -2
+    assert call(B.sampler_cfg_c(synth.sampler_cfg(262143))) == -2
+    assert call(B.sampler_cfg_c(synth.sampler_cfg(262144)), ldt=3) == -5
+    assert call(B.sampler_cfg_c(synth.sampler_cfg(262144)), wsb=8) == -4
+    assert L.dg_sample_renoise(None, 1, p, 0, p, p, p, None, p, p, 1 << 30, None) == -1
+
+
+def test_workspace_queries_grow_with_tokens():
+    L = B.lib()
+    c = _attn_c()
+    a = L.dg_attn_workspace_bytes(ctypes.byref(c), 64)
+    b = L.dg_attn_workspace_bytes(ctypes.byref(c), 256)
+    assert 0 < a < b
+    m = B.model_cfg_c(synth.full_model_cfg())
+    s1 = L.dg_workspace_bytes(ctypes.byref(m), 256, 0)
+    s2 = L.dg_workspace_bytes(ctypes.byref(m), 256, 4096)
+    assert 0 < s1 <= s2
+    # canvas workspace holds the fp32 logits of the 262,144-wide head
+    assert s1 > 256 * 262144 * 4
+    bad = B.model_cfg_c(dict(synth.full_model_cfg(), n_layers=0))
+    assert L.dg_workspace_bytes(ctypes.byref(bad), 256, 0) == 0
+
+
+def test_model_entry_points_validate():
+    L = B.lib()
+    m = B.model_cfg_c(synth.full_model_cfg())
+    s = B.sampler_cfg_c(synth.sampler_cfg(262144))
+    assert L.dg_canvas_step(ctypes.byref(m), None, None, None, ctypes.byref(s), None, 0, None) == -1
+    assert L.dg_commit_canvas(ctypes.byref(m), None, None, None, 256, None, 0, None) == -1
+    mm = B.model_cfg_c(dict(synth.full_model_cfg(), dtype="f32"))   # layer dtypes disagree
+    assert L.dg_canvas_step(ctypes.byref(mm), None, None, None, ctypes.byref(s), None, 0, None) == -5
