@@ -1,0 +1,228 @@
+#!/usr/bin/env python
+"""Canvas denoising-step throughput on one MI355X.
+
+Workload: the 30-layer DiffusionGemma-style stack (25 sliding-window + 5
+global layers, one global every 6th; hidden 2816; 16 q heads with 8 kv heads
+(d_h 256) or 2 kv heads (d_h 512, shared K/V); 128 experts top-8 + 1 shared,
+SwiGLU 704; tied 262,144-wide head; self-conditioning MLP 704) with seeded
+random bf16 weights (~25B parameters, generated on the device).  A 4,096-token
+prompt is committed first; a step is one dg_canvas_step over a 256-token
+canvas (embedding + self-conditioning, 30 x (attention + MoE), head, sampler,
+P.E) with every input resident in HBM.  Adaptive stop is off in the timed
+loop (random weights make every position commit at the first step), so the
+timed steps are the fixed 48-step schedule of one canvas.
+
+Prints one JSON line: steps/s, effective tokens/s at stated tokens-per-forward,
+the dominant kernel's roofline (timed with HIP events recorded by the library
+on its own stream) and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+CANVAS = 256
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gateup_bytes(mcfg, n_tok):
+    """Algorithmic HBM bytes of one expert gate/up launch: every expert's gate
+    and up matrices once (128 routed + 1 shared), the gathered token rows and
+    the SwiGLU output rows."""
+    m = mcfg["moe"]
+    D, F, Fs, E, k = m["hidden"], m["ffn"], m["shared_ffn"], m["n_experts"], m["top_k"]
+    weights = (E * 2 * F * D + 2 * Fs * D) * 2
+    rows = n_tok * (k + 1)
+    return weights + rows * D * 2 + rows * F * 2
+
+
+def cpu_baseline(mcfg, P, budget_note):
+    """Oracle (float64 numpy) on a bounded sample of one step: one sliding and
+    one global layer (attention decode + MoE) and the head / sampler / P.E,
+    scaled to a full 30-layer step."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from discrete_text_diffusion_step_amd import synth
+    from oracle import dg_oracle as O
+
+    def f32np(t):
+        return t.float().numpy() if t is not None else None
+
+    g = synth.generator(7)
+    D, V = mcfg["hidden"], mcfg["vocab"]
+    times = {}
+    x = synth.hidden_states(CANVAS, D, g, "bf16").double().numpy()
+    for name, acfg in (("sliding", mcfg["sliding"]), ("global", mcfg["global"])):
+        aw = {k: f32np(v) for k, v in synth.attn_weights(acfg, g).items()}
+        mw = {k: f32np(v) for k, v in synth.moe_weights(mcfg["moe"], g).items()}
+        Hkv, dh = acfg["n_kv_heads"], acfg["head_dim"]
+        ck = np.random.default_rng(0).standard_normal((Hkv, P, dh)).astype(np.float32)
+        cv = np.random.default_rng(1).standard_normal((Hkv, P, dh)).astype(np.float32)
+        t0 = time.perf_counter()
+        xo, _, _ = O.attn_layer(acfg, aw, ck, cv, P, x, 0, "bf16")
+        O.moe_block_grouped(mcfg["moe"], mw, xo, "bf16")
+        times[name] = time.perf_counter() - t0
+        del aw, mw, ck, cv
+    E = synth.embed_table(V, D, g, "bf16").float().numpy()
+    wn = np.ones(D)
+    s = synth.sampler_cfg(V)
+    t0 = time.perf_counter()
+    lg = O.lm_head(x, wn, E, 1e-6, "bf16")
+    out = O.sample_renoise(lg, s)
+    p = O.probs(lg, out["row_max"], out["row_z"], out["temperature"])
+    O.soft_embed(p, E, "bf16")
+    times["head"] = time.perf_counter() - t0
+    n_sl = sum(1 for l in range(mcfg["n_layers"]) if l % mcfg["global_every"] != mcfg["global_every"] - 1)
+    n_gl = mcfg["n_layers"] - n_sl
+    t_step = n_sl * times["sliding"] + n_gl * times["global"] + times["head"]
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    cores = min(threads, len(os.sched_getaffinity(0)))
+    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 numpy oracle on one sliding and one global layer (decode over {P} committed "
+                       f"rows + MoE) and the head/sampler/P.E at the 256-token canvas, "
+                       f"{times['sliding']:.1f}+{times['global']:.1f}+{times['head']:.1f} s, "
+                       f"scaled to {n_sl} sliding + {n_gl} global layers ({budget_note})"),
+            "seconds_measured": round(sum(times.values()), 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--prompt", type=int, default=4096)
+    ap.add_argument("--canvases", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-generate", action="store_true", help="skip the adaptive-stop generation run")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "multi-GPU runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from discrete_text_diffusion_step_amd import binding as B
+    from discrete_text_diffusion_step_amd import synth
+    from discrete_text_diffusion_step_amd.generate import generate
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    mcfg = synth.full_model_cfg()
+    V, D = mcfg["vocab"], mcfg["hidden"]
+    t0 = time.time()
+    w = synth.model_weights(mcfg, seed=1, device=dev)
+    torch.cuda.synchronize()
+    n_params = sum(t.numel() for t in [w["embed"], w["w_final_norm"]] + list(w["sc"].values())) + sum(
+        t.numel() for layer in w["attn"] + w["moe"] for t in layer.values() if t is not None)
+    log(f"weights: {n_params / 1e9:.2f}B params generated in {time.time() - t0:.1f}s")
+    model = B.Model(mcfg, w)
+    cap = args.prompt + args.canvases * CANVAS
+    kv = B.KV(mcfg, cap, device=dev)
+    ws = torch.empty(B.dg_workspace_bytes(model.c_cfg, CANVAS, max(args.prompt, CANVAS)), dtype=torch.uint8,
+                     device=dev)
+    prompt = synth.tokens(args.prompt, V, synth.generator(2, dev), device=dev)
+
+    # prompt prefill (causal encode of 4096 tokens)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    B.dg_commit_canvas(model, kv, prompt, ws=ws)
+    torch.cuda.synchronize()
+    prefill_ms = (time.perf_counter() - t0) * 1e3
+    P = kv.kv_len
+    log(f"prefill {args.prompt} tokens: {prefill_ms:.1f} ms, kv_len {P}")
+
+    canvas = B.Canvas(CANVAS, D, "bf16", device=dev)
+    canvas.tokens.copy_(B.dg_canvas_noise(CANVAS, V, 1, 0, device=dev))
+
+    def step(i):
+        s = synth.sampler_cfg(V, n_steps=48, step=i % 48, canvas_idx=0, final_step=(i % 48 == 47))
+        B.dg_canvas_step(model, kv, canvas, s, ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    K = args.steps
+    timer = B.kernel_timer("moe_gateup", capacity=K * mcfg["n_layers"] + 8)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with timer:
+        for i in range(K):
+            step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / K
+    durs = timer.durations_ms()
+    log(f"timed {K} steps: {ms_step:.3f} ms/step; gate/up launches timed: {len(durs)}")
+
+    # commit cost of one canvas (the encode pass appends 256 rows)
+    commit_ms = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        B.dg_commit_canvas(model, kv, canvas.tokens, ws=ws)
+        torch.cuda.synchronize()
+        commit_ms.append((time.perf_counter() - t1) * 1e3)
+        kv.set_len(P)   # rewind: the rows appended are scratch here
+    commit = sorted(commit_ms)[1]
+
+    gen = None
+    if not args.no_generate:
+        kv.set_len(P)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        toks, used = generate(model, kv, torch.empty(0, dtype=torch.int32, device=dev), args.canvases,
+                              canvas_len=CANVAS, max_steps=48, seed=1, adaptive=True)
+        torch.cuda.synchronize()
+        gt = time.perf_counter() - t1
+        gen = {"canvases": args.canvases, "steps_per_canvas": used,
+               "tok_s": round(args.canvases * CANVAS / gt, 1), "seconds": round(gt, 3)}
+        log(f"adaptive generation: {gen}")
+
+    avg_ms = sum(durs) / len(durs)
+    bytes_launch = gateup_bytes(mcfg, CANVAS)
+    achieved = bytes_launch / (avg_ms * 1e-3) / 1e9
+    roof = {"kernel": "moe expert gate/up (grouped MFMA GEMM + SwiGLU)", "bound": "hbm",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": bytes_launch, "launches": len(durs)}
+
+    tpf_full = CANVAS / 48.0
+    eff = {"tpf_5.33_incl_commit": round(CANVAS / (48 * ms_step + commit) * 1e3, 1),
+           "tpf_20": round(20.0 / ms_step * 1e3, 1)}
+    result = {
+        "metric": "canvas denoise steps/s (256-tok canvas) + eff. tok/s; % of MFMA/HBM roofline",
+        "value": round(K / elapsed, 3), "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded random-init weights and tokens)",
+        "config": {"workload": "30-layer DiffusionGemma-style canvas denoise step: 25 sliding (W 1024) + 5 global "
+                               "layers, hidden 2816, 128 experts top-8 + shared (SwiGLU 704), vocab 262144, "
+                               "256-token canvas after a 4096-token prompt",
+                   "canvas": CANVAS, "committed_rows": P, "params": n_params, "adaptive_stop_in_timed_loop": False},
+        "eff_tok_s": eff, "tokens_per_forward": {"full_schedule": round(tpf_full, 3), "pages": 20},
+        "commit_ms": round(commit, 3), "prefill_ms": round(prefill_ms, 1),
+        "roofline": roof,
+        "generation": gen,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle sample)...")
+        result["cpu_baseline"] = cpu_baseline(mcfg, P, "about 10-30 s of CPU work")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -79,6 +79,13 @@ class CanvasState(ctypes.Structure):
                 ("entropy", c_void), ("n_renoised", c_void), ("logits", c_void), ("canvas_len", c_int)]
 
 
+class KernelTimer(ctypes.Structure):
+    _fields_ = [("start", ctypes.POINTER(c_void)), ("stop", ctypes.POINTER(c_void)), ("capacity", c_int),
+                ("count", c_int), ("kernel", c_int)]
+
+
+DG_KT = {"moe_gateup": 1, "moe_down": 2, "lm_head": 3, "attn": 4, "soft_embed": 5}
+
 _LIB = None
 
 
@@ -115,6 +122,7 @@ def lib():
             "dg_commit_canvas": (c_int, [P(ModelCfg), P(ModelW), P(KVCache), c_void, c_int, c_void, c_size,
                                          c_void]),
             "dg_rmsnorm": (c_int, [c_int, c_int, c_float, c_int, c_void, c_void, c_void, c_void]),
+            "dg_set_kernel_timer": (None, [P(KernelTimer)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -378,3 +386,33 @@ def dg_commit_canvas(model, kv, tokens, ws=None, stream=None):
         ws = workspace(L.dg_workspace_bytes(ctypes.byref(model.c_cfg), 0, n), tokens.device)
     check(L.dg_commit_canvas(ctypes.byref(model.c_cfg), ctypes.byref(model.c_w), ctypes.byref(kv.c), ptr(tokens), n,
                              ptr(ws), ws.numel(), stream_handle(stream)), "dg_commit_canvas")
+
+
+class kernel_timer:
+    """Context manager timing every launch of one kernel class with HIP events
+    recorded by the library on the launching stream."""
+
+    def __init__(self, kind, capacity=4096):
+        self.kind = DG_KT[kind]
+        self.cap = capacity
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(capacity)]
+        for a, b in self.ev:   # materialise the underlying hipEvent_t handles
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        self._start = (c_void * capacity)(*[a.cuda_event for a, _ in self.ev])
+        self._stop = (c_void * capacity)(*[b.cuda_event for _, b in self.ev])
+        self.t = KernelTimer(self._start, self._stop, capacity, 0, self.kind)
+
+    def __enter__(self):
+        lib().dg_set_kernel_timer(ctypes.byref(self.t))
+        return self
+
+    def __exit__(self, *exc):
+        lib().dg_set_kernel_timer(None)
+        return False
+
+    def durations_ms(self):
+        torch.cuda.synchronize()
+        return [self.ev[i][0].elapsed_time(self.ev[i][1]) for i in range(self.t.count)]

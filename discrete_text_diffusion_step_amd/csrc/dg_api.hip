@@ -41,6 +41,25 @@ struct Carve {
   void *bytes(size_t n) { return take<char>(n); }
 };
 
+thread_local dg_kernel_timer *g_timer = nullptr;
+
+// Records the attached timer's events around one launch of kernel class `kt`.
+struct TimedLaunch {
+  dg_kernel_timer *t;
+  hipStream_t s;
+  int slot;
+  TimedLaunch(int kt, hipStream_t st) : t(nullptr), s(st), slot(-1) {
+    if (g_timer && g_timer->kernel == kt && g_timer->count < g_timer->capacity) {
+      t = g_timer;
+      slot = t->count++;
+      hipEventRecord(static_cast<hipEvent_t>(t->start[slot]), s);
+    }
+  }
+  ~TimedLaunch() {
+    if (t) hipEventRecord(static_cast<hipEvent_t>(t->stop[slot]), s);
+  }
+};
+
 hipError_t gemm(int dtype, const GemmArgs &a, int mode, int bm, int bn, hipStream_t s) {
   return dtype == DG_BF16 ? launch_gemm<bf16_t>(a, mode, bm, bn, s) : launch_gemm<float>(a, mode, bm, bn, s);
 }
@@ -225,7 +244,10 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   at.ml_part = ws.ml_part;
   at.out = ws.o;
   at.out_ld = p.Nq;
-  DG_HIP(launch_attention(at, dt, dh, s));
+  {
+    TimedLaunch tl(DG_KT_ATTN, s);
+    DG_HIP(launch_attention(at, dt, dh, s));
+  }
 
   // x += o W_o^T
   if (p.oproj_ks > 1) {
@@ -348,7 +370,10 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   gu.k_splits = 1;
   gu.C = ws.H;
   gu.ldc = fmax;
-  DG_HIP(gemm(dt, gu, EPI_SWIGLU, bm, 64, s));
+  {
+    TimedLaunch tl(DG_KT_MOE_GATEUP, s);
+    DG_HIP(gemm(dt, gu, EPI_SWIGLU, bm, 64, s));
+  }
 
   // down projection, scaled by the routing weight of each row
   GemmArgs dn;
@@ -371,7 +396,10 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   dn.C = ws.Y;
   dn.ldc = D;
   dn.rowscale = ws.row_weight;
-  DG_HIP(gemm(dt, dn, EPI_ROWSCALE_F32, bm, 64, s));
+  {
+    TimedLaunch tl(DG_KT_MOE_DOWN, s);
+    DG_HIP(gemm(dt, dn, EPI_ROWSCALE_F32, bm, 64, s));
+  }
 
   DG_HIP(launch_moe_combine(dt, x, ws.Y, ws.pair_row, n, k, D, c->layer_scalar, s));
   return DG_OK;
@@ -484,6 +512,7 @@ int soft_embed_impl(const dg_sampler_cfg *sc, int n, int D, int dt, const float 
     g.seg_B0[0] = embed_t;
     g.k_splits = ks;
     g.tile_order = 1;
+    TimedLaunch tl(DG_KT_SOFT_EMBED, s);
     DG_HIP(gemm(dt, g, EPI_PARTIAL_F32, 64, 128, s));
     DG_HIP(dt == DG_BF16 ? launch_splitk_reduce<bf16_t>(ws.part, ks, n, D, D, u, EPI_STORE, s)
                          : launch_splitk_reduce<float>(ws.part, ks, n, D, D, u, EPI_STORE, s));
@@ -504,6 +533,7 @@ int lm_head_impl(int n, int D, int V, float eps, int dt, const void *x, const vo
   GemmArgs g = dense_args(h, D, n, V, D, logits, V);
   g.seg_B0[0] = E;
   g.tile_order = 0;
+  TimedLaunch tl(DG_KT_LM_HEAD, s);
   DG_HIP(gemm(dt, g, EPI_STORE_F32, 64, 128, s));
   return DG_OK;
 }
@@ -572,6 +602,8 @@ StepWs step_carve(const dg_model_cfg *c, int n, bool need_logits, Carve &cv) {
 // ====================================================================== ABI
 
 extern "C" {
+
+void dg_set_kernel_timer(dg_kernel_timer *timer) { g_timer = timer; }
 
 const char *dg_status_string(int st) {
   switch (st) {

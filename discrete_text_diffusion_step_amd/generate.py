@@ -1,0 +1,48 @@
+"""Block-autoregressive generation over the C ABI (host loop).
+
+aibars.net news, block-autoregressive denoising: a 256-token block is
+denoised fully, committed to the KV cache, then the next block starts.
+DiffusionGemma Technical Report review, section 1 (Adaptive Stopping): the
+denoising loop stops early; here it stops once a step re-noises no position
+(the only device-to-host read per step), or after max_steps, when the final
+step commits every position.
+"""
+import torch
+
+from . import binding as B
+
+
+def generate(model, kv, prompt, n_canvases, canvas_len=256, max_steps=48, seed=1, t_max=1.0, t_min=1.0,
+             tau=None, adaptive=True, stream=None):
+    """Commit `prompt`, then denoise and commit n_canvases canvases.
+
+    Returns (tokens [n_canvases, canvas_len] int32 on the device, steps used per canvas).
+    """
+    import math
+    V = model.cfg["vocab"]
+    tau = 0.5 * math.log(V) if tau is None else tau
+    if prompt is not None and prompt.numel() > 0:
+        B.dg_commit_canvas(model, kv, prompt, stream=stream)
+    out = torch.empty(n_canvases, canvas_len, dtype=torch.int32, device=prompt.device)
+    steps_used = []
+    canvas = B.Canvas(canvas_len, model.cfg["hidden"], model.cfg["dtype"], device=prompt.device)
+    host_count = torch.empty(1, dtype=torch.int32, pin_memory=True)
+    for c in range(n_canvases):
+        canvas.tokens.copy_(B.dg_canvas_noise(canvas_len, V, seed, c, device=prompt.device, stream=stream))
+        canvas.use_u = 0
+        used = 0
+        for i in range(max_steps):
+            final = i == max_steps - 1
+            s = dict(vocab=V, tau=tau, t_max=t_max, t_min=t_min, n_steps=max_steps, step=i,
+                     canvas_idx=c, seed=seed, final_step=final)
+            B.dg_canvas_step(model, kv, canvas, s, stream=stream)
+            used += 1
+            if adaptive and not final:
+                host_count.copy_(canvas.n_renoised, non_blocking=True)
+                torch.cuda.current_stream().synchronize()
+                if int(host_count.item()) == 0:
+                    break
+        out[c].copy_(canvas.tokens)
+        B.dg_commit_canvas(model, kv, canvas.tokens, stream=stream)
+        steps_used.append(used)
+    return out, steps_used

@@ -283,6 +283,32 @@ int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cac
 int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *kv,
                      const int32_t *tokens, int n_tok, void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------ profiling */
+
+/* Optional kernel timer.  The caller creates `capacity` pairs of hipEvent_t
+ * and attaches the record with dg_set_kernel_timer; while attached, the
+ * library records start[i] / stop[i] on the launching stream around each
+ * launch of the selected kernel class and increments `count` (launches past
+ * `capacity` are not timed).  The attachment is per host thread; NULL
+ * detaches.  This pointer is the library's only state and is off by default. */
+enum {
+  DG_KT_NONE = 0,
+  DG_KT_MOE_GATEUP = 1,  /* grouped expert gate/up product with the SwiGLU epilogue */
+  DG_KT_MOE_DOWN = 2,    /* grouped expert down product */
+  DG_KT_LM_HEAD = 3,     /* tied-head product */
+  DG_KT_ATTN = 4,        /* attention core */
+  DG_KT_SOFT_EMBED = 5   /* P.E product */
+};
+typedef struct {
+  void **start;   /* hipEvent_t[capacity] */
+  void **stop;    /* hipEvent_t[capacity] */
+  int capacity;
+  int count;
+  int kernel;     /* DG_KT_* */
+} dg_kernel_timer;
+
+void dg_set_kernel_timer(dg_kernel_timer *timer);
+
 /* ------------------------------------------------------------------ misc */
 
 /* RMSNorm rows (aitrends rms code): y = w * x * sqrt(D) / (||x|| + eps).

@@ -76,7 +76,8 @@ def test_sample_renoise(n, V, dtype, temp):
     np.testing.assert_array_equal(commit, ref["commit"])
     np.testing.assert_array_equal(out["tokens"].cpu().numpy(), ref["tokens"])
     assert int(out["n_renoised"].item()) == ref["n_renoised"]
-    assert rel_err(out["entropy"].cpu().numpy(), ref["entropy"]) < 1e-4
+    # entropy lives on the scale [0, ln V]: its error is measured against ln V
+    assert np.max(np.abs(out["entropy"].cpu().numpy() - ref["entropy"])) < 1e-4 * math.log(V)
     rs = out["rowstats"].cpu().numpy()
     np.testing.assert_allclose(rs[:, 0], ref["row_max"], rtol=1e-6, atol=1e-6)
     np.testing.assert_allclose(rs[:, 1], ref["row_z"], rtol=1e-4)
@@ -356,7 +357,7 @@ def test_tiny_commit_then_two_steps():
         sync()
         ref = O.canvas_step(mcfg, wn, rkv, dict(tokens=tokens, u=u), s, "f32")
         assert_close(canvas.logits.cpu().numpy(), ref["logits"], "f32", f"step {step} logits")
-        assert rel_err(canvas.entropy.cpu().numpy(), ref["entropy"]) < 1e-4
+        assert np.max(np.abs(canvas.entropy.cpu().numpy() - ref["entropy"])) < 1e-4 * math.log(V)
         H = ref["entropy"]
         clear = np.abs(H - s["tau"]) > 1e-3
         np.testing.assert_array_equal(canvas.commit.cpu().numpy().astype(bool)[clear], ref["commit"][clear])
