@@ -60,8 +60,16 @@ struct TimedLaunch {
   }
 };
 
-hipError_t gemm(int dtype, const GemmArgs &a, int mode, int bm, int bn, hipStream_t s) {
-  return dtype == DG_BF16 ? launch_gemm<bf16_t>(a, mode, bm, bn, s) : launch_gemm<float>(a, mode, bm, bn, s);
+// Streaming MFMA product (tile 16*mt x 16*nt; the four waves split k).
+hipError_t sgemm(int dtype, const GemmArgs &a, int mode, int mt, int nt, hipStream_t s) {
+  return dtype == DG_BF16 ? launch_gemm_stream<bf16_t>(a, mode, mt, nt, s)
+                          : launch_gemm_stream<float>(a, mode, mt, nt, s);
+}
+
+hipError_t reduce(int dtype, const float *part, int splits, int M, int N, long long ldc, void *C, int mode,
+                  hipStream_t s) {
+  return dtype == DG_BF16 ? launch_splitk_reduce<bf16_t>(part, splits, M, N, ldc, C, mode, s)
+                          : launch_splitk_reduce<float>(part, splits, M, N, ldc, C, mode, s);
 }
 
 GemmArgs dense_args(const void *A, long long lda, int M, int N, int K, void *C, long long ldc) {
@@ -82,12 +90,27 @@ GemmArgs dense_args(const void *A, long long lda, int M, int N, int K, void *C, 
   return g;
 }
 
-// split count for a dense product so that the grid covers the chip
+// Split count for a dense product so that the grid covers the chip: doubles
+// while fewer than `target` workgroups would run and each split keeps at
+// least 8 k steps of 32 (two per wave).
 int choose_ksplit(int M, int N, int K, int bm, int bn, int target, int max_split) {
   const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   int ks = 1;
-  while (tiles * ks < target && ks * 2 <= max_split && K % (64 * ks * 2) == 0) ks *= 2;
+  while (tiles * ks < target && ks * 2 <= max_split && K % (32 * ks * 2) == 0 && K / (ks * 2) >= 256) ks *= 2;
   return ks;
+}
+
+// x (or C) <- dense product with split-K through fp32 partials when it pays.
+hipError_t dense_product(int dt, GemmArgs g, int mode, float *part, int ks, hipStream_t s) {
+  if (ks <= 1) return sgemm(dt, g, mode, 4, 4, s);
+  void *C = g.C;
+  const long long ldc = g.ldc;
+  g.C = part;
+  g.ldc = g.N;
+  g.k_splits = ks;
+  hipError_t e = sgemm(dt, g, EPI_PARTIAL_F32, 4, 4, s);
+  if (e != hipSuccess) return e;
+  return reduce(dt, part, ks, g.M, g.N, ldc, C, mode, s);
 }
 
 // ------------------------------------------------------------ attention
@@ -108,7 +131,7 @@ AttnPlan attn_plan(const dg_attn_cfg *c, int n) {
   const int blocks = c->n_kv_heads * ((p.R + bq - 1) / (bq > 0 ? bq : 1));
   int ns = (512 + blocks - 1) / (blocks > 0 ? blocks : 1);
   p.n_split_max = ns < 1 ? 1 : (ns > 16 ? 16 : ns);
-  p.oproj_ks = choose_ksplit(n, c->hidden, p.Nq, 64, 128, 256, 8);
+  p.oproj_ks = choose_ksplit(n, c->hidden, p.Nq, 64, 64, 512, 8);
   return p;
 }
 
@@ -174,7 +197,7 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   g.seg_B0[1] = w->w_k;
   g.seg_B0[2] = w->w_v;
   g.seg_start[g.nseg] = p.Ntot;
-  DG_HIP(gemm(dt, g, EPI_STORE, 64, 128, s));
+  DG_HIP(sgemm(dt, g, EPI_STORE, 4, 4, s));
 
   NormRopeArgs nr;
   nr.qkv = ws.qkv;
@@ -250,17 +273,10 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   }
 
   // x += o W_o^T
-  if (p.oproj_ks > 1) {
-    GemmArgs o = dense_args(ws.o, p.Nq, n, D, p.Nq, ws.oproj_part, D);
-    o.seg_B0[0] = w->w_o;
-    o.k_splits = p.oproj_ks;
-    DG_HIP(gemm(dt, o, EPI_PARTIAL_F32, 64, 128, s));
-    DG_HIP(dt == DG_BF16 ? launch_splitk_reduce<bf16_t>(ws.oproj_part, p.oproj_ks, n, D, D, x, EPI_ADD, s)
-                         : launch_splitk_reduce<float>(ws.oproj_part, p.oproj_ks, n, D, D, x, EPI_ADD, s));
-  } else {
+  {
     GemmArgs o = dense_args(ws.o, p.Nq, n, D, p.Nq, x, D);
     o.seg_B0[0] = w->w_o;
-    DG_HIP(gemm(dt, o, EPI_ADD, 64, 128, s));
+    DG_HIP(dense_product(dt, o, EPI_ADD, ws.oproj_part, p.oproj_ks, s));
   }
   if (causal) kv->kv_len = P + n;
   return DG_OK;
@@ -292,9 +308,11 @@ struct MoeWs {
   float *rl, *tw;
   int32_t *idx;
   int *g_off, *row_token, *pair_row;
-  float *row_weight, *Y;
+  float *row_weight, *Y, *rpart;
   void *H;
 };
+
+int router_ksplit(const dg_moe_cfg *c, int n) { return choose_ksplit(n, c->n_experts, c->hidden, 64, 64, 256, 16); }
 
 MoeWs moe_carve(const dg_moe_cfg *c, int n, Carve &cv) {
   const size_t es = esize(c->dtype);
@@ -311,6 +329,7 @@ MoeWs moe_carve(const dg_moe_cfg *c, int n, Carve &cv) {
   w.pair_row = cv.take<int>(static_cast<size_t>(n) * c->top_k);
   w.H = cv.bytes(rows * fmax * es);
   w.Y = cv.take<float>(rows * c->hidden);
+  w.rpart = cv.take<float>(static_cast<size_t>(router_ksplit(c, n)) * n * c->n_experts);
   return w;
 }
 
@@ -336,7 +355,7 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   if (!rl) {
     GemmArgs g = dense_args(ws.h, D, n, E, D, ws.rl, E);
     g.seg_B0[0] = w->w_router;
-    DG_HIP(gemm(dt, g, EPI_STORE_F32, 64, 128, s));
+    DG_HIP(dense_product(dt, g, EPI_STORE_F32, ws.rpart, router_ksplit(c, n), s));
     rl = ws.rl;
   }
   int32_t *idx = idx_out ? idx_out : ws.idx;
@@ -345,7 +364,7 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   DG_HIP(launch_moe_permute(idx, tw, n, k, E, ws.g_off, ws.row_token, ws.row_weight, ws.pair_row, s));
 
   const int rows_per_expert = (n * k + E - 1) / E;
-  const int bm = (dt == DG_BF16 && rows_per_expert > 48) ? 128 : 32;
+  const int mtile = rows_per_expert > 48 ? 4 : 2;   // 64- or 32-row tiles
 
   // gate/up of every expert (group 0 = shared) with the SwiGLU epilogue
   GemmArgs gu;
@@ -372,7 +391,7 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   gu.ldc = fmax;
   {
     TimedLaunch tl(DG_KT_MOE_GATEUP, s);
-    DG_HIP(gemm(dt, gu, EPI_SWIGLU, bm, 64, s));
+    DG_HIP(sgemm(dt, gu, EPI_SWIGLU, mtile, 2, s));
   }
 
   // down projection, scaled by the routing weight of each row
@@ -398,7 +417,7 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   dn.rowscale = ws.row_weight;
   {
     TimedLaunch tl(DG_KT_MOE_DOWN, s);
-    DG_HIP(gemm(dt, dn, EPI_ROWSCALE_F32, bm, 64, s));
+    DG_HIP(sgemm(dt, dn, EPI_ROWSCALE_F32, mtile, 4, s));
   }
 
   DG_HIP(launch_moe_combine(dt, x, ws.Y, ws.pair_row, n, k, D, c->layer_scalar, s));
@@ -485,7 +504,7 @@ int sample_impl(const dg_sampler_cfg *c, int n, const void *logits, int ldt, int
 
 // ----------------------------------------------------- head, soft embedding
 
-int softembed_ksplit(int n, int D, int V) { return choose_ksplit(n, D, V, 64, 128, 512, 32); }
+int softembed_ksplit(int n, int D, int V) { return choose_ksplit(n, D, V, 64, 64, 512, 32); }
 
 struct SoftWs {
   void *P;
@@ -507,20 +526,12 @@ int soft_embed_impl(const dg_sampler_cfg *sc, int n, int D, int dt, const float 
   if (n == 0) return DG_OK;
   DG_HIP(launch_probs(dt, logits, rowstats, n, V, static_cast<float>(1.0 / temperature(sc)), ws.P, s));
   const int ks = softembed_ksplit(n, D, V);
-  if (ks > 1) {
-    GemmArgs g = dense_args(ws.P, V, n, D, V, ws.part, D);
-    g.seg_B0[0] = embed_t;
-    g.k_splits = ks;
-    g.tile_order = 1;
-    TimedLaunch tl(DG_KT_SOFT_EMBED, s);
-    DG_HIP(gemm(dt, g, EPI_PARTIAL_F32, 64, 128, s));
-    DG_HIP(dt == DG_BF16 ? launch_splitk_reduce<bf16_t>(ws.part, ks, n, D, D, u, EPI_STORE, s)
-                         : launch_splitk_reduce<float>(ws.part, ks, n, D, D, u, EPI_STORE, s));
-  } else {
+  {
     GemmArgs g = dense_args(ws.P, V, n, D, V, u, D);
     g.seg_B0[0] = embed_t;
     g.tile_order = 1;
-    DG_HIP(gemm(dt, g, EPI_STORE, 64, 128, s));
+    TimedLaunch tl(DG_KT_SOFT_EMBED, s);
+    DG_HIP(dense_product(dt, g, EPI_STORE, ws.part, ks, s));
   }
   return DG_OK;
 }
@@ -534,7 +545,7 @@ int lm_head_impl(int n, int D, int V, float eps, int dt, const void *x, const vo
   g.seg_B0[0] = E;
   g.tile_order = 0;
   TimedLaunch tl(DG_KT_LM_HEAD, s);
-  DG_HIP(gemm(dt, g, EPI_STORE_F32, 64, 128, s));
+  DG_HIP(sgemm(dt, g, EPI_STORE_F32, 4, 4, s));
   return DG_OK;
 }
 
@@ -778,10 +789,10 @@ int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cac
     GemmArgs g = dense_args(st->u, D, n, cfg->sc_ffn, D, sw.g_sc, cfg->sc_ffn);
     g.seg_B0[0] = w->sc_gate;
     g.seg_B1[0] = w->sc_up;
-    DG_HIP(gemm(dt, g, EPI_SWIGLU, 64, 64, s));
+    DG_HIP(sgemm(dt, g, EPI_SWIGLU, 2, 2, s));
     GemmArgs d = dense_args(sw.g_sc, cfg->sc_ffn, n, D, cfg->sc_ffn, sw.x, D);
     d.seg_B0[0] = w->sc_down;
-    DG_HIP(gemm(dt, d, EPI_ADD, 64, 128, s));
+    DG_HIP(sgemm(dt, d, EPI_ADD, 4, 4, s));
   }
   for (int l = 0; l < cfg->n_layers; ++l) {
     Carve c1(sw.rest);
@@ -845,7 +856,7 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
       g.seg_start[2] = p.Nk + p.Nv;
       g.seg_B0[0] = w->attn[l].w_k;
       g.seg_B0[1] = w->attn[l].w_v;
-      DG_HIP(gemm(dt, g, EPI_STORE, 64, 128, s));
+      DG_HIP(sgemm(dt, g, EPI_STORE, 4, 4, s));
       NormRopeArgs nr;
       nr.qkv = aw.qkv;
       nr.ld = p.Ntot;

@@ -187,6 +187,9 @@ struct GemmArgs {
 
 template <typename T>
 hipError_t launch_gemm(const GemmArgs &a, int mode, int bm, int bn, hipStream_t s);
+// streaming variant: tile (16*mt) x (16*nt), waves split k (K per split a multiple of 32)
+template <typename T>
+hipError_t launch_gemm_stream(const GemmArgs &a, int mode, int mt, int nt, hipStream_t s);
 template <typename T>
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, long long ldc,
                                 void *C, int mode, hipStream_t s);

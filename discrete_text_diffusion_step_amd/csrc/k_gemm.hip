@@ -283,6 +283,217 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *part, i
   }
 }
 
+// ----------------------------------------------------------------------------
+// Streaming variant for the weight-bound products (few activation rows per
+// weight tile).  The four waves of a workgroup split the k range of the
+// whole BM x BN tile between them (wave w takes k steps w, w+4, w+8, ...,
+// so together they walk each weight row's bytes in order), load both
+// operands straight from global memory into MFMA fragments through a ring
+// of S k steps -- S-1 steps of loads stay in flight behind the MFMAs -- and
+// meet only once, at the end, to add their partial tiles through LDS.  No
+// barrier sits in the main loop.
+
+template <typename T, int MT, int NT, int NB, int MODE, int S>
+__device__ __forceinline__ void stream_tile(const GemmArgs &a, float *red, int row_begin, int rows,
+                                            const T *const *Bp, int n0, int ncols, int kb, int ke, int split) {
+  constexpr int EL = NB * MT * NT * 4;   // accumulator floats per lane
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loop control
+  const int l16 = lane & 15, lg = lane >> 4;
+  const T *A = static_cast<const T *>(a.A);
+
+  // Wave-uniform bases + 32-bit per-lane byte offsets, so loads take the
+  // scalar-base form.  Rows past `rows` and columns past `ncols` are
+  // clamped onto row 0 of the tile and loaded anyway: an MFMA output element
+  // depends only on its own A row and B column, and those outputs are never
+  // stored, so no lane needs a branch around its loads.
+  uint32_t ao[MT];
+  bool av[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = mt * 16 + l16;
+    av[mt] = r < rows;
+    int pr = row_begin + (av[mt] ? r : 0);
+    if (a.a_rows) pr = a.a_rows[pr];
+    ao[mt] = (static_cast<uint32_t>(pr) * static_cast<uint32_t>(a.lda) + lg * 8) * sizeof(T);
+  }
+  uint32_t bo[NT];
+  bool bv[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int c = nt * 16 + l16;
+    bv[nt] = c < ncols;
+    bo[nt] = (static_cast<uint32_t>(bv[nt] ? c : 0) * static_cast<uint32_t>(a.ldb) + lg * 8) * sizeof(T);
+  }
+  const char *Ab = reinterpret_cast<const char *>(A);
+  const char *B0 = reinterpret_cast<const char *>(Bp[0]);
+  const char *B1 = reinterpret_cast<const char *>(Bp[NB - 1]);
+
+  f32x4 acc[NB][MT][NT];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nb][mt][nt] = zero4();
+
+  const int nsteps = (ke - kb) / 32;
+  const int my = nsteps > wave ? (nsteps - wave + 3) / 4 : 0;
+  Frag<T> fa[S][MT];
+  Frag<T> fb[S][NB][NT];
+
+  auto load = [&](int it, Frag<T>(&xa)[MT], Frag<T>(&xb)[NB][NT]) {
+    const uint32_t kbyte = static_cast<uint32_t>(kb + (wave + 4 * it) * 32) * sizeof(T);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        xb[nb][nt].load(reinterpret_cast<const T *>((nb == 0 ? B0 : B1) + (bo[nt] + kbyte)));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) xa[mt].load(reinterpret_cast<const T *>(Ab + (ao[mt] + kbyte)));
+  };
+
+#pragma unroll
+  for (int r = 0; r < S - 1; ++r)
+    if (r < my) load(r, fa[r], fb[r]);
+  for (int i = 0; i < my; i += S) {
+#pragma unroll
+    for (int r = 0; r < S; ++r) {
+      const int it = i + r;
+      if (it < my) {
+        if (it + S - 1 < my) load(it + S - 1, fa[(r + S - 1) % S], fb[(r + S - 1) % S]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) mma(acc[nb][mt][nt], fa[r][mt], fb[r][nb][nt]);
+      }
+    }
+  }
+
+  // cross-wave reduction: every wave parks its partial tile in LDS, then all
+  // 256 threads each add up and store a slice of the tile
+  __syncthreads();   // LDS may still be read by the previous tile's epilogue
+  {
+    float *dst = red + wave * EL * 64;
+    int e = 0;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i, ++e) dst[e * 64 + lane] = acc[nb][mt][nt][i];
+  }
+  __syncthreads();
+  constexpr int EH = EL / NB;   // elements per lane of one product
+  for (int q = tid; q < EH * 64; q += 256) {
+    const int ln = q & 63, e = q >> 6;
+    const int i = e & 3, nt = (e >> 2) % NT, mt = (e >> 2) / NT;
+    const int r = mt * 16 + (ln >> 4) * 4 + i;
+    const int c = nt * 16 + (ln & 15);
+    if (r >= rows || c >= ncols) continue;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v += red[(w * EL + e) * 64 + ln];
+    const long long row = row_begin + r;
+    const int col = n0 + c;
+    if constexpr (MODE == EPI_STORE) {
+      static_cast<T *>(a.C)[row * a.ldc + col] = from_f32<T>(v);
+    } else if constexpr (MODE == EPI_STORE_F32) {
+      static_cast<float *>(a.C)[row * a.ldc + col] = v;
+    } else if constexpr (MODE == EPI_ADD) {
+      T *cp = static_cast<T *>(a.C) + row * a.ldc + col;
+      *cp = from_f32<T>(to_f32<T>(*cp) + v);
+    } else if constexpr (MODE == EPI_SWIGLU) {
+      float u = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) u += red[(w * EL + EH + e) * 64 + ln];
+      static_cast<T *>(a.C)[row * a.ldc + col] = from_f32<T>(silu_f(v) * u);
+    } else if constexpr (MODE == EPI_ROWSCALE_F32) {
+      static_cast<float *>(a.C)[row * a.ldc + col] = v * a.rowscale[row];
+    } else if constexpr (MODE == EPI_PARTIAL_F32) {
+      static_cast<float *>(a.C)[(static_cast<long long>(split) * a.M + row) * a.ldc + col] = v;
+    }
+  }
+}
+
+template <typename T, int MT, int NT, int NB, int MODE, int S>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmArgs a) {
+  constexpr int BM = MT * 16, BN = NT * 16;
+  __shared__ __attribute__((aligned(16))) float red[4 * NB * MT * NT * 4 * 64];
+  if (a.g_off == nullptr) {
+    int L = blockIdx.x;
+    const int total = gridDim.x;
+    if ((total & 7) == 0) {
+      const int per = total >> 3;
+      L = (L & 7) * per + (L >> 3);
+    }
+    const int m_tiles = (a.M + BM - 1) / BM;
+    const int n_tiles = (a.N + BN - 1) / BN;
+    int m_tile, n_tile, split;
+    if (a.tile_order == 0) {
+      m_tile = L % m_tiles;
+      const int r = L / m_tiles;
+      n_tile = r % n_tiles;
+      split = r / n_tiles;
+    } else {
+      n_tile = L % n_tiles;
+      const int r = L / n_tiles;
+      m_tile = r % m_tiles;
+      split = r / m_tiles;
+    }
+    const int n0 = n_tile * BN;
+    int s = 0;
+    while (s + 1 < a.nseg && n0 >= a.seg_start[s + 1]) ++s;
+    const T *Bp[NB];
+    Bp[0] = static_cast<const T *>(a.seg_B0[s]) + static_cast<long long>(n0 - a.seg_start[s]) * a.ldb;
+    if (NB > 1) Bp[NB - 1] = static_cast<const T *>(a.seg_B1[s]) + static_cast<long long>(n0 - a.seg_start[s]) * a.ldb;
+    const int kper = a.K / a.k_splits;
+    const int row0 = m_tile * BM;
+    stream_tile<T, MT, NT, NB, MODE, S>(a, red, row0, min(BM, a.M - row0), Bp, n0, a.seg_start[s + 1] - n0,
+                                        split * kper, (split + 1) * kper, split);
+  } else {
+    const int g = blockIdx.y;
+    const int n0 = blockIdx.x * BN;
+    const int Ng = (g == 0) ? a.N_x : a.N;
+    if (n0 >= Ng) return;
+    const T *Bp[NB];
+    GemmArgs ga = a;
+    if (g == 0) {
+      ga.K = a.K_x;
+      ga.ldb = a.ldb_x;
+      Bp[0] = static_cast<const T *>(a.Bx0) + static_cast<long long>(n0) * a.ldb_x;
+      if (NB > 1) Bp[NB - 1] = static_cast<const T *>(a.Bx1) + static_cast<long long>(n0) * a.ldb_x;
+    } else {
+      const long long off = static_cast<long long>(g - 1) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
+      Bp[0] = static_cast<const T *>(a.seg_B0[0]) + off;
+      if (NB > 1) Bp[NB - 1] = static_cast<const T *>(a.seg_B1[0]) + off;
+    }
+    const int r0 = a.g_off[g], r1 = a.g_off[g + 1];
+    for (int rb = r0; rb < r1; rb += BM)
+      stream_tile<T, MT, NT, NB, MODE, S>(ga, red, rb, min(BM, r1 - rb), Bp, n0, Ng - n0, 0, ga.K, 0);
+  }
+}
+
+template <typename T, int MT, int NT, int NB, int MODE, int S>
+hipError_t launch_stream_one(const GemmArgs &a, hipStream_t s) {
+  constexpr int BM = MT * 16, BN = NT * 16;
+  dim3 grid;
+  if (a.g_off) {
+    const int nmax = a.N > a.N_x ? a.N : a.N_x;
+    grid = dim3((nmax + BN - 1) / BN, a.n_groups);
+  } else {
+    const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
+    grid = dim3(mt * nt * a.k_splits, 1);
+  }
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_stream_kernel<T, MT, NT, NB, MODE, S>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 template <typename T>
@@ -305,6 +516,22 @@ hipError_t launch_gemm(const GemmArgs &a, int mode, int bm, int bn, hipStream_t 
 }
 
 template <typename T>
+hipError_t launch_gemm_stream(const GemmArgs &a, int mode, int mt, int nt, hipStream_t s) {
+#define DG_STREAM_CASE(MT_, NT_, NB_, MODE_, S_) \
+  if (mt == MT_ && nt == NT_ && mode == MODE_) return launch_stream_one<T, MT_, NT_, NB_, MODE_, S_>(a, s);
+  DG_STREAM_CASE(4, 4, 1, EPI_STORE, 3)
+  DG_STREAM_CASE(4, 4, 1, EPI_STORE_F32, 3)
+  DG_STREAM_CASE(4, 4, 1, EPI_ADD, 3)
+  DG_STREAM_CASE(4, 4, 1, EPI_PARTIAL_F32, 3)
+  DG_STREAM_CASE(4, 2, 2, EPI_SWIGLU, 3)
+  DG_STREAM_CASE(2, 2, 2, EPI_SWIGLU, 4)
+  DG_STREAM_CASE(2, 4, 1, EPI_ROWSCALE_F32, 4)
+  DG_STREAM_CASE(4, 4, 1, EPI_ROWSCALE_F32, 3)
+#undef DG_STREAM_CASE
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, long long ldc, void *C,
                                 int mode, hipStream_t s) {
   const long long n8 = static_cast<long long>(M) * N / 8;
@@ -316,6 +543,8 @@ hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, lon
 
 template hipError_t launch_gemm<bf16_t>(const GemmArgs &, int, int, int, hipStream_t);
 template hipError_t launch_gemm<float>(const GemmArgs &, int, int, int, hipStream_t);
+template hipError_t launch_gemm_stream<bf16_t>(const GemmArgs &, int, int, int, hipStream_t);
+template hipError_t launch_gemm_stream<float>(const GemmArgs &, int, int, int, hipStream_t);
 template hipError_t launch_splitk_reduce<bf16_t>(const float *, int, int, int, long long, void *, int, hipStream_t);
 template hipError_t launch_splitk_reduce<float>(const float *, int, int, int, long long, void *, int, hipStream_t);
 

@@ -14,7 +14,7 @@ import torch
 from discrete_text_diffusion_step_amd import binding as B
 from discrete_text_diffusion_step_amd import synth
 from oracle import dg_oracle as O
-from tests.helpers import assert_close, cuda, np64, npw, rel_err
+from tests.helpers import assert_close, assert_delta_close, cuda, np64, npw, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -204,7 +204,7 @@ def test_attn_sliding_bf16(n_tok, P):
     ref, _, _ = O.attn_layer(cfg, npw(w), np64(ck), np64(cv), P, np64(x), 0, "bf16")
     assert_close(np64(xo), ref, "bf16", "sliding x")
     # the residual update itself (x_out - x) to the same bar
-    assert_close(np64(xo) - np64(x), ref - np64(x), "bf16", "sliding delta")
+    assert_delta_close(np64(xo), ref, np64(x), "bf16", "sliding delta")
 
 
 def test_attn_global_bf16_32k():
@@ -216,7 +216,7 @@ def test_attn_global_bf16_32k():
     x = synth.hidden_states(256, cfg["hidden"], g, "bf16")
     xo, _, _, _ = run_gpu_attn(cfg, w, ck, cv, P, x, 0)
     ref, _, _ = O.attn_layer(cfg, npw(w), np64(ck), np64(cv), P, np64(x), 0, "bf16")
-    assert_close(np64(xo) - np64(x), ref - np64(x), "bf16", "global delta")
+    assert_delta_close(np64(xo), ref, np64(x), "bf16", "global delta")
 
 
 def test_attn_encode_bf16_ragged():
@@ -230,7 +230,7 @@ def test_attn_encode_bf16_ragged():
     xo, kd, vd, n1 = run_gpu_attn(cfg, w, ck, cv, 100, x, 1)
     assert n1 == 400
     ref, rk, rv = O.attn_layer(cfg, npw(w), np64(ck), np64(cv), 100, np64(x), 1, "bf16")
-    assert_close(np64(xo) - np64(x), ref - np64(x), "bf16", "encode delta")
+    assert_delta_close(np64(xo), ref, np64(x), "bf16", "encode delta")
     assert_close(np64(kd)[:, 100:400], rk, "bf16", "appended k")
     assert_close(np64(vd)[:, 100:400], rv, "bf16", "appended v")
     # rows outside [100, 400) untouched
@@ -288,7 +288,7 @@ def test_moe_bf16_full_injected():
     np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
     assert rel_err(wts.cpu().numpy(), rw) < 1e-5
     assert_close(np64(xd), ref, "bf16", "moe x")
-    assert_close(np64(xd) - np64(x), ref - np64(x), "bf16", "moe delta")
+    assert_delta_close(np64(xd), ref, np64(x), "bf16", "moe delta")
 
 
 def test_moe_bf16_prefill_rows():
@@ -303,7 +303,7 @@ def test_moe_bf16_prefill_rows():
     sync()
     ref, ridx, _, _ = O.moe_block_grouped(cfg, npw(w), np64(x), "bf16", router_logits=np64(rl))
     np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
-    assert_close(np64(xd) - np64(x), ref - np64(x), "bf16", "moe prefill delta")
+    assert_delta_close(np64(xd), ref, np64(x), "bf16", "moe prefill delta")
 
 
 # ----------------------------------------------------------------- whole step / commit (tiny)
