@@ -84,18 +84,20 @@ class KernelTimer(ctypes.Structure):
                 ("count", c_int), ("kernel", c_int)]
 
 
-DG_KT = {"moe_gateup": 1, "moe_down": 2, "lm_head": 3, "attn": 4, "soft_embed": 5}
+DG_KT = {"moe_gateup": 1, "moe_down": 2, "lm_head": 3, "attn": 4, "soft_embed": 5, "qkv": 6, "oproj": 7}
 
 _LIB = None
 
 
-def lib():
-    """Load libdgstep.so (built in-tree by build.py); raise if it is missing."""
+def lib(path=None):
+    """Load libdgstep.so (built in-tree by build.py); raise if it is missing.
+    `path` selects another build of the library on the first call."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: run discrete_text_diffusion_step_amd/build.py")
-        L = ctypes.CDLL(LIB_PATH)
+        path = path or LIB_PATH
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: run discrete_text_diffusion_step_amd/build.py")
+        L = ctypes.CDLL(path)
         P = ctypes.POINTER
         sig = {
             "dg_status_string": (ctypes.c_char_p, [c_int]),
@@ -200,7 +202,8 @@ def dg_status_string(status):
 
 
 def dg_attn_layer(cfg, w, k_cache, v_cache, kv_len, x, causal, stream=None):
-    """x <- x + Attention(x) in place; returns the new committed length."""
+    """x <- x + Attention(x) in place; returns the new committed length.
+    k_cache [Hkv][capacity][d_h]; v_cache transposed, [Hkv][d_h][capacity]."""
     L = lib()
     c = attn_cfg_c(cfg)
     n = x.shape[0]
@@ -315,7 +318,8 @@ class Model:
 
 
 class KV:
-    """Per-layer K/V caches [Hkv][capacity][d_h] and the C record over them."""
+    """Per-layer caches, K [Hkv][capacity][d_h] and V transposed [Hkv][d_h][capacity],
+    and the C record over them."""
 
     def __init__(self, mcfg, capacity, device="cuda", tensors=None):
         L = mcfg["n_layers"]
@@ -324,13 +328,12 @@ class KV:
         for l in range(L):
             glob = (l % mcfg["global_every"]) == mcfg["global_every"] - 1
             c = mcfg["global"] if glob else mcfg["sliding"]
-            shape = (c["n_kv_heads"], capacity, c["head_dim"])
             if tensors is not None:
                 self.k.append(tensors[0][l])
                 self.v.append(tensors[1][l])
             else:
-                self.k.append(torch.zeros(shape, dtype=dt, device=device))
-                self.v.append(torch.zeros(shape, dtype=dt, device=device))
+                self.k.append(torch.zeros(c["n_kv_heads"], capacity, c["head_dim"], dtype=dt, device=device))
+                self.v.append(torch.zeros(c["n_kv_heads"], c["head_dim"], capacity, dtype=dt, device=device))
         self._layers = (KVLayer * L)(*[KVLayer(ptr(self.k[l]), ptr(self.v[l]), capacity, 0) for l in range(L)])
         self.c = KVCache(self._layers, L)
 

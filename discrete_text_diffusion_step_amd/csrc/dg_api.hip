@@ -102,13 +102,13 @@ int choose_ksplit(int M, int N, int K, int bm, int bn, int target, int max_split
 
 // x (or C) <- dense product with split-K through fp32 partials when it pays.
 hipError_t dense_product(int dt, GemmArgs g, int mode, float *part, int ks, hipStream_t s) {
-  if (ks <= 1) return sgemm(dt, g, mode, 4, 4, s);
+  if (ks <= 1) return sgemm(dt, g, mode, DG_DENSE_MT, DG_DENSE_NT, s);
   void *C = g.C;
   const long long ldc = g.ldc;
   g.C = part;
   g.ldc = g.N;
   g.k_splits = ks;
-  hipError_t e = sgemm(dt, g, EPI_PARTIAL_F32, 4, 4, s);
+  hipError_t e = sgemm(dt, g, EPI_PARTIAL_F32, DG_DENSE_MT, DG_DENSE_NT, s);
   if (e != hipSuccess) return e;
   return reduce(dt, part, ks, g.M, g.N, ldc, C, mode, s);
 }
@@ -129,14 +129,15 @@ AttnPlan attn_plan(const dg_attn_cfg *c, int n) {
   p.R = (c->n_q_heads / c->n_kv_heads) * n;
   const int bq = attn_block_rows(c->dtype, c->head_dim);
   const int blocks = c->n_kv_heads * ((p.R + bq - 1) / (bq > 0 ? bq : 1));
-  int ns = (512 + blocks - 1) / (blocks > 0 ? blocks : 1);
+  const int target = attn_target_workgroups(c->dtype, c->head_dim);
+  int ns = (target + blocks - 1) / (blocks > 0 ? blocks : 1);
   p.n_split_max = ns < 1 ? 1 : (ns > 16 ? 16 : ns);
-  p.oproj_ks = choose_ksplit(n, c->hidden, p.Nq, 64, 64, 512, 8);
+  p.oproj_ks = choose_ksplit(n, c->hidden, p.Nq, 16 * DG_DENSE_MT, 16 * DG_DENSE_NT, 512, 8);
   return p;
 }
 
 struct AttnWs {
-  void *h, *qkv, *k_new, *v_new, *o;
+  void *h, *qkv, *v_rows, *o;
   float *o_part, *ml_part, *oproj_part;
 };
 
@@ -146,8 +147,7 @@ AttnWs attn_carve(const dg_attn_cfg *c, const AttnPlan &p, Carve &cv) {
   const size_t n = static_cast<size_t>(p.n);
   w.h = cv.bytes(n * c->hidden * es);
   w.qkv = cv.bytes(n * p.Ntot * es);
-  w.k_new = cv.bytes(n * p.Nk * es);
-  w.v_new = cv.bytes(n * p.Nk * es);
+  w.v_rows = cv.bytes(n * p.Nk * es);   // [Hkv][n][dh] from the norm pass
   w.o = cv.bytes(n * p.Nq * es);
   const size_t rows = static_cast<size_t>(c->n_kv_heads) * p.R;
   if (p.n_split_max > 1) {
@@ -197,7 +197,10 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   g.seg_B0[1] = w->w_k;
   g.seg_B0[2] = w->w_v;
   g.seg_start[g.nseg] = p.Ntot;
-  DG_HIP(sgemm(dt, g, EPI_STORE, 4, 4, s));
+  {
+    TimedLaunch tl(DG_KT_QKV, s);
+    DG_HIP(sgemm(dt, g, EPI_STORE, DG_DENSE_MT, DG_DENSE_NT, s));
+  }
 
   NormRopeArgs nr;
   nr.qkv = ws.qkv;
@@ -211,17 +214,15 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   nr.v_off = c->shared_kv ? p.Nq : p.Nq + p.Nk;
   nr.q_norm = w->q_norm;
   nr.k_norm = w->k_norm;
-  if (causal) {
-    nr.k_dst = kv->k;
-    nr.v_dst = kv->v;
-    nr.dst_head_stride = static_cast<long long>(kv->capacity) * dh;
-    nr.dst_row0 = P;
-  } else {
-    nr.k_dst = ws.k_new;
-    nr.v_dst = ws.v_new;
-    nr.dst_head_stride = static_cast<long long>(n) * dh;
-    nr.dst_row0 = 0;
-  }
+  // This call's K rows go to the cache at rows [P, P + n); its V rows go to
+  // the workspace and are then written transposed into cache columns
+  // [P, P + n).  Decode uses those rows as scratch (kv_len stays P); encode
+  // keeps them and advances kv_len.
+  nr.k_dst = kv->k;
+  nr.k_head_stride = static_cast<long long>(kv->capacity) * dh;
+  nr.k_row0 = P;
+  nr.v_dst = ws.v_rows;
+  nr.v_head_stride = static_cast<long long>(n) * dh;
   nr.pos0 = P;
   nr.rope_base = c->rope_base;
   const double rf = c->layer_type == 1 ? c->rotary_factor : 1.0;
@@ -230,23 +231,17 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   nr.sqrt_dh = static_cast<float>(sqrt(static_cast<double>(dh)));
   nr.v_unit_rms = c->v_unit_rms;
   DG_HIP(launch_norm_rope(nr, dt, s));
+  const long long vt_cache_hs = static_cast<long long>(dh) * kv->capacity;
+  DG_HIP(launch_v_transpose(dt, ws.v_rows, n, Hkv, dh, kv->v, vt_cache_hs, kv->capacity, P, s));
 
   AttnArgs at;
   at.q = ws.qkv;
   at.q_ld = p.Ntot;
   at.k_cache = kv->k;
-  at.v_cache = kv->v;
   at.cache_hs = static_cast<long long>(kv->capacity) * dh;
-  if (causal) {
-    const size_t es = esize(dt);
-    at.k_new = static_cast<const char *>(kv->k) + static_cast<size_t>(P) * dh * es;
-    at.v_new = static_cast<const char *>(kv->v) + static_cast<size_t>(P) * dh * es;
-    at.new_hs = at.cache_hs;
-  } else {
-    at.k_new = ws.k_new;
-    at.v_new = ws.v_new;
-    at.new_hs = static_cast<long long>(n) * dh;
-  }
+  at.v_cache = kv->v;
+  at.vcache_hs = vt_cache_hs;
+  at.vcache_ld = kv->capacity;
   at.n_tok = n;
   at.Hq = Hq;
   at.Hkv = Hkv;
@@ -276,6 +271,7 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   {
     GemmArgs o = dense_args(ws.o, p.Nq, n, D, p.Nq, x, D);
     o.seg_B0[0] = w->w_o;
+    TimedLaunch tl(DG_KT_OPROJ, s);
     DG_HIP(dense_product(dt, o, EPI_ADD, ws.oproj_part, p.oproj_ks, s));
   }
   if (causal) kv->kv_len = P + n;
@@ -289,9 +285,10 @@ int check_attn_call(const dg_attn_cfg *c, const dg_attn_w *w, const dg_kv_layer 
   if (!w->w_in_norm || !w->w_q || !w->w_k || !w->w_o || !w->q_norm || !w->k_norm) return DG_ERR_NULL;
   if (!c->shared_kv && !w->w_v) return DG_ERR_NULL;
   if (n < 0 || kv->kv_len < 0 || kv->capacity < 0 || kv->kv_len > kv->capacity) return DG_ERR_SHAPE;
-  if (n > 0 && (!kv->k || !kv->v) && (causal || kv->kv_len > 0)) return DG_ERR_NULL;
+  if (kv->capacity % 8) return DG_ERR_SHAPE;
+  if (n > 0 && (!kv->k || !kv->v)) return DG_ERR_NULL;
   if (causal != 0 && causal != 1) return DG_ERR_SHAPE;
-  if (causal && kv->kv_len + n > kv->capacity) return DG_ERR_CAPACITY;
+  if (kv->kv_len + n > kv->capacity) return DG_ERR_CAPACITY;   // this call's rows sit at [kv_len, kv_len + n)
   return DG_OK;
 }
 
@@ -312,7 +309,9 @@ struct MoeWs {
   void *H;
 };
 
-int router_ksplit(const dg_moe_cfg *c, int n) { return choose_ksplit(n, c->n_experts, c->hidden, 64, 64, 256, 16); }
+int router_ksplit(const dg_moe_cfg *c, int n) {
+  return choose_ksplit(n, c->n_experts, c->hidden, 16 * DG_DENSE_MT, 16 * DG_DENSE_NT, 256, 16);
+}
 
 MoeWs moe_carve(const dg_moe_cfg *c, int n, Carve &cv) {
   const size_t es = esize(c->dtype);
@@ -364,7 +363,7 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   DG_HIP(launch_moe_permute(idx, tw, n, k, E, ws.g_off, ws.row_token, ws.row_weight, ws.pair_row, s));
 
   const int rows_per_expert = (n * k + E - 1) / E;
-  const int mtile = rows_per_expert > 48 ? 4 : 2;   // 64- or 32-row tiles
+  const int mtile = rows_per_expert > 48 ? 4 : DG_MOE_MT;   // 64-row tiles for long groups
 
   // gate/up of every expert (group 0 = shared) with the SwiGLU epilogue
   GemmArgs gu;
@@ -391,7 +390,7 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   gu.ldc = fmax;
   {
     TimedLaunch tl(DG_KT_MOE_GATEUP, s);
-    DG_HIP(sgemm(dt, gu, EPI_SWIGLU, mtile, 2, s));
+    DG_HIP(sgemm(dt, gu, EPI_SWIGLU, mtile, DG_MOE_NT_GU, s));
   }
 
   // down projection, scaled by the routing weight of each row
@@ -417,7 +416,7 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   dn.rowscale = ws.row_weight;
   {
     TimedLaunch tl(DG_KT_MOE_DOWN, s);
-    DG_HIP(sgemm(dt, dn, EPI_ROWSCALE_F32, mtile, 4, s));
+    DG_HIP(sgemm(dt, dn, EPI_ROWSCALE_F32, mtile, DG_MOE_NT_DN, s));
   }
 
   DG_HIP(launch_moe_combine(dt, x, ws.Y, ws.pair_row, n, k, D, c->layer_scalar, s));
@@ -504,7 +503,7 @@ int sample_impl(const dg_sampler_cfg *c, int n, const void *logits, int ldt, int
 
 // ----------------------------------------------------- head, soft embedding
 
-int softembed_ksplit(int n, int D, int V) { return choose_ksplit(n, D, V, 64, 64, 512, 32); }
+int softembed_ksplit(int n, int D, int V) { return choose_ksplit(n, D, V, 16 * DG_DENSE_MT, 16 * DG_DENSE_NT, 512, 32); }
 
 struct SoftWs {
   void *P;
@@ -545,7 +544,7 @@ int lm_head_impl(int n, int D, int V, float eps, int dt, const void *x, const vo
   g.seg_B0[0] = E;
   g.tile_order = 0;
   TimedLaunch tl(DG_KT_LM_HEAD, s);
-  DG_HIP(sgemm(dt, g, EPI_STORE_F32, 4, 4, s));
+  DG_HIP(sgemm(dt, g, EPI_STORE_F32, DG_DENSE_MT, DG_DENSE_NT, s));
   return DG_OK;
 }
 
@@ -761,8 +760,8 @@ static int check_kv(const dg_model_cfg *c, const dg_kv_cache *kv) {
   const int P = kv->layer[0].kv_len;
   for (int l = 0; l < c->n_layers; ++l) {
     const dg_kv_layer &L = kv->layer[l];
-    if (L.kv_len != P || L.kv_len < 0 || L.kv_len > L.capacity) return DG_ERR_SHAPE;
-    if ((!L.k || !L.v) && L.capacity > 0) return DG_ERR_NULL;
+    if (L.kv_len != P || L.kv_len < 0 || L.kv_len > L.capacity || L.capacity % 8) return DG_ERR_SHAPE;
+    if (!L.k || !L.v) return DG_ERR_NULL;
   }
   return DG_OK;
 }
@@ -777,6 +776,8 @@ int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cac
   if (scfg->vocab != cfg->vocab) return DG_ERR_SHAPE;
   const int n = st->canvas_len;
   if (n <= 0) return DG_ERR_SHAPE;
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if (kv->layer[l].kv_len + n > kv->layer[l].capacity) return DG_ERR_CAPACITY;
   if (!ws) return DG_ERR_NULL;
   Carve cv(ws);
   const StepWs sw = step_carve(cfg, n, st->logits == nullptr, cv);
@@ -792,7 +793,7 @@ int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cac
     DG_HIP(sgemm(dt, g, EPI_SWIGLU, 2, 2, s));
     GemmArgs d = dense_args(sw.g_sc, cfg->sc_ffn, n, D, cfg->sc_ffn, sw.x, D);
     d.seg_B0[0] = w->sc_down;
-    DG_HIP(sgemm(dt, d, EPI_ADD, 4, 4, s));
+    DG_HIP(sgemm(dt, d, EPI_ADD, DG_DENSE_MT, DG_DENSE_NT, s));
   }
   for (int l = 0; l < cfg->n_layers; ++l) {
     Carve c1(sw.rest);
@@ -856,7 +857,7 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
       g.seg_start[2] = p.Nk + p.Nv;
       g.seg_B0[0] = w->attn[l].w_k;
       g.seg_B0[1] = w->attn[l].w_v;
-      DG_HIP(sgemm(dt, g, EPI_STORE, 4, 4, s));
+      DG_HIP(sgemm(dt, g, EPI_STORE, DG_DENSE_MT, DG_DENSE_NT, s));
       NormRopeArgs nr;
       nr.qkv = aw.qkv;
       nr.ld = p.Ntot;
@@ -870,9 +871,10 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
       nr.q_norm = w->attn[l].q_norm;
       nr.k_norm = w->attn[l].k_norm;
       nr.k_dst = KL.k;
-      nr.v_dst = KL.v;
-      nr.dst_head_stride = static_cast<long long>(KL.capacity) * ac->head_dim;
-      nr.dst_row0 = KL.kv_len;
+      nr.k_head_stride = static_cast<long long>(KL.capacity) * ac->head_dim;
+      nr.k_row0 = KL.kv_len;
+      nr.v_dst = aw.v_rows;
+      nr.v_head_stride = static_cast<long long>(n) * ac->head_dim;
       nr.pos0 = KL.kv_len;
       nr.rope_base = ac->rope_base;
       const double rf = ac->layer_type == 1 ? ac->rotary_factor : 1.0;
@@ -881,6 +883,8 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
       nr.sqrt_dh = static_cast<float>(sqrt(static_cast<double>(ac->head_dim)));
       nr.v_unit_rms = ac->v_unit_rms;
       DG_HIP(launch_norm_rope(nr, dt, s));
+      DG_HIP(launch_v_transpose(dt, aw.v_rows, n, ac->n_kv_heads, ac->head_dim, KL.v,
+                                static_cast<long long>(ac->head_dim) * KL.capacity, KL.capacity, KL.kv_len, s));
       KL.kv_len += n;
       break;
     }

@@ -21,10 +21,10 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
 
 // Round to nearest even, as the storage rounding of a bf16 tensor.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<bf16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t qnan = (u >> 16) | 0x40u;                       // NaN stays a (quiet) NaN
+  return static_cast<bf16_t>((u & 0x7fffffffu) > 0x7f800000u ? qnan : rne);
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);
@@ -51,6 +51,12 @@ template <> struct Frag<bf16_t> {
     uint4 z = make_uint4(0, 0, 0, 0);
     v = *reinterpret_cast<bf16x8 *>(&z);
   }
+  // keep the fragment (mask all ones) or zero it (mask 0) without a branch
+  __device__ __forceinline__ void mask(uint32_t m) {
+    uint4 u = *reinterpret_cast<uint4 *>(&v);
+    u.x &= m; u.y &= m; u.z &= m; u.w &= m;
+    v = *reinterpret_cast<bf16x8 *>(&u);
+  }
   __device__ __forceinline__ void from_floats(const float *f) {
     uint32_t w[4];
 #pragma unroll
@@ -71,6 +77,10 @@ template <> struct Frag<float> {
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = 0.f;
+  }
+  __device__ __forceinline__ void mask(uint32_t m) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(__float_as_uint(v[j]) & m);
   }
   __device__ __forceinline__ void from_floats(const float *f) {
 #pragma unroll
@@ -187,6 +197,29 @@ struct GemmArgs {
 
 template <typename T>
 hipError_t launch_gemm(const GemmArgs &a, int mode, int bm, int bn, hipStream_t s);
+// Tile shapes of the streaming products (in 16x16 MFMA tiles) and ring depth.
+#ifndef DG_DENSE_MT
+#define DG_DENSE_MT 4
+#endif
+#ifndef DG_DENSE_NT
+#define DG_DENSE_NT 4
+#endif
+#ifndef DG_DENSE_S
+#define DG_DENSE_S 3
+#endif
+#ifndef DG_MOE_MT
+#define DG_MOE_MT 2
+#endif
+#ifndef DG_MOE_NT_GU
+#define DG_MOE_NT_GU 2
+#endif
+#ifndef DG_MOE_NT_DN
+#define DG_MOE_NT_DN 4
+#endif
+#ifndef DG_MOE_S
+#define DG_MOE_S 4
+#endif
+
 // streaming variant: tile (16*mt) x (16*nt), waves split k (K per split a multiple of 32)
 template <typename T>
 hipError_t launch_gemm_stream(const GemmArgs &a, int mode, int mt, int nt, hipStream_t s);

@@ -10,9 +10,11 @@ struct NormRopeArgs {
   int n_tok, Hq, Hkv, dh;
   int q_off, k_off, v_off;   // column offsets of q, k, v (v_off = k_off when K/V are shared)
   const void *q_norm, *k_norm;
-  void *k_dst, *v_dst;       // [Hkv][..][dh], row dst_row0 + j
-  long long dst_head_stride; // elements between heads
-  int dst_row0;
+  void *k_dst;               // [Hkv][..][dh], row k_row0 + j
+  long long k_head_stride;   // elements between heads
+  int k_row0;
+  void *v_dst;               // [Hkv][n_tok][dh], row j
+  long long v_head_stride;
   int pos0;
   double rope_base;
   int n_rot;                 // frequencies kept (the rest are zero)
@@ -23,10 +25,11 @@ struct NormRopeArgs {
 struct AttnArgs {
   const void *q;             // row (token j, head h) at q + j*q_ld + h*dh
   long long q_ld;
-  const void *k_cache, *v_cache;  // [Hkv][cap][dh]: committed rows (position m at row m)
+  const void *k_cache;       // [Hkv][cap][dh]: keys, position m at row m
   long long cache_hs;
-  const void *k_new, *v_new; // rows of positions >= kv_len: row m - kv_len
-  long long new_hs;
+  const void *v_cache;       // [Hkv][dh][cap]: values transposed, position m at column m
+  long long vcache_hs;
+  int vcache_ld;
   int n_tok, Hq, Hkv, n_rep;
   int kv_len, key_lo;
   int causal, sliding, window;
@@ -55,6 +58,10 @@ struct SampleArgs {
 
 hipError_t launch_norm_rope(const NormRopeArgs &a, int dtype, hipStream_t s);
 hipError_t launch_attention(const AttnArgs &a, int dtype, int dh, hipStream_t s);
+// dst[h][d][col0 + j] = src[h][j][d] for j < n (values to the transposed layout)
+hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh, void *dst, long long dst_hs,
+                              int dst_ld, int col0, hipStream_t s);
+int attn_target_workgroups(int dtype, int dh);
 int attn_block_rows(int dtype, int dh);
 hipError_t launch_router_topk(const float *logits, int n_tok, int E, int k, float scale, int32_t *idx, float *w,
                               hipStream_t s);

@@ -53,12 +53,12 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
     } else if (it < a.Hq + a.Hkv) {
       const int h = it - a.Hq;
       src = row + a.k_off + h * a.dh;
-      dst = static_cast<T *>(a.k_dst) + h * a.dst_head_stride + static_cast<long long>(a.dst_row0 + j) * a.dh;
+      dst = static_cast<T *>(a.k_dst) + h * a.k_head_stride + static_cast<long long>(a.k_row0 + j) * a.dh;
       w = static_cast<const T *>(a.k_norm);
     } else {
       const int h = it - a.Hq - a.Hkv;
       src = row + a.v_off + h * a.dh;
-      dst = static_cast<T *>(a.v_dst) + h * a.dst_head_stride + static_cast<long long>(a.dst_row0 + j) * a.dh;
+      dst = static_cast<T *>(a.v_dst) + h * a.v_head_stride + static_cast<long long>(j) * a.dh;
       rope = false;
       norm = a.v_unit_rms != 0;
     }
@@ -105,45 +105,93 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
 
 constexpr int kBKV = 32;  // keys per tile
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Tiles go from global memory straight into LDS (global_load_lds_dwordx4:
+// each instruction writes 64 lanes x 16 B = 1 KB contiguous at a wave-
+// uniform LDS address), so the layouts are unpadded and the 16-byte chunks
+// of a row are XOR-swizzled by the row index to spread MFMA operand reads
+// over the LDS banks.
 template <typename T, int DH>
 struct AttnCfg {
   static constexpr int QT = DH >= 512 ? 1 : 2;      // 16-query tiles per wave
   static constexpr int BQ = 4 * 16 * QT;            // query rows per workgroup
-  static constexpr int PADK = 16 / sizeof(T);
-  static constexpr int KROW = DH + PADK;            // sK row (elements)
-  static constexpr int PADV = 4;                    // keeps bf16 rows 8-B and fp32 rows 16-B aligned
-  static constexpr int VROW = kBKV + PADV;          // sVt row (elements)
+  static constexpr int VEC = 16 / sizeof(T);        // elements per 16-B chunk
+  static constexpr int KCPR = DH / VEC;             // K tile: chunks per key row
+  static constexpr int VCPR = kBKV / VEC;           // V^T tile: chunks per d row
+  static constexpr int KCH = kBKV * KCPR;           // chunks per K tile
+  static constexpr int VCH = DH * VCPR;             // chunks per V^T tile
+  static constexpr int KINS = KCH / 64;             // 1-KB loads per K tile
+  static constexpr int VINS = VCH / 64;
+  static constexpr int KSW = KCPR >= 16 ? 15 : KCPR - 1;
+  static constexpr int VSW = VCPR - 1;
   static constexpr int DS = DH / 32;                // 32-wide d steps
   static constexpr int DT = DH / 16;                // 16-wide d tiles
+  static_assert(KINS % 4 == 0 && VINS % 4 == 0, "each wave issues an equal share of a tile");
 };
 
-__device__ __forceinline__ void store_pair(bf16_t *p, float a, float b) {
-  *reinterpret_cast<uint32_t *>(p) = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-}
-__device__ __forceinline__ void store_pair(float *p, float a, float b) {
-  *reinterpret_cast<float2 *>(p) = make_float2(a, b);
+// K fragment: elements [e0, e0+8) of key row r of a swizzled K tile
+template <typename T, int DH>
+__device__ __forceinline__ void load_k_frag(Frag<T> &f, const T *tile, int r, int e0) {
+  using C = AttnCfg<T, DH>;
+  if constexpr (sizeof(T) == 2) {
+    const int c = e0 / 8;
+    f.load(tile + (r * C::KCPR + (c ^ (r & C::KSW))) * 8);
+  } else {
+    const int c = e0 / 4;
+    const float4 a = *reinterpret_cast<const float4 *>(tile + (r * C::KCPR + (c ^ (r & C::KSW))) * 4);
+    const float4 b = *reinterpret_cast<const float4 *>(tile + (r * C::KCPR + ((c + 1) ^ (r & C::KSW))) * 4);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+  }
 }
 
-__device__ __forceinline__ void load_vt_frag(Frag<bf16_t> &f, const bf16_t *row, int lg) {
-  const uint2 a = *reinterpret_cast<const uint2 *>(row + lg * 4);
-  const uint2 b = *reinterpret_cast<const uint2 *>(row + 16 + lg * 4);
-  uint4 u = make_uint4(a.x, a.y, b.x, b.y);
+// V^T fragment of row d holding keys {4g..4g+3, 16+4g..16+4g+3} (g = lane/16),
+// the key order of the P^T fragment built from the S^T accumulators.
+template <typename T, int DH>
+__device__ __forceinline__ void load_v_frag(Frag<T> &f, const T *tile, int d, int lg) {
+  using C = AttnCfg<T, DH>;
+  if constexpr (sizeof(T) == 2) {
+    const bf16_t *row = tile + d * C::VCPR * 8;
+    const int c0 = lg >> 1, c1 = 2 + (lg >> 1), h = (lg & 1) * 4;
+    const uint2 a = *reinterpret_cast<const uint2 *>(row + (c0 ^ (d & C::VSW)) * 8 + h);
+    const uint2 b = *reinterpret_cast<const uint2 *>(row + (c1 ^ (d & C::VSW)) * 8 + h);
+    uint4 u = make_uint4(a.x, a.y, b.x, b.y);
+    f.v = *reinterpret_cast<bf16x8 *>(&u);
+  } else {
+    const float *row = tile + d * C::VCPR * 4;
+    const float4 a = *reinterpret_cast<const float4 *>(row + (lg ^ (d & C::VSW)) * 4);
+    const float4 b = *reinterpret_cast<const float4 *>(row + ((4 + lg) ^ (d & C::VSW)) * 4);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ void mask_frag(Frag<bf16_t> &f, const uint32_t *m) {
+  uint4 u = *reinterpret_cast<uint4 *>(&f.v);
+  u.x &= m[0]; u.y &= m[1]; u.z &= m[2]; u.w &= m[3];
   f.v = *reinterpret_cast<bf16x8 *>(&u);
 }
-__device__ __forceinline__ void load_vt_frag(Frag<float> &f, const float *row, int lg) {
-  const float4 a = *reinterpret_cast<const float4 *>(row + lg * 4);
-  const float4 b = *reinterpret_cast<const float4 *>(row + 16 + lg * 4);
-  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+__device__ __forceinline__ void mask_frag(Frag<float> &f, const uint32_t *m) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.v[j] = __uint_as_float(__float_as_uint(f.v[j]) & m[j]);
 }
 
+// One workgroup: kv head g, query rows [r0, r1) of the heads sharing it,
+// keys [k_lo, k_hi), all read from the cache (this call's rows sit at
+// [kv_len, kv_len + n_tok)).  32-key tiles start at multiples of 32; two
+// LDS buffers alternate: tile t+1 streams in while tile t is computed.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
   using C = AttnCfg<T, DH>;
-  __shared__ __attribute__((aligned(16))) T sK[kBKV * C::KROW];
-  __shared__ __attribute__((aligned(16))) T sVt[DH * C::VROW];
+  __shared__ __attribute__((aligned(16))) T sK0[C::KCH * C::VEC];
+  __shared__ __attribute__((aligned(16))) T sK1[C::KCH * C::VEC];
+  __shared__ __attribute__((aligned(16))) T sV0[C::VCH * C::VEC];
+  __shared__ __attribute__((aligned(16))) T sV1[C::VCH * C::VEC];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
   const int R = a.n_rep * a.n_tok;
   const int qblocks = (R + C::BQ - 1) / C::BQ;
@@ -170,6 +218,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
   chunk = (chunk + kBKV - 1) / kBKV * kBKV;
   const int k_lo = lo + split * chunk;
   const int k_hi = min(hi, k_lo + chunk);
+  const int t_first = (k_lo / kBKV) * kBKV;
+  const int n_tiles = k_hi > k_lo ? (k_hi - t_first + kBKV - 1) / kBKV : 0;
 
   // this lane's query rows (one per 16-query tile) and their q fragments
   int qrow[C::QT], qpos[C::QT];
@@ -205,66 +255,58 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
     l_run[qt] = 0.f;
   }
 
-  const T *Kc = static_cast<const T *>(a.k_cache) + g * a.cache_hs;
-  const T *Vc = static_cast<const T *>(a.v_cache) + g * a.cache_hs;
-  const T *Kn = static_cast<const T *>(a.k_new) + g * a.new_hs;
-  const T *Vn = static_cast<const T *>(a.v_new) + g * a.new_hs;
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int KCH = kBKV * DH / VEC;   // 16-byte chunks of a K tile
-  constexpr int VPAIRS = (kBKV / 2) * (DH / 8);
+  const T *Kg = static_cast<const T *>(a.k_cache) + g * a.cache_hs;    // [cap][DH]
+  const T *Vg = static_cast<const T *>(a.v_cache) + g * a.vcache_hs;   // [DH][cap]
+  const int vld = a.vcache_ld;
 
-  for (int t0 = k_lo; t0 < k_hi; t0 += kBKV) {
-    // ---- stage K tile [key][d] and V^T tile [d][key] in LDS
-    for (int c = tid; c < KCH; c += 256) {
-      const int kk = c / (DH / VEC), d0 = (c % (DH / VEC)) * VEC;
-      const int m = t0 + kk;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < k_hi) {
-        const T *src = (m < a.kv_len) ? Kc + static_cast<long long>(m) * DH : Kn + static_cast<long long>(m - a.kv_len) * DH;
-        v = *reinterpret_cast<const uint4 *>(src + d0);
-      }
-      *reinterpret_cast<uint4 *>(sK + kk * C::KROW + d0) = v;
+  // Stream one tile into LDS.  Keys outside [k_lo, k_hi) read a valid row
+  // instead (their scores are masked and their values zeroed at use).
+  auto issue = [&](int t0, T *kb, T *vb) {
+#pragma unroll
+    for (int j = 0; j < C::KINS / 4; ++j) {
+      const int blk = wave + 4 * j;
+      const int p = blk * 64 + lane;
+      const int r = p / C::KCPR, c = (p % C::KCPR) ^ (r & C::KSW);
+      int m = t0 + r;
+      m = m < k_lo ? k_lo : (m >= k_hi ? k_hi - 1 : m);
+      const T *src = Kg + static_cast<long long>(m) * DH + c * C::VEC;
+      __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(kb + blk * 64 * C::VEC), 16, 0, 0);
     }
-    for (int c = tid; c < VPAIRS; c += 256) {
-      const int kp = c % (kBKV / 2), d0 = (c / (kBKV / 2)) * 8;
-      float va[8], vb[8];
-      const int m0 = t0 + 2 * kp, m1 = m0 + 1;
-      if (m0 < k_hi) {
-        const T *src = (m0 < a.kv_len) ? Vc + static_cast<long long>(m0) * DH : Vn + static_cast<long long>(m0 - a.kv_len) * DH;
-        load8(src + d0, va);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) va[e] = 0.f;
-      }
-      if (m1 < k_hi) {
-        const T *src = (m1 < a.kv_len) ? Vc + static_cast<long long>(m1) * DH : Vn + static_cast<long long>(m1 - a.kv_len) * DH;
-        load8(src + d0, vb);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vb[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) store_pair(sVt + (d0 + e) * C::VROW + 2 * kp, va[e], vb[e]);
+    for (int j = 0; j < C::VINS / 4; ++j) {
+      const int blk = wave + 4 * j;
+      const int p = blk * 64 + lane;
+      const int d = p / C::VCPR, c = (p % C::VCPR) ^ (d & C::VSW);
+      int k0 = t0 + c * C::VEC;
+      k0 = k0 > vld - C::VEC ? vld - C::VEC : k0;
+      const T *src = Vg + static_cast<long long>(d) * vld + k0;
+      __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(vb + blk * 64 * C::VEC), 16, 0, 0);
     }
-    __syncthreads();
+  };
 
+  auto compute = [&](int t0, const T *kb, const T *vb) {
     // ---- S^T = K Q^T for 32 keys x (16*QT) queries of this wave
     f32x4 st[2][C::QT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int qt = 0; qt < C::QT; ++qt) st[kt][qt] = zero4();
+    // K fragments double-buffered in registers: step s+1 is read from LDS
+    // while the MFMAs of step s run
+    Frag<T> kf[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) load_k_frag<T, DH>(kf[0][kt], kb, kt * 16 + l16, lg * 8);
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
+      if (s + 1 < C::DS) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        Frag<T> kf;
-        kf.load(sK + (kt * 16 + l16) * C::KROW + s * 32 + lg * 8);
-#pragma unroll
-        for (int qt = 0; qt < C::QT; ++qt) mma(st[kt][qt], kf, qf[qt][s]);
+        for (int kt = 0; kt < 2; ++kt) load_k_frag<T, DH>(kf[(s + 1) & 1][kt], kb, kt * 16 + l16, (s + 1) * 32 + lg * 8);
       }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < C::QT; ++qt) mma(st[kt][qt], kf[s & 1][kt], qf[qt][s]);
     }
-
     // ---- mask, online softmax (lane owns one query per tile)
     Frag<T> pf[C::QT];
 #pragma unroll
@@ -276,10 +318,10 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = t0 + kt * 16 + lg * 4 + i;
-          bool ok = m < k_hi;
+          bool ok = m >= k_lo && m < k_hi;
           if (a.causal) {
-            const int p = qpos[qt];
-            ok = ok && (m <= p) && (!a.sliding || m > p - a.window);
+            const int pq = qpos[qt];
+            ok = ok && (m <= pq) && (!a.sliding || m > pq - a.window);
           }
           const float v = ok ? st[kt][qt][i] : -INFINITY;
           sv[kt * 4 + i] = v;
@@ -297,24 +339,62 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
       }
       l_run[qt] = l_run[qt] * corr + psum;
       m_run[qt] = m_new;
+      // rescale the output accumulators only when some lane's running max
+      // grew (corr == 1 exactly otherwise): after the first tiles this is rare
+      if (__ballot(corr != 1.0f) != 0ull) {
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        o[dt][qt][0] *= corr;
-        o[dt][qt][1] *= corr;
-        o[dt][qt][2] *= corr;
-        o[dt][qt][3] *= corr;
+        for (int dt = 0; dt < C::DT; ++dt) {
+          o[dt][qt][0] *= corr;
+          o[dt][qt][1] *= corr;
+          o[dt][qt][2] *= corr;
+          o[dt][qt][3] *= corr;
+        }
       }
       pf[qt].from_floats(sv);
     }
-
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T; on edge tiles values of keys outside the range
+    // are zeroed (their rows may hold anything, e.g. never-written memory)
+    const bool edge = (t0 < k_lo) || (t0 + kBKV > k_hi);
+    constexpr int NW = sizeof(T) == 2 ? 4 : 8;
+    uint32_t vm[NW];
+    if (edge) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int m = t0 + (e >> 2) * 16 + lg * 4 + (e & 3);
+        const bool ok = m >= k_lo && m < k_hi;
+        if constexpr (sizeof(T) == 2) {
+          if ((e & 1) == 0) vm[e >> 1] = 0;
+          vm[e >> 1] |= ok ? ((e & 1) ? 0xffff0000u : 0x0000ffffu) : 0u;
+        } else {
+          vm[e] = ok ? 0xffffffffu : 0u;
+        }
+      }
+    }
+    Frag<T> vf[2];
+    load_v_frag<T, DH>(vf[0], vb, l16, lg);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      Frag<T> vf;
-      load_vt_frag(vf, sVt + (dt * 16 + l16) * C::VROW, lg);
+      if (dt + 1 < C::DT) load_v_frag<T, DH>(vf[(dt + 1) & 1], vb, (dt + 1) * 16 + l16, lg);
+      Frag<T> v = vf[dt & 1];
+      if (edge) mask_frag(v, vm);
 #pragma unroll
-      for (int qt = 0; qt < C::QT; ++qt) mma(o[dt][qt], vf, pf[qt]);
+      for (int qt = 0; qt < C::QT; ++qt) mma(o[dt][qt], v, pf[qt]);
     }
+  };
+
+  if (n_tiles > 0) issue(t_first, sK0, sV0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int it = 0; it < n_tiles; it += 2) {
+    const int t0 = t_first + it * kBKV;
+    if (it + 1 < n_tiles) issue(t0 + kBKV, sK1, sV1);
+    compute(t0, sK0, sV0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 1 >= n_tiles) break;
+    if (it + 2 < n_tiles) issue(t0 + 2 * kBKV, sK0, sV0);
+    compute(t0 + kBKV, sK1, sV1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
@@ -350,30 +430,67 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
   }
 }
 
+// Merge the key slices of one query row: weights w_s = exp(m_s - M) / L are
+// computed once per row, then every thread adds its columns.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a, int dh) {
+  __shared__ float ws[32];
   const int R = a.n_rep * a.n_tok;
   const int idx = blockIdx.x;  // g * R + rr
   const int g = idx / R, rr = idx % R;
   const long long rows = static_cast<long long>(a.Hkv) * R;
-  float M = -1e30f;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, a.ml_part[(s * rows + idx) * 2]);
-  float L = 0.f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const float* ml = a.ml_part + (s * rows + idx) * 2;
-    L += ml[1] * __expf(ml[0] - M);
+  if (threadIdx.x == 0) {
+    float M = -1e30f;
+    for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, a.ml_part[(s * rows + idx) * 2]);
+    float L = 0.f;
+    for (int s = 0; s < a.n_split; ++s) {
+      const float *ml = a.ml_part + (s * rows + idx) * 2;
+      ws[s] = __expf(ml[0] - M);
+      L += ml[1] * ws[s];
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    for (int s = 0; s < a.n_split; ++s) ws[s] *= inv;
   }
-  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  __syncthreads();
   const int h = g * a.n_rep + rr / a.n_tok;
   const int j = rr % a.n_tok;
   T *op = static_cast<T *>(a.out) + static_cast<long long>(j) * a.out_ld + h * dh;
-  for (int d = threadIdx.x; d < dh; d += blockDim.x) {
-    float acc = 0.f;
+  for (int d = threadIdx.x * 4; d < dh; d += blockDim.x * 4) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < a.n_split; ++s) {
-      const float w = __expf(a.ml_part[(s * rows + idx) * 2] - M);
-      acc += w * a.o_part[(s * rows + idx) * dh + d];
+      const float4 v = *reinterpret_cast<const float4 *>(a.o_part + (s * rows + idx) * dh + d);
+      const float w = ws[s];
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+      acc.z += w * v.z;
+      acc.w += w * v.w;
     }
-    op[d] = from_f32<T>(acc * inv);
+    op[d] = from_f32<T>(acc.x);
+    op[d + 1] = from_f32<T>(acc.y);
+    op[d + 2] = from_f32<T>(acc.z);
+    op[d + 3] = from_f32<T>(acc.w);
+  }
+}
+
+// dst[h][d][col0 + j] = src[h][j][d]: values stored dimension-major (V^T)
+// through a 64 x 64 LDS tile.
+template <typename T>
+__global__ __launch_bounds__(256) void v_transpose_kernel(const T *src, int n, int dh, T *dst, long long dst_hs,
+                                                          int dst_ld, int col0) {
+  __shared__ T tile[64][65];
+  const int h = blockIdx.z;
+  const int j0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
+  const T *s = src + static_cast<long long>(h) * n * dh;
+  T *o = dst + h * dst_hs;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int j = j0 + i, d = d0 + tx;
+    if (j < n && d < dh) tile[i][tx] = s[static_cast<long long>(j) * dh + d];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int d = d0 + i, j = j0 + tx;
+    if (j < n && d < dh) o[static_cast<long long>(d) * dst_ld + col0 + j] = tile[tx][i];
   }
 }
 
@@ -385,11 +502,31 @@ hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((attn_fwd_kernel<T, DH>), dim3(a.Hkv * qblocks, a.n_split), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(a.Hkv * R), dim3(DH < 256 ? DH : 256), 0, s, a, DH);
+  hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(a.Hkv * R), dim3(DH / 4 < 256 ? DH / 4 : 256), 0, s, a, DH);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh, void *dst, long long dst_hs,
+                              int dst_ld, int col0, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid((n + 63) / 64, (dh + 63) / 64, Hkv);
+  if (dtype == DG_BF16)
+    hipLaunchKernelGGL(v_transpose_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t *>(src), n, dh,
+                       static_cast<bf16_t *>(dst), dst_hs, dst_ld, col0);
+  else
+    hipLaunchKernelGGL(v_transpose_kernel<float>, grid, dim3(256), 0, s, static_cast<const float *>(src), n, dh,
+                       static_cast<float *>(dst), dst_hs, dst_ld, col0);
+  return hipGetLastError();
+}
+
+// Workgroups that fill the chip once: one per CU where the double-buffered
+// 512-wide tiles take most of the LDS, two per CU otherwise.
+int attn_target_workgroups(int dtype, int dh) {
+  const int lds = 2 * (kBKV * dh + dh * kBKV) * (dtype == DG_BF16 ? 2 : 4);   // two K + two V^T tiles
+  return lds > 80 * 1024 ? 256 : 512;
+}
 
 int attn_block_rows(int dtype, int dh) {
   if (dtype == DG_BF16) {

@@ -21,6 +21,10 @@ namespace {
 
 constexpr int kBK = 64;  // k elements per LDS stage (two 32-wide MFMA steps)
 
+#ifndef DG_RING_MASKED
+#define DG_RING_MASKED 0
+#endif
+
 template <typename T, int BM, int BN, int NB, int MODE>
 struct GemmTile {
   static constexpr int PAD = 16 / sizeof(T);
@@ -339,9 +343,49 @@ __device__ __forceinline__ void stream_tile(const GemmArgs &a, float *red, int r
 
   const int nsteps = (ke - kb) / 32;
   const int my = nsteps > wave ? (nsteps - wave + 3) / 4 : 0;
+  const int last = my > 0 ? my - 1 : 0;
+
   Frag<T> fa[S][MT];
   Frag<T> fb[S][NB][NT];
 
+#if DG_RING_MASKED
+  // Variant: no branch in the loop body.  Steps past the wave's last one
+  // re-read that last step (in-bounds, cached) and get an all-zero A
+  // fragment at use, so their MFMAs add exactly nothing.
+  auto load = [&](int it, Frag<T>(&xa)[MT], Frag<T>(&xb)[NB][NT]) {
+    const int st = it < last ? it : last;
+    const uint32_t kbyte = static_cast<uint32_t>(kb + (wave + 4 * st) * 32) * sizeof(T);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        xb[nb][nt].load(reinterpret_cast<const T *>((nb == 0 ? B0 : B1) + (bo[nt] + kbyte)));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) xa[mt].load(reinterpret_cast<const T *>(Ab + (ao[mt] + kbyte)));
+  };
+#pragma unroll
+  for (int r = 0; r < S - 1; ++r) load(r, fa[r], fb[r]);
+  for (int i = 0; i < my; i += S) {
+#pragma unroll
+    for (int r = 0; r < S; ++r) {
+      load(i + r + S - 1, fa[(r + S - 1) % S], fb[(r + S - 1) % S]);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t keep = (i + r) < my ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        Frag<T> am = fa[r][mt];
+        am.mask(keep);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) mma(acc[nb][mt][nt], am, fb[r][nb][nt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#else
+  // The prefetch of step it+S-1 and the MFMAs of step it are both skipped
+  // past the wave's last step (wave-uniform branches).
   auto load = [&](int it, Frag<T>(&xa)[MT], Frag<T>(&xb)[NB][NT]) {
     const uint32_t kbyte = static_cast<uint32_t>(kb + (wave + 4 * it) * 32) * sizeof(T);
 #pragma unroll
@@ -352,7 +396,6 @@ __device__ __forceinline__ void stream_tile(const GemmArgs &a, float *red, int r
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) xa[mt].load(reinterpret_cast<const T *>(Ab + (ao[mt] + kbyte)));
   };
-
 #pragma unroll
   for (int r = 0; r < S - 1; ++r)
     if (r < my) load(r, fa[r], fb[r]);
@@ -371,6 +414,7 @@ __device__ __forceinline__ void stream_tile(const GemmArgs &a, float *red, int r
       }
     }
   }
+#endif
 
   // cross-wave reduction: every wave parks its partial tile in LDS, then all
   // 256 threads each add up and store a slice of the tile
@@ -519,14 +563,15 @@ template <typename T>
 hipError_t launch_gemm_stream(const GemmArgs &a, int mode, int mt, int nt, hipStream_t s) {
 #define DG_STREAM_CASE(MT_, NT_, NB_, MODE_, S_) \
   if (mt == MT_ && nt == NT_ && mode == MODE_) return launch_stream_one<T, MT_, NT_, NB_, MODE_, S_>(a, s);
-  DG_STREAM_CASE(4, 4, 1, EPI_STORE, 3)
-  DG_STREAM_CASE(4, 4, 1, EPI_STORE_F32, 3)
-  DG_STREAM_CASE(4, 4, 1, EPI_ADD, 3)
-  DG_STREAM_CASE(4, 4, 1, EPI_PARTIAL_F32, 3)
-  DG_STREAM_CASE(4, 2, 2, EPI_SWIGLU, 3)
-  DG_STREAM_CASE(2, 2, 2, EPI_SWIGLU, 4)
-  DG_STREAM_CASE(2, 4, 1, EPI_ROWSCALE_F32, 4)
-  DG_STREAM_CASE(4, 4, 1, EPI_ROWSCALE_F32, 3)
+  DG_STREAM_CASE(DG_DENSE_MT, DG_DENSE_NT, 1, EPI_STORE, DG_DENSE_S)
+  DG_STREAM_CASE(DG_DENSE_MT, DG_DENSE_NT, 1, EPI_STORE_F32, DG_DENSE_S)
+  DG_STREAM_CASE(DG_DENSE_MT, DG_DENSE_NT, 1, EPI_ADD, DG_DENSE_S)
+  DG_STREAM_CASE(DG_DENSE_MT, DG_DENSE_NT, 1, EPI_PARTIAL_F32, DG_DENSE_S)
+  DG_STREAM_CASE(2, 2, 2, EPI_SWIGLU, 3)
+  DG_STREAM_CASE(DG_MOE_MT, DG_MOE_NT_GU, 2, EPI_SWIGLU, DG_MOE_S)
+  DG_STREAM_CASE(DG_MOE_MT, DG_MOE_NT_DN, 1, EPI_ROWSCALE_F32, DG_MOE_S)
+  DG_STREAM_CASE(4, DG_MOE_NT_GU, 2, EPI_SWIGLU, 3)
+  DG_STREAM_CASE(4, DG_MOE_NT_DN, 1, EPI_ROWSCALE_F32, 3)
 #undef DG_STREAM_CASE
   return hipErrorInvalidValue;
 }

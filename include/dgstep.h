@@ -93,9 +93,15 @@ typedef struct {
   const void *k_norm;    /* [d_h] */
 } dg_attn_w;
 
-/* Committed keys/values of one layer, stored after QK-norm and RoPE at their
- * own positions: k, v are [Hkv][capacity][d_h] in the layer dtype.  Rows
- * [0, kv_len) are valid. */
+/* Keys/values of one layer, stored after QK-norm and RoPE at their own
+ * positions, in the layer dtype:
+ *   k: [Hkv][capacity][d_h]  (position m at row m)
+ *   v: [Hkv][d_h][capacity]  (transposed: position m at column m, so the
+ *                             probability-times-value product reads values
+ *                             key-contiguously)
+ * Positions [0, kv_len) are committed.  Every call places its own n_tok rows
+ * at positions [kv_len, kv_len + n_tok), so capacity must be at least
+ * kv_len + n_tok, and a multiple of 8. */
 typedef struct {
   void *k;
   void *v;
@@ -108,7 +114,8 @@ size_t dg_attn_workspace_bytes(const dg_attn_cfg *cfg, int n_tok);
 
 /* x <- x + Attention(rms(x)) for n_tok tokens at positions kv_len.. .
  * causal = 0 (decode): the canvas attends bidirectionally to the visible
- *   committed rows and to itself; the cache is read only.
+ *   committed rows and to itself; its K/V rows are written at
+ *   [kv_len, kv_len + n_tok) as scratch and kv_len is left unchanged.
  * causal = 1 (encode/commit): key m is visible to the query at position p iff
  *   m <= p (and m > p - window in sliding layers); this call's post-norm/RoPE
  *   K/V rows are written to the cache at [kv_len, kv_len + n_tok) and
@@ -271,7 +278,8 @@ size_t dg_workspace_bytes(const dg_model_cfg *cfg, int max_canvas_tokens, int ma
 
 /* One denoising step: x = E[tokens] + MLP_sc(u); every layer in decode mode
  * (attention then MoE); final norm + tied head; sampler; u <- P.E for the next
- * step.  The KV cache is read only.  No device-to-host transfer. */
+ * step.  Committed rows are only read; cache rows [kv_len, kv_len +
+ * canvas_len) are scratch.  No device-to-host transfer. */
 int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cache *kv,
                    dg_canvas_state *state, const dg_sampler_cfg *scfg, void *ws, size_t ws_bytes,
                    void *stream);
@@ -297,7 +305,9 @@ enum {
   DG_KT_MOE_DOWN = 2,    /* grouped expert down product */
   DG_KT_LM_HEAD = 3,     /* tied-head product */
   DG_KT_ATTN = 4,        /* attention core */
-  DG_KT_SOFT_EMBED = 5   /* P.E product */
+  DG_KT_SOFT_EMBED = 5,  /* P.E product */
+  DG_KT_QKV = 6,         /* fused Q|K|V projection */
+  DG_KT_OPROJ = 7        /* output projection (with its split-K partials) */
 };
 typedef struct {
   void **start;   /* hipEvent_t[capacity] */

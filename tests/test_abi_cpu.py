@@ -57,7 +57,7 @@ def test_attn_validation_codes():
     assert call(_attn_c(), n=-1) == -2
     assert call(_attn_c(), causal=2) == -2
     assert call(_attn_c(), wsb=1024) == -4
-    full = B.KVLayer(ctypes.c_void_p(256), ctypes.c_void_p(256), 2100, 2048)
+    full = B.KVLayer(ctypes.c_void_p(256), ctypes.c_void_p(256), 2104, 2048)
     assert call(_attn_c(), causal=1, kvv=full) == -7
     c = _attn_c()
     c.dtype = 7

@@ -154,11 +154,13 @@ def test_embed_transpose():
 
 
 def run_gpu_attn(cfg, w, ck, cv, P, x, causal):
+    """ck, cv: [Hkv][cap][dh] (the oracle's layout); the device cache holds V
+    transposed.  Returns the device x and the cache with V back in row layout."""
     xd = x.clone().cuda()
-    kd, vd = ck.cuda(), cv.cuda()
-    new_len = B.dg_attn_layer(cfg, cuda(w), kd, vd, P, xd, causal)
+    kd, vtd = ck.cuda(), cv.transpose(1, 2).contiguous().cuda()
+    new_len = B.dg_attn_layer(cfg, cuda(w), kd, vtd, P, xd, causal)
     sync()
-    return xd, kd, vd, new_len
+    return xd, kd, vtd.transpose(1, 2), new_len
 
 
 @pytest.mark.parametrize("layer_type", [0, 1])
@@ -182,7 +184,7 @@ def test_attn_tiny_encode_then_decode(layer_type):
     assert_close(np64(vd)[:, :64], ref_v, "f32", "encode v")
     # decode over the GPU's own cache vs the oracle's own cache
     xd = xc.clone().cuda()
-    B.dg_attn_layer(cfg, cuda(w), kd, vd, 64, xd, 0)
+    B.dg_attn_layer(cfg, cuda(w), kd, vd.transpose(1, 2).contiguous(), 64, xd, 0)
     sync()
     ckr = np.zeros((Hkv, 128, dh))
     cvr = np.zeros((Hkv, 128, dh))
@@ -197,7 +199,8 @@ def test_attn_sliding_bf16(n_tok, P):
     cfg = synth.sliding_cfg()
     g = synth.generator(41)
     w = synth.attn_weights(cfg, g)
-    ck, cv = synth.kv_cache_random(cfg["n_kv_heads"], P, cfg["head_dim"], g, "bf16")
+    cap = (P + n_tok + 7) // 8 * 8          # capacity: a multiple of 8 holding the canvas rows
+    ck, cv = synth.kv_cache_random(cfg["n_kv_heads"], cap, cfg["head_dim"], g, "bf16")
     x = synth.hidden_states(n_tok, cfg["hidden"], g, "bf16")
     xo, _, _, n1 = run_gpu_attn(cfg, w, ck, cv, P, x, 0)
     assert n1 == P
@@ -212,7 +215,7 @@ def test_attn_global_bf16_32k():
     g = synth.generator(43)
     w = synth.attn_weights(cfg, g)
     P = 32768
-    ck, cv = synth.kv_cache_random(cfg["n_kv_heads"], P, cfg["head_dim"], g, "bf16")
+    ck, cv = synth.kv_cache_random(cfg["n_kv_heads"], P + 256, cfg["head_dim"], g, "bf16")
     x = synth.hidden_states(256, cfg["hidden"], g, "bf16")
     xo, _, _, _ = run_gpu_attn(cfg, w, ck, cv, P, x, 0)
     ref, _, _ = O.attn_layer(cfg, npw(w), np64(ck), np64(cv), P, np64(x), 0, "bf16")
@@ -241,7 +244,7 @@ def test_attn_poisoned_out_of_window_rows_are_not_read():
     cfg = synth.sliding_cfg()
     g = synth.generator(49)
     w = synth.attn_weights(cfg, g)
-    ck, cv = synth.kv_cache_random(cfg["n_kv_heads"], 2048, cfg["head_dim"], g, "bf16")
+    ck, cv = synth.kv_cache_random(cfg["n_kv_heads"], 2048 + 256, cfg["head_dim"], g, "bf16")
     x = synth.hidden_states(256, cfg["hidden"], g, "bf16")
     a, _, _, _ = run_gpu_attn(cfg, w, ck, cv, 2048, x, 0)
     ck2, cv2 = ck.clone(), cv.clone()
@@ -343,7 +346,7 @@ def test_tiny_commit_then_two_steps():
     kn, vn = O.commit_canvas(mcfg, wn, rkv, prompt.numpy(), "f32")
     for l in range(L):
         assert_close(np64(kv.k[l])[:, :64], kn[l], "f32", f"commit k[{l}]")
-        assert_close(np64(kv.v[l])[:, :64], vn[l], "f32", f"commit v[{l}]")
+        assert_close(np64(kv.v[l].transpose(1, 2))[:, :64], vn[l], "f32", f"commit v[{l}]")
         rkv["k"][l][:, :64], rkv["v"][l][:, :64] = kn[l], vn[l]
     rkv["kv_len"] = 64
 
