@@ -113,6 +113,51 @@ hipError_t dense_product(int dt, GemmArgs g, int mode, float *part, int ks, hipS
   return reduce(dt, part, ks, g.M, g.N, ldc, C, mode, s);
 }
 
+// The wide-tile bf16 kernel takes operands with 16-byte aligned rows, a depth
+// that is a whole number of its k stages and byte offsets that fit 32 bits
+// (A up to a_rows rows; each weight matrix N x K).
+bool wide_ok(int dt, const GemmArgs &g, int cfg, long long a_rows) {
+  if (dt != DG_BF16) return false;
+  const int kst = wide_kstage(cfg);
+  if (g.K % kst || g.lda % 8 || g.ldb % 8) return false;
+  if (g.g_off && (g.K_x % kst || g.ldb_x % 8)) return false;
+  const long long lim = 1LL << 31;
+  if (a_rows * g.lda * 2 >= lim) return false;
+  const long long nb = g.g_off ? (g.N > g.N_x ? g.N : g.N_x) : g.N;
+  const long long ldb = g.g_off && g.ldb_x > g.ldb ? g.ldb_x : g.ldb;
+  return nb * ldb * 2 < lim;
+}
+
+// Split count of a wide dense product: about one workgroup per compute unit
+// (the 256-row tiles run one workgroup per CU), each split a whole number of
+// k stages; returns the number of non-empty splits.
+int wide_ksplit(const GemmArgs &g, int cfg, int target) {
+  int tiles = ((g.M + wide_bm(cfg) - 1) / wide_bm(cfg)) * ((g.N + wide_bn(cfg) - 1) / wide_bn(cfg));
+  if (tiles < 1) tiles = 1;
+  int ks = target / tiles;   // whole rounds of workgroups: no straggler round
+  const int kst = wide_kstage(cfg);
+  const int steps = g.K / kst;
+  if (ks > steps / 4) ks = steps / 4;   // at least four k stages per split
+  if (ks < 1) ks = 1;
+  if (g.K <= 0) return 1;
+  const int kper = (g.K + ks - 1) / ks;
+  const int kper_r = (kper + kst - 1) / kst * kst;
+  return (g.K + kper_r - 1) / kper_r;
+}
+
+// Wide dense product, through fp32 partials when split.
+hipError_t wide_product(GemmArgs g, int mode, int cfg, float *part, int ks, hipStream_t s) {
+  if (ks <= 1) return launch_gemm_wide(g, mode, cfg, s);
+  void *C = g.C;
+  const long long ldc = g.ldc;
+  g.C = part;
+  g.ldc = g.N;
+  g.k_splits = ks;
+  hipError_t e = launch_gemm_wide(g, EPI_PARTIAL_F32, cfg, s);
+  if (e != hipSuccess) return e;
+  return launch_splitk_reduce<bf16_t>(part, ks, g.M, g.N, ldc, C, mode, s);
+}
+
 // ------------------------------------------------------------ attention
 
 struct AttnPlan {
@@ -388,9 +433,13 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   gu.k_splits = 1;
   gu.C = ws.H;
   gu.ldc = fmax;
+  const long long moe_rows = static_cast<long long>(n) * (k + 1);
+  // the wide-tile kernel measured slower than the streaming one on expert groups
+  const bool wide = DG_WIDE_EXPERTS && rows_per_expert <= 48 && wide_ok(dt, gu, WIDE_EXPERT_GU, n);
   {
     TimedLaunch tl(DG_KT_MOE_GATEUP, s);
-    DG_HIP(sgemm(dt, gu, EPI_SWIGLU, mtile, DG_MOE_NT_GU, s));
+    if (wide) DG_HIP(launch_gemm_wide(gu, EPI_SWIGLU, WIDE_EXPERT_GU, s));
+    else DG_HIP(sgemm(dt, gu, EPI_SWIGLU, mtile, DG_MOE_NT_GU, s));
   }
 
   // down projection, scaled by the routing weight of each row
@@ -416,7 +465,9 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   dn.rowscale = ws.row_weight;
   {
     TimedLaunch tl(DG_KT_MOE_DOWN, s);
-    DG_HIP(sgemm(dt, dn, EPI_ROWSCALE_F32, mtile, DG_MOE_NT_DN, s));
+    if (wide && wide_ok(dt, dn, WIDE_EXPERT_DN, moe_rows))
+      DG_HIP(launch_gemm_wide(dn, EPI_ROWSCALE_F32, WIDE_EXPERT_DN, s));
+    else DG_HIP(sgemm(dt, dn, EPI_ROWSCALE_F32, mtile, DG_MOE_NT_DN, s));
   }
 
   DG_HIP(launch_moe_combine(dt, x, ws.Y, ws.pair_row, n, k, D, c->layer_scalar, s));
@@ -503,7 +554,20 @@ int sample_impl(const dg_sampler_cfg *c, int n, const void *logits, int ldt, int
 
 // ----------------------------------------------------- head, soft embedding
 
-int softembed_ksplit(int n, int D, int V) { return choose_ksplit(n, D, V, 16 * DG_DENSE_MT, 16 * DG_DENSE_NT, 512, 32); }
+struct SoftPlan {
+  bool wide;
+  int ks;
+};
+
+// P.E contracts over the vocabulary: split-K over it, through fp32 partials.
+SoftPlan softembed_plan(int dt, int n, int D, int V) {
+  GemmArgs g = dense_args(nullptr, V, n, D, V, nullptr, D);
+  SoftPlan p;
+  p.wide = wide_ok(dt, g, DG_SOFT_CFG, n);
+  p.ks = p.wide ? wide_ksplit(g, DG_SOFT_CFG, 256)
+                : choose_ksplit(n, D, V, 16 * DG_DENSE_MT, 16 * DG_DENSE_NT, 512, 32);
+  return p;
+}
 
 struct SoftWs {
   void *P;
@@ -513,7 +577,7 @@ struct SoftWs {
 SoftWs soft_carve(int n, int D, int V, int dtype, Carve &cv) {
   SoftWs w;
   w.P = cv.bytes(static_cast<size_t>(n) * V * esize(dtype));
-  const int ks = softembed_ksplit(n, D, V);
+  const int ks = softembed_plan(dtype, n, D, V).ks;
   w.part = ks > 1 ? cv.take<float>(static_cast<size_t>(ks) * n * D) : nullptr;
   return w;
 }
@@ -524,13 +588,14 @@ int soft_embed_impl(const dg_sampler_cfg *sc, int n, int D, int dt, const float 
   const SoftWs ws = soft_carve(n, D, V, dt, cv);
   if (n == 0) return DG_OK;
   DG_HIP(launch_probs(dt, logits, rowstats, n, V, static_cast<float>(1.0 / temperature(sc)), ws.P, s));
-  const int ks = softembed_ksplit(n, D, V);
+  const SoftPlan pl = softembed_plan(dt, n, D, V);
   {
     GemmArgs g = dense_args(ws.P, V, n, D, V, u, D);
     g.seg_B0[0] = embed_t;
     g.tile_order = 1;
     TimedLaunch tl(DG_KT_SOFT_EMBED, s);
-    DG_HIP(dense_product(dt, g, EPI_STORE, ws.part, ks, s));
+    if (pl.wide) DG_HIP(wide_product(g, EPI_STORE, DG_SOFT_CFG, ws.part, pl.ks, s));
+    else DG_HIP(dense_product(dt, g, EPI_STORE, ws.part, pl.ks, s));
   }
   return DG_OK;
 }
@@ -544,7 +609,8 @@ int lm_head_impl(int n, int D, int V, float eps, int dt, const void *x, const vo
   g.seg_B0[0] = E;
   g.tile_order = 0;
   TimedLaunch tl(DG_KT_LM_HEAD, s);
-  DG_HIP(sgemm(dt, g, EPI_STORE_F32, DG_DENSE_MT, DG_DENSE_NT, s));
+  if (wide_ok(dt, g, DG_HEAD_CFG, n)) DG_HIP(launch_gemm_wide(g, EPI_STORE_F32, DG_HEAD_CFG, s));
+  else DG_HIP(sgemm(dt, g, EPI_STORE_F32, DG_DENSE_MT, DG_DENSE_NT, s));
   return DG_OK;
 }
 

@@ -104,6 +104,35 @@ __device__ __forceinline__ f32x4 zero4() {
   return z;
 }
 
+// ------------------------------------------------ row-contiguous fragments
+//
+// A 16-row x 64-deep bf16 block (two 32-wide k slices) loaded with whole
+// 128-byte row segments instead of the fragment order: with lane l = 16g + r,
+// load 0 takes row r%8 and load 1 row 8 + r%8, both at 16-byte chunk
+// 4*(r/8) + g.  Each load then covers 8 full rows (8 cache lines instead of
+// 16 half lines).  Fragment 0 (chunks 0-3) needs row r, chunk g at lane l:
+// lanes r < 8 of load 0 hold it, lanes r >= 8 take load 1 from lane l-8;
+// fragment 1 (chunks 4-7) keeps load 1 in lanes r >= 8 and takes load 0
+// from lane l+8 in lanes r < 8.  Both moves are DPP row shifts by 8 inside
+// each 16-lane row, restricted to half the row by the bank mask.
+
+// lane offsets of the two loads inside a 16-row block: row (r%8) [+8], byte chunk
+__device__ __forceinline__ int contig_row(int lane) { return (lane & 15) & 7; }
+__device__ __forceinline__ int contig_chunk(int lane) { return ((lane & 15) >> 3) * 4 + (lane >> 4); }
+
+__device__ __forceinline__ void contig_to_frags(const bf16x8 &x0, const bf16x8 &x1, bf16x8 &f0, bf16x8 &f1) {
+  int a[4], b[4], o0[4], o1[4];
+  __builtin_memcpy(a, &x0, 16);
+  __builtin_memcpy(b, &x1, 16);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o0[j] = __builtin_amdgcn_update_dpp(a[j], b[j], 0x118 /* row_shr:8 */, 0xF, 0xC, false);
+    o1[j] = __builtin_amdgcn_update_dpp(b[j], a[j], 0x108 /* row_shl:8 */, 0xF, 0x3, false);
+  }
+  __builtin_memcpy(&f0, o0, 16);
+  __builtin_memcpy(&f1, o1, 16);
+}
+
 // ---------------------------------------------------------- wave reductions
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -216,6 +245,9 @@ hipError_t launch_gemm(const GemmArgs &a, int mode, int bm, int bn, hipStream_t 
 #ifndef DG_MOE_NT_DN
 #define DG_MOE_NT_DN 4
 #endif
+#ifndef DG_CONTIG
+#define DG_CONTIG 1
+#endif
 #ifndef DG_MOE_S
 #define DG_MOE_S 4
 #endif
@@ -223,6 +255,41 @@ hipError_t launch_gemm(const GemmArgs &a, int mode, int bm, int bn, hipStream_t 
 // streaming variant: tile (16*mt) x (16*nt), waves split k (K per split a multiple of 32)
 template <typename T>
 hipError_t launch_gemm_stream(const GemmArgs &a, int mode, int mt, int nt, hipStream_t s);
+// Wide-tile bf16 products (A shared through LDS by the workgroup's waves).
+enum WideCfg {
+  WIDE_ROWS256_N256 = 0,  // 256 x 256 tile, 8 waves x 32 columns
+  WIDE_ROWS256_N128 = 1,  // 256 x 128 tile, 8 waves x 16 columns
+  WIDE_EXPERT_GU = 2,     // expert gate/up: 16*DG_WMOE_MT rows x 64 columns (x2 matrices), 4 waves
+  WIDE_EXPERT_DN = 3,     // expert down: 16*DG_WMOE_MT rows x 128 columns, 4 waves
+  // every configuration walks k in stages of 64
+};
+#ifndef DG_WIDE_P
+#define DG_WIDE_P 3
+#endif
+#ifndef DG_WIDE256_P
+#define DG_WIDE256_P 2
+#endif
+#ifndef DG_HEAD_CFG
+#define DG_HEAD_CFG WIDE_ROWS256_N256
+#endif
+#ifndef DG_SOFT_CFG
+#define DG_SOFT_CFG WIDE_ROWS256_N256
+#endif
+#ifndef DG_WIDE_EXPERTS
+#define DG_WIDE_EXPERTS 0
+#endif
+#ifndef DG_WMOE_MT
+#define DG_WMOE_MT 2
+#endif
+#ifndef DG_WMOE_P
+#define DG_WMOE_P 3
+#endif
+// column tile width and k-stage depth of each wide configuration
+inline int wide_bn(int cfg) { return cfg == WIDE_ROWS256_N256 ? 256 : (cfg == WIDE_EXPERT_GU ? 64 : 128); }
+inline int wide_bm(int cfg) { return cfg <= WIDE_ROWS256_N128 ? 256 : 16 * DG_WMOE_MT; }
+inline int wide_kstage(int) { return 64; }
+hipError_t launch_gemm_wide(const GemmArgs &a, int mode, int cfg, hipStream_t s);
+
 template <typename T>
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, long long ldc,
                                 void *C, int mode, hipStream_t s);

@@ -464,7 +464,161 @@ __device__ __forceinline__ void stream_tile(const GemmArgs &a, float *red, int r
   }
 }
 
-template <typename T, int MT, int NT, int NB, int MODE, int S>
+// bf16 form with row-contiguous loads: 64-deep k stages (wave w takes
+// stages w, w+4, ...), each 16-row block of A and B fetched as two loads of
+// 8 whole rows and turned into the two fragments of the stage with DPP row
+// shifts (contig_to_frags).  Same ring, same epilogue as stream_tile.
+template <int MT, int NT, int NB, int MODE, int S>
+__device__ __forceinline__ void stream_tile_c(const GemmArgs &a, float *red, int row_begin, int rows,
+                                              const bf16_t *const *Bp, int n0, int ncols, int kb, int ke,
+                                              int split) {
+  constexpr int EL = NB * MT * NT * 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cr = contig_row(lane), cc = contig_chunk(lane);
+
+  // rows past `rows` / columns past `ncols` are clamped onto row 0 of the
+  // tile (loaded, never stored), as in stream_tile
+  uint32_t ao[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = mt * 16 + h * 8 + cr;
+      int pr = row_begin + (r < rows ? r : 0);
+      if (a.a_rows) pr = a.a_rows[pr];
+      ao[mt][h] = (static_cast<uint32_t>(pr) * static_cast<uint32_t>(a.lda) + cc * 8) * 2u;
+    }
+  uint32_t bo[NT][2];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = nt * 16 + h * 8 + cr;
+      bo[nt][h] = (static_cast<uint32_t>(c < ncols ? c : 0) * static_cast<uint32_t>(a.ldb) + cc * 8) * 2u;
+    }
+  const char *Ab = static_cast<const char *>(a.A);
+  const char *B0 = reinterpret_cast<const char *>(Bp[0]);
+  const char *B1 = reinterpret_cast<const char *>(Bp[NB - 1]);
+
+  f32x4 acc[NB][MT][NT];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nb][mt][nt] = zero4();
+
+  const int nsteps = (ke - kb) / 64;
+  const int my = nsteps > wave ? (nsteps - wave + 3) / 4 : 0;
+
+  bf16x8 xa[S][MT][2];
+  bf16x8 xb[S][NB][NT][2];
+  auto load = [&](int it, bf16x8(&ya)[MT][2], bf16x8(&yb)[NB][NT][2]) {
+    const uint32_t kbyte = static_cast<uint32_t>(kb + (wave + 4 * it) * 64) * 2u;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          yb[nb][nt][h] = *reinterpret_cast<const bf16x8 *>((nb == 0 ? B0 : B1) + (bo[nt][h] + kbyte));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) ya[mt][h] = *reinterpret_cast<const bf16x8 *>(Ab + (ao[mt][h] + kbyte));
+  };
+  auto compute = [&](const bf16x8(&ya)[MT][2], const bf16x8(&yb)[NB][NT][2]) {
+    Frag<bf16_t> fb[NB][NT][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) contig_to_frags(yb[nb][nt][0], yb[nb][nt][1], fb[nb][nt][0].v, fb[nb][nt][1].v);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      Frag<bf16_t> fa[2];
+      contig_to_frags(ya[mt][0], ya[mt][1], fa[0].v, fa[1].v);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) mma(acc[nb][mt][nt], fa[ks], fb[nb][nt][ks]);
+    }
+  };
+#pragma unroll
+  for (int r = 0; r < S - 1; ++r)
+    if (r < my) load(r, xa[r], xb[r]);
+  for (int i = 0; i < my; i += S) {
+#pragma unroll
+    for (int r = 0; r < S; ++r) {
+      const int it = i + r;
+      if (it < my) {
+        if (it + S - 1 < my) load(it + S - 1, xa[(r + S - 1) % S], xb[(r + S - 1) % S]);
+        compute(xa[r], xb[r]);
+      }
+    }
+  }
+
+  __syncthreads();   // LDS may still be read by the previous tile's epilogue
+  {
+    float *dst = red + wave * EL * 64;
+    int e = 0;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i, ++e) dst[e * 64 + lane] = acc[nb][mt][nt][i];
+  }
+  __syncthreads();
+  constexpr int EH = EL / NB;
+  for (int q = tid; q < EH * 64; q += 256) {
+    const int ln = q & 63, e = q >> 6;
+    const int i = e & 3, nt = (e >> 2) % NT, mt = (e >> 2) / NT;
+    const int r = mt * 16 + (ln >> 4) * 4 + i;
+    const int c = nt * 16 + (ln & 15);
+    if (r >= rows || c >= ncols) continue;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v += red[(w * EL + e) * 64 + ln];
+    const long long row = row_begin + r;
+    const int col = n0 + c;
+    if constexpr (MODE == EPI_STORE) {
+      static_cast<bf16_t *>(a.C)[row * a.ldc + col] = f32_to_bf16(v);
+    } else if constexpr (MODE == EPI_STORE_F32) {
+      static_cast<float *>(a.C)[row * a.ldc + col] = v;
+    } else if constexpr (MODE == EPI_ADD) {
+      bf16_t *cp = static_cast<bf16_t *>(a.C) + row * a.ldc + col;
+      *cp = f32_to_bf16(bf16_to_f32(*cp) + v);
+    } else if constexpr (MODE == EPI_SWIGLU) {
+      float u = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) u += red[(w * EL + EH + e) * 64 + ln];
+      static_cast<bf16_t *>(a.C)[row * a.ldc + col] = f32_to_bf16(silu_f(v) * u);
+    } else if constexpr (MODE == EPI_ROWSCALE_F32) {
+      static_cast<float *>(a.C)[row * a.ldc + col] = v * a.rowscale[row];
+    } else if constexpr (MODE == EPI_PARTIAL_F32) {
+      static_cast<float *>(a.C)[(static_cast<long long>(split) * a.M + row) * a.ldc + col] = v;
+    }
+  }
+}
+
+// Tile body of the streaming kernel: the row-contiguous bf16 form when every
+// k range of the launch is a whole number of 64-deep stages (CONTIG).
+template <typename T, int MT, int NT, int NB, int MODE, int S, bool CONTIG>
+__device__ __forceinline__ void stream_any(const GemmArgs &a, float *red, int row_begin, int rows,
+                                           const T *const *Bp, int n0, int ncols, int kb, int ke, int split) {
+  if constexpr (CONTIG && sizeof(T) == 2)
+    stream_tile_c<MT, NT, NB, MODE, (S + 1) / 2>(a, red, row_begin, rows, reinterpret_cast<const bf16_t *const *>(Bp),
+                                                 n0, ncols, kb, ke, split);
+  else
+    stream_tile<T, MT, NT, NB, MODE, S>(a, red, row_begin, rows, Bp, n0, ncols, kb, ke, split);
+}
+
+template <typename T, int MT, int NT, int NB, int MODE, int S, bool CONTIG>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmArgs a) {
   constexpr int BM = MT * 16, BN = NT * 16;
   __shared__ __attribute__((aligned(16))) float red[4 * NB * MT * NT * 4 * 64];
@@ -497,8 +651,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmArgs a) {
     if (NB > 1) Bp[NB - 1] = static_cast<const T *>(a.seg_B1[s]) + static_cast<long long>(n0 - a.seg_start[s]) * a.ldb;
     const int kper = a.K / a.k_splits;
     const int row0 = m_tile * BM;
-    stream_tile<T, MT, NT, NB, MODE, S>(a, red, row0, min(BM, a.M - row0), Bp, n0, a.seg_start[s + 1] - n0,
-                                        split * kper, (split + 1) * kper, split);
+    stream_any<T, MT, NT, NB, MODE, S, CONTIG>(a, red, row0, min(BM, a.M - row0), Bp, n0, a.seg_start[s + 1] - n0,
+                                               split * kper, (split + 1) * kper, split);
   } else {
     const int g = blockIdx.y;
     const int n0 = blockIdx.x * BN;
@@ -518,7 +672,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmArgs a) {
     }
     const int r0 = a.g_off[g], r1 = a.g_off[g + 1];
     for (int rb = r0; rb < r1; rb += BM)
-      stream_tile<T, MT, NT, NB, MODE, S>(ga, red, rb, min(BM, r1 - rb), Bp, n0, Ng - n0, 0, ga.K, 0);
+      stream_any<T, MT, NT, NB, MODE, S, CONTIG>(ga, red, rb, min(BM, r1 - rb), Bp, n0, Ng - n0, 0, ga.K, 0);
   }
 }
 
@@ -534,7 +688,274 @@ hipError_t launch_stream_one(const GemmArgs &a, hipStream_t s) {
     grid = dim3(mt * nt * a.k_splits, 1);
   }
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_stream_kernel<T, MT, NT, NB, MODE, S>), grid, dim3(256), 0, s, a);
+  // row-contiguous bf16 form when every k range is whole 64-deep stages
+  const bool contig = DG_CONTIG && sizeof(T) == 2 &&
+                      (a.g_off ? (a.K % 64 == 0 && a.K_x % 64 == 0) : ((a.K / a.k_splits) % 64 == 0));
+  if (contig)
+    hipLaunchKernelGGL((gemm_stream_kernel<T, MT, NT, NB, MODE, S, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_stream_kernel<T, MT, NT, NB, MODE, S, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// Wide-tile variant (bfloat16) for products whose activation operand is
+// re-read by many weight tiles: the 256-row canvas products (LM head, the
+// soft embedding P.E, projections) and the expert products.  A workgroup of
+// NW waves owns a (16*MT) x (NW*NTW*16) output tile and walks k in stages of
+// 64.  The A slice of a stage is fetched once per workgroup with row-
+// contiguous loads (8 rows x 128 bytes per wave instruction: whole cache
+// lines, the cheap pattern for the load units) and written to an LDS tile,
+// where every wave reads its MFMA fragments.  Each wave streams its own
+// weight rows (B) with the same row-contiguous loads, P stages ahead, and
+// turns them into fragments through a private LDS region (no barrier).
+//
+// Order inside stage it: load A(it+1) into registers, then issue B(it+P), run
+// the MFMAs of stage it, write A(it+1) to the other LDS buffer, barrier.  A is
+// issued before B, so waiting for A never waits for the younger B loads; the
+// barrier waits only for LDS traffic (lgkmcnt), leaving the B loads in flight.
+//
+// LDS tile: BM rows x 128 bytes; 16-byte chunk c of row r sits at chunk
+// c ^ ((r >> 1) & 7), which keeps both the row-contiguous writes and the
+// 16-row fragment reads free of bank conflicts.
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int MT, int NTW, int NB, int NW, int KSUB, int P, int MODE>
+__device__ __forceinline__ void wide_tile(const GemmArgs &a, bf16_t *lds, bf16_t *ldsb, int row_begin, int rows,
+                                          const bf16_t *const *Bp, int n0, int ncols, int kb, int ke,
+                                          int split) {
+  static_assert(KSUB == 2, "stages are 64 deep (128 bytes per A row)");
+  constexpr int BM = MT * 16;
+  constexpr int D = BM / 8 / NW;         // A load instructions per wave per stage
+  static_assert(D * 8 * NW == BM, "A rows must split evenly over the waves");
+  constexpr int DB = NTW * 2;            // B load instructions per weight matrix per stage
+  constexpr int R = P + 1;               // B ring slots
+  constexpr int STAGE = BM * 64;         // bf16 elements per LDS buffer of A
+  constexpr int WB = NB * NTW * 16 * 64; // bf16 elements of one wave's B region
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int lr = lane >> 3, lc = lane & 7;   // row-contiguous pattern: 8 rows x 8 chunks
+
+  // A: instruction j of this wave covers rows 8*(wave + NW*j) + lane/8, chunk lane%8
+  uint32_t ao[D];
+  int aw[D];   // LDS element offset of this lane's chunk
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    const int r = (wave + NW * j) * 8 + lr;
+    int pr = row_begin + (r < rows ? r : 0);
+    if (a.a_rows) pr = a.a_rows[pr];
+    ao[j] = (static_cast<uint32_t>(pr) * static_cast<uint32_t>(a.lda) + lc * 8) * 2u;
+    aw[j] = r * 64 + ((lc ^ ((r >> 1) & 7)) * 8);
+  }
+  // fragment read offsets inside a swizzled 16-row block (A and B alike)
+  int fo[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) fo[ks] = l16 * 64 + (((4 * ks + lg) ^ (l16 >> 1)) * 8);
+  // B: the wave's NTW*16 weight rows, 8 per instruction, columns past ncols
+  // re-read column 0 of the tile
+  uint32_t bo[DB];
+  int bw[DB];
+#pragma unroll
+  for (int j = 0; j < DB; ++j) {
+    const int r = j * 8 + lr;                       // row inside the wave's block
+    const int c = wave * (NTW * 16) + r;
+    bo[j] = (static_cast<uint32_t>(c < ncols ? c : 0) * static_cast<uint32_t>(a.ldb) + lc * 8) * 2u;
+    bw[j] = r * 64 + ((lc ^ ((r >> 1) & 7)) * 8);
+  }
+  bf16_t *myb = ldsb + wave * WB;
+  const char *Ab = static_cast<const char *>(a.A);
+  const char *Bb[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) Bb[nb] = reinterpret_cast<const char *>(Bp[nb]);
+
+  f32x4 acc[NB][MT][NTW];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) acc[nb][mi][nt] = zero4();
+
+  Frag<bf16_t> ra[D];                    // native vectors: must stay in registers
+  Frag<bf16_t> rb[R][NB][DB];
+
+  auto load_a = [&](int st) {
+    const uint32_t kbyte = static_cast<uint32_t>(kb + st * 64) * 2u;
+#pragma unroll
+    for (int j = 0; j < D; ++j) ra[j].load(reinterpret_cast<const bf16_t *>(Ab + (ao[j] + kbyte)));
+  };
+  auto load_b = [&](int st, Frag<bf16_t>(&xb)[NB][DB]) {
+    const uint32_t kbyte = static_cast<uint32_t>(kb + st * 64) * 2u;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < DB; ++j) xb[nb][j].load(reinterpret_cast<const bf16_t *>(Bb[nb] + (bo[j] + kbyte)));
+  };
+  auto stage_a = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) *reinterpret_cast<bf16x8 *>(lds + buf * STAGE + aw[j]) = ra[j].v;
+  };
+  auto compute = [&](int buf, const Frag<bf16_t>(&xb)[NB][DB]) {
+    // this wave's B slice: rows to its own LDS region, back as fragments
+    // (wave-local: LDS operations of one wave complete in order)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < DB; ++j) *reinterpret_cast<bf16x8 *>(myb + nb * (NTW * 16 * 64) + bw[j]) = xb[nb][j].v;
+    Frag<bf16_t> fb[NB][NTW][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) fb[nb][nt][ks].load(myb + nb * (NTW * 16 * 64) + nt * 16 * 64 + fo[ks]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+        Frag<bf16_t> fa;
+        fa.load(lds + buf * STAGE + mi * 16 * 64 + fo[ks]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) mma(acc[nb][mi][nt], fa, fb[nb][nt][ks]);
+      }
+  };
+
+  // No memory operation of the loop body sits under a branch, so the
+  // compiler's count of loads in flight stays exact: stages past the last
+  // re-load the last one (in bounds) and only their MFMAs are skipped.
+  const int nst = (ke - kb) / 64;
+  const int lastst = nst > 0 ? nst - 1 : 0;
+  if (nst > 0) {
+    load_a(0);
+#pragma unroll
+    for (int r = 0; r < P; ++r) load_b(r < lastst ? r : lastst, rb[r]);
+    stage_a(0);
+  }
+  lds_barrier();
+  for (int i = 0; i < nst; i += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int it = i + r;
+      load_a(it + 1 < lastst ? it + 1 : lastst);
+      load_b(it + P < lastst ? it + P : lastst, rb[(r + P) % R]);
+      if (it < nst) compute(it & 1, rb[r]);
+      stage_a((it + 1) & 1);
+      lds_barrier();
+    }
+  }
+
+  // epilogue straight from the accumulators: lane holds rows 4*lg+i, column l16
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int c = wave * (NTW * 16) + nt * 16 + l16;
+    if (c >= ncols) continue;
+    const int col = n0 + c;
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mi * 16 + lg * 4 + i;
+        if (r >= rows) continue;
+        const long long row = row_begin + r;
+        const float v = acc[0][mi][nt][i];
+        if constexpr (MODE == EPI_STORE) {
+          static_cast<bf16_t *>(a.C)[row * a.ldc + col] = f32_to_bf16(v);
+        } else if constexpr (MODE == EPI_STORE_F32) {
+          static_cast<float *>(a.C)[row * a.ldc + col] = v;
+        } else if constexpr (MODE == EPI_ADD) {
+          bf16_t *cp = static_cast<bf16_t *>(a.C) + row * a.ldc + col;
+          *cp = f32_to_bf16(bf16_to_f32(*cp) + v);
+        } else if constexpr (MODE == EPI_SWIGLU) {
+          static_cast<bf16_t *>(a.C)[row * a.ldc + col] = f32_to_bf16(silu_f(v) * acc[NB - 1][mi][nt][i]);
+        } else if constexpr (MODE == EPI_ROWSCALE_F32) {
+          static_cast<float *>(a.C)[row * a.ldc + col] = v * a.rowscale[row];
+        } else if constexpr (MODE == EPI_PARTIAL_F32) {
+          static_cast<float *>(a.C)[(static_cast<long long>(split) * a.M + row) * a.ldc + col] = v;
+        }
+      }
+  }
+}
+
+template <int MT, int NTW, int NB, int NW, int KSUB, int P, int MODE>
+__global__ __launch_bounds__(64 * NW) void gemm_wide_kernel(const GemmArgs a) {
+  constexpr int BM = MT * 16, BN = NW * NTW * 16, KS = 64;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * MT * 16 * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t ldsb[NW * NB * NTW * 16 * 64];
+  if (a.g_off == nullptr) {
+    int L = blockIdx.x;
+    const int total = gridDim.x;
+    if ((total & 7) == 0) {
+      const int per = total >> 3;
+      L = (L & 7) * per + (L >> 3);
+    }
+    const int m_tiles = (a.M + BM - 1) / BM;
+    const int n_tiles = (a.N + BN - 1) / BN;
+    int m_tile, n_tile, split;
+    if (a.tile_order == 0) {
+      m_tile = L % m_tiles;
+      const int r = L / m_tiles;
+      n_tile = r % n_tiles;
+      split = r / n_tiles;
+    } else {
+      n_tile = L % n_tiles;
+      const int r = L / n_tiles;
+      m_tile = r % m_tiles;
+      split = r / m_tiles;
+    }
+    const int n0 = n_tile * BN;
+    int s = 0;
+    while (s + 1 < a.nseg && n0 >= a.seg_start[s + 1]) ++s;
+    const bf16_t *Bp[NB];
+    Bp[0] = static_cast<const bf16_t *>(a.seg_B0[s]) + static_cast<long long>(n0 - a.seg_start[s]) * a.ldb;
+    if (NB > 1)
+      Bp[NB - 1] = static_cast<const bf16_t *>(a.seg_B1[s]) + static_cast<long long>(n0 - a.seg_start[s]) * a.ldb;
+    // split s covers [s*kper, min(K, (s+1)*kper)), kper a multiple of the stage depth
+    const int kper = ((a.K + a.k_splits - 1) / a.k_splits + KS - 1) / KS * KS;
+    const int kb = split * kper, ke = min(a.K, kb + kper);
+    const int row0 = m_tile * BM;
+    wide_tile<MT, NTW, NB, NW, KSUB, P, MODE>(a, lds, ldsb, row0, min(BM, a.M - row0), Bp, n0,
+                                              min(BN, a.seg_start[s + 1] - n0), kb, ke > kb ? ke : kb, split);
+  } else {
+    const int g = blockIdx.y;
+    const int n0 = blockIdx.x * BN;
+    const int Ng = (g == 0) ? a.N_x : a.N;
+    if (n0 >= Ng) return;
+    const bf16_t *Bp[NB];
+    GemmArgs ga = a;
+    if (g == 0) {
+      ga.K = a.K_x;
+      ga.ldb = a.ldb_x;
+      Bp[0] = static_cast<const bf16_t *>(a.Bx0) + static_cast<long long>(n0) * a.ldb_x;
+      if (NB > 1) Bp[NB - 1] = static_cast<const bf16_t *>(a.Bx1) + static_cast<long long>(n0) * a.ldb_x;
+    } else {
+      const long long off = static_cast<long long>(g - 1) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
+      Bp[0] = static_cast<const bf16_t *>(a.seg_B0[0]) + off;
+      if (NB > 1) Bp[NB - 1] = static_cast<const bf16_t *>(a.seg_B1[0]) + off;
+    }
+    const int r0 = a.g_off[g], r1 = a.g_off[g + 1];
+    for (int rb = r0; rb < r1; rb += BM)
+      wide_tile<MT, NTW, NB, NW, KSUB, P, MODE>(ga, lds, ldsb, rb, min(BM, r1 - rb), Bp, n0, min(BN, Ng - n0), 0,
+                                                ga.K, 0);
+  }
+}
+
+template <int MT, int NTW, int NB, int NW, int KSUB, int P, int MODE>
+hipError_t launch_wide_one(const GemmArgs &a, hipStream_t s) {
+  constexpr int BM = MT * 16, BN = NW * NTW * 16;
+  dim3 grid;
+  if (a.g_off) {
+    const int nmax = a.N > a.N_x ? a.N : a.N_x;
+    grid = dim3((nmax + BN - 1) / BN, a.n_groups);
+  } else {
+    const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
+    grid = dim3(mt * nt * a.k_splits, 1);
+  }
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_wide_kernel<MT, NTW, NB, NW, KSUB, P, MODE>), grid, dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -573,6 +994,23 @@ hipError_t launch_gemm_stream(const GemmArgs &a, int mode, int mt, int nt, hipSt
   DG_STREAM_CASE(4, DG_MOE_NT_GU, 2, EPI_SWIGLU, 3)
   DG_STREAM_CASE(4, DG_MOE_NT_DN, 1, EPI_ROWSCALE_F32, 3)
 #undef DG_STREAM_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_wide(const GemmArgs &a, int mode, int cfg, hipStream_t s) {
+#define DG_WIDE_CASE(CFG_, MT_, NTW_, NB_, NW_, KSUB_, P_, MODE_) \
+  if (cfg == CFG_ && mode == MODE_) return launch_wide_one<MT_, NTW_, NB_, NW_, KSUB_, P_, MODE_>(a, s);
+  DG_WIDE_CASE(WIDE_ROWS256_N256, 16, 2, 1, 8, 2, DG_WIDE256_P, EPI_STORE_F32)
+  DG_WIDE_CASE(WIDE_ROWS256_N256, 16, 2, 1, 8, 2, DG_WIDE256_P, EPI_PARTIAL_F32)
+  DG_WIDE_CASE(WIDE_ROWS256_N256, 16, 2, 1, 8, 2, DG_WIDE256_P, EPI_STORE)
+  DG_WIDE_CASE(WIDE_ROWS256_N256, 16, 2, 1, 8, 2, DG_WIDE256_P, EPI_ADD)
+  DG_WIDE_CASE(WIDE_ROWS256_N128, 16, 1, 1, 8, 2, DG_WIDE_P, EPI_STORE)
+  DG_WIDE_CASE(WIDE_ROWS256_N128, 16, 1, 1, 8, 2, DG_WIDE_P, EPI_PARTIAL_F32)
+  DG_WIDE_CASE(WIDE_ROWS256_N128, 16, 1, 1, 8, 2, DG_WIDE_P, EPI_STORE_F32)
+  DG_WIDE_CASE(WIDE_ROWS256_N128, 16, 1, 1, 8, 2, DG_WIDE_P, EPI_ADD)
+  DG_WIDE_CASE(WIDE_EXPERT_GU, DG_WMOE_MT, 1, 2, 4, 2, DG_WMOE_P, EPI_SWIGLU)
+  DG_WIDE_CASE(WIDE_EXPERT_DN, DG_WMOE_MT, 2, 1, 4, 2, DG_WMOE_P, EPI_ROWSCALE_F32)
+#undef DG_WIDE_CASE
   return hipErrorInvalidValue;
 }
 

@@ -74,26 +74,32 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *logits, i
   }
 }
 
-// Single wave: counts, scan, then a stable scatter.  Within a 64-pair chunk
-// a pair's rank among the pairs of the same expert comes from ballots over
-// the bits of the expert id; chunks are walked in order, so rows of an
-// expert are sorted by (token, slot).  Integer work only: bit-exact.
-__global__ __launch_bounds__(64) void moe_permute_kernel(const int32_t *idx, const float *w, int n_tok, int k,
-                                                         int E, int *g_off, int *row_token, float *row_weight,
-                                                         int *pair_row) {
+// One workgroup: counts (LDS integer atomics, all threads), exclusive scan,
+// then a stable scatter.  The pairs are staged in LDS in chunks; one wave
+// walks each chunk 64 pairs at a time in order, ranking a pair among the
+// pairs of the same expert in its 64 with ballots over the bits of the
+// expert id, so rows of an expert come out sorted by (token, slot).
+// Integer work only: bit-exact and independent of scheduling.
+constexpr int kPermChunk = 4096;
+
+__global__ __launch_bounds__(256) void moe_permute_kernel(const int32_t *idx, const float *w, int n_tok, int k,
+                                                          int E, int *g_off, int *row_token, float *row_weight,
+                                                          int *pair_row) {
   __shared__ int cnt[258];
   __shared__ int cur[258];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < E + 2; e += 64) cnt[e] = 0;
+  __shared__ int s_e[kPermChunk];
+  __shared__ float s_w[kPermChunk];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E + 2; e += 256) cnt[e] = 0;
   __syncthreads();
   const int n_pairs = n_tok * k;
-  for (int p = lane; p < n_pairs; p += 64) {
+  for (int p = tid; p < n_pairs; p += 256) {
     int e = idx[p];
     e = e < 0 ? 0 : (e >= E ? E - 1 : e);
     atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  if (lane == 0) {
+  if (tid == 0) {
     int acc = n_tok;
     g_off[0] = 0;
     g_off[1] = n_tok;
@@ -103,37 +109,43 @@ __global__ __launch_bounds__(64) void moe_permute_kernel(const int32_t *idx, con
       g_off[e + 2] = acc;
     }
   }
-  __syncthreads();
-  for (int t = lane; t < n_tok; t += 64) {
+  for (int t = tid; t < n_tok; t += 256) {
     row_token[t] = t;
     row_weight[t] = 1.0f;
   }
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < n_pairs; base += 64) {
-    const int p = base + lane;
-    const bool valid = p < n_pairs;
-    int e = valid ? idx[p] : -1;
-    if (valid) e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-    const unsigned key = static_cast<unsigned>(e + 1);  // 0 = no pair
-    uint64_t peers = __ballot(1);
-#pragma unroll
-    for (int b = 0; b < 9; ++b) {
-      const bool bit = (key >> b) & 1u;
-      const uint64_t m = __ballot(bit);
-      peers &= bit ? m : ~m;
+  for (int base = 0; base < n_pairs; base += kPermChunk) {
+    const int len = min(kPermChunk, n_pairs - base);
+    __syncthreads();   // previous chunk consumed; scan visible
+    for (int p = tid; p < len; p += 256) {
+      int e = idx[base + p];
+      s_e[p] = e < 0 ? 0 : (e >= E ? E - 1 : e);
+      s_w[p] = w[base + p];
     }
-    int basev = 0;
-    if (valid) basev = cur[e];
-    const int rank = __popcll(peers & lt_mask);
-    const bool leader = valid && rank == 0;
     __syncthreads();
-    if (leader) cur[e] = basev + __popcll(peers);
-    __syncthreads();
-    if (valid) {
-      const int row = basev + rank;
-      row_token[row] = p / k;
-      row_weight[row] = w[p];
-      pair_row[p] = row;
+    if (wave != 0) continue;
+    for (int b = 0; b < len; b += 64) {
+      const int q = b + lane;
+      const bool valid = q < len;
+      const int e = valid ? s_e[q] : -1;
+      const unsigned key = static_cast<unsigned>(e + 1);  // 0 = no pair
+      uint64_t peers = __ballot(1);
+#pragma unroll
+      for (int bit = 0; bit < 9; ++bit) {
+        const bool on = (key >> bit) & 1u;
+        const uint64_t m = __ballot(on);
+        peers &= on ? m : ~m;
+      }
+      const int rank = __popcll(peers & lt_mask);
+      const int start = valid ? cur[e] : 0;   // all lanes read before the leaders write
+      if (valid && rank == 0) cur[e] = start + __popcll(peers);
+      if (valid) {
+        const int p = base + q;
+        const int row = start + rank;
+        row_token[row] = p / k;
+        row_weight[row] = s_w[q];
+        pair_row[p] = row;
+      }
     }
   }
 }
@@ -173,7 +185,7 @@ hipError_t launch_router_topk(const float *logits, int n_tok, int E, int k, floa
 
 hipError_t launch_moe_permute(const int32_t *idx, const float *w, int n_tok, int k, int E, int *g_off,
                               int *row_token, float *row_weight, int *pair_row, hipStream_t s) {
-  hipLaunchKernelGGL(moe_permute_kernel, dim3(1), dim3(64), 0, s, idx, w, n_tok, k, E, g_off, row_token,
+  hipLaunchKernelGGL(moe_permute_kernel, dim3(1), dim3(256), 0, s, idx, w, n_tok, k, E, g_off, row_token,
                      row_weight, pair_row);
   return hipGetLastError();
 }

@@ -111,7 +111,7 @@ def test_canvas_noise():
 
 
 @pytest.mark.parametrize("dtype,n,D,V", [("f32", 32, 256, 4096), ("bf16", 45, 256, 4096),
-                                         ("bf16", 256, 2816, 262144)])
+                                         ("bf16", 45, 320, 4040), ("bf16", 256, 2816, 262144)])
 def test_lm_head(dtype, n, D, V):
     g = synth.generator(21)
     E = synth.embed_table(V, D, g, dtype)
@@ -125,7 +125,8 @@ def test_lm_head(dtype, n, D, V):
     assert_close(lg.cpu().numpy()[:, cols], ref, "f32" if dtype == "f32" else "bf16", "logits")
 
 
-@pytest.mark.parametrize("dtype,n,D,V", [("f32", 32, 256, 4096), ("bf16", 256, 2816, 262144)])
+@pytest.mark.parametrize("dtype,n,D,V", [("f32", 32, 256, 4096), ("bf16", 45, 320, 8000),
+                                         ("bf16", 256, 2816, 262144)])
 def test_soft_embed(dtype, n, D, V):
     g = synth.generator(31)
     E = synth.embed_table(V, D, g, dtype)
@@ -292,6 +293,23 @@ def test_moe_bf16_full_injected():
     assert rel_err(wts.cpu().numpy(), rw) < 1e-5
     assert_close(np64(xd), ref, "bf16", "moe x")
     assert_delta_close(np64(xd), ref, np64(x), "bf16", "moe delta")
+
+
+def test_moe_bf16_ragged_groups():
+    """45 tokens over 16 experts (top-4): short groups, ragged column tiles
+    (ffn 192, shared 128, hidden 320)."""
+    cfg = synth.moe_cfg(320, 16, 4, 192, 128, dtype="bf16")
+    g = synth.generator(57)
+    w = synth.moe_weights(cfg, g)
+    x = synth.hidden_states(45, 320, g, "bf16")
+    rl = synth.router_logits(45, 16, g)
+    xd = x.clone().cuda()
+    idx, _ = B.dg_moe_block(cfg, cuda(w), xd, rl.cuda(), want_topk=True)
+    sync()
+    ref, ridx, _, _ = O.moe_block_grouped(cfg, npw(w), np64(x), "bf16", router_logits=np64(rl))
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    assert_close(np64(xd), ref, "bf16", "moe x")
+    assert_delta_close(np64(xd), ref, np64(x), "bf16", "moe ragged delta")
 
 
 def test_moe_bf16_prefill_rows():
