@@ -105,6 +105,8 @@ def main():
     ap.add_argument("--canvases", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-generate", action="store_true", help="skip the adaptive-stop generation run")
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="only run the counter workload (copy calibration + MoE layer) for rocprofv3 --pmc")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -114,6 +116,11 @@ def main():
 
     import torch
 
+    from discrete_text_diffusion_step_amd import profiling
+    if args.pmc_workload:
+        torch.cuda.set_device(0)
+        profiling.pmc_workload()
+        return
     from discrete_text_diffusion_step_amd import binding as B
     from discrete_text_diffusion_step_amd import synth
     from discrete_text_diffusion_step_amd.generate import generate
@@ -198,7 +205,7 @@ def main():
     achieved = bytes_launch / (avg_ms * 1e-3) / 1e9
     roof = {"kernel": "moe expert gate/up (grouped MFMA GEMM + SwiGLU)", "bound": "hbm",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiling.read_traffic(),
             "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": bytes_launch, "launches": len(durs)}
 
     tpf_full = CANVAS / 48.0

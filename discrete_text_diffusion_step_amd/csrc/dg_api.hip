@@ -856,7 +856,7 @@ int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cac
     GemmArgs g = dense_args(st->u, D, n, cfg->sc_ffn, D, sw.g_sc, cfg->sc_ffn);
     g.seg_B0[0] = w->sc_gate;
     g.seg_B1[0] = w->sc_up;
-    DG_HIP(sgemm(dt, g, EPI_SWIGLU, 2, 2, s));
+    DG_HIP(sgemm(dt, g, EPI_SWIGLU, 4, DG_MOE_NT_GU, s));   // 64-row tiles: its own kernel instance
     GemmArgs d = dense_args(sw.g_sc, cfg->sc_ffn, n, D, cfg->sc_ffn, sw.x, D);
     d.seg_B0[0] = w->sc_down;
     DG_HIP(sgemm(dt, d, EPI_ADD, DG_DENSE_MT, DG_DENSE_NT, s));
