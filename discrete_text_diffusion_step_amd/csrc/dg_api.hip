@@ -161,7 +161,9 @@ hipError_t wide_product(GemmArgs g, int mode, int cfg, float *part, int ks, hipS
 // ------------------------------------------------------------ attention
 
 struct AttnPlan {
-  int n, Ntot, Nq, Nk, Nv, R, n_split_max, oproj_ks;
+  int n, Ntot, Nq, Nk, Nv, R, n_split_max;
+  bool qkv_wide, oproj_wide;   // 256-row wide-tile products (bf16)
+  int qkv_ks, oproj_ks;        // their split-K counts (fp32 partials when > 1)
 };
 
 AttnPlan attn_plan(const dg_attn_cfg *c, int n) {
@@ -177,13 +179,19 @@ AttnPlan attn_plan(const dg_attn_cfg *c, int n) {
   const int target = attn_target_workgroups(c->dtype, c->head_dim);
   int ns = (target + blocks - 1) / (blocks > 0 ? blocks : 1);
   p.n_split_max = ns < 1 ? 1 : (ns > 16 ? 16 : ns);
-  p.oproj_ks = choose_ksplit(n, c->hidden, p.Nq, 16 * DG_DENSE_MT, 16 * DG_DENSE_NT, 512, 8);
+  const GemmArgs gq = dense_args(nullptr, c->hidden, n, p.Ntot, c->hidden, nullptr, p.Ntot);
+  p.qkv_wide = DG_PROJ_WIDE && wide_ok(c->dtype, gq, DG_PROJ_CFG, n);
+  p.qkv_ks = p.qkv_wide ? wide_ksplit(gq, DG_PROJ_CFG, DG_PROJ_TARGET) : 1;
+  const GemmArgs go = dense_args(nullptr, p.Nq, n, c->hidden, p.Nq, nullptr, c->hidden);
+  p.oproj_wide = DG_PROJ_WIDE && wide_ok(c->dtype, go, DG_PROJ_CFG, n);
+  p.oproj_ks = p.oproj_wide ? wide_ksplit(go, DG_PROJ_CFG, DG_PROJ_TARGET)
+                            : choose_ksplit(n, c->hidden, p.Nq, 16 * DG_DENSE_MT, 16 * DG_DENSE_NT, 512, 8);
   return p;
 }
 
 struct AttnWs {
   void *h, *qkv, *v_rows, *o;
-  float *o_part, *ml_part, *oproj_part;
+  float *o_part, *ml_part, *oproj_part, *qkv_part;
 };
 
 AttnWs attn_carve(const dg_attn_cfg *c, const AttnPlan &p, Carve &cv) {
@@ -202,6 +210,7 @@ AttnWs attn_carve(const dg_attn_cfg *c, const AttnPlan &p, Carve &cv) {
     w.o_part = w.ml_part = nullptr;
   }
   w.oproj_part = p.oproj_ks > 1 ? cv.take<float>(p.oproj_ks * n * c->hidden) : nullptr;
+  w.qkv_part = p.qkv_ks > 1 ? cv.take<float>(p.qkv_ks * n * p.Ntot) : nullptr;
   return w;
 }
 
@@ -244,7 +253,8 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   g.seg_start[g.nseg] = p.Ntot;
   {
     TimedLaunch tl(DG_KT_QKV, s);
-    DG_HIP(sgemm(dt, g, EPI_STORE, DG_DENSE_MT, DG_DENSE_NT, s));
+    if (p.qkv_wide) DG_HIP(wide_product(g, EPI_STORE, DG_PROJ_CFG, ws.qkv_part, p.qkv_ks, s));
+    else DG_HIP(sgemm(dt, g, EPI_STORE, DG_DENSE_MT, DG_DENSE_NT, s));
   }
 
   NormRopeArgs nr;
@@ -317,7 +327,8 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
     GemmArgs o = dense_args(ws.o, p.Nq, n, D, p.Nq, x, D);
     o.seg_B0[0] = w->w_o;
     TimedLaunch tl(DG_KT_OPROJ, s);
-    DG_HIP(dense_product(dt, o, EPI_ADD, ws.oproj_part, p.oproj_ks, s));
+    if (p.oproj_wide) DG_HIP(wide_product(o, EPI_ADD, DG_PROJ_CFG, ws.oproj_part, p.oproj_ks, s));
+    else DG_HIP(dense_product(dt, o, EPI_ADD, ws.oproj_part, p.oproj_ks, s));
   }
   if (causal) kv->kv_len = P + n;
   return DG_OK;
@@ -467,6 +478,8 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
     TimedLaunch tl(DG_KT_MOE_DOWN, s);
     if (wide && wide_ok(dt, dn, WIDE_EXPERT_DN, moe_rows))
       DG_HIP(launch_gemm_wide(dn, EPI_ROWSCALE_F32, WIDE_EXPERT_DN, s));
+    else if (DG_DOWN_COLS && mtile == DG_MOE_MT && wide_ok(dt, dn, WIDE_EXPERT_DN, moe_rows))
+      DG_HIP(launch_gemm_cols(dn, EPI_ROWSCALE_F32, DG_MOE_MT, DG_COLS_NT, s));   // k = ffn is short
     else DG_HIP(sgemm(dt, dn, EPI_ROWSCALE_F32, mtile, DG_MOE_NT_DN, s));
   }
 

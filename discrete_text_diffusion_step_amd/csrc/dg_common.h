@@ -248,6 +248,9 @@ hipError_t launch_gemm(const GemmArgs &a, int mode, int bm, int bn, hipStream_t 
 #ifndef DG_CONTIG
 #define DG_CONTIG 1
 #endif
+#ifndef DG_GU_S
+#define DG_GU_S 3
+#endif
 #ifndef DG_MOE_S
 #define DG_MOE_S 4
 #endif
@@ -275,6 +278,15 @@ enum WideCfg {
 #ifndef DG_SOFT_CFG
 #define DG_SOFT_CFG WIDE_ROWS256_N256
 #endif
+#ifndef DG_PROJ_WIDE
+#define DG_PROJ_WIDE 1
+#endif
+#ifndef DG_PROJ_CFG
+#define DG_PROJ_CFG WIDE_ROWS256_N128
+#endif
+#ifndef DG_PROJ_TARGET
+#define DG_PROJ_TARGET 256
+#endif
 #ifndef DG_WIDE_EXPERTS
 #define DG_WIDE_EXPERTS 0
 #endif
@@ -289,6 +301,18 @@ inline int wide_bn(int cfg) { return cfg == WIDE_ROWS256_N256 ? 256 : (cfg == WI
 inline int wide_bm(int cfg) { return cfg <= WIDE_ROWS256_N128 ? 256 : 16 * DG_WMOE_MT; }
 inline int wide_kstage(int) { return 64; }
 hipError_t launch_gemm_wide(const GemmArgs &a, int mode, int cfg, hipStream_t s);
+// Column-split bf16 streaming product (waves own adjacent 16*nt-column slices,
+// whole k each); tile (16*mt) x (64*nt).  Needs every k range in whole 64-deep stages.
+#ifndef DG_COLS_NT
+#define DG_COLS_NT 2
+#endif
+#ifndef DG_COLS_S
+#define DG_COLS_S 3
+#endif
+#ifndef DG_DOWN_COLS
+#define DG_DOWN_COLS 0
+#endif
+hipError_t launch_gemm_cols(const GemmArgs &a, int mode, int mt, int nt, hipStream_t s);
 
 template <typename T>
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, long long ldc,

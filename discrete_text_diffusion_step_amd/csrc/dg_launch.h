@@ -61,6 +61,14 @@ hipError_t launch_attention(const AttnArgs &a, int dtype, int dh, hipStream_t s)
 // dst[h][d][col0 + j] = src[h][j][d] for j < n (values to the transposed layout)
 hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh, void *dst, long long dst_hs,
                               int dst_ld, int col0, hipStream_t s);
+// Workgroups the split-KV attention grid aims for: kernels whose LDS tiles
+// exceed 80 KB run one workgroup per CU, the others two.
+#ifndef DG_ATTN_TGT_SMALL
+#define DG_ATTN_TGT_SMALL 256
+#endif
+#ifndef DG_ATTN_TGT_LARGE
+#define DG_ATTN_TGT_LARGE 256
+#endif
 int attn_target_workgroups(int dtype, int dh);
 int attn_block_rows(int dtype, int dh);
 hipError_t launch_router_topk(const float *logits, int n_tok, int E, int k, float scale, int32_t *idx, float *w,

@@ -525,7 +525,7 @@ hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh
 // 512-wide tiles take most of the LDS, two per CU otherwise.
 int attn_target_workgroups(int dtype, int dh) {
   const int lds = 2 * (kBKV * dh + dh * kBKV) * (dtype == DG_BF16 ? 2 : 4);   // two K + two V^T tiles
-  return lds > 80 * 1024 ? 256 : 512;
+  return lds > 80 * 1024 ? DG_ATTN_TGT_LARGE : DG_ATTN_TGT_SMALL;
 }
 
 int attn_block_rows(int dtype, int dh) {
