@@ -91,10 +91,11 @@ _LIB = None
 
 def lib(path=None):
     """Load libdgstep.so (built in-tree by build.py); raise if it is missing.
-    `path` selects another build of the library on the first call."""
+    `path` (or the DGSTEP_LIB environment variable) selects another build of
+    the library on the first call."""
     global _LIB
     if _LIB is None:
-        path = path or LIB_PATH
+        path = path or os.environ.get("DGSTEP_LIB") or LIB_PATH
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: run discrete_text_diffusion_step_amd/build.py")
         L = ctypes.CDLL(path)

@@ -231,17 +231,36 @@ int check_attn_cfg(const dg_attn_cfg *c) {
   return DG_OK;
 }
 
+// Inside a step the kernel that finishes a residual update also writes the
+// next block's pre-norm activations: h = rms(x, w, eps) into `h` (null: none).
+struct NextNorm {
+  void *h = nullptr;
+  const void *w = nullptr;
+  float eps = 0.f;
+};
+
+bool fused_norm_ok(int D) { return D <= residual_norm_max_width() && D % 8 == 0; }
+int rope_rot(const dg_attn_cfg *c) {
+  const double rf = c->layer_type == 1 ? c->rotary_factor : 1.0;
+  return static_cast<int>(floor(rf * (c->head_dim / 2) + 0.5));
+}
+
+// x <- x + Attention(x).  h_in, when given, already holds rms(x, w_in_norm).
 int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, int causal, void *x,
-              Carve &cv, hipStream_t s) {
+              Carve &cv, hipStream_t s, const void *h_in = nullptr, NextNorm next = NextNorm()) {
   const AttnPlan p = attn_plan(c, n);
   const AttnWs ws = attn_carve(c, p, cv);
   const int dt = c->dtype;
   const int D = c->hidden, dh = c->head_dim, Hq = c->n_q_heads, Hkv = c->n_kv_heads;
   const int P = kv->kv_len;
 
-  DG_HIP(launch_rmsnorm(dt, n, D, c->rms_eps, x, w->w_in_norm, ws.h, s));
+  const void *h = h_in;
+  if (!h) {
+    DG_HIP(launch_rmsnorm(dt, n, D, c->rms_eps, x, w->w_in_norm, ws.h, s));
+    h = ws.h;
+  }
 
-  GemmArgs g = dense_args(ws.h, D, n, p.Ntot, D, ws.qkv, p.Ntot);
+  GemmArgs g = dense_args(h, D, n, p.Ntot, D, ws.qkv, p.Ntot);
   g.nseg = c->shared_kv ? 2 : 3;
   g.seg_start[0] = 0;
   g.seg_start[1] = p.Nq;
@@ -253,8 +272,17 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   g.seg_start[g.nseg] = p.Ntot;
   {
     TimedLaunch tl(DG_KT_QKV, s);
-    if (p.qkv_wide) DG_HIP(wide_product(g, EPI_STORE, DG_PROJ_CFG, ws.qkv_part, p.qkv_ks, s));
-    else DG_HIP(sgemm(dt, g, EPI_STORE, DG_DENSE_MT, DG_DENSE_NT, s));
+    if (DG_QKV_FUSED && p.qkv_wide && p.qkv_ks > 1) {
+      // split-K partials; the norm/RoPE pass below sums them
+      g.C = ws.qkv_part;
+      g.ldc = p.Ntot;
+      g.k_splits = p.qkv_ks;
+      DG_HIP(launch_gemm_wide(g, EPI_PARTIAL_F32, DG_PROJ_CFG, s));
+    } else if (p.qkv_wide) {
+      DG_HIP(wide_product(g, EPI_STORE, DG_PROJ_CFG, ws.qkv_part, p.qkv_ks, s));
+    } else {
+      DG_HIP(sgemm(dt, g, EPI_STORE, DG_DENSE_MT, DG_DENSE_NT, s));
+    }
   }
 
   NormRopeArgs nr;
@@ -280,11 +308,14 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   nr.v_head_stride = static_cast<long long>(n) * dh;
   nr.pos0 = P;
   nr.rope_base = c->rope_base;
-  const double rf = c->layer_type == 1 ? c->rotary_factor : 1.0;
-  nr.n_rot = static_cast<int>(floor(rf * (dh / 2) + 0.5));
+  nr.n_rot = rope_rot(c);
   nr.eps = c->rms_eps;
   nr.sqrt_dh = static_cast<float>(sqrt(static_cast<double>(dh)));
   nr.v_unit_rms = c->v_unit_rms;
+  if (DG_QKV_FUSED && p.qkv_wide && p.qkv_ks > 1) {
+    nr.part = ws.qkv_part;
+    nr.n_part = p.qkv_ks;
+  }
   DG_HIP(launch_norm_rope(nr, dt, s));
   const long long vt_cache_hs = static_cast<long long>(dh) * kv->capacity;
   DG_HIP(launch_v_transpose(dt, ws.v_rows, n, Hkv, dh, kv->v, vt_cache_hs, kv->capacity, P, s));
@@ -327,9 +358,21 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
     GemmArgs o = dense_args(ws.o, p.Nq, n, D, p.Nq, x, D);
     o.seg_B0[0] = w->w_o;
     TimedLaunch tl(DG_KT_OPROJ, s);
-    if (p.oproj_wide) DG_HIP(wide_product(o, EPI_ADD, DG_PROJ_CFG, ws.oproj_part, p.oproj_ks, s));
-    else DG_HIP(dense_product(dt, o, EPI_ADD, ws.oproj_part, p.oproj_ks, s));
+    if (next.h && p.oproj_wide && p.oproj_ks > 1 && fused_norm_ok(D)) {
+      // split-K partials, then one pass: residual add + the MoE block's pre-norm
+      o.C = ws.oproj_part;
+      o.ldc = D;
+      o.k_splits = p.oproj_ks;
+      DG_HIP(launch_gemm_wide(o, EPI_PARTIAL_F32, DG_PROJ_CFG, s));
+      DG_HIP(launch_reduce_add_rmsnorm(dt, ws.oproj_part, p.oproj_ks, n, D, x, next.w, next.eps, next.h, s));
+      next.h = nullptr;
+    } else if (p.oproj_wide) {
+      DG_HIP(wide_product(o, EPI_ADD, DG_PROJ_CFG, ws.oproj_part, p.oproj_ks, s));
+    } else {
+      DG_HIP(dense_product(dt, o, EPI_ADD, ws.oproj_part, p.oproj_ks, s));
+    }
   }
+  if (next.h) DG_HIP(launch_rmsnorm(dt, n, D, next.eps, x, next.w, next.h, s));
   if (causal) kv->kv_len = P + n;
   return DG_OK;
 }
@@ -365,7 +408,12 @@ struct MoeWs {
   void *H;
 };
 
+// bf16 router logits with whole 64-deep stages: one 16 x 16 tile per
+// workgroup over the full depth (no split, no reduce); otherwise split-K.
+bool router_small_tiles(const dg_moe_cfg *c) { return c->dtype == DG_BF16 && c->hidden % 64 == 0; }
+
 int router_ksplit(const dg_moe_cfg *c, int n) {
+  if (router_small_tiles(c)) return 1;
   return choose_ksplit(n, c->n_experts, c->hidden, 16 * DG_DENSE_MT, 16 * DG_DENSE_NT, 256, 16);
 }
 
@@ -399,18 +447,25 @@ int check_moe_cfg(const dg_moe_cfg *c) {
   return DG_OK;
 }
 
+// x <- layer_scalar * (x + MoE(x)).  h_in, when given, already holds
+// rms(x, w_in_norm); next (optional) receives the next layer's pre-norm.
 int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float *rl_in, int32_t *idx_out,
-             float *w_out, Carve &cv, hipStream_t s) {
+             float *w_out, Carve &cv, hipStream_t s, const void *h_in = nullptr, NextNorm next = NextNorm()) {
   const MoeWs ws = moe_carve(c, n, cv);
   if (n == 0) return DG_OK;
   const int dt = c->dtype, D = c->hidden, E = c->n_experts, k = c->top_k, F = c->ffn, Fs = c->shared_ffn;
   const int fmax = F > Fs ? F : Fs;
-  DG_HIP(launch_rmsnorm(dt, n, D, c->rms_eps, x, w->w_in_norm, ws.h, s));
+  const void *h = h_in;
+  if (!h) {
+    DG_HIP(launch_rmsnorm(dt, n, D, c->rms_eps, x, w->w_in_norm, ws.h, s));
+    h = ws.h;
+  }
   const float *rl = rl_in;
   if (!rl) {
-    GemmArgs g = dense_args(ws.h, D, n, E, D, ws.rl, E);
+    GemmArgs g = dense_args(h, D, n, E, D, ws.rl, E);
     g.seg_B0[0] = w->w_router;
-    DG_HIP(dense_product(dt, g, EPI_STORE_F32, ws.rpart, router_ksplit(c, n), s));
+    if (router_small_tiles(c)) DG_HIP(sgemm(dt, g, EPI_STORE_F32, 1, 1, s));
+    else DG_HIP(dense_product(dt, g, EPI_STORE_F32, ws.rpart, router_ksplit(c, n), s));
     rl = ws.rl;
   }
   int32_t *idx = idx_out ? idx_out : ws.idx;
@@ -424,7 +479,7 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   // gate/up of every expert (group 0 = shared) with the SwiGLU epilogue
   GemmArgs gu;
   memset(&gu, 0, sizeof(gu));
-  gu.A = ws.h;
+  gu.A = h;
   gu.lda = D;
   gu.a_rows = ws.row_token;
   gu.seg_B0[0] = w->w_gate;
@@ -483,7 +538,12 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
     else DG_HIP(sgemm(dt, dn, EPI_ROWSCALE_F32, mtile, DG_MOE_NT_DN, s));
   }
 
-  DG_HIP(launch_moe_combine(dt, x, ws.Y, ws.pair_row, n, k, D, c->layer_scalar, s));
+  if (next.h && fused_norm_ok(D)) {
+    DG_HIP(launch_combine_rmsnorm(dt, x, ws.Y, ws.pair_row, n, k, D, c->layer_scalar, next.w, next.eps, next.h, s));
+  } else {
+    DG_HIP(launch_moe_combine(dt, x, ws.Y, ws.pair_row, n, k, D, c->layer_scalar, s));
+    if (next.h) DG_HIP(launch_rmsnorm(dt, n, D, next.eps, x, next.w, next.h, s));
+  }
   return DG_OK;
 }
 
@@ -657,7 +717,7 @@ size_t layer_ws_bytes(const dg_model_cfg *c, int n) {
 }
 
 struct StepWs {
-  void *x, *g_sc;
+  void *x, *h, *g_sc;   // h: pre-norm activations handed from block to block
   float *logits, *rowstats;
   void *rest;
 };
@@ -667,6 +727,7 @@ StepWs step_carve(const dg_model_cfg *c, int n, bool need_logits, Carve &cv) {
   const int D = c->sliding.hidden;
   StepWs w;
   w.x = cv.bytes(static_cast<size_t>(n) * D * es);
+  w.h = cv.bytes(static_cast<size_t>(n) * D * es);
   w.g_sc = cv.bytes(static_cast<size_t>(n) * (c->sc_ffn > 0 ? c->sc_ffn : 1) * es);
   w.logits = need_logits ? cv.take<float>(static_cast<size_t>(n) * c->vocab) : nullptr;
   w.rowstats = cv.take<float>(static_cast<size_t>(n) * 2);
@@ -877,11 +938,22 @@ int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cac
   for (int l = 0; l < cfg->n_layers; ++l) {
     Carve c1(sw.rest);
     dg_kv_layer L = kv->layer[l];
-    DG_TRY(attn_impl(layer_cfg(cfg, l), &w->attn[l], &L, n, 0, sw.x, c1, s));
     dg_moe_cfg mc = cfg->moe;
     mc.layer_scalar = w->layer_scalar[l];
+    NextNorm to_moe;
+    to_moe.h = sw.h;
+    to_moe.w = w->moe[l].w_in_norm;
+    to_moe.eps = mc.rms_eps;
+    const dg_attn_cfg *ac = layer_cfg(cfg, l);
+    DG_TRY(attn_impl(ac, &w->attn[l], &L, n, 0, sw.x, c1, s, l == 0 ? nullptr : sw.h, to_moe));
+    NextNorm to_attn;
+    if (l + 1 < cfg->n_layers) {
+      to_attn.h = sw.h;
+      to_attn.w = w->attn[l + 1].w_in_norm;
+      to_attn.eps = layer_cfg(cfg, l + 1)->rms_eps;
+    }
     Carve c2(sw.rest);
-    DG_TRY(moe_impl(&mc, &w->moe[l], n, sw.x, nullptr, nullptr, nullptr, c2, s));
+    DG_TRY(moe_impl(&mc, &w->moe[l], n, sw.x, nullptr, nullptr, nullptr, c2, s, sw.h, to_attn));
   }
   float *logits = st->logits ? st->logits : sw.logits;
   {
@@ -926,8 +998,12 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
       Carve c1(sw.rest);
       const AttnPlan p = attn_plan(ac, n);
       const AttnWs aw = attn_carve(ac, p, c1);
-      DG_HIP(launch_rmsnorm(dt, n, D, ac->rms_eps, sw.x, w->attn[l].w_in_norm, aw.h, s));
-      GemmArgs g = dense_args(aw.h, D, n, p.Nk + p.Nv, D, aw.qkv, p.Ntot);
+      const void *hA = sw.h;   // written by the previous MoE block
+      if (l == 0) {
+        DG_HIP(launch_rmsnorm(dt, n, D, ac->rms_eps, sw.x, w->attn[l].w_in_norm, aw.h, s));
+        hA = aw.h;
+      }
+      GemmArgs g = dense_args(hA, D, n, p.Nk + p.Nv, D, aw.qkv, p.Ntot);
       // write k|v at column Nq of the qkv rows so the norm/RoPE pass reads the usual layout
       g.C = static_cast<char *>(aw.qkv) + static_cast<size_t>(p.Nq) * esize(dt);
       g.nseg = ac->shared_kv ? 1 : 2;
@@ -956,8 +1032,7 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
       nr.v_head_stride = static_cast<long long>(n) * ac->head_dim;
       nr.pos0 = KL.kv_len;
       nr.rope_base = ac->rope_base;
-      const double rf = ac->layer_type == 1 ? ac->rotary_factor : 1.0;
-      nr.n_rot = static_cast<int>(floor(rf * (ac->head_dim / 2) + 0.5));
+      nr.n_rot = rope_rot(ac);
       nr.eps = ac->rms_eps;
       nr.sqrt_dh = static_cast<float>(sqrt(static_cast<double>(ac->head_dim)));
       nr.v_unit_rms = ac->v_unit_rms;
@@ -968,11 +1043,19 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
       break;
     }
     Carve c1(sw.rest);
-    DG_TRY(attn_impl(ac, &w->attn[l], &KL, n, 1, sw.x, c1, s));
     dg_moe_cfg mc = cfg->moe;
     mc.layer_scalar = w->layer_scalar[l];
+    NextNorm to_moe;
+    to_moe.h = sw.h;
+    to_moe.w = w->moe[l].w_in_norm;
+    to_moe.eps = mc.rms_eps;
+    DG_TRY(attn_impl(ac, &w->attn[l], &KL, n, 1, sw.x, c1, s, l == 0 ? nullptr : sw.h, to_moe));
+    NextNorm to_attn;   // the next layer (possibly the K/V-only last one) reads its pre-norm from sw.h
+    to_attn.h = sw.h;
+    to_attn.w = w->attn[l + 1].w_in_norm;
+    to_attn.eps = layer_cfg(cfg, l + 1)->rms_eps;
     Carve c2(sw.rest);
-    DG_TRY(moe_impl(&mc, &w->moe[l], n, sw.x, nullptr, nullptr, nullptr, c2, s));
+    DG_TRY(moe_impl(&mc, &w->moe[l], n, sw.x, nullptr, nullptr, nullptr, c2, s, sw.h, to_attn));
   }
   return DG_OK;
 }

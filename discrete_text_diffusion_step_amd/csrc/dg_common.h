@@ -287,6 +287,9 @@ enum WideCfg {
 #ifndef DG_PROJ_TARGET
 #define DG_PROJ_TARGET 256
 #endif
+#ifndef DG_QKV_FUSED
+#define DG_QKV_FUSED 0
+#endif
 #ifndef DG_WIDE_EXPERTS
 #define DG_WIDE_EXPERTS 0
 #endif

@@ -20,6 +20,10 @@ struct NormRopeArgs {
   int n_rot;                 // frequencies kept (the rest are zero)
   float eps, sqrt_dh;
   int v_unit_rms;
+  // Optional: the projections still as split-K fp32 partials [n_part][n_tok][ld];
+  // the pass sums them (split order) and rounds to the model dtype first.
+  const float *part = nullptr;
+  int n_part = 0;
 };
 
 struct AttnArgs {
@@ -87,5 +91,12 @@ hipError_t launch_rmsnorm(int dtype, int n, int D, float eps, const void *x, con
 hipError_t launch_embed(int dtype, const int32_t *tokens, int n, int D, int vocab, const void *E, void *x,
                         hipStream_t s);
 hipError_t launch_transpose(int dtype, int rows, int cols, const void *in, void *out, hipStream_t s);
+
+// Residual update + the next block's RMSNorm (rows up to residual_norm_max_width()).
+int residual_norm_max_width();
+hipError_t launch_reduce_add_rmsnorm(int dtype, const float *part, int splits, int n, int D, void *x, const void *w,
+                                     float eps, void *h, hipStream_t s);
+hipError_t launch_combine_rmsnorm(int dtype, void *x, const float *Y, const int *pair_row, int n, int k, int D,
+                                  float layer_scalar, const void *w, float eps, void *h, hipStream_t s);
 
 }  // namespace dg

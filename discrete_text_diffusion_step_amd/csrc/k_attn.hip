@@ -21,21 +21,23 @@ namespace dg {
 
 namespace {
 
+// cos/sin of the rotation angle of position pos and frequency t (fp64 angle).
+__device__ __forceinline__ float2 rope_angle(int pos, int t, int dh, double base, int n_rot) {
+  if (t >= n_rot) return make_float2(1.0f, 0.0f);
+  const double f = pow(base, -2.0 * static_cast<double>(t) / static_cast<double>(dh));
+  const double th = static_cast<double>(pos) * f;
+  return make_float2(static_cast<float>(cos(th)), static_cast<float>(sin(th)));
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
   __shared__ float cs[256], sn[256];
   const int j = blockIdx.x;
   const int half = a.dh >> 1;
   for (int t = threadIdx.x; t < half; t += blockDim.x) {
-    if (t < a.n_rot) {
-      const double f = pow(a.rope_base, -2.0 * static_cast<double>(t) / static_cast<double>(a.dh));
-      const double th = static_cast<double>(a.pos0 + j) * f;
-      cs[t] = static_cast<float>(cos(th));
-      sn[t] = static_cast<float>(sin(th));
-    } else {
-      cs[t] = 1.0f;
-      sn[t] = 0.0f;
-    }
+    const float2 v = rope_angle(a.pos0 + j, t, a.dh, a.rope_base, a.n_rot);
+    cs[t] = v.x;
+    sn[t] = v.y;
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -62,19 +64,44 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
       rope = false;
       norm = a.v_unit_rms != 0;
     }
-    float x0[4], x1[4];
+    // lane handles the 4 consecutive pair indices t0 = 4*lane + 256*i (t0 < half)
+    // and their partners t0 + half; the sources are the stored projections,
+    // or the sum of the split-K partials rounded to the model dtype
+    const long long col0 = src - row;
+    auto load4 = [&](int t, float *o) {
+      if (!a.part) {
+        if constexpr (sizeof(T) == 2) {
+          const uint2 u = *reinterpret_cast<const uint2 *>(src + t);
+          o[0] = __uint_as_float(u.x << 16);
+          o[1] = __uint_as_float(u.x & 0xffff0000u);
+          o[2] = __uint_as_float(u.y << 16);
+          o[3] = __uint_as_float(u.y & 0xffff0000u);
+        } else {
+          const float4 f = *reinterpret_cast<const float4 *>(src + t);
+          o[0] = f.x; o[1] = f.y; o[2] = f.z; o[3] = f.w;
+        }
+        return;
+      }
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int z = 0; z < a.n_part; ++z) {
+        const float4 f = *reinterpret_cast<const float4 *>(a.part + (static_cast<long long>(z) * a.n_tok + j) * a.ld +
+                                                           col0 + t);
+        acc[0] += f.x; acc[1] += f.y; acc[2] += f.z; acc[3] += f.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = to_f32<T>(from_f32<T>(acc[e]));
+    };
+    float x0[2][4], x1[2][4];
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = lane + 64 * i;
-      if (t < half) {
-        x0[i] = to_f32<T>(src[t]);
-        x1[i] = to_f32<T>(src[t + half]);
-      } else {
-        x0[i] = 0.f;
-        x1[i] = 0.f;
+    for (int i = 0; i < 2; ++i) {
+      const int t0 = 4 * lane + 256 * i;
+      if (t0 < half) {
+        load4(t0, x0[i]);
+        load4(t0 + half, x1[i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += x0[i][e] * x0[i][e] + x1[i][e] * x1[i][e];
       }
-      ss += x0[i] * x0[i] + x1[i] * x1[i];
     }
     float scale = 1.0f;
     if (norm) {
@@ -82,23 +109,40 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
       scale = a.sqrt_dh / (sqrtf(ss) + a.eps);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = lane + 64 * i;
-      if (t >= half) continue;
-      float p = x0[i] * scale, q = x1[i] * scale;
-      if (w) {
-        p *= to_f32<T>(w[t]);
-        q *= to_f32<T>(w[t + half]);
+    for (int i = 0; i < 2; ++i) {
+      const int t0 = 4 * lane + 256 * i;
+      if (t0 >= half) continue;
+      float po[4], qo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + e;
+        float p = x0[i][e] * scale, q = x1[i][e] * scale;
+        if (w) {
+          p *= to_f32<T>(w[t]);
+          q *= to_f32<T>(w[t + half]);
+        }
+        if (rope) {
+          const float c = cs[t], sv = sn[t];
+          const float o0 = p * c - q * sv;
+          const float o1 = q * c + p * sv;
+          p = o0;
+          q = o1;
+        }
+        po[e] = p;
+        qo[e] = q;
       }
-      if (rope) {
-        const float c = cs[t], s = sn[t];
-        const float o0 = p * c - q * s;
-        const float o1 = q * c + p * s;
-        p = o0;
-        q = o1;
+      if constexpr (sizeof(T) == 2) {
+        uint2 u, v;
+        u.x = static_cast<uint32_t>(f32_to_bf16(po[0])) | (static_cast<uint32_t>(f32_to_bf16(po[1])) << 16);
+        u.y = static_cast<uint32_t>(f32_to_bf16(po[2])) | (static_cast<uint32_t>(f32_to_bf16(po[3])) << 16);
+        v.x = static_cast<uint32_t>(f32_to_bf16(qo[0])) | (static_cast<uint32_t>(f32_to_bf16(qo[1])) << 16);
+        v.y = static_cast<uint32_t>(f32_to_bf16(qo[2])) | (static_cast<uint32_t>(f32_to_bf16(qo[3])) << 16);
+        *reinterpret_cast<uint2 *>(dst + t0) = u;
+        *reinterpret_cast<uint2 *>(dst + t0 + half) = v;
+      } else {
+        *reinterpret_cast<float4 *>(dst + t0) = make_float4(po[0], po[1], po[2], po[3]);
+        *reinterpret_cast<float4 *>(dst + t0 + half) = make_float4(qo[0], qo[1], qo[2], qo[3]);
       }
-      dst[t] = from_f32<T>(p);
-      dst[t + half] = from_f32<T>(q);
     }
   }
 }

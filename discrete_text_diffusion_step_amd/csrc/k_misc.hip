@@ -34,6 +34,78 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int n, int D, float eps, f
   }
 }
 
+// Residual update fused with the next block's RMSNorm, one workgroup per
+// row (rows up to 256 * 8 * MAXC wide, held in registers between the passes).
+// The stored row is rounded to T first and the norm is taken over the
+// stored values (fp32 sum of squares, block reduction).
+//   reduce_add: x <- T(x + sum_s part[s])      (split-K partials, s ascending)
+//   combine:    x <- T(ls * (x + Y[t] + sum_j Y[pair_row[t*k+j]]))
+//   then        h <- T(w * x * sqrt(D) / (||x||_2 + eps))
+template <typename T, int MAXC, bool COMBINE>
+__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const float *part, int splits, const int *pair_row,
+                                                               int k, float ls, int n, int D, T *x, const T *w,
+                                                               float eps, float sqrt_d, T *h) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
+  T *xr = x + static_cast<long long>(row) * D;
+  float v[MAXC][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = tid * 8 + 2048 * i;
+    if (c >= D) break;
+    float a[8], o[8];
+    if constexpr (COMBINE) {
+      // Y rows: the shared expert's row is the token's own, then its k experts
+      load8(part + static_cast<long long>(row) * D + c, a);
+      for (int j = 0; j < k; ++j) {
+        float t[8];
+        load8(part + static_cast<long long>(pair_row[row * k + j]) * D + c, t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] += t[e];
+      }
+      load8(xr + c, o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = ls * (o[e] + a[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = 0.f;
+      for (int z = 0; z < splits; ++z) {
+        float t[8];
+        load8(part + (static_cast<long long>(z) * n + row) * D + c, t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] += t[e];
+      }
+      load8(xr + c, o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] += o[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[i][e] = to_f32<T>(from_f32<T>(a[e]));
+      ss += v[i][e] * v[i][e];
+    }
+    store8(xr + c, v[i]);
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  ss = (red[0] + red[1]) + (red[2] + red[3]);
+  const float scale = sqrt_d / (sqrtf(ss) + eps);
+  T *hr = h + static_cast<long long>(row) * D;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = tid * 8 + 2048 * i;
+    if (c >= D) break;
+    float g[8], o[8];
+    load8(w + c, g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = g[e] * v[i][e] * scale;
+    store8(hr + c, o);
+  }
+}
+
 // x[j] = E[tokens[j]]; ids outside [0, vocab) are clamped into range.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t *tokens, int n, int D, int vocab, const T *E,
@@ -101,6 +173,43 @@ hipError_t launch_transpose(int dtype, int rows, int cols, const void *in, void 
   else
     hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, rows, cols, static_cast<const float *>(in),
                        static_cast<float *>(out));
+  return hipGetLastError();
+}
+
+
+int residual_norm_max_width() { return 256 * 8 * 2; }
+
+hipError_t launch_reduce_add_rmsnorm(int dtype, const float *part, int splits, int n, int D, void *x, const void *w,
+                                     float eps, void *h, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (D > residual_norm_max_width() || D % 8) return hipErrorInvalidValue;
+  const float sq = static_cast<float>(__builtin_sqrt(static_cast<double>(D)));   // as launch_rmsnorm
+  const dim3 grid(n);
+  if (dtype == DG_BF16)
+    hipLaunchKernelGGL((residual_rmsnorm_kernel<bf16_t, 2, false>), grid, dim3(256), 0, s, part, splits, nullptr, 0,
+                       1.0f, n, D, static_cast<bf16_t *>(x), static_cast<const bf16_t *>(w), eps, sq,
+                       static_cast<bf16_t *>(h));
+  else
+    hipLaunchKernelGGL((residual_rmsnorm_kernel<float, 2, false>), grid, dim3(256), 0, s, part, splits, nullptr, 0,
+                       1.0f, n, D, static_cast<float *>(x), static_cast<const float *>(w), eps, sq,
+                       static_cast<float *>(h));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_rmsnorm(int dtype, void *x, const float *Y, const int *pair_row, int n, int k, int D,
+                                  float layer_scalar, const void *w, float eps, void *h, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (D > residual_norm_max_width() || D % 8) return hipErrorInvalidValue;
+  const float sq = static_cast<float>(__builtin_sqrt(static_cast<double>(D)));   // as launch_rmsnorm
+  const dim3 grid(n);
+  if (dtype == DG_BF16)
+    hipLaunchKernelGGL((residual_rmsnorm_kernel<bf16_t, 2, true>), grid, dim3(256), 0, s, Y, 0, pair_row, k,
+                       layer_scalar, n, D, static_cast<bf16_t *>(x), static_cast<const bf16_t *>(w), eps, sq,
+                       static_cast<bf16_t *>(h));
+  else
+    hipLaunchKernelGGL((residual_rmsnorm_kernel<float, 2, true>), grid, dim3(256), 0, s, Y, 0, pair_row, k,
+                       layer_scalar, n, D, static_cast<float *>(x), static_cast<const float *>(w), eps, sq,
+                       static_cast<float *>(h));
   return hipGetLastError();
 }
 
