@@ -426,7 +426,7 @@ MoeWs moe_carve(const dg_moe_cfg *c, int n, Carve &cv) {
   w.rl = cv.take<float>(static_cast<size_t>(n) * c->n_experts);
   w.idx = cv.take<int32_t>(static_cast<size_t>(n) * c->top_k);
   w.tw = cv.take<float>(static_cast<size_t>(n) * c->top_k);
-  w.g_off = cv.take<int>(c->n_experts + 2);
+  w.g_off = cv.take<int>(c->n_experts + 2 + n / 16);   // shared-expert chunks of >= 16 rows
   w.row_token = cv.take<int>(rows);
   w.row_weight = cv.take<float>(rows);
   w.pair_row = cv.take<int>(static_cast<size_t>(n) * c->top_k);
@@ -471,10 +471,13 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   int32_t *idx = idx_out ? idx_out : ws.idx;
   float *tw = w_out ? w_out : ws.tw;
   DG_HIP(launch_router_topk(rl, n, E, k, c->route_scale, idx, tw, s));
-  DG_HIP(launch_moe_permute(idx, tw, n, k, E, ws.g_off, ws.row_token, ws.row_weight, ws.pair_row, s));
-
   const int rows_per_expert = (n * k + E - 1) / E;
   const int mtile = rows_per_expert > 48 ? 4 : DG_MOE_MT;   // 64-row tiles for long groups
+  // the shared expert's rows are cut into chunks of one row tile, so its
+  // workgroups run side by side with the routed experts' instead of looping
+  const int chunk = 16 * mtile;
+  const int n_x = (n + chunk - 1) / chunk;
+  DG_HIP(launch_moe_permute(idx, tw, n, k, E, chunk, ws.g_off, ws.row_token, ws.row_weight, ws.pair_row, s));
 
   // gate/up of every expert (group 0 = shared) with the SwiGLU epilogue
   GemmArgs gu;
@@ -487,7 +490,8 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   gu.ldb = D;
   gu.b_gstride = static_cast<long long>(F) * D;
   gu.g_off = ws.g_off;
-  gu.n_groups = E + 1;
+  gu.n_groups = E + n_x;
+  gu.n_xgroups = n_x;
   gu.Bx0 = w->ws_gate;
   gu.Bx1 = w->ws_up;
   gu.N_x = Fs;
@@ -517,7 +521,8 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   dn.ldb = F;
   dn.b_gstride = static_cast<long long>(D) * F;
   dn.g_off = ws.g_off;
-  dn.n_groups = E + 1;
+  dn.n_groups = E + n_x;
+  dn.n_xgroups = n_x;
   dn.Bx0 = w->ws_down;
   dn.N_x = D;
   dn.K_x = Fs;
@@ -535,7 +540,7 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
       DG_HIP(launch_gemm_wide(dn, EPI_ROWSCALE_F32, WIDE_EXPERT_DN, s));
     else if (DG_DOWN_COLS && mtile == DG_MOE_MT && wide_ok(dt, dn, WIDE_EXPERT_DN, moe_rows))
       DG_HIP(launch_gemm_cols(dn, EPI_ROWSCALE_F32, DG_MOE_MT, DG_COLS_NT, s));   // k = ffn is short
-    else DG_HIP(sgemm(dt, dn, EPI_ROWSCALE_F32, mtile, DG_MOE_NT_DN, s));
+    else DG_HIP(sgemm(dt, dn, EPI_ROWSCALE_F32, mtile == DG_MOE_MT ? DG_DN_MT : mtile, DG_MOE_NT_DN, s));
   }
 
   if (next.h && fused_norm_ok(D)) {

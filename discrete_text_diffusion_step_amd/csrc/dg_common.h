@@ -205,11 +205,13 @@ struct GemmArgs {
   const void *seg_B0[4];
   const void *seg_B1[4];  // second matrix for the dual (SwiGLU) mode
   long long ldb;
-  // Grouped mode (g_off != nullptr): group 0 uses (Bx0, Bx1, N_x); groups
-  // 1..n_groups-1 use B0 + (g-1)*b_gstride (and B1) with N columns.  Rows of
-  // group g are logical rows [g_off[g], g_off[g+1]).
+  // Grouped mode (g_off != nullptr): groups 0..n_xgroups-1 (row chunks of the
+  // shared expert) use (Bx0, Bx1, N_x); groups n_xgroups..n_groups-1 use
+  // B0 + (g-n_xgroups)*b_gstride (and B1) with N columns.  Rows of group g
+  // are logical rows [g_off[g], g_off[g+1]).
   const int *g_off;
   int n_groups;
+  int n_xgroups;
   const void *Bx0, *Bx1;
   int N_x, K_x;           // group 0 columns and depth
   long long ldb_x;        // group 0 weight row stride
@@ -247,6 +249,9 @@ hipError_t launch_gemm(const GemmArgs &a, int mode, int bm, int bn, hipStream_t 
 #endif
 #ifndef DG_CONTIG
 #define DG_CONTIG 1
+#endif
+#ifndef DG_DN_MT
+#define DG_DN_MT DG_MOE_MT
 #endif
 #ifndef DG_GU_S
 #define DG_GU_S 3

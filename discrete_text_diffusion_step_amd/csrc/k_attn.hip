@@ -239,9 +239,15 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
   const int l16 = lane & 15, lg = lane >> 4;
   const int R = a.n_rep * a.n_tok;
   const int qblocks = (R + C::BQ - 1) / C::BQ;
-  const int g = blockIdx.x / qblocks;
-  const int qb = blockIdx.x % qblocks;
-  const int split = blockIdx.y;
+  // Consecutive workgroups are dealt round-robin to the 8 XCDs.  Renumber
+  // them so that each XCD receives whole runs of query blocks reading the
+  // same (kv head, key slice): that slice then stays in the XCD's L2.
+  int L = blockIdx.y * gridDim.x + blockIdx.x;
+  const int total = gridDim.x * gridDim.y;
+  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  const int qb = L % qblocks;
+  const int split = (L / qblocks) % a.n_split;
+  const int g = L / (qblocks * a.n_split);
   const int r0 = qb * C::BQ;
   const int r1 = min(R, r0 + C::BQ);
 

@@ -225,17 +225,17 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmArgs a) {
   } else {
     const int g = blockIdx.y;
     const int n0 = blockIdx.x * BN;
-    const int Ng = (g == 0) ? a.N_x : a.N;
+    const int Ng = (g < a.n_xgroups) ? a.N_x : a.N;
     if (n0 >= Ng) return;
     const T *Bp[NB];
     GemmArgs ga = a;   // group 0 (shared expert) may have its own depth and row stride
-    if (g == 0) {
+    if (g < a.n_xgroups) {
       ga.K = a.K_x;
       ga.ldb = a.ldb_x;
       Bp[0] = static_cast<const T *>(a.Bx0) + static_cast<long long>(n0) * a.ldb_x;
       if (NB > 1) Bp[NB - 1] = static_cast<const T *>(a.Bx1) + static_cast<long long>(n0) * a.ldb_x;
     } else {
-      const long long off = static_cast<long long>(g - 1) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
+      const long long off = static_cast<long long>(g - a.n_xgroups) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
       Bp[0] = static_cast<const T *>(a.seg_B0[0]) + off;
       if (NB > 1) Bp[NB - 1] = static_cast<const T *>(a.seg_B1[0]) + off;
     }
@@ -769,17 +769,17 @@ __global__ __launch_bounds__(256) void gemm_cols_kernel(const GemmArgs a) {
   } else {
     const int g = blockIdx.y;
     const int n0 = blockIdx.x * BN;
-    const int Ng = (g == 0) ? a.N_x : a.N;
+    const int Ng = (g < a.n_xgroups) ? a.N_x : a.N;
     if (n0 >= Ng) return;
     const bf16_t *Bp[NB];
     GemmArgs ga = a;
-    if (g == 0) {
+    if (g < a.n_xgroups) {
       ga.K = a.K_x;
       ga.ldb = a.ldb_x;
       Bp[0] = static_cast<const bf16_t *>(a.Bx0) + static_cast<long long>(n0) * a.ldb_x;
       if (NB > 1) Bp[NB - 1] = static_cast<const bf16_t *>(a.Bx1) + static_cast<long long>(n0) * a.ldb_x;
     } else {
-      const long long off = static_cast<long long>(g - 1) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
+      const long long off = static_cast<long long>(g - a.n_xgroups) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
       Bp[0] = static_cast<const bf16_t *>(a.seg_B0[0]) + off;
       if (NB > 1) Bp[NB - 1] = static_cast<const bf16_t *>(a.seg_B1[0]) + off;
     }
@@ -855,17 +855,17 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmArgs a) {
   } else {
     const int g = blockIdx.y;
     const int n0 = blockIdx.x * BN;
-    const int Ng = (g == 0) ? a.N_x : a.N;
+    const int Ng = (g < a.n_xgroups) ? a.N_x : a.N;
     if (n0 >= Ng) return;
     const T *Bp[NB];
     GemmArgs ga = a;
-    if (g == 0) {
+    if (g < a.n_xgroups) {
       ga.K = a.K_x;
       ga.ldb = a.ldb_x;
       Bp[0] = static_cast<const T *>(a.Bx0) + static_cast<long long>(n0) * a.ldb_x;
       if (NB > 1) Bp[NB - 1] = static_cast<const T *>(a.Bx1) + static_cast<long long>(n0) * a.ldb_x;
     } else {
-      const long long off = static_cast<long long>(g - 1) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
+      const long long off = static_cast<long long>(g - a.n_xgroups) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
       Bp[0] = static_cast<const T *>(a.seg_B0[0]) + off;
       if (NB > 1) Bp[NB - 1] = static_cast<const T *>(a.seg_B1[0]) + off;
     }
@@ -1121,17 +1121,17 @@ __global__ __launch_bounds__(64 * NW) void gemm_wide_kernel(const GemmArgs a) {
   } else {
     const int g = blockIdx.y;
     const int n0 = blockIdx.x * BN;
-    const int Ng = (g == 0) ? a.N_x : a.N;
+    const int Ng = (g < a.n_xgroups) ? a.N_x : a.N;
     if (n0 >= Ng) return;
     const bf16_t *Bp[NB];
     GemmArgs ga = a;
-    if (g == 0) {
+    if (g < a.n_xgroups) {
       ga.K = a.K_x;
       ga.ldb = a.ldb_x;
       Bp[0] = static_cast<const bf16_t *>(a.Bx0) + static_cast<long long>(n0) * a.ldb_x;
       if (NB > 1) Bp[NB - 1] = static_cast<const bf16_t *>(a.Bx1) + static_cast<long long>(n0) * a.ldb_x;
     } else {
-      const long long off = static_cast<long long>(g - 1) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
+      const long long off = static_cast<long long>(g - a.n_xgroups) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
       Bp[0] = static_cast<const bf16_t *>(a.seg_B0[0]) + off;
       if (NB > 1) Bp[NB - 1] = static_cast<const bf16_t *>(a.seg_B1[0]) + off;
     }
@@ -1189,6 +1189,7 @@ hipError_t launch_gemm_stream(const GemmArgs &a, int mode, int mt, int nt, hipSt
   DG_STREAM_CASE(DG_DENSE_MT, DG_DENSE_NT, 1, EPI_PARTIAL_F32, DG_DENSE_S)
   DG_STREAM_CASE(1, 1, 1, EPI_STORE_F32, 3)   // router logits: 16 x 16 tiles, whole depth
   DG_STREAM_CASE(DG_MOE_MT, DG_MOE_NT_GU, 2, EPI_SWIGLU, DG_GU_S)
+  DG_STREAM_CASE(DG_DN_MT, DG_MOE_NT_DN, 1, EPI_ROWSCALE_F32, DG_MOE_S)
   DG_STREAM_CASE(DG_MOE_MT, DG_MOE_NT_DN, 1, EPI_ROWSCALE_F32, DG_MOE_S)
   DG_STREAM_CASE(4, DG_MOE_NT_GU, 2, EPI_SWIGLU, 3)
   DG_STREAM_CASE(4, DG_MOE_NT_DN, 1, EPI_ROWSCALE_F32, 3)

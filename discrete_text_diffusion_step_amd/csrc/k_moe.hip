@@ -5,9 +5,10 @@
 // expert is always added).
 //
 // Group layout produced by moe_permute (consumed by the grouped GEMM):
-//   group 0          : the shared expert, rows [0, n_tok) in token order
-//   group 1 + e      : routed expert e, rows sorted by (token, slot)
-// so g_off has n_experts + 2 entries.  row_token[r] is the token of row r,
+//   groups 0..X-1    : the shared expert, rows [0, n_tok) in token order, cut
+//                      into X chunks of `chunk` rows (parallel workgroups)
+//   group X + e      : routed expert e, rows sorted by (token, slot)
+// so g_off has X + n_experts + 1 entries.  row_token[r] is the token of row r,
 // row_weight[r] its mixing weight (1 for the shared expert) and pair_row[t*k+j]
 // the row holding token t's j-th expert.
 #include "dg_launch.h"
@@ -119,8 +120,9 @@ constexpr int kPermWaves = 16;
 constexpr int kPermChunk = 4096;
 
 __global__ __launch_bounds__(64 * kPermWaves) void moe_permute_kernel(const int32_t *idx, const float *w, int n_tok,
-                                                                      int k, int E, int *g_off, int *row_token,
-                                                                      float *row_weight, int *pair_row) {
+                                                                      int k, int E, int chunk, int *g_off,
+                                                                      int *row_token, float *row_weight,
+                                                                      int *pair_row) {
   __shared__ int cnt[256];
   __shared__ int start[256];   // next free row of each expert
   __shared__ int hist[kPermWaves][256];
@@ -153,20 +155,18 @@ __global__ __launch_bounds__(64 * kPermWaves) void moe_permute_kernel(const int3
       const int y = __shfl_up(incl, o, 64);
       if (lane >= o) incl += y;
     }
+    const int X = (n_tok + chunk - 1) / chunk;   // shared-expert row chunks
     int run = n_tok + incl - local;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
       if (e < E) {
         start[e] = run;
-        g_off[e + 2] = run + c[i];
+        g_off[X + 1 + e] = run + c[i];
       }
       run += c[i];
     }
-    if (lane == 0) {
-      g_off[0] = 0;
-      g_off[1] = n_tok;
-    }
+    for (int x = lane; x <= X; x += 64) g_off[x] = min(x * chunk, n_tok);
   }
   for (int t = tid; t < n_tok; t += NT) {
     row_token[t] = t;
@@ -260,9 +260,10 @@ hipError_t launch_router_topk(const float *logits, int n_tok, int E, int k, floa
   return hipGetLastError();
 }
 
-hipError_t launch_moe_permute(const int32_t *idx, const float *w, int n_tok, int k, int E, int *g_off,
+hipError_t launch_moe_permute(const int32_t *idx, const float *w, int n_tok, int k, int E, int chunk, int *g_off,
                               int *row_token, float *row_weight, int *pair_row, hipStream_t s) {
-  hipLaunchKernelGGL(moe_permute_kernel, dim3(1), dim3(64 * kPermWaves), 0, s, idx, w, n_tok, k, E, g_off,
+  if (chunk <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(moe_permute_kernel, dim3(1), dim3(64 * kPermWaves), 0, s, idx, w, n_tok, k, E, chunk, g_off,
                      row_token, row_weight, pair_row);
   return hipGetLastError();
 }
