@@ -274,6 +274,9 @@ enum WideCfg {
 #ifndef DG_WIDE_P
 #define DG_WIDE_P 3
 #endif
+#ifndef DG_WIDE_PA
+#define DG_WIDE_PA 1
+#endif
 #ifndef DG_WIDE256_P
 #define DG_WIDE256_P 2
 #endif

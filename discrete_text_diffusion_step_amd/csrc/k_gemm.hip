@@ -574,34 +574,70 @@ __device__ __forceinline__ void stream_tile_c(const GemmArgs &a, float *red, int
           for (int i = 0; i < 4; ++i, ++e) dst[e * 64 + lane] = acc[nb][mt][nt][i];
   }
   __syncthreads();
+  // Each thread adds up and stores 4 neighbouring lanes of one accumulator
+  // element: 4 consecutive columns of one row (float4 LDS reads, 16- or
+  // 8-byte stores).
   constexpr int EH = EL / NB;
-  for (int q = tid; q < EH * 64; q += 256) {
-    const int ln = q & 63, e = q >> 6;
+  for (int q = tid; q < EH * 16; q += 256) {
+    const int l4 = (q & 15) * 4, e = q >> 4;
     const int i = e & 3, nt = (e >> 2) % NT, mt = (e >> 2) / NT;
-    const int r = mt * 16 + (ln >> 4) * 4 + i;
-    const int c = nt * 16 + (ln & 15);
+    const int r = mt * 16 + (l4 >> 4) * 4 + i;
+    const int c = nt * 16 + (l4 & 15);
     if (r >= rows || c >= ncols) continue;
-    float v = 0.f;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) v += red[(w * EL + e) * 64 + ln];
+    for (int w = 0; w < 4; ++w) {
+      const float4 t = *reinterpret_cast<const float4 *>(red + (w * EL + e) * 64 + l4);
+      v[0] += t.x; v[1] += t.y; v[2] += t.z; v[3] += t.w;
+    }
+    if constexpr (MODE == EPI_SWIGLU) {
+      float u[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float4 t = *reinterpret_cast<const float4 *>(red + (w * EL + EH + e) * 64 + l4);
+        u[0] += t.x; u[1] += t.y; u[2] += t.z; u[3] += t.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = silu_f(v[j]) * u[j];
+    }
     const long long row = row_begin + r;
     const int col = n0 + c;
-    if constexpr (MODE == EPI_STORE) {
-      static_cast<bf16_t *>(a.C)[row * a.ldc + col] = f32_to_bf16(v);
-    } else if constexpr (MODE == EPI_STORE_F32) {
-      static_cast<float *>(a.C)[row * a.ldc + col] = v;
-    } else if constexpr (MODE == EPI_ADD) {
-      bf16_t *cp = static_cast<bf16_t *>(a.C) + row * a.ldc + col;
-      *cp = f32_to_bf16(bf16_to_f32(*cp) + v);
-    } else if constexpr (MODE == EPI_SWIGLU) {
-      float u = 0.f;
+    const int nv = ncols - c < 4 ? ncols - c : 4;   // valid columns of the four
+    if constexpr (MODE == EPI_STORE_F32 || MODE == EPI_ROWSCALE_F32 || MODE == EPI_PARTIAL_F32) {
+      if constexpr (MODE == EPI_ROWSCALE_F32) {
+        const float rs = a.rowscale[row];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) u += red[(w * EL + EH + e) * 64 + ln];
-      static_cast<bf16_t *>(a.C)[row * a.ldc + col] = f32_to_bf16(silu_f(v) * u);
-    } else if constexpr (MODE == EPI_ROWSCALE_F32) {
-      static_cast<float *>(a.C)[row * a.ldc + col] = v * a.rowscale[row];
-    } else if constexpr (MODE == EPI_PARTIAL_F32) {
-      static_cast<float *>(a.C)[(static_cast<long long>(split) * a.M + row) * a.ldc + col] = v;
+        for (int j = 0; j < 4; ++j) v[j] *= rs;
+      }
+      const long long off = (MODE == EPI_PARTIAL_F32 ? (static_cast<long long>(split) * a.M + row) : row) * a.ldc + col;
+      float *cp = static_cast<float *>(a.C) + off;
+      if (nv == 4 && (off & 3) == 0) {
+        *reinterpret_cast<float4 *>(cp) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        for (int j = 0; j < nv; ++j) cp[j] = v[j];
+      }
+    } else {
+      bf16_t *cp = static_cast<bf16_t *>(a.C) + row * a.ldc + col;
+      const bool vec = nv == 4 && ((row * a.ldc + col) & 3) == 0;
+      if constexpr (MODE == EPI_ADD) {
+        if (vec) {
+          const uint2 o = *reinterpret_cast<const uint2 *>(cp);
+          v[0] += __uint_as_float(o.x << 16);
+          v[1] += __uint_as_float(o.x & 0xffff0000u);
+          v[2] += __uint_as_float(o.y << 16);
+          v[3] += __uint_as_float(o.y & 0xffff0000u);
+        } else {
+          for (int j = 0; j < nv; ++j) v[j] += bf16_to_f32(cp[j]);
+        }
+      }
+      if (vec) {
+        uint2 o;
+        o.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+        o.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        *reinterpret_cast<uint2 *>(cp) = o;
+      } else {
+        for (int j = 0; j < nv; ++j) cp[j] = f32_to_bf16(v[j]);
+      }
     }
   }
 }
@@ -925,6 +961,9 @@ __device__ __forceinline__ void wide_tile(const GemmArgs &a, bf16_t *lds, bf16_t
                                           const bf16_t *const *Bp, int n0, int ncols, int kb, int ke,
                                           int split) {
   static_assert(KSUB == 2, "stages are 64 deep (128 bytes per A row)");
+  // A is fetched PA stages ahead (ring of PA register slots); PA = 2 needs
+  // an even ring length R so slot parity is fixed inside the unrolled body
+  constexpr int PA = ((P + 1) % 2 == 0) ? DG_WIDE_PA : 1;
   constexpr int BM = MT * 16;
   constexpr int D = BM / 8 / NW;         // A load instructions per wave per stage
   static_assert(D * 8 * NW == BM, "A rows must split evenly over the waves");
@@ -977,13 +1016,13 @@ __device__ __forceinline__ void wide_tile(const GemmArgs &a, bf16_t *lds, bf16_t
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) acc[nb][mi][nt] = zero4();
 
-  Frag<bf16_t> ra[D];                    // native vectors: must stay in registers
+  Frag<bf16_t> ra[PA][D];                // native vectors: must stay in registers
   Frag<bf16_t> rb[R][NB][DB];
 
-  auto load_a = [&](int st) {
+  auto load_a = [&](int st, Frag<bf16_t>(&xa)[D]) {
     const uint32_t kbyte = static_cast<uint32_t>(kb + st * 64) * 2u;
 #pragma unroll
-    for (int j = 0; j < D; ++j) ra[j].load(reinterpret_cast<const bf16_t *>(Ab + (ao[j] + kbyte)));
+    for (int j = 0; j < D; ++j) xa[j].load(reinterpret_cast<const bf16_t *>(Ab + (ao[j] + kbyte)));
   };
   auto load_b = [&](int st, Frag<bf16_t>(&xb)[NB][DB]) {
     const uint32_t kbyte = static_cast<uint32_t>(kb + st * 64) * 2u;
@@ -992,9 +1031,9 @@ __device__ __forceinline__ void wide_tile(const GemmArgs &a, bf16_t *lds, bf16_t
 #pragma unroll
       for (int j = 0; j < DB; ++j) xb[nb][j].load(reinterpret_cast<const bf16_t *>(Bb[nb] + (bo[j] + kbyte)));
   };
-  auto stage_a = [&](int buf) {
+  auto stage_a = [&](int buf, const Frag<bf16_t>(&xa)[D]) {
 #pragma unroll
-    for (int j = 0; j < D; ++j) *reinterpret_cast<bf16x8 *>(lds + buf * STAGE + aw[j]) = ra[j].v;
+    for (int j = 0; j < D; ++j) *reinterpret_cast<bf16x8 *>(lds + buf * STAGE + aw[j]) = xa[j].v;
   };
   auto compute = [&](int buf, const Frag<bf16_t>(&xb)[NB][DB]) {
     // this wave's B slice: rows to its own LDS region, back as fragments
@@ -1029,20 +1068,23 @@ __device__ __forceinline__ void wide_tile(const GemmArgs &a, bf16_t *lds, bf16_t
   const int nst = (ke - kb) / 64;
   const int lastst = nst > 0 ? nst - 1 : 0;
   if (nst > 0) {
-    load_a(0);
+    load_a(0, ra[0]);
+    if constexpr (PA == 2) load_a(1 < lastst ? 1 : lastst, ra[1]);
 #pragma unroll
     for (int r = 0; r < P; ++r) load_b(r < lastst ? r : lastst, rb[r]);
-    stage_a(0);
+    stage_a(0, ra[0]);
   }
   lds_barrier();
   for (int i = 0; i < nst; i += R) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int it = i + r;
-      load_a(it + 1 < lastst ? it + 1 : lastst);
+      // A slot of stage s is s % PA (R is even when PA == 2, so r's parity is it's)
+      if constexpr (PA == 2) load_a(it + 2 < lastst ? it + 2 : lastst, ra[r & 1]);
+      else load_a(it + 1 < lastst ? it + 1 : lastst, ra[0]);
       load_b(it + P < lastst ? it + P : lastst, rb[(r + P) % R]);
       if (it < nst) compute(it & 1, rb[r]);
-      stage_a((it + 1) & 1);
+      stage_a((it + 1) & 1, ra[PA == 2 ? ((r + 1) & 1) : 0]);
       lds_barrier();
     }
   }
