@@ -67,6 +67,9 @@ hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh
                               int dst_ld, int col0, hipStream_t s);
 // Workgroups the split-KV attention grid aims for: kernels whose LDS tiles
 // exceed 80 KB run one workgroup per CU, the others two.
+#ifndef DG_ATTN_PAIR
+#define DG_ATTN_PAIR 1
+#endif
 #ifndef DG_ATTN_TGT_SMALL
 #define DG_ATTN_TGT_SMALL 256
 #endif

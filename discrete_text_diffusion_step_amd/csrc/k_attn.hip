@@ -170,6 +170,11 @@ struct AttnCfg {
   static constexpr int VINS = VCH / 64;
   static constexpr int KSW = KCPR >= 16 ? 15 : KCPR - 1;
   static constexpr int VSW = VCPR - 1;
+  // chunk swizzles: K rows by a hash that is distinct over the 16 rows one
+  // MFMA reads (keys 8q + {0..3} (+4): see key_row), V^T rows by d / 4 for
+  // 16-byte chunks (rows are 64 bytes, four to a bank period)
+  __device__ static int kswz(int r) { return ((((r >> 3) << 2) | (r & 3)) & KSW); }
+  __device__ static int vswz(int d) { return sizeof(T) == 2 ? ((d >> 2) & VSW) : (d & VSW); }
   static constexpr int DS = DH / 32;                // 32-wide d steps
   static constexpr int DT = DH / 16;                // 16-wide d tiles
   static_assert(KINS % 4 == 0 && VINS % 4 == 0, "each wave issues an equal share of a tile");
@@ -181,36 +186,37 @@ __device__ __forceinline__ void load_k_frag(Frag<T> &f, const T *tile, int r, in
   using C = AttnCfg<T, DH>;
   if constexpr (sizeof(T) == 2) {
     const int c = e0 / 8;
-    f.load(tile + (r * C::KCPR + (c ^ (r & C::KSW))) * 8);
+    f.load(tile + (r * C::KCPR + (c ^ C::kswz(r))) * 8);
   } else {
     const int c = e0 / 4;
-    const float4 a = *reinterpret_cast<const float4 *>(tile + (r * C::KCPR + (c ^ (r & C::KSW))) * 4);
-    const float4 b = *reinterpret_cast<const float4 *>(tile + (r * C::KCPR + ((c + 1) ^ (r & C::KSW))) * 4);
+    const float4 a = *reinterpret_cast<const float4 *>(tile + (r * C::KCPR + (c ^ C::kswz(r))) * 4);
+    const float4 b = *reinterpret_cast<const float4 *>(tile + (r * C::KCPR + ((c + 1) ^ C::kswz(r))) * 4);
     f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
     f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
   }
 }
 
-// V^T fragment of row d holding keys {4g..4g+3, 16+4g..16+4g+3} (g = lane/16),
-// the key order of the P^T fragment built from the S^T accumulators.
+// V^T fragment of row d holding keys 8g..8g+7 (g = lane/16): the key order of
+// the P^T fragment built from the S^T accumulators (see key_row).
 template <typename T, int DH>
 __device__ __forceinline__ void load_v_frag(Frag<T> &f, const T *tile, int d, int lg) {
   using C = AttnCfg<T, DH>;
   if constexpr (sizeof(T) == 2) {
-    const bf16_t *row = tile + d * C::VCPR * 8;
-    const int c0 = lg >> 1, c1 = 2 + (lg >> 1), h = (lg & 1) * 4;
-    const uint2 a = *reinterpret_cast<const uint2 *>(row + (c0 ^ (d & C::VSW)) * 8 + h);
-    const uint2 b = *reinterpret_cast<const uint2 *>(row + (c1 ^ (d & C::VSW)) * 8 + h);
-    uint4 u = make_uint4(a.x, a.y, b.x, b.y);
-    f.v = *reinterpret_cast<bf16x8 *>(&u);
+    f.load(tile + (d * C::VCPR + (lg ^ C::vswz(d))) * 8);
   } else {
     const float *row = tile + d * C::VCPR * 4;
-    const float4 a = *reinterpret_cast<const float4 *>(row + (lg ^ (d & C::VSW)) * 4);
-    const float4 b = *reinterpret_cast<const float4 *>(row + ((4 + lg) ^ (d & C::VSW)) * 4);
+    const float4 a = *reinterpret_cast<const float4 *>(row + ((2 * lg) ^ C::vswz(d)) * 4);
+    const float4 b = *reinterpret_cast<const float4 *>(row + ((2 * lg + 1) ^ C::vswz(d)) * 4);
     f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
     f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
   }
 }
+
+// Key order of the score tiles: MFMA row q (0..15) of key tile kt holds key
+// 8*(q/4) + 4*kt + q%4 of the 32-key tile, so the accumulator element i of
+// lane group g is key 8g + 4kt + i and a lane's eight probabilities are the
+// consecutive keys 8g..8g+7.
+__device__ __forceinline__ int key_row(int q, int kt) { return ((q >> 2) << 3) | (kt << 2) | (q & 3); }
 
 __device__ __forceinline__ void mask_frag(Frag<bf16_t> &f, const uint32_t *m) {
   uint4 u = *reinterpret_cast<uint4 *>(&f.v);
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
     for (int j = 0; j < C::KINS / 4; ++j) {
       const int blk = wave + 4 * j;
       const int p = blk * 64 + lane;
-      const int r = p / C::KCPR, c = (p % C::KCPR) ^ (r & C::KSW);
+      const int r = p / C::KCPR, c = (p % C::KCPR) ^ C::kswz(r);
       int m = t0 + r;
       m = m < k_lo ? k_lo : (m >= k_hi ? k_hi - 1 : m);
       const T *src = Kg + static_cast<long long>(m) * DH + c * C::VEC;
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
     for (int j = 0; j < C::VINS / 4; ++j) {
       const int blk = wave + 4 * j;
       const int p = blk * 64 + lane;
-      const int d = p / C::VCPR, c = (p % C::VCPR) ^ (d & C::VSW);
+      const int d = p / C::VCPR, c = (p % C::VCPR) ^ C::vswz(d);
       int k0 = t0 + c * C::VEC;
       k0 = k0 > vld - C::VEC ? vld - C::VEC : k0;
       const T *src = Vg + static_cast<long long>(d) * vld + k0;
@@ -345,12 +351,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
     // while the MFMAs of step s run
     Frag<T> kf[2][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) load_k_frag<T, DH>(kf[0][kt], kb, kt * 16 + l16, lg * 8);
+    for (int kt = 0; kt < 2; ++kt) load_k_frag<T, DH>(kf[0][kt], kb, key_row(l16, kt), lg * 8);
 #pragma unroll
     for (int s = 0; s < C::DS; ++s) {
       if (s + 1 < C::DS) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) load_k_frag<T, DH>(kf[(s + 1) & 1][kt], kb, kt * 16 + l16, (s + 1) * 32 + lg * 8);
+        for (int kt = 0; kt < 2; ++kt) load_k_frag<T, DH>(kf[(s + 1) & 1][kt], kb, key_row(l16, kt), (s + 1) * 32 + lg * 8);
       }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -367,7 +373,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = t0 + kt * 16 + lg * 4 + i;
+          const int m = t0 + lg * 8 + kt * 4 + i;
           bool ok = m >= k_lo && m < k_hi;
           if (a.causal) {
             const int pq = qpos[qt];
@@ -410,7 +416,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
     if (edge) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int m = t0 + (e >> 2) * 16 + lg * 4 + (e & 3);
+        const int m = t0 + lg * 8 + e;
         const bool ok = m >= k_lo && m < k_hi;
         if constexpr (sizeof(T) == 2) {
           if ((e & 1) == 0) vm[e >> 1] = 0;
@@ -473,6 +479,275 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
         *reinterpret_cast<float4 *>(op + dt * 16 + lg * 4) =
             make_float4(o[dt][qt][0], o[dt][qt][1], o[dt][qt][2], o[dt][qt][3]);
       if (lg == 0) {
+        a.ml_part[prow * 2] = m_run[qt];
+        a.ml_part[prow * 2 + 1] = l;
+      }
+    }
+  }
+}
+
+// Split-head form (bf16, d_h 256 / 512): eight waves in four pairs.  The two
+// waves of a pair take the same 16*QT query rows and one half of the head
+// dimension each, so a wave holds Q and the O accumulator of its half only
+// (half the registers: two waves per SIMD instead of one).  Per 32-key tile
+// each wave computes the partial scores S^T over its half, the pair swaps
+// them through LDS and adds (IEEE addition commutes: both waves hold the
+// same scores), both run the same online softmax, and each wave computes
+// P V for its half of the output.  Grid, query blocks, key slices and the
+// split partials are those of attn_fwd_kernel.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int DH>
+__global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
+  using T = bf16_t;
+  using C = AttnCfg<T, DH>;
+  constexpr int QT = C::QT;
+  constexpr int HALF = DH / 2, DSH = HALF / 32, DTH = HALF / 16;
+  static_assert(C::KINS % 8 == 0 && C::VINS % 8 == 0, "eight waves share each tile");
+  __shared__ __attribute__((aligned(16))) T sK0[C::KCH * C::VEC];
+  __shared__ __attribute__((aligned(16))) T sK1[C::KCH * C::VEC];
+  __shared__ __attribute__((aligned(16))) T sV0[C::VCH * C::VEC];
+  __shared__ __attribute__((aligned(16))) T sV1[C::VCH * C::VEC];
+  __shared__ __attribute__((aligned(16))) float xs[8][2 * QT * 4][64];   // partial scores per wave
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave >> 1, hf = wave & 1;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int R = a.n_rep * a.n_tok;
+  const int qblocks = (R + C::BQ - 1) / C::BQ;
+  int L = blockIdx.y * gridDim.x + blockIdx.x;
+  const int total = gridDim.x * gridDim.y;
+  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  const int qb = L % qblocks;
+  const int split = (L / qblocks) % a.n_split;
+  const int g = L / (qblocks * a.n_split);
+  const int r0 = qb * C::BQ;
+  const int r1 = min(R, r0 + C::BQ);
+
+  int lo = a.key_lo, hi = a.kv_len + a.n_tok;
+  if (a.causal) {
+    int jmin = r0 % a.n_tok, jmax = (r1 - 1) % a.n_tok;
+    if (r0 / a.n_tok != (r1 - 1) / a.n_tok) {
+      jmin = 0;
+      jmax = a.n_tok - 1;
+    }
+    hi = a.kv_len + jmax + 1;
+    lo = a.sliding ? max(0, a.kv_len + jmin - a.window + 1) : 0;
+  }
+  const int span = max(0, hi - lo);
+  int chunk = (span + a.n_split - 1) / a.n_split;
+  chunk = (chunk + kBKV - 1) / kBKV * kBKV;
+  const int k_lo = lo + split * chunk;
+  const int k_hi = min(hi, k_lo + chunk);
+  const int t_first = (k_lo / kBKV) * kBKV;
+  const int n_tiles = k_hi > k_lo ? (k_hi - t_first + kBKV - 1) / kBKV : 0;
+
+  int qrow[QT], qpos[QT];
+  bool qval[QT];
+  Frag<T> qf[QT][DSH];
+  const T *Q = static_cast<const T *>(a.q);
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int r = r0 + pair * 16 * QT + qt * 16 + l16;
+    qval[qt] = r < r1;
+    const int rr = qval[qt] ? r : r0;
+    const int h = g * a.n_rep + rr / a.n_tok;
+    const int j = rr % a.n_tok;
+    qrow[qt] = rr;
+    qpos[qt] = a.kv_len + j;
+    const T *qp = Q + static_cast<long long>(j) * a.q_ld + h * DH + hf * HALF;
+#pragma unroll
+    for (int s = 0; s < DSH; ++s) {
+      if (qval[qt]) qf[qt][s].load(qp + s * 32 + lg * 8);
+      else qf[qt][s].zero();
+    }
+  }
+
+  f32x4 o[DTH][QT];
+#pragma unroll
+  for (int dt = 0; dt < DTH; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) o[dt][qt] = zero4();
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -1e30f;
+    l_run[qt] = 0.f;
+  }
+
+  const T *Kg = static_cast<const T *>(a.k_cache) + g * a.cache_hs;
+  const T *Vg = static_cast<const T *>(a.v_cache) + g * a.vcache_hs;
+  const int vld = a.vcache_ld;
+
+  auto issue = [&](int t0, T *kb, T *vb) {
+#pragma unroll
+    for (int j = 0; j < C::KINS / 8; ++j) {
+      const int blk = wave + 8 * j;
+      const int p = blk * 64 + lane;
+      const int r = p / C::KCPR, c = (p % C::KCPR) ^ C::kswz(r);
+      int m = t0 + r;
+      m = m < k_lo ? k_lo : (m >= k_hi ? k_hi - 1 : m);
+      const T *src = Kg + static_cast<long long>(m) * DH + c * C::VEC;
+      __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(kb + blk * 64 * C::VEC), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < C::VINS / 8; ++j) {
+      const int blk = wave + 8 * j;
+      const int p = blk * 64 + lane;
+      const int d = p / C::VCPR, c = (p % C::VCPR) ^ C::vswz(d);
+      int k0 = t0 + c * C::VEC;
+      k0 = k0 > vld - C::VEC ? vld - C::VEC : k0;
+      const T *src = Vg + static_cast<long long>(d) * vld + k0;
+      __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(vb + blk * 64 * C::VEC), 16, 0, 0);
+    }
+  };
+
+  auto compute = [&](int t0, const T *kb, const T *vb) {
+    // ---- partial S^T = K Q^T over this wave's half of the head dimension
+    f32x4 st[2][QT];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) st[kt][qt] = zero4();
+    Frag<T> kf[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) load_k_frag<T, DH>(kf[0][kt], kb, key_row(l16, kt), hf * HALF + lg * 8);
+#pragma unroll
+    for (int s = 0; s < DSH; ++s) {
+      if (s + 1 < DSH) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          load_k_frag<T, DH>(kf[(s + 1) & 1][kt], kb, key_row(l16, kt), hf * HALF + (s + 1) * 32 + lg * 8);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) mma(st[kt][qt], kf[s & 1][kt], qf[qt][s]);
+    }
+    // ---- swap halves with the partner wave and add
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[wave][(kt * QT + qt) * 4 + i][lane] = st[kt][qt][i];
+    lds_sync();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[kt][qt][i] += xs[wave ^ 1][(kt * QT + qt) * 4 + i][lane];
+    // ---- mask, online softmax (identical in both waves of the pair)
+    Frag<T> pf[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float sv[8];
+      float mt = -1e30f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = t0 + lg * 8 + kt * 4 + i;
+          bool ok = m >= k_lo && m < k_hi;
+          if (a.causal) {
+            const int pq = qpos[qt];
+            ok = ok && (m <= pq) && (!a.sliding || m > pq - a.window);
+          }
+          const float v = ok ? st[kt][qt][i] : -INFINITY;
+          sv[kt * 4 + i] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run[qt], mt);
+      const float corr = __expf(m_run[qt] - m_new);
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sv[e] = __expf(sv[e] - m_new);
+        psum += sv[e];
+      }
+      l_run[qt] = l_run[qt] * corr + psum;
+      m_run[qt] = m_new;
+      if (__ballot(corr != 1.0f) != 0ull) {
+#pragma unroll
+        for (int dt = 0; dt < DTH; ++dt) {
+          o[dt][qt][0] *= corr;
+          o[dt][qt][1] *= corr;
+          o[dt][qt][2] *= corr;
+          o[dt][qt][3] *= corr;
+        }
+      }
+      pf[qt].from_floats(sv);
+    }
+    // ---- O^T += V^T P^T over this wave's half (edge tiles: values of keys
+    // outside the range are zeroed)
+    const bool edge = (t0 < k_lo) || (t0 + kBKV > k_hi);
+    uint32_t vm[4];
+    if (edge) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int m = t0 + lg * 8 + e;
+        const bool ok = m >= k_lo && m < k_hi;
+        if ((e & 1) == 0) vm[e >> 1] = 0;
+        vm[e >> 1] |= ok ? ((e & 1) ? 0xffff0000u : 0x0000ffffu) : 0u;
+      }
+    }
+    Frag<T> vf[2];
+    load_v_frag<T, DH>(vf[0], vb, hf * HALF + l16, lg);
+#pragma unroll
+    for (int dt = 0; dt < DTH; ++dt) {
+      if (dt + 1 < DTH) load_v_frag<T, DH>(vf[(dt + 1) & 1], vb, hf * HALF + (dt + 1) * 16 + l16, lg);
+      Frag<T> v = vf[dt & 1];
+      if (edge) mask_frag(v, vm);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) mma(o[dt][qt], v, pf[qt]);
+    }
+  };
+
+  if (n_tiles > 0) issue(t_first, sK0, sV0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int it = 0; it < n_tiles; it += 2) {
+    const int t0 = t_first + it * kBKV;
+    if (it + 1 < n_tiles) issue(t0 + kBKV, sK1, sV1);
+    compute(t0, sK0, sV0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 1 >= n_tiles) break;
+    if (it + 2 < n_tiles) issue(t0 + 2 * kBKV, sK0, sV0);
+    compute(t0 + kBKV, sK1, sV1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---- finish: lanes sharing a query (same l16) hold partial sums of l
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float l = l_run[qt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (!qval[qt]) continue;
+    const int rr = qrow[qt];
+    if (a.n_split == 1) {
+      const int h = g * a.n_rep + rr / a.n_tok;
+      const int j = rr % a.n_tok;
+      T *op = static_cast<T *>(a.out) + static_cast<long long>(j) * a.out_ld + h * DH + hf * HALF;
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DTH; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) op[dt * 16 + lg * 4 + i] = f32_to_bf16(o[dt][qt][i] * inv);
+    } else {
+      const long long prow = static_cast<long long>(split) * a.Hkv * R + static_cast<long long>(g) * R + rr;
+      float *op = a.o_part + prow * DH + hf * HALF;
+#pragma unroll
+      for (int dt = 0; dt < DTH; ++dt)
+        *reinterpret_cast<float4 *>(op + dt * 16 + lg * 4) =
+            make_float4(o[dt][qt][0], o[dt][qt][1], o[dt][qt][2], o[dt][qt][3]);
+      if (lg == 0 && hf == 0) {
         a.ml_part[prow * 2] = m_run[qt];
         a.ml_part[prow * 2 + 1] = l;
       }
@@ -549,7 +824,14 @@ hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
   using C = AttnCfg<T, DH>;
   const int R = a.n_rep * a.n_tok;
   const int qblocks = (R + C::BQ - 1) / C::BQ;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, DH>), dim3(a.Hkv * qblocks, a.n_split), dim3(256), 0, s, a);
+  if constexpr (sizeof(T) == 2 && (DH == 256 || DH == 512)) {
+    if (DG_ATTN_PAIR)
+      hipLaunchKernelGGL((attn_pair_kernel<DH>), dim3(a.Hkv * qblocks, a.n_split), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<T, DH>), dim3(a.Hkv * qblocks, a.n_split), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DH>), dim3(a.Hkv * qblocks, a.n_split), dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(a.Hkv * R), dim3(DH / 4 < 256 ? DH / 4 : 256), 0, s, a, DH);
