@@ -44,12 +44,17 @@ class KVLayer(ctypes.Structure):
 class MoeCfg(ctypes.Structure):
     _fields_ = [("hidden", c_int), ("n_experts", c_int), ("top_k", c_int), ("ffn", c_int),
                 ("shared_ffn", c_int), ("route_scale", c_float), ("rms_eps", c_float),
-                ("layer_scalar", c_float), ("dtype", c_int)]
+                ("layer_scalar", c_float), ("dtype", c_int), ("expert_format", c_int)]
+
+
+MOE_W_NAMES = ("w_in_norm", "w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
+               "s_gate", "s_up", "s_down", "ss_gate", "ss_up", "ss_down")
+EXPERT_MATRICES = ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+_EF = {"dtype": 0, "fp8_e4m3": 1}
 
 
 class MoeW(ctypes.Structure):
-    _fields_ = [(n, c_void) for n in ("w_in_norm", "w_router", "w_gate", "w_up", "w_down",
-                                      "ws_gate", "ws_up", "ws_down")]
+    _fields_ = [(n, c_void) for n in MOE_W_NAMES]
 
 
 class SamplerCfg(ctypes.Structure):
@@ -108,6 +113,7 @@ def lib(path=None):
             "dg_moe_workspace_bytes": (c_size, [P(MoeCfg), c_int]),
             "dg_moe_block": (c_int, [P(MoeCfg), P(MoeW), c_int, c_void, c_void, c_void, c_void, c_void, c_size,
                                      c_void]),
+            "dg_quantize_fp8": (c_int, [c_int, c_void, ctypes.c_longlong, c_int, c_void, c_void, c_void]),
             "dg_sample_workspace_bytes": (c_size, [c_int, c_int]),
             "dg_sample_renoise": (c_int, [P(SamplerCfg), c_int, c_void, c_int, c_void, c_void, c_void, c_void,
                                           c_void, c_void, c_size, c_void]),
@@ -177,12 +183,12 @@ def attn_w_c(w):
 
 def moe_cfg_c(c, layer_scalar=None):
     return MoeCfg(c["hidden"], c["n_experts"], c["top_k"], c["ffn"], c["shared_ffn"], c["route_scale"],
-                  c["rms_eps"], c["layer_scalar"] if layer_scalar is None else layer_scalar, _DT[c["dtype"]])
+                  c["rms_eps"], c["layer_scalar"] if layer_scalar is None else layer_scalar, _DT[c["dtype"]],
+                  _EF[c.get("expert_format", "dtype")])
 
 
 def moe_w_c(w):
-    return MoeW(*(ptr(w.get(n)) for n in ("w_in_norm", "w_router", "w_gate", "w_up", "w_down",
-                                          "ws_gate", "ws_up", "ws_down")))
+    return MoeW(*(ptr(w.get(n)) for n in MOE_W_NAMES))
 
 
 def sampler_cfg_c(c):
@@ -231,6 +237,37 @@ def dg_moe_block(cfg, w, x, router_logits=None, want_topk=False, stream=None):
     check(L.dg_moe_block(ctypes.byref(c), ctypes.byref(moe_w_c(w)), n, ptr(x), ptr(rl), ptr(idx), ptr(wts),
                          ptr(ws), ws.numel(), stream_handle(stream)), "dg_moe_block")
     return idx, wts
+
+
+def _dtype_name(t):
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.float32:
+        return "f32"
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def dg_quantize_fp8(w, stream=None):
+    """Row-wise OCP E4M3 codes and fp32 row scales of w [..., K] (bf16/fp32)."""
+    w = w.contiguous()
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    sc = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    check(lib().dg_quantize_fp8(_DT[_dtype_name(w)], ptr(w), rows, K, ptr(q), ptr(sc), stream_handle(stream)),
+          "dg_quantize_fp8")
+    return q, sc
+
+
+def quantize_moe_weights(w, stream=None):
+    """A MoE weight dict with every expert matrix as E4M3 codes + row scales
+    (use with cfg["expert_format"] = "fp8_e4m3")."""
+    out = dict(w)
+    for n in EXPERT_MATRICES:
+        q, sc = dg_quantize_fp8(w[n], stream)
+        out[n] = q
+        out["s" + n[1:] if n.startswith("w_") else "ss" + n[2:]] = sc
+    return out
 
 
 def dg_sample_renoise(scfg, logits, want_rowstats=True, stream=None):

@@ -444,6 +444,8 @@ int check_moe_cfg(const dg_moe_cfg *c) {
     return DG_ERR_SHAPE;
   if (c->n_experts <= 0 || c->n_experts > 256 || c->top_k <= 0 || c->top_k > 8 || c->top_k > c->n_experts)
     return DG_ERR_SHAPE;
+  if (c->expert_format != DG_EXPERTS_DTYPE && c->expert_format != DG_EXPERTS_FP8_E4M3) return DG_ERR_UNSUPPORTED;
+  if (c->expert_format == DG_EXPERTS_FP8_E4M3 && c->dtype != DG_BF16) return DG_ERR_UNSUPPORTED;
   return DG_OK;
 }
 
@@ -504,11 +506,17 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   gu.C = ws.H;
   gu.ldc = fmax;
   const long long moe_rows = static_cast<long long>(n) * (k + 1);
+  const bool fp8 = c->expert_format == DG_EXPERTS_FP8_E4M3;
+  gu.bs0 = w->s_gate;
+  gu.bs1 = w->s_up;
+  gu.bxs0 = w->ss_gate;
+  gu.bxs1 = w->ss_up;
   // the wide-tile kernel measured slower than the streaming one on expert groups
-  const bool wide = DG_WIDE_EXPERTS && rows_per_expert <= 48 && wide_ok(dt, gu, WIDE_EXPERT_GU, n);
+  const bool wide = !fp8 && DG_WIDE_EXPERTS && rows_per_expert <= 48 && wide_ok(dt, gu, WIDE_EXPERT_GU, n);
   {
     TimedLaunch tl(DG_KT_MOE_GATEUP, s);
-    if (wide) DG_HIP(launch_gemm_wide(gu, EPI_SWIGLU, WIDE_EXPERT_GU, s));
+    if (fp8) DG_HIP(launch_gemm_f8_grouped(gu, EPI_SWIGLU, mtile, s));
+    else if (wide) DG_HIP(launch_gemm_wide(gu, EPI_SWIGLU, WIDE_EXPERT_GU, s));
     else DG_HIP(sgemm(dt, gu, EPI_SWIGLU, mtile, DG_MOE_NT_GU, s));
   }
 
@@ -534,9 +542,12 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   dn.C = ws.Y;
   dn.ldc = D;
   dn.rowscale = ws.row_weight;
+  dn.bs0 = w->s_down;
+  dn.bxs0 = w->ss_down;
   {
     TimedLaunch tl(DG_KT_MOE_DOWN, s);
-    if (wide && wide_ok(dt, dn, WIDE_EXPERT_DN, moe_rows))
+    if (fp8) DG_HIP(launch_gemm_f8_grouped(dn, EPI_ROWSCALE_F32, mtile, s));
+    else if (wide && wide_ok(dt, dn, WIDE_EXPERT_DN, moe_rows))
       DG_HIP(launch_gemm_wide(dn, EPI_ROWSCALE_F32, WIDE_EXPERT_DN, s));
     else if (DG_DOWN_COLS && mtile == DG_MOE_MT && wide_ok(dt, dn, WIDE_EXPERT_DN, moe_rows))
       DG_HIP(launch_gemm_cols(dn, EPI_ROWSCALE_F32, DG_MOE_MT, DG_COLS_NT, s));   // k = ffn is short
@@ -558,6 +569,9 @@ int check_moe_call(const dg_moe_cfg *c, const dg_moe_w *w, int n, const void *x,
   if (!w->w_in_norm || !w->w_gate || !w->w_up || !w->w_down || !w->ws_gate || !w->ws_up || !w->ws_down)
     return DG_ERR_NULL;
   if (!rl_in && !w->w_router) return DG_ERR_NULL;
+  if (c->expert_format == DG_EXPERTS_FP8_E4M3 &&
+      (!w->s_gate || !w->s_up || !w->s_down || !w->ss_gate || !w->ss_up || !w->ss_down))
+    return DG_ERR_NULL;
   if (n < 0) return DG_ERR_SHAPE;
   return DG_OK;
 }
@@ -802,6 +816,16 @@ int dg_moe_block(const dg_moe_cfg *cfg, const dg_moe_w *w, int n_tok, void *x, c
   if (ws_bytes < moe_ws_bytes(cfg, n_tok)) return DG_ERR_WORKSPACE;
   Carve cv(ws);
   return moe_impl(cfg, w, n_tok, x, rl_in, idx_out, w_out, cv, static_cast<hipStream_t>(stream));
+}
+
+int dg_quantize_fp8(int dtype, const void *w, long long rows, int cols, uint8_t *q, float *scale, void *stream) {
+  if (!dtype_ok(dtype)) return DG_ERR_DTYPE;
+  if (rows < 0 || cols <= 0 || rows > 0x7fffffffLL) return DG_ERR_SHAPE;
+  if (rows == 0) return DG_OK;
+  if (!w || !q || !scale) return DG_ERR_NULL;
+  if (launch_quantize_fp8(dtype, w, rows, cols, q, scale, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DG_ERR_HIP;
+  return DG_OK;
 }
 
 size_t dg_sample_workspace_bytes(int n_pos, int vocab) {

@@ -224,10 +224,25 @@ struct GemmArgs {
   long long ldc;
   const float *rowscale;
   int tile_order;   // 0: consecutive tiles share B columns (m fastest), 1: share A rows (n fastest)
+  // fp8 weights (launch_gemm_f8_grouped): one fp32 scale per weight row;
+  // routed expert e's rows scale by bs0/bs1 + e*N, the shared expert's by bxs0/bxs1
+  const float *bs0, *bs1, *bxs0, *bxs1;
 };
 
 template <typename T>
 hipError_t launch_gemm(const GemmArgs &a, int mode, int bm, int bn, hipStream_t s);
+// Grouped expert product with OCP E4M3 weights ([N][K] bytes per expert) and
+// bf16 activations; mode EPI_SWIGLU or EPI_ROWSCALE_F32, mt = 2 or 4.
+hipError_t launch_gemm_f8_grouped(const GemmArgs &a, int mode, int mt, hipStream_t s);
+#ifndef DG_F8_NT_GU
+#define DG_F8_NT_GU 2
+#endif
+#ifndef DG_F8_NT_DN
+#define DG_F8_NT_DN 4
+#endif
+#ifndef DG_F8_S
+#define DG_F8_S 2
+#endif
 // Tile shapes of the streaming products (in 16x16 MFMA tiles) and ring depth.
 #ifndef DG_DENSE_MT
 #define DG_DENSE_MT 4

@@ -94,6 +94,9 @@ hipError_t launch_rmsnorm(int dtype, int n, int D, float eps, const void *x, con
 hipError_t launch_embed(int dtype, const int32_t *tokens, int n, int D, int vocab, const void *E, void *x,
                         hipStream_t s);
 hipError_t launch_transpose(int dtype, int rows, int cols, const void *in, void *out, hipStream_t s);
+// q[r][c] = E4M3(w[r][c] / scale[r]), scale[r] = max_c |w[r][c]| / 448
+hipError_t launch_quantize_fp8(int dtype, const void *w, long long rows, int cols, uint8_t *q, float *scale,
+                               hipStream_t s);
 
 // Residual update + the next block's RMSNorm (rows up to residual_norm_max_width()).
 int residual_norm_max_width();

@@ -464,6 +464,109 @@ __device__ __forceinline__ void stream_tile(const GemmArgs &a, float *red, int r
   }
 }
 
+// Epilogue of the streaming tiles: the four waves' partial accumulators
+// (each over its own k stages) are summed through LDS in wave order, so the
+// result does not depend on timing.  SCALED multiplies column c of the first
+// (and second) product by sc0[c] (sc1[c]) before the mode's operation: the
+// per-row scales of fp8 weight matrices, sc0/sc1 pointing at the tile's
+// first column.
+template <int MT, int NT, int NB, int MODE, bool SCALED>
+__device__ __forceinline__ void stream_epilogue(const GemmArgs &a, float *red, const f32x4 (&acc)[NB][MT][NT],
+                                                int row_begin, int rows, int n0, int ncols, int split,
+                                                const float *sc0, const float *sc1) {
+  constexpr int EL = NB * MT * NT * 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __syncthreads();   // LDS may still be read by the previous tile's epilogue
+  {
+    float *dst = red + wave * EL * 64;
+    int e = 0;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i, ++e) dst[e * 64 + lane] = acc[nb][mt][nt][i];
+  }
+  __syncthreads();
+  // Each thread adds up and stores 4 neighbouring lanes of one accumulator
+  // element: 4 consecutive columns of one row (float4 LDS reads, 16- or
+  // 8-byte stores).
+  constexpr int EH = EL / NB;
+  for (int q = tid; q < EH * 16; q += 256) {
+    const int l4 = (q & 15) * 4, e = q >> 4;
+    const int i = e & 3, nt = (e >> 2) % NT, mt = (e >> 2) / NT;
+    const int r = mt * 16 + (l4 >> 4) * 4 + i;
+    const int c = nt * 16 + (l4 & 15);
+    if (r >= rows || c >= ncols) continue;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4 t = *reinterpret_cast<const float4 *>(red + (w * EL + e) * 64 + l4);
+      v[0] += t.x; v[1] += t.y; v[2] += t.z; v[3] += t.w;
+    }
+    if constexpr (SCALED) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] *= sc0[c + (j < ncols - c ? j : 0)];
+    }
+    if constexpr (MODE == EPI_SWIGLU) {
+      float u[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float4 t = *reinterpret_cast<const float4 *>(red + (w * EL + EH + e) * 64 + l4);
+        u[0] += t.x; u[1] += t.y; u[2] += t.z; u[3] += t.w;
+      }
+      if constexpr (SCALED) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] *= sc1[c + (j < ncols - c ? j : 0)];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = silu_f(v[j]) * u[j];
+    }
+    const long long row = row_begin + r;
+    const int col = n0 + c;
+    const int nv = ncols - c < 4 ? ncols - c : 4;   // valid columns of the four
+    if constexpr (MODE == EPI_STORE_F32 || MODE == EPI_ROWSCALE_F32 || MODE == EPI_PARTIAL_F32) {
+      if constexpr (MODE == EPI_ROWSCALE_F32) {
+        const float rs = a.rowscale[row];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] *= rs;
+      }
+      const long long off = (MODE == EPI_PARTIAL_F32 ? (static_cast<long long>(split) * a.M + row) : row) * a.ldc + col;
+      float *cp = static_cast<float *>(a.C) + off;
+      if (nv == 4 && (off & 3) == 0) {
+        *reinterpret_cast<float4 *>(cp) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        for (int j = 0; j < nv; ++j) cp[j] = v[j];
+      }
+    } else {
+      bf16_t *cp = static_cast<bf16_t *>(a.C) + row * a.ldc + col;
+      const bool vec = nv == 4 && ((row * a.ldc + col) & 3) == 0;
+      if constexpr (MODE == EPI_ADD) {
+        if (vec) {
+          const uint2 o = *reinterpret_cast<const uint2 *>(cp);
+          v[0] += __uint_as_float(o.x << 16);
+          v[1] += __uint_as_float(o.x & 0xffff0000u);
+          v[2] += __uint_as_float(o.y << 16);
+          v[3] += __uint_as_float(o.y & 0xffff0000u);
+        } else {
+          for (int j = 0; j < nv; ++j) v[j] += bf16_to_f32(cp[j]);
+        }
+      }
+      if (vec) {
+        uint2 o;
+        o.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+        o.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        *reinterpret_cast<uint2 *>(cp) = o;
+      } else {
+        for (int j = 0; j < nv; ++j) cp[j] = f32_to_bf16(v[j]);
+      }
+    }
+  }
+}
+
 // bf16 form with row-contiguous loads: 64-deep k stages (wave w takes
 // stages w, w+4, ...), each 16-row block of A and B fetched as two loads of
 // 8 whole rows and turned into the two fragments of the stage with DPP row
@@ -472,7 +575,6 @@ template <int MT, int NT, int NB, int MODE, int S>
 __device__ __forceinline__ void stream_tile_c(const GemmArgs &a, float *red, int row_begin, int rows,
                                               const bf16_t *const *Bp, int n0, int ncols, int kb, int ke,
                                               int split) {
-  constexpr int EL = NB * MT * NT * 4;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cr = contig_row(lane), cc = contig_chunk(lane);
@@ -560,86 +662,200 @@ __device__ __forceinline__ void stream_tile_c(const GemmArgs &a, float *red, int
     }
   }
 
-  __syncthreads();   // LDS may still be read by the previous tile's epilogue
-  {
-    float *dst = red + wave * EL * 64;
-    int e = 0;
+  stream_epilogue<MT, NT, NB, MODE, false>(a, red, acc, row_begin, rows, n0, ncols, split, nullptr, nullptr);
+}
+
+// ----------------------------------------------------------------------------
+// Expert products with OCP E4M3 weights (one fp32 scale per weight row) and
+// bf16 activations.  The kernel is bound by streaming the weights, so the
+// bytes are what fp8 saves; each weight byte is widened to bf16 in registers
+// (exact: every E4M3 value is a bf16 value) and the products run on the
+// bf16 MFMA, with the row scales applied in the epilogue.
+//
+// k stages are 128 deep (128 weight bytes per row, one whole cache line).
+// A 16-row weight block of a stage is two row-contiguous loads (8 rows x
+// 128 bytes each), turned by contig_to_frags into two 16-byte pieces per
+// lane: row l16, bytes 16*lg.. (f0) and 64 + 16*lg.. (f1).  Each piece
+// widens to two bf16 fragments.  The MFMA k order inside the stage is
+// therefore: step ks, lane group lg, element i  <->  depth
+// 64*(ks/2) + 16*lg + 8*(ks%2) + i; the activation fragments are loaded in
+// the same order (per 64-deep half, lane group lg takes the 8-element
+// chunks 2*lg and 2*lg+1 of its rows, again as 8 rows x 128 bytes).
+// With k % 128 == 64 the last stage is 64 deep: its second-half loads
+// re-read the first half (in bounds) and the second-half activation
+// fragments are zeroed, so those products add exactly 0.
+
+__device__ __forceinline__ void e4m3x16_to_bf16(const bf16x8 &raw, bf16x8 &lo, bf16x8 &hi) {
+  uint32_t w[4], o[8];
+  __builtin_memcpy(w, &raw, 16);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], 1.0f, false);   // bytes 0, 1
+    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], 1.0f, true);    // bytes 2, 3
+    __builtin_memcpy(&o[2 * j], &p0, 4);
+    __builtin_memcpy(&o[2 * j + 1], &p1, 4);
+  }
+  __builtin_memcpy(&lo, &o[0], 16);
+  __builtin_memcpy(&hi, &o[4], 16);
+}
+
+template <int MT, int NT, int NB, int MODE, int S>
+__device__ __forceinline__ void stream_tile_f8(const GemmArgs &a, float *red, int row_begin, int rows,
+                                               const uint8_t *const *Bp, const float *const *Sp, int n0,
+                                               int ncols, int K) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cr = contig_row(lane), cb = contig_chunk(lane);
+  const int hb = (lane & 15) >> 3, lg = lane >> 4;
+  const int ca = 2 * lg + hb;   // activation chunk (8 elements) inside a 64-deep half
+
+  uint32_t ao[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = mt * 16 + h * 8 + cr;
+      int pr = row_begin + (r < rows ? r : 0);
+      if (a.a_rows) pr = a.a_rows[pr];
+      ao[mt][h] = (static_cast<uint32_t>(pr) * static_cast<uint32_t>(a.lda) + ca * 8) * 2u;
+    }
+  uint32_t bo[NT][2];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = nt * 16 + h * 8 + cr;
+      bo[nt][h] = static_cast<uint32_t>(c < ncols ? c : 0) * static_cast<uint32_t>(a.ldb) + cb * 16;
+    }
+  const char *Ab = static_cast<const char *>(a.A);
+  const char *B0 = reinterpret_cast<const char *>(Bp[0]);
+  const char *B1 = reinterpret_cast<const char *>(Bp[NB - 1]);
+
+  f32x4 acc[NB][MT][NT];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nb][mt][nt] = zero4();
+
+  const int nst = (K + 127) >> 7;
+  const int my = nst > wave ? (nst - wave + 3) / 4 : 0;
+
+  bf16x8 xa[S][MT][2][2];   // [slot][mt][64-deep half][8-row load]
+  bf16x8 xb[S][NB][NT][2];
+  auto load = [&](int it, bf16x8(&ya)[MT][2][2], bf16x8(&yb)[NB][NT][2]) {
+    const int st = wave + 4 * it;
+    const bool half = (st + 1) * 128 > K;
+    const uint32_t kb = static_cast<uint32_t>(st) * 128u - ((half && hb) ? 64u : 0u);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          yb[nb][nt][h] = *reinterpret_cast<const bf16x8 *>((nb == 0 ? B0 : B1) + (bo[nt][h] + kb));
+#pragma unroll
+    for (int jh = 0; jh < 2; ++jh) {
+      const uint32_t ka = (static_cast<uint32_t>(st) * 128u + (half ? 0u : 64u * jh)) * 2u;
+#pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i, ++e) dst[e * 64 + lane] = acc[nb][mt][nt][i];
-  }
-  __syncthreads();
-  // Each thread adds up and stores 4 neighbouring lanes of one accumulator
-  // element: 4 consecutive columns of one row (float4 LDS reads, 16- or
-  // 8-byte stores).
-  constexpr int EH = EL / NB;
-  for (int q = tid; q < EH * 16; q += 256) {
-    const int l4 = (q & 15) * 4, e = q >> 4;
-    const int i = e & 3, nt = (e >> 2) % NT, mt = (e >> 2) / NT;
-    const int r = mt * 16 + (l4 >> 4) * 4 + i;
-    const int c = nt * 16 + (l4 & 15);
-    if (r >= rows || c >= ncols) continue;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float4 t = *reinterpret_cast<const float4 *>(red + (w * EL + e) * 64 + l4);
-      v[0] += t.x; v[1] += t.y; v[2] += t.z; v[3] += t.w;
+        for (int h = 0; h < 2; ++h) ya[mt][jh][h] = *reinterpret_cast<const bf16x8 *>(Ab + (ao[mt][h] + ka));
     }
-    if constexpr (MODE == EPI_SWIGLU) {
-      float u[4] = {0.f, 0.f, 0.f, 0.f};
+  };
+  auto compute = [&](int it, const bf16x8(&ya)[MT][2][2], const bf16x8(&yb)[NB][NT][2]) {
+    const bool half = (wave + 4 * it + 1) * 128 > K;
+    Frag<bf16_t> fa[MT][4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float4 t = *reinterpret_cast<const float4 *>(red + (w * EL + EH + e) * 64 + l4);
-        u[0] += t.x; u[1] += t.y; u[2] += t.z; u[3] += t.w;
+    for (int mt = 0; mt < MT; ++mt) {
+      contig_to_frags(ya[mt][0][0], ya[mt][0][1], fa[mt][0].v, fa[mt][1].v);
+      contig_to_frags(ya[mt][1][0], ya[mt][1][1], fa[mt][2].v, fa[mt][3].v);
+      if (half) {
+        fa[mt][2].v = bf16x8{};
+        fa[mt][3].v = bf16x8{};
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = silu_f(v[j]) * u[j];
     }
-    const long long row = row_begin + r;
-    const int col = n0 + c;
-    const int nv = ncols - c < 4 ? ncols - c : 4;   // valid columns of the four
-    if constexpr (MODE == EPI_STORE_F32 || MODE == EPI_ROWSCALE_F32 || MODE == EPI_PARTIAL_F32) {
-      if constexpr (MODE == EPI_ROWSCALE_F32) {
-        const float rs = a.rowscale[row];
+    // weight fragments are widened one 16-column block at a time
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] *= rs;
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        bf16x8 f0, f1;
+        contig_to_frags(yb[nb][nt][0], yb[nb][nt][1], f0, f1);
+        Frag<bf16_t> fb[4];
+        e4m3x16_to_bf16(f0, fb[0].v, fb[1].v);
+        e4m3x16_to_bf16(f1, fb[2].v, fb[3].v);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) mma(acc[nb][mt][nt], fa[mt][ks], fb[ks]);
       }
-      const long long off = (MODE == EPI_PARTIAL_F32 ? (static_cast<long long>(split) * a.M + row) : row) * a.ldc + col;
-      float *cp = static_cast<float *>(a.C) + off;
-      if (nv == 4 && (off & 3) == 0) {
-        *reinterpret_cast<float4 *>(cp) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
-        for (int j = 0; j < nv; ++j) cp[j] = v[j];
-      }
-    } else {
-      bf16_t *cp = static_cast<bf16_t *>(a.C) + row * a.ldc + col;
-      const bool vec = nv == 4 && ((row * a.ldc + col) & 3) == 0;
-      if constexpr (MODE == EPI_ADD) {
-        if (vec) {
-          const uint2 o = *reinterpret_cast<const uint2 *>(cp);
-          v[0] += __uint_as_float(o.x << 16);
-          v[1] += __uint_as_float(o.x & 0xffff0000u);
-          v[2] += __uint_as_float(o.y << 16);
-          v[3] += __uint_as_float(o.y & 0xffff0000u);
-        } else {
-          for (int j = 0; j < nv; ++j) v[j] += bf16_to_f32(cp[j]);
-        }
-      }
-      if (vec) {
-        uint2 o;
-        o.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-        o.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-        *reinterpret_cast<uint2 *>(cp) = o;
-      } else {
-        for (int j = 0; j < nv; ++j) cp[j] = f32_to_bf16(v[j]);
+  };
+#pragma unroll
+  for (int r = 0; r < S - 1; ++r)
+    if (r < my) load(r, xa[r], xb[r]);
+  for (int i = 0; i < my; i += S) {
+#pragma unroll
+    for (int r = 0; r < S; ++r) {
+      const int it = i + r;
+      if (it < my) {
+        if (it + S - 1 < my) load(it + S - 1, xa[(r + S - 1) % S], xb[(r + S - 1) % S]);
+        compute(it, xa[r], xb[r]);
       }
     }
   }
+  stream_epilogue<MT, NT, NB, MODE, true>(a, red, acc, row_begin, rows, n0, ncols, 0, Sp[0], Sp[NB - 1]);
+}
+
+// Grouped expert product with fp8 weights: blockIdx.y = group (shared-expert
+// row chunks first, then the routed experts), blockIdx.x = column tile.
+// Weight rows are K bytes apart (ldb, ldb_x in bytes); routed expert e's
+// scales start at bs0 + e*N, the shared expert's at bxs0.
+template <int MT, int NT, int NB, int MODE, int S>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 2 ? 2 : 1, 2))) void gemm_f8_grouped_kernel(const GemmArgs a) {
+  constexpr int BM = MT * 16, BN = NT * 16;
+  __shared__ __attribute__((aligned(16))) float red[4 * NB * MT * NT * 4 * 64];
+  const int g = blockIdx.y;
+  const int n0 = blockIdx.x * BN;
+  const bool sh = g < a.n_xgroups;
+  const int Ng = sh ? a.N_x : a.N;
+  if (n0 >= Ng) return;
+  GemmArgs ga = a;
+  const uint8_t *Bp[NB];
+  const float *Sp[NB];
+  if (sh) {
+    ga.K = a.K_x;
+    ga.ldb = a.ldb_x;
+    Bp[0] = static_cast<const uint8_t *>(a.Bx0) + static_cast<long long>(n0) * a.ldb_x;
+    Sp[0] = a.bxs0 + n0;
+    if (NB > 1) {
+      Bp[NB - 1] = static_cast<const uint8_t *>(a.Bx1) + static_cast<long long>(n0) * a.ldb_x;
+      Sp[NB - 1] = a.bxs1 + n0;
+    }
+  } else {
+    const int e = g - a.n_xgroups;
+    const long long off = static_cast<long long>(e) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
+    Bp[0] = static_cast<const uint8_t *>(a.seg_B0[0]) + off;
+    Sp[0] = a.bs0 + static_cast<long long>(e) * a.N + n0;
+    if (NB > 1) {
+      Bp[NB - 1] = static_cast<const uint8_t *>(a.seg_B1[0]) + off;
+      Sp[NB - 1] = a.bs1 + static_cast<long long>(e) * a.N + n0;
+    }
+  }
+  const int r0 = a.g_off[g], r1 = a.g_off[g + 1];
+  for (int rb = r0; rb < r1; rb += BM)
+    stream_tile_f8<MT, NT, NB, MODE, S>(ga, red, rb, min(BM, r1 - rb), Bp, Sp, n0, Ng - n0, ga.K);
+}
+
+template <int MT, int NT, int NB, int MODE, int S>
+hipError_t launch_f8_one(const GemmArgs &a, hipStream_t s) {
+  constexpr int BN = NT * 16;
+  const int nmax = a.N > a.N_x ? a.N : a.N_x;
+  const dim3 grid((nmax + BN - 1) / BN, a.n_groups);
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_f8_grouped_kernel<MT, NT, NB, MODE, S>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 // Column-split form for short depths (the expert down projection, k = 704):
@@ -1236,6 +1452,18 @@ hipError_t launch_gemm_stream(const GemmArgs &a, int mode, int mt, int nt, hipSt
   DG_STREAM_CASE(4, DG_MOE_NT_GU, 2, EPI_SWIGLU, 3)
   DG_STREAM_CASE(4, DG_MOE_NT_DN, 1, EPI_ROWSCALE_F32, 3)
 #undef DG_STREAM_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_f8_grouped(const GemmArgs &a, int mode, int mt, hipStream_t s) {
+  if (!a.g_off || a.K % 64 || a.K_x % 64 || a.ldb % 16 || a.ldb_x % 16 || a.lda % 8) return hipErrorInvalidValue;
+#define DG_F8_CASE(MODE_, MT_, NT_, NB_, S_) \
+  if (mode == MODE_ && mt == MT_) return launch_f8_one<MT_, NT_, NB_, MODE_, S_>(a, s);
+  DG_F8_CASE(EPI_SWIGLU, DG_MOE_MT, DG_F8_NT_GU, 2, DG_F8_S)
+  DG_F8_CASE(EPI_ROWSCALE_F32, DG_MOE_MT, DG_F8_NT_DN, 1, DG_F8_S)
+  DG_F8_CASE(EPI_SWIGLU, 4, DG_F8_NT_GU, 2, DG_F8_S)
+  DG_F8_CASE(EPI_ROWSCALE_F32, 4, DG_F8_NT_DN, 1, DG_F8_S)
+#undef DG_F8_CASE
   return hipErrorInvalidValue;
 }
 

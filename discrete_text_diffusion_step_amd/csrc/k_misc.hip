@@ -138,6 +138,44 @@ __global__ __launch_bounds__(256) void transpose_kernel(int rows, int cols, cons
   }
 }
 
+// fp32 -> OCP E4M3 code: round to nearest, ties to even, magnitudes above
+// 448 saturate to 448 (S.1111.110).  Subnormals are steps of 2^-9 below
+// 2^-6; normals round the fp32 mantissa to 3 bits (a carry moves into the
+// exponent) and rebias the exponent from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), 448.0f);
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+  } else {
+    const uint32_t u = __float_as_uint(a);
+    code = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return (code > 0x7Eu ? 0x7Eu : code) | sign;
+}
+
+// Row-wise E4M3 quantisation, one workgroup per row:
+//   scale = max|w| / 448 (fp32, correctly rounded; 1 for a zero row)
+//   q     = E4M3(w / scale)  (fp32 division, correctly rounded)
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const T *w, int cols, uint8_t *q, float *scale) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long long row = blockIdx.x;
+  const T *wr = w + row * cols;
+  float m = 0.f;
+  for (int c = tid; c < cols; c += 256) m = fmaxf(m, fabsf(to_f32<T>(wr[c])));
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
+  uint8_t *qr = q + row * cols;
+  for (int c = tid; c < cols; c += 256) qr[c] = static_cast<uint8_t>(e4m3_code(__fdiv_rn(to_f32<T>(wr[c]), sc)));
+  if (tid == 0) scale[row] = sc;
+}
+
 }  // namespace
 
 hipError_t launch_rmsnorm(int dtype, int n, int D, float eps, const void *x, const void *w, void *y,
@@ -210,6 +248,20 @@ hipError_t launch_combine_rmsnorm(int dtype, void *x, const float *Y, const int 
     hipLaunchKernelGGL((residual_rmsnorm_kernel<float, 2, true>), grid, dim3(256), 0, s, Y, 0, pair_row, k,
                        layer_scalar, n, D, static_cast<float *>(x), static_cast<const float *>(w), eps, sq,
                        static_cast<float *>(h));
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(int dtype, const void *w, long long rows, int cols, uint8_t *q, float *scale,
+                               hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(rows));
+  if (dtype == DG_BF16)
+    hipLaunchKernelGGL(quantize_fp8_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t *>(w), cols, q,
+                       scale);
+  else
+    hipLaunchKernelGGL(quantize_fp8_kernel<float>, grid, dim3(256), 0, s, static_cast<const float *>(w), cols, q,
+                       scale);
   return hipGetLastError();
 }
 

@@ -143,7 +143,18 @@ typedef struct {
   float rms_eps;
   float layer_scalar;
   int dtype;
+  int expert_format;   /* dg_expert_format */
 } dg_moe_cfg;
+
+/* Storage of the expert matrices (routed and shared).
+ * DG_EXPERTS_DTYPE: in the layer dtype.
+ * DG_EXPERTS_FP8_E4M3: OCP 8-bit E4M3 codes (1 byte each, same [.., N, K]
+ *   layout) with one fp32 scale per matrix row (s_* / ss_* below), as made by
+ *   dg_quantize_fp8; the weight is scale * value(code).  Activations stay in
+ *   the layer dtype, which must be DG_BF16.  The pages run the model in FP8
+ *   (aitrends notebook summary, generation-speed paragraph) without fixing a
+ *   scheme; weight-only FP8 with row scales is the reading taken. */
+typedef enum { DG_EXPERTS_DTYPE = 0, DG_EXPERTS_FP8_E4M3 = 1 } dg_expert_format;
 
 typedef struct {
   const void *w_in_norm; /* [D] pre-MoE RMSNorm weight */
@@ -154,7 +165,23 @@ typedef struct {
   const void *ws_gate;   /* [F_s, D] shared expert */
   const void *ws_up;     /* [F_s, D] */
   const void *ws_down;   /* [D, F_s] */
+  /* fp32 row scales, DG_EXPERTS_FP8_E4M3 only (NULL otherwise) */
+  const float *s_gate;   /* [E, F] */
+  const float *s_up;     /* [E, F] */
+  const float *s_down;   /* [E, D] */
+  const float *ss_gate;  /* [F_s] */
+  const float *ss_up;    /* [F_s] */
+  const float *ss_down;  /* [D] */
 } dg_moe_w;
+
+/* Row-wise OCP E4M3 quantisation of a [rows, cols] matrix w (dtype, device):
+ *   scale[r] = max_c |w[r][c]| / 448 in fp32 (1 for an all-zero row),
+ *   q[r][c]  = E4M3(w[r][c] / scale[r]), fp32 division, rounded to nearest
+ *              with ties to even, saturating at 448.
+ * q [rows, cols] uint8 and scale [rows] fp32 are device buffers owned by the
+ * caller.  Expert stacks [E, N, K] are quantised as E*N rows of K.
+ * Enqueued on stream; returns DG_ERR_SHAPE for rows < 0 or cols <= 0. */
+int dg_quantize_fp8(int dtype, const void *w, long long rows, int cols, uint8_t *q, float *scale, void *stream);
 
 size_t dg_moe_workspace_bytes(const dg_moe_cfg *cfg, int n_tok);
 

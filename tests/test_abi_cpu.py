@@ -118,3 +118,28 @@ def test_model_entry_points_validate():
     assert L.dg_commit_canvas(ctypes.byref(m), None, None, None, 256, None, 0, None) == -1
     mm = B.model_cfg_c(dict(synth.full_model_cfg(), dtype="f32"))   # layer dtypes disagree
     assert L.dg_canvas_step(ctypes.byref(mm), None, None, None, ctypes.byref(s), None, 0, None) == -5
+
+
+def test_fp8_expert_validation_codes():
+    L = B.lib()
+    m = synth.moe_cfg(2816, 128, 8, 704, 704)
+    w8 = B.MoeW(*(ctypes.c_void_p(256) for _ in range(len(B.MOE_W_NAMES))))
+    call = lambda c, ww=w8: L.dg_moe_block(ctypes.byref(c), ctypes.byref(ww), 256, ctypes.c_void_p(256), None,
+                                           None, None, ctypes.c_void_p(256), 1 << 40, None)
+    bad = B.moe_cfg_c(m)
+    bad.expert_format = 5
+    assert call(bad) == -3
+    assert call(B.moe_cfg_c(dict(m, dtype="f32", expert_format="fp8_e4m3"))) == -3
+    no_scale = B.MoeW(*(ctypes.c_void_p(256) for _ in range(len(B.MOE_W_NAMES))))
+    no_scale.s_down = None
+    assert call(B.moe_cfg_c(dict(m, expert_format="fp8_e4m3")), ww=no_scale) == -1
+
+
+def test_quantize_fp8_validation_codes():
+    L = B.lib()
+    p = ctypes.c_void_p(256)
+    assert L.dg_quantize_fp8(7, p, 4, 64, p, p, None) == -5
+    assert L.dg_quantize_fp8(1, p, -1, 64, p, p, None) == -2
+    assert L.dg_quantize_fp8(1, p, 4, 0, p, p, None) == -2
+    assert L.dg_quantize_fp8(1, None, 4, 64, p, p, None) == -1
+    assert L.dg_quantize_fp8(1, p, 0, 64, None, None, None) == 0
