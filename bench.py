@@ -36,11 +36,15 @@ def log(*a):
 
 def gateup_bytes(mcfg, n_tok):
     """Algorithmic HBM bytes of one expert gate/up launch: every expert's gate
-    and up matrices once (128 routed + 1 shared), the gathered token rows and
-    the SwiGLU output rows."""
+    and up matrices once (128 routed + 1 shared; 2 bytes per weight, or 1 byte
+    plus a 4-byte scale per row for fp8 e4m3), the gathered token rows and the
+    SwiGLU output rows."""
     m = mcfg["moe"]
     D, F, Fs, E, k = m["hidden"], m["ffn"], m["shared_ffn"], m["n_experts"], m["top_k"]
-    weights = (E * 2 * F * D + 2 * Fs * D) * 2
+    if m.get("expert_format", "dtype") == "fp8_e4m3":
+        weights = (E * 2 * F * D + 2 * Fs * D) + (E * 2 * F + 2 * Fs) * 4
+    else:
+        weights = (E * 2 * F * D + 2 * Fs * D) * 2
     rows = n_tok * (k + 1)
     return weights + rows * D * 2 + rows * F * 2
 
@@ -109,6 +113,8 @@ def main():
     ap.add_argument("--no-generate", action="store_true", help="skip the adaptive-stop generation run")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="only run the counter workload (copy calibration + MoE layer) for rocprofv3 --pmc")
+    ap.add_argument("--experts", choices=("bf16", "fp8"), default="bf16",
+                    help="expert weight storage: bf16 (the model dtype) or OCP e4m3 with row scales")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -121,7 +127,7 @@ def main():
     from discrete_text_diffusion_step_amd import profiling
     if args.pmc_workload:
         torch.cuda.set_device(0)
-        profiling.pmc_workload()
+        profiling.pmc_workload(fp8=args.experts == "fp8")
         return
     from discrete_text_diffusion_step_amd import binding as B
     from discrete_text_diffusion_step_amd import synth
@@ -137,6 +143,15 @@ def main():
     n_params = sum(t.numel() for t in [w["embed"], w["w_final_norm"]] + list(w["sc"].values())) + sum(
         t.numel() for layer in w["attn"] + w["moe"] for t in layer.values() if t is not None)
     log(f"weights: {n_params / 1e9:.2f}B params generated in {time.time() - t0:.1f}s")
+    fp8 = args.experts == "fp8"
+    if fp8:
+        # every expert matrix (routed and shared) to e4m3 codes + row scales
+        mcfg["moe"]["expert_format"] = "fp8_e4m3"
+        for l in range(len(w["moe"])):
+            w["moe"][l] = B.quantize_moe_weights(w["moe"][l])
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        log("expert weights quantised to fp8 e4m3")
     model = B.Model(mcfg, w)
     cap = args.prompt + args.canvases * CANVAS
     kv = B.KV(mcfg, cap, device=dev)
@@ -205,9 +220,11 @@ def main():
     avg_ms = sum(durs) / len(durs)
     bytes_launch = gateup_bytes(mcfg, CANVAS)
     achieved = bytes_launch / (avg_ms * 1e-3) / 1e9
-    roof = {"kernel": "moe expert gate/up (grouped MFMA GEMM + SwiGLU)", "bound": "hbm",
+    kname = ("moe expert gate/up (grouped MFMA GEMM + SwiGLU, fp8 e4m3 weights widened to bf16)" if fp8 else
+             "moe expert gate/up (grouped MFMA GEMM + SwiGLU)")
+    roof = {"kernel": kname, "bound": "hbm",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiling.read_traffic(),
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiling.read_traffic(fp8=fp8),
             "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": bytes_launch, "launches": len(durs)}
 
     tpf_full = CANVAS / 48.0
@@ -221,13 +238,14 @@ def main():
         "config": {"workload": "30-layer DiffusionGemma-style canvas denoise step: 25 sliding (W 1024) + 5 global "
                                "layers, hidden 2816, 128 experts top-8 + shared (SwiGLU 704), vocab 262144, "
                                "256-token canvas after a 4096-token prompt",
-                   "canvas": CANVAS, "committed_rows": P, "params": n_params, "adaptive_stop_in_timed_loop": False},
+                   "canvas": CANVAS, "committed_rows": P, "params": n_params, "adaptive_stop_in_timed_loop": False,
+                   "expert_weights": "fp8_e4m3 (row scales)" if fp8 else "bf16"},
         "eff_tok_s": eff, "tokens_per_forward": {"full_schedule": round(tpf_full, 3), "pages": 20},
         "commit_ms": round(commit, 3), "prefill_ms": round(prefill_ms, 1),
         "roofline": roof,
         "generation": gen,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fp8:
         log("cpu baseline (oracle sample)...")
         result["cpu_baseline"] = cpu_baseline(mcfg, P, "about 10-30 s of CPU work")
     print(json.dumps(result), flush=True)

@@ -18,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 COPY_BYTES = 1 << 30
 GATEUP_KERNEL = "gemm_stream_kernel<unsigned short, 2, 2, 2, 3, 3, true>"   # expert gate/up (SwiGLU)
+GATEUP_KERNEL_FP8 = "gemm_f8_grouped_kernel<2, 2, 2, 3, 2>"                  # the same with e4m3 weights
 COPY_KERNEL = "copyBuffer"
 GEMM_SOURCES = ("csrc/k_gemm.hip", "csrc/dg_common.h", "csrc/dg_api.hip")
 
@@ -30,8 +31,9 @@ def gemm_source_hash():
     return h.hexdigest()[:16]
 
 
-def pmc_workload(n_reps=5):
-    """Copy calibration + MoE layer launches (run under rocprofv3 --pmc)."""
+def pmc_workload(n_reps=5, fp8=False):
+    """Copy calibration + MoE layer launches (run under rocprofv3 --pmc);
+    fp8 quantises the expert weights to e4m3 first."""
     import torch
 
     from . import binding as B
@@ -46,6 +48,9 @@ def pmc_workload(n_reps=5):
     mc = synth.moe_cfg(2816, 128, 8, 704, 704)
     g = synth.generator(53, dev)
     w = synth.moe_weights(mc, g, device=dev)
+    if fp8:
+        w = B.quantize_moe_weights(w)
+        mc["expert_format"] = "fp8_e4m3"
     x = synth.hidden_states(256, 2816, g, "bf16", dev)
     for _ in range(n_reps):
         B.dg_moe_block(mc, w, x)
@@ -71,18 +76,21 @@ def _per_dispatch(rows, name_part, counter):
     return sum(v) / len(v), len(v)
 
 
-def summarize_traffic(fetch_csv, write_csv, command, algorithmic_bytes):
+def summarize_traffic(fetch_csv, write_csv, command, algorithmic_bytes, fp8=False):
+    kern = GATEUP_KERNEL_FP8 if fp8 else GATEUP_KERNEL
     fr, wr = _rows(fetch_csv), _rows(write_csv)
     cf, ncf = _per_dispatch(fr, COPY_KERNEL, "FETCH_SIZE")
     cw, ncw = _per_dispatch(wr, COPY_KERNEL, "WRITE_SIZE")
-    gf, ngf = _per_dispatch(fr, GATEUP_KERNEL, "FETCH_SIZE")
-    gw, ngw = _per_dispatch(wr, GATEUP_KERNEL, "WRITE_SIZE")
+    gf, ngf = _per_dispatch(fr, kern, "FETCH_SIZE")
+    gw, ngw = _per_dispatch(wr, kern, "WRITE_SIZE")
     kib = COPY_BYTES / 1024.0
     ff, fw = kib / cf, kib / cw          # bytes actually moved per counted KiB, in KiB
     fetch_b = gf * ff * 1024.0
     write_b = gw * fw * 1024.0
     lines = [
-        "# HBM traffic of the expert gate/up launch (MoE layer, 256-token canvas, 128 experts top-8 + shared)",
+        "# HBM traffic of the expert gate/up launch (MoE layer, 256-token canvas, 128 experts top-8 + shared"
+        + (", fp8 e4m3 weights)" if fp8 else ")"),
+        f"kernel: {kern}",
         f"command: {command}",
         f"gemm_source_hash: {gemm_source_hash()}",
         f"copy calibration: {COPY_BYTES} B device copy; FETCH_SIZE {cf:.0f} KiB ({ncf} dispatches), "
@@ -134,8 +142,14 @@ def summarize_step(trace_csv, marker="sample_finalize_kernel"):
     return "\n".join(out) + "\n"
 
 
-def read_traffic(path=os.path.join(ROOT, "profiles", "moe_gateup_traffic_canvas256.txt")):
+def traffic_path(fp8=False):
+    name = "moe_gateup_fp8_traffic_canvas256.txt" if fp8 else "moe_gateup_traffic_canvas256.txt"
+    return os.path.join(ROOT, "profiles", name)
+
+
+def read_traffic(path=None, fp8=False):
     """Stored traffic per launch, or None when absent or taken on other GEMM sources."""
+    path = path or traffic_path(fp8)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -156,7 +170,8 @@ if __name__ == "__main__":
     what = sys.argv[1]
     if what == "traffic":
         fetch_csv, write_csv, command, alg = sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5])
-        sys.stdout.write(summarize_traffic(fetch_csv, write_csv, command, alg))
+        fp8 = len(sys.argv) > 6 and sys.argv[6] == "fp8"
+        sys.stdout.write(summarize_traffic(fetch_csv, write_csv, command, alg, fp8=fp8))
     elif what == "stats":
         sys.stdout.write(summarize_stats(sys.argv[2], sys.argv[3]))
         if len(sys.argv) > 4:
