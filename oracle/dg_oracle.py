@@ -408,7 +408,59 @@ def canvas_noise(n_pos, vocab, seed, canvas_idx):
     return renoise_tokens(n_pos, vocab, seed, 0xFFFFFFFF, canvas_idx)
 
 
-def sample_renoise(logits, scfg):
+def gumbel_noise(rows, vocab, seed, step, canvas_idx):
+    """Gumbel(0, 1) noise g[j, v] for the sampled-token variant.
+
+    Gumbel-max: argmax_v (l_v/t + g_v) is a draw from softmax(l/t)
+    (textbook; used here for the reading "sample the committed token"
+    instead of taking the argmax).  Uniforms: Philox4x32-10 with key
+    (seed lo, seed hi) and counter (position, step, canvas, 1 + v // 4); word
+    v % 4 gives k = word >> 9 (23 bits) and u = (k + 1/2) 2^-23, exact in
+    fp32; E = -ln u, taken as -ln(1 - w) with w = 1 - u (exact) through
+    log1p when u >= 1/2; g = -ln E.  Float64 throughout.
+    rows: position indices.  Returns float64 [len(rows), vocab].
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    nq = (vocab + 3) // 4
+    ctr = np.zeros((len(rows), nq, 4), dtype=np.uint64)
+    ctr[..., 0] = rows[:, None]
+    ctr[..., 1] = step & 0xFFFFFFFF
+    ctr[..., 2] = canvas_idx & 0xFFFFFFFF
+    ctr[..., 3] = 1 + np.arange(nq)[None, :]
+    key = np.array([seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF], dtype=np.uint64)
+    x = philox4x32_10(ctr, key).reshape(len(rows), nq * 4)[:, :vocab].astype(np.int64)
+    k = x >> 9
+    u = (k + 0.5) * 2.0 ** -23
+    w = ((2 ** 23 - 1 - k) + 0.5) * 2.0 ** -23
+    e = np.where(u < 0.5, -np.log(u), -np.log1p(-w))
+    return -np.log(e)
+
+
+def sorted_cumulative_commit(H, bound):
+    """Commit rule "prefix within the entropy bound" read as a sorted
+    cumulative bound ([AIT] sampler paragraph and its generation-config
+    note; the EB-sampler of Ben-Hamu et al. 2025 is the published form).
+
+    Positions are taken in ascending entropy (ties: lower position first);
+    the position at each rank commits iff the summed entropy of the
+    positions ranked before it is <= bound.  The committed set is the
+    longest low-entropy prefix whose entropy sum minus its largest member
+    stays within the bound; the lowest-entropy position always commits
+    (bound >= 0).  Returns (commit bool [n], prior_sum float64 [n]).
+    """
+    H = np.asarray(H, dtype=np.float64)
+    order = sorted(range(len(H)), key=lambda j: (H[j], j))
+    commit = np.zeros(len(H), dtype=bool)
+    prior = np.zeros(len(H))
+    cum = 0.0
+    for j in order:
+        prior[j] = cum
+        commit[j] = cum <= bound
+        cum += H[j]
+    return commit, prior
+
+
+def sample_renoise(logits, scfg, pred_prev=None):
     """Entropy-bound commit / uniform re-noise for every canvas position.
 
     [AIT] sampler paragraph: per-position entropy of the tempered
@@ -419,17 +471,41 @@ def sample_renoise(logits, scfg):
     commits.
     scfg: dict(vocab, tau, t_max, t_min, n_steps, step, canvas_idx, seed,
     final_step).  Returns a dict.
+
+    Variants (alternative readings of the same passages):
+      scfg["commit_rule"] = "sorted_cumulative": sorted_cumulative_commit
+        with bound tau;
+      scfg["token_rule"] = "gumbel": the proposal is the Gumbel-max draw
+        argmax_v (l_v/t + g_v) (lowest id on ties) instead of the argmax;
+      pred_prev: the previous step's proposals; n_changed counts the
+        positions whose proposal differs (output stability, [REV] section 1
+        Adaptive Stopping).
     """
     t = temperature(scfg["t_max"], scfg["t_min"], scfg["step"], scfg["n_steps"])
     m, Z, S, H, amax = row_stats(logits, t)
-    commit = H < scfg["tau"]
+    n = logits.shape[0]
+    margin = None
+    if scfg.get("token_rule", "argmax") == "gumbel":
+        sc = np.asarray(logits, dtype=np.float64) / t + gumbel_noise(
+            np.arange(n), scfg["vocab"], scfg["seed"], scfg["step"], scfg["canvas_idx"])
+        pred = np.argmax(sc, axis=1)
+        top2 = -np.sort(-sc, axis=1)[:, :2]
+        margin = top2[:, 0] - top2[:, 1]
+    else:
+        pred = amax
+    prior = None
+    if scfg.get("commit_rule", "entropy") == "sorted_cumulative":
+        commit, prior = sorted_cumulative_commit(H, scfg["tau"])
+    else:
+        commit = H < scfg["tau"]
     if scfg.get("final_step", False):
         commit[:] = True
-    noise = renoise_tokens(logits.shape[0], scfg["vocab"], scfg["seed"],
-                           scfg["step"], scfg["canvas_idx"])
-    tokens = np.where(commit, amax, noise)
+    noise = renoise_tokens(n, scfg["vocab"], scfg["seed"], scfg["step"], scfg["canvas_idx"])
+    tokens = np.where(commit, pred, noise)
+    n_changed = None if pred_prev is None else int(np.sum(np.asarray(pred_prev) != pred))
     return dict(tokens=tokens.astype(np.int64), commit=commit, entropy=H,
-                n_renoised=int(np.sum(~commit)), argmax=amax, row_max=m,
+                n_renoised=int(np.sum(~commit)), argmax=amax, pred=pred.astype(np.int64),
+                n_changed=n_changed, gumbel_margin=margin, prior_sum=prior, row_max=m,
                 row_z=Z, temperature=t)
 
 
