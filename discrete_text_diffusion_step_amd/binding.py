@@ -60,7 +60,11 @@ class MoeW(ctypes.Structure):
 class SamplerCfg(ctypes.Structure):
     _fields_ = [("vocab", c_int), ("tau", c_float), ("t_max", c_float), ("t_min", c_float),
                 ("n_steps", c_int), ("step", c_int), ("canvas_idx", ctypes.c_uint32),
-                ("seed", ctypes.c_uint64), ("final_step", c_int)]
+                ("seed", ctypes.c_uint64), ("final_step", c_int), ("commit_rule", c_int), ("token_rule", c_int)]
+
+
+COMMIT_RULES = {"entropy": 0, "sorted_cumulative": 1}
+TOKEN_RULES = {"argmax": 0, "gumbel": 1}
 
 
 class ModelCfg(ctypes.Structure):
@@ -81,7 +85,8 @@ class KVCache(ctypes.Structure):
 
 class CanvasState(ctypes.Structure):
     _fields_ = [("tokens", c_void), ("u", c_void), ("use_u", c_int), ("commit", c_void),
-                ("entropy", c_void), ("n_renoised", c_void), ("logits", c_void), ("canvas_len", c_int)]
+                ("entropy", c_void), ("n_renoised", c_void), ("logits", c_void), ("canvas_len", c_int),
+                ("pred", c_void), ("n_changed", c_void)]
 
 
 class KernelTimer(ctypes.Structure):
@@ -116,7 +121,7 @@ def lib(path=None):
             "dg_quantize_fp8": (c_int, [c_int, c_void, ctypes.c_longlong, c_int, c_void, c_void, c_void]),
             "dg_sample_workspace_bytes": (c_size, [c_int, c_int]),
             "dg_sample_renoise": (c_int, [P(SamplerCfg), c_int, c_void, c_int, c_void, c_void, c_void, c_void,
-                                          c_void, c_void, c_size, c_void]),
+                                          c_void, c_void, c_void, c_void, c_size, c_void]),
             "dg_canvas_noise": (c_int, [c_int, c_int, ctypes.c_uint64, ctypes.c_uint32, c_void, c_void]),
             "dg_lm_head_workspace_bytes": (c_size, [c_int, c_int, c_int]),
             "dg_lm_head": (c_int, [c_int, c_int, c_int, c_float, c_int, c_void, c_void, c_void, c_void, c_void,
@@ -193,7 +198,8 @@ def moe_w_c(w):
 
 def sampler_cfg_c(c):
     return SamplerCfg(c["vocab"], c["tau"], c["t_max"], c["t_min"], c["n_steps"], c["step"],
-                      c["canvas_idx"] & 0xFFFFFFFF, c["seed"], 1 if c.get("final_step") else 0)
+                      c["canvas_idx"] & 0xFFFFFFFF, c["seed"], 1 if c.get("final_step") else 0,
+                      COMMIT_RULES[c.get("commit_rule", "entropy")], TOKEN_RULES[c.get("token_rule", "argmax")])
 
 
 def model_cfg_c(m):
@@ -270,7 +276,10 @@ def quantize_moe_weights(w, stream=None):
     return out
 
 
-def dg_sample_renoise(scfg, logits, want_rowstats=True, stream=None):
+def dg_sample_renoise(scfg, logits, want_rowstats=True, pred=None, stream=None):
+    """Sampler outputs; pred (optional int32 [n], -1 before the first step)
+    holds the previous proposals and receives this step's, and the result
+    then carries n_changed."""
     L = lib()
     n, V = logits.shape
     dev = logits.device
@@ -278,13 +287,15 @@ def dg_sample_renoise(scfg, logits, want_rowstats=True, stream=None):
                commit=torch.empty(n, dtype=torch.uint8, device=dev),
                entropy=torch.empty(n, dtype=torch.float32, device=dev),
                n_renoised=torch.empty(1, dtype=torch.int32, device=dev),
-               rowstats=torch.empty(n, 2, dtype=torch.float32, device=dev) if want_rowstats else None)
+               rowstats=torch.empty(n, 2, dtype=torch.float32, device=dev) if want_rowstats else None,
+               n_changed=torch.empty(1, dtype=torch.int32, device=dev) if pred is not None else None)
     c = sampler_cfg_c(scfg)
     ws = workspace(L.dg_sample_workspace_bytes(n, V), dev)
     ldt = DG_BF16 if logits.dtype == torch.bfloat16 else DG_F32
     check(L.dg_sample_renoise(ctypes.byref(c), n, ptr(logits), ldt, ptr(out["tokens"]), ptr(out["commit"]),
-                              ptr(out["entropy"]), ptr(out["rowstats"]), ptr(out["n_renoised"]), ptr(ws),
-                              ws.numel(), stream_handle(stream)), "dg_sample_renoise")
+                              ptr(out["entropy"]), ptr(out["rowstats"]), ptr(out["n_renoised"]), ptr(pred),
+                              ptr(out["n_changed"]), ptr(ws), ws.numel(), stream_handle(stream)),
+          "dg_sample_renoise")
     return out
 
 
@@ -402,10 +413,13 @@ class Canvas:
                        if keep_logits_vocab else None)
         self.use_u = 0
         self.n = n
+        # proposals of the previous step (-1: none yet) and how many changed
+        self.pred = torch.full((n,), -1, dtype=torch.int32, device=device)
+        self.n_changed = torch.zeros(1, dtype=torch.int32, device=device)
 
     def c_state(self):
         return CanvasState(ptr(self.tokens), ptr(self.u), self.use_u, ptr(self.commit), ptr(self.entropy),
-                           ptr(self.n_renoised), ptr(self.logits), self.n)
+                           ptr(self.n_renoised), ptr(self.logits), self.n, ptr(self.pred), ptr(self.n_changed))
 
 
 def dg_canvas_step(model, kv, canvas, scfg, ws=None, stream=None):

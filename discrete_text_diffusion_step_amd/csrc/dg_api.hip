@@ -614,12 +614,16 @@ int check_sampler_cfg(const dg_sampler_cfg *c) {
   if (c->vocab <= 0 || c->vocab % 8) return DG_ERR_SHAPE;
   if (!(c->t_max > 0.f) || !(c->t_min > 0.f) || c->n_steps < 1 || c->step < 0) return DG_ERR_SHAPE;
   if (!(temperature(c) > 0.0)) return DG_ERR_SHAPE;
+  if (c->commit_rule != DG_COMMIT_ENTROPY && c->commit_rule != DG_COMMIT_SORTED_CUMULATIVE) return DG_ERR_UNSUPPORTED;
+  if (c->token_rule != DG_TOKEN_ARGMAX && c->token_rule != DG_TOKEN_GUMBEL) return DG_ERR_UNSUPPORTED;
   return DG_OK;
 }
 
 int sample_impl(const dg_sampler_cfg *c, int n, const void *logits, int ldt, int32_t *tok, uint8_t *commit,
-                float *ent, float *rowstats, int32_t *nre, Carve &cv, hipStream_t s) {
+                float *ent, float *rowstats, int32_t *nre, int32_t *pred, int32_t *n_changed, Carve &cv,
+                hipStream_t s) {
   const SampleWs ws = sample_carve(n, c->vocab, cv);
+  if (c->commit_rule == DG_COMMIT_SORTED_CUMULATIVE && n > kSortedMaxRows) return DG_ERR_SHAPE;
   SampleArgs a;
   a.logits = logits;
   a.logits_bf16 = ldt == DG_BF16;
@@ -640,6 +644,10 @@ int sample_impl(const dg_sampler_cfg *c, int n, const void *logits, int ldt, int
   a.entropy = ent;
   a.rowstats = rowstats;
   a.n_renoised = nre;
+  a.commit_rule = c->commit_rule;
+  a.token_rule = c->token_rule;
+  a.pred = pred;
+  a.n_changed = pred ? n_changed : nullptr;
   DG_HIP(launch_sampler(a, s));
   return DG_OK;
 }
@@ -836,15 +844,15 @@ size_t dg_sample_workspace_bytes(int n_pos, int vocab) {
 }
 
 int dg_sample_renoise(const dg_sampler_cfg *cfg, int n_pos, const void *logits, int logits_dtype, int32_t *tok,
-                      uint8_t *commit, float *ent, float *rowstats, int32_t *nre, void *ws, size_t ws_bytes,
-                      void *stream) {
+                      uint8_t *commit, float *ent, float *rowstats, int32_t *nre, int32_t *pred,
+                      int32_t *n_changed, void *ws, size_t ws_bytes, void *stream) {
   DG_TRY(check_sampler_cfg(cfg));
   if (!dtype_ok(logits_dtype)) return DG_ERR_DTYPE;
   if (n_pos < 0) return DG_ERR_SHAPE;
   if (!logits || !tok || !commit || !ent || !nre || !ws) return DG_ERR_NULL;
   if (ws_bytes < dg_sample_workspace_bytes(n_pos, cfg->vocab)) return DG_ERR_WORKSPACE;
   Carve cv(ws);
-  return sample_impl(cfg, n_pos, logits, logits_dtype, tok, commit, ent, rowstats, nre, cv,
+  return sample_impl(cfg, n_pos, logits, logits_dtype, tok, commit, ent, rowstats, nre, pred, n_changed, cv,
                      static_cast<hipStream_t>(stream));
 }
 
@@ -992,7 +1000,7 @@ int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cac
   {
     Carve c(sw.rest);
     DG_TRY(sample_impl(scfg, n, logits, DG_F32, st->tokens, st->commit, st->entropy, sw.rowstats, st->n_renoised,
-                       c, s));
+                       st->pred, st->n_changed, c, s));
   }
   if (cfg->sc_ffn > 0) {
     Carve c(sw.rest);

@@ -58,7 +58,13 @@ struct SampleArgs {
   float *entropy;
   float *rowstats;      // optional [n_pos][2]
   int32_t *n_renoised;
+  int commit_rule;      // 0: H < tau per position, 1: sorted cumulative bound
+  int token_rule;       // 0: argmax, 1: Gumbel-max draw
+  int32_t *pred;        // optional [n_pos] proposals in/out
+  int32_t *n_changed;   // optional [1] (with pred)
 };
+// rows the sorted cumulative commit rule handles (one workgroup, LDS)
+constexpr int kSortedMaxRows = 4096;
 
 hipError_t launch_norm_rope(const NormRopeArgs &a, int dtype, hipStream_t s);
 hipError_t launch_attention(const AttnArgs &a, int dtype, int dh, hipStream_t s);

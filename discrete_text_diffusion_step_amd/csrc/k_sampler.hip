@@ -11,6 +11,10 @@
 // sample_finalize: merges the slices of every row, H = ln Z - S/Z, commit iff
 //   H < tau (or on the final step), token = argmax or a Philox4x32-10 draw,
 //   and counts the re-noised positions with a block reduction (no atomics).
+// Variants: the Gumbel-max proposal argmax_v (l_v/t + g_v) in place of the
+//   argmax (the slice pass draws g from Philox as it streams the row), the
+//   sorted cumulative commit rule (ranks by entropy inside the one-workgroup
+//   finalize), and the count of proposals changed since the previous step.
 // probs: p = exp(l/t - m) / Z stored in the model dtype (input of P.E).
 #include "dg_launch.h"
 
@@ -21,8 +25,8 @@ namespace {
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
 // 4x32 bijection with multipliers 0xD2511F53 / 0xCD9E8D57, key advanced by
 // the Weyl constants 0x9E3779B9 / 0xBB67AE85 between rounds.
-__device__ __forceinline__ uint32_t philox_x0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
-                                              uint32_t k1) {
+__device__ __forceinline__ uint4 philox4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                         uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r > 0) {
@@ -37,7 +41,23 @@ __device__ __forceinline__ uint32_t philox_x0(uint32_t c0, uint32_t c1, uint32_t
     c2 = n2;
     c3 = lo0;
   }
-  return c0;
+  return make_uint4(c0, c1, c2, c3);
+}
+
+__device__ __forceinline__ uint32_t philox_x0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                              uint32_t k1) {
+  return philox4(c0, c1, c2, c3, k0, k1).x;
+}
+
+// Gumbel(0,1) value of one 32-bit word: k = word >> 9, u = (k + 1/2) 2^-23
+// (exact), E = -ln u (through log1p(-(1-u)) for u >= 1/2, where 1-u is exact
+// and ln u is small), g = -ln E.
+__device__ __forceinline__ float gumbel_of(uint32_t x) {
+  const uint32_t k = x >> 9;
+  const float u = (static_cast<float>(k) + 0.5f) * 0x1p-23f;
+  const float w = (static_cast<float>(0x7FFFFFu - k) + 0.5f) * 0x1p-23f;
+  const float e = k < 0x400000u ? -logf(u) : -log1pf(-w);
+  return -logf(e);
 }
 
 __device__ __forceinline__ int32_t uniform_token(uint32_t x0, int vocab) {
@@ -70,6 +90,7 @@ __device__ __forceinline__ void load_logits8(const void *p, int bf16, long long 
   else load8(static_cast<const float *>(p) + off, f);
 }
 
+template <bool GUMBEL>
 __global__ __launch_bounds__(256) void rowstats_partial_kernel(const SampleArgs a) {
   const int row = blockIdx.y, chunk = blockIdx.x;
   const int clen = a.vocab / a.n_chunks;
@@ -80,10 +101,23 @@ __global__ __launch_bounds__(256) void rowstats_partial_kernel(const SampleArgs 
     float l[8];
     load_logits8(a.logits, a.logits_bf16, base + c, l);
     float mx = -INFINITY;
+    if constexpr (GUMBEL) {
+      // proposal score l/t + g, noise words for v = v0 .. v0+7 (v0 % 8 == 0)
+      const uint32_t v0 = static_cast<uint32_t>(chunk * clen + c);
+      const uint4 r0 = philox4(static_cast<uint32_t>(row), a.step, a.canvas_idx, 1u + (v0 >> 2), a.key0, a.key1);
+      const uint4 r1 = philox4(static_cast<uint32_t>(row), a.step, a.canvas_idx, 2u + (v0 >> 2), a.key0, a.key1);
+      const uint32_t wd[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      better(bv, bi, l[j], chunk * clen + c + j);
-      mx = fmaxf(mx, l[j] * a.inv_t);
+      for (int j = 0; j < 8; ++j) {
+        better(bv, bi, l[j] * a.inv_t + gumbel_of(wd[j]), chunk * clen + c + j);
+        mx = fmaxf(mx, l[j] * a.inv_t);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        better(bv, bi, l[j], chunk * clen + c + j);
+        mx = fmaxf(mx, l[j] * a.inv_t);
+      }
     }
     if (mx > m) {
       if (m != -INFINITY) {
@@ -153,9 +187,24 @@ __global__ __launch_bounds__(256) void rowstats_partial_kernel(const SampleArgs 
   }
 }
 
+__device__ __forceinline__ int block_sum(int v, int *red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  const int r = red[0];
+  __syncthreads();
+  return r;
+}
+
 __global__ __launch_bounds__(256) void sample_finalize_kernel(const SampleArgs a) {
   __shared__ int red[256];
-  int renoised = 0;
+  __shared__ float sH[kSortedMaxRows];
+  __shared__ int sP[kSortedMaxRows];
+  const bool sorted = a.commit_rule == 1;
+  int renoised = 0, changed = 0;
   for (int row = threadIdx.x; row < a.n_pos; row += 256) {
     const float *p = a.part + static_cast<long long>(row) * a.n_chunks * 4;
     const int *pi = a.part_idx + static_cast<long long>(row) * a.n_chunks;
@@ -166,6 +215,20 @@ __global__ __launch_bounds__(256) void sample_finalize_kernel(const SampleArgs a
       better(bv, bi, p[c * 4 + 3], pi[c]);
     }
     const float H = __logf(Z) - S / Z;
+    if (a.pred) {
+      changed += a.pred[row] != bi;
+      a.pred[row] = bi;
+    }
+    a.entropy[row] = H;
+    if (a.rowstats) {
+      a.rowstats[2 * row] = M;
+      a.rowstats[2 * row + 1] = Z;
+    }
+    if (sorted) {
+      sH[row] = H;
+      sP[row] = bi;
+      continue;
+    }
     const bool commit = a.final_step || (H < a.tau);
     int32_t tok = bi;
     if (!commit) {
@@ -175,19 +238,35 @@ __global__ __launch_bounds__(256) void sample_finalize_kernel(const SampleArgs a
     }
     a.tokens[row] = tok;
     a.commit[row] = commit ? 1 : 0;
-    a.entropy[row] = H;
-    if (a.rowstats) {
-      a.rowstats[2 * row] = M;
-      a.rowstats[2 * row + 1] = Z;
+  }
+  if (sorted) {
+    __syncthreads();
+    // rank by (H, position); a position commits iff the entropy summed over
+    // the positions ranked before it (added in position order) is <= tau
+    for (int row = threadIdx.x; row < a.n_pos; row += 256) {
+      const float H = sH[row];
+      float prior = 0.f;
+      for (int i = 0; i < a.n_pos; ++i) {
+        const float Hi = sH[i];
+        if (Hi < H || (Hi == H && i < row)) prior += Hi;
+      }
+      const bool commit = a.final_step || prior <= a.tau;
+      int32_t tok = sP[row];
+      if (!commit) {
+        const uint32_t x0 = philox_x0(static_cast<uint32_t>(row), a.step, a.canvas_idx, 0u, a.key0, a.key1);
+        tok = uniform_token(x0, a.vocab);
+        ++renoised;
+      }
+      a.tokens[row] = tok;
+      a.commit[row] = commit ? 1 : 0;
     }
   }
-  red[threadIdx.x] = renoised;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
+  const int nre = block_sum(renoised, red);
+  if (a.pred && a.n_changed) {
+    const int nch = block_sum(changed, red);
+    if (threadIdx.x == 0) *a.n_changed = nch;
   }
-  if (threadIdx.x == 0) *a.n_renoised = red[0];
+  if (threadIdx.x == 0) *a.n_renoised = nre;
 }
 
 __global__ __launch_bounds__(256) void canvas_noise_kernel(int n_pos, int vocab, uint32_t k0, uint32_t k1,
@@ -215,7 +294,11 @@ __global__ __launch_bounds__(256) void probs_kernel(const float *logits, const f
 
 hipError_t launch_sampler(const SampleArgs &a, hipStream_t s) {
   if (a.n_pos <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rowstats_partial_kernel, dim3(a.n_chunks, a.n_pos), dim3(256), 0, s, a);
+  if (a.commit_rule == 1 && a.n_pos > kSortedMaxRows) return hipErrorInvalidValue;
+  if (a.token_rule == 1)
+    hipLaunchKernelGGL(rowstats_partial_kernel<true>, dim3(a.n_chunks, a.n_pos), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(rowstats_partial_kernel<false>, dim3(a.n_chunks, a.n_pos), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sample_finalize_kernel, dim3(1), dim3(256), 0, s, a);

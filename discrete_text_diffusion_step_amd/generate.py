@@ -3,9 +3,12 @@
 aibars.net news, block-autoregressive denoising: a 256-token block is
 denoised fully, committed to the KV cache, then the next block starts.
 DiffusionGemma Technical Report review, section 1 (Adaptive Stopping): the
-denoising loop stops early; here it stops once a step re-noises no position
-(the only device-to-host read per step), or after max_steps, when the final
-step commits every position.
+denoising loop stops early on prediction entropy and output stability.
+stop_rule "renoised" (default): stop once a step re-noises no position.
+stop_rule "stable": stop once no proposal changed since the previous step;
+the canvas then takes the stable proposals at every position, as a final
+step would.  Either way one 4-byte device-to-host read per step; after
+max_steps the final step commits every position.
 """
 import torch
 
@@ -13,7 +16,8 @@ from . import binding as B
 
 
 def generate(model, kv, prompt, n_canvases, canvas_len=256, max_steps=48, seed=1, t_max=1.0, t_min=1.0,
-             tau=None, adaptive=True, stream=None):
+             tau=None, adaptive=True, stream=None, commit_rule="entropy", token_rule="argmax",
+             stop_rule="renoised"):
     """Commit `prompt`, then denoise and commit n_canvases canvases.
 
     Returns (tokens [n_canvases, canvas_len] int32 on the device, steps used per canvas).
@@ -30,17 +34,23 @@ def generate(model, kv, prompt, n_canvases, canvas_len=256, max_steps=48, seed=1
     for c in range(n_canvases):
         canvas.tokens.copy_(B.dg_canvas_noise(canvas_len, V, seed, c, device=prompt.device, stream=stream))
         canvas.use_u = 0
+        canvas.pred.fill_(-1)
         used = 0
         for i in range(max_steps):
             final = i == max_steps - 1
             s = dict(vocab=V, tau=tau, t_max=t_max, t_min=t_min, n_steps=max_steps, step=i,
-                     canvas_idx=c, seed=seed, final_step=final)
+                     canvas_idx=c, seed=seed, final_step=final, commit_rule=commit_rule, token_rule=token_rule)
             B.dg_canvas_step(model, kv, canvas, s, stream=stream)
             used += 1
             if adaptive and not final:
-                host_count.copy_(canvas.n_renoised, non_blocking=True)
+                stable = stop_rule == "stable"
+                if stable and i == 0:
+                    continue
+                host_count.copy_(canvas.n_changed if stable else canvas.n_renoised, non_blocking=True)
                 torch.cuda.current_stream().synchronize()
                 if int(host_count.item()) == 0:
+                    if stable:
+                        canvas.tokens.copy_(canvas.pred)
                     break
         out[c].copy_(canvas.tokens)
         B.dg_commit_canvas(model, kv, canvas.tokens, stream=stream)

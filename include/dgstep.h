@@ -213,7 +213,28 @@ typedef struct {
   uint32_t canvas_idx;
   uint64_t seed;
   int final_step;
+  int commit_rule;     /* dg_commit_rule (0: per position) */
+  int token_rule;      /* dg_token_rule (0: argmax) */
 } dg_sampler_cfg;
+
+/* Variants of the sampler (the pages fix the low-entropy "prefix within the
+ * entropy bound" and an adaptive stop on entropy and output stability, not
+ * their exact form; aitrends sampler paragraph, secrett2633 review
+ * section 1 Adaptive Stopping):
+ * DG_COMMIT_ENTROPY: position j commits iff H_j < tau.
+ * DG_COMMIT_SORTED_CUMULATIVE: positions in ascending entropy order (ties:
+ *   lower position first); the position at each rank commits iff the summed
+ *   entropy of the positions ranked before it is <= tau (the EB-sampler of
+ *   Ben-Hamu et al. 2025); the lowest-entropy position always commits.
+ *   n_pos <= 4096.
+ * DG_TOKEN_ARGMAX: the proposal is the argmax of the logits (lowest id).
+ * DG_TOKEN_GUMBEL: the proposal is argmax_v (l_v/t + g_v), a draw from
+ *   softmax(l/t) by the Gumbel-max property; g_v = -ln(-ln u_v) with u from
+ *   Philox4x32-10, counter (position, step, canvas_idx, 1 + v/4), word v%4:
+ *   k = word >> 9, u = (k + 1/2) 2^-23 (-ln u through log1p of -(1-u) when
+ *   u >= 1/2). */
+typedef enum { DG_COMMIT_ENTROPY = 0, DG_COMMIT_SORTED_CUMULATIVE = 1 } dg_commit_rule;
+typedef enum { DG_TOKEN_ARGMAX = 0, DG_TOKEN_GUMBEL = 1 } dg_token_rule;
 
 size_t dg_sample_workspace_bytes(int n_pos, int vocab);
 
@@ -221,11 +242,15 @@ size_t dg_sample_workspace_bytes(int n_pos, int vocab);
  * Outputs (device): tokens_out [n_pos] int32, commit_out [n_pos] uint8 (1 =
  * committed), entropy_out [n_pos] fp32, n_renoised_out [1] int32.
  * rowstats_out: optional [n_pos, 2] fp32 = (max of l/t, sum of exp(l/t - max)),
- * the statistics dg_soft_embed needs. */
+ * the statistics dg_soft_embed needs.
+ * pred_inout: optional [n_pos] int32: in, the previous step's proposals (-1
+ *   before the first step); out, this step's.  n_changed_out: optional [1]
+ *   int32, the number of positions whose proposal changed (read only with
+ *   pred_inout): the output-stability signal for adaptive stop. */
 int dg_sample_renoise(const dg_sampler_cfg *cfg, int n_pos, const void *logits, int logits_dtype,
                       int32_t *tokens_out, uint8_t *commit_out, float *entropy_out,
-                      float *rowstats_out, int32_t *n_renoised_out, void *ws, size_t ws_bytes,
-                      void *stream);
+                      float *rowstats_out, int32_t *n_renoised_out, int32_t *pred_inout,
+                      int32_t *n_changed_out, void *ws, size_t ws_bytes, void *stream);
 
 /* Initial canvas: n_pos uniform random tokens (counter step word 0xFFFFFFFF;
  * aibars text-diffusion paragraph: generation starts from a noise block). */
@@ -296,6 +321,8 @@ typedef struct {
   int32_t *n_renoised; /* [1] out: positions re-noised this step (adaptive stop when 0) */
   float *logits;       /* [canvas_len, vocab] fp32 out (optional: NULL keeps them in ws) */
   int canvas_len;
+  int32_t *pred;       /* optional [canvas_len]: proposals in/out, as dg_sample_renoise's pred_inout */
+  int32_t *n_changed;  /* optional [1] out: proposals changed this step (needs pred) */
 } dg_canvas_state;
 
 /* Workspace bytes for dg_canvas_step with canvases of up to max_canvas_tokens

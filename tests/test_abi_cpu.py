@@ -86,12 +86,21 @@ def test_sampler_validation_codes():
     L = B.lib()
     p = ctypes.c_void_p(256)
     call = lambda s, n=256, ldt=0, wsb=1 << 30: L.dg_sample_renoise(
-        ctypes.byref(s), n, p, ldt, p, p, p, None, p, p, wsb, None)
+        ctypes.byref(s), n, p, ldt, p, p, p, None, p, None, None, p, wsb, None)
     assert call(B.sampler_cfg_c(synth.sampler_cfg(262144, t_max=0.0))) == -2
     assert call(B.sampler_cfg_c(synth.sampler_cfg(262143))) == -2
     assert call(B.sampler_cfg_c(synth.sampler_cfg(262144)), ldt=3) == -5
     assert call(B.sampler_cfg_c(synth.sampler_cfg(262144)), wsb=8) == -4
-    assert L.dg_sample_renoise(None, 1, p, 0, p, p, p, None, p, p, 1 << 30, None) == -1
+    assert L.dg_sample_renoise(None, 1, p, 0, p, p, p, None, p, None, None, p, 1 << 30, None) == -1
+    bad = B.sampler_cfg_c(synth.sampler_cfg(262144))
+    bad.commit_rule = 2
+    assert call(bad) == -3
+    bad = B.sampler_cfg_c(synth.sampler_cfg(262144))
+    bad.token_rule = 5
+    assert call(bad) == -3
+    # the sorted cumulative rule ranks at most 4096 positions in one workgroup
+    big = B.sampler_cfg_c(dict(synth.sampler_cfg(262144), commit_rule="sorted_cumulative"))
+    assert call(big, n=4097) == -2
 
 
 def test_workspace_queries_grow_with_tokens():
