@@ -115,6 +115,10 @@ def main():
                     help="only run the counter workload (copy calibration + MoE layer) for rocprofv3 --pmc")
     ap.add_argument("--experts", choices=("bf16", "fp8"), default="bf16",
                     help="expert weight storage: bf16 (the model dtype) or OCP e4m3 with row scales")
+    ap.add_argument("--commit-rule", choices=("entropy", "sorted_cumulative"), default="entropy")
+    ap.add_argument("--token-rule", choices=("argmax", "gumbel"), default="argmax")
+    ap.add_argument("--stop-rule", choices=("renoised", "stable"), default="renoised",
+                    help="adaptive stop of the generation run")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -172,7 +176,8 @@ def main():
     canvas.tokens.copy_(B.dg_canvas_noise(CANVAS, V, 1, 0, device=dev))
 
     def step(i):
-        s = synth.sampler_cfg(V, n_steps=48, step=i % 48, canvas_idx=0, final_step=(i % 48 == 47))
+        s = dict(synth.sampler_cfg(V, n_steps=48, step=i % 48, canvas_idx=0, final_step=(i % 48 == 47)),
+                 commit_rule=args.commit_rule, token_rule=args.token_rule)
         B.dg_canvas_step(model, kv, canvas, s, ws=ws)
 
     for i in range(args.warmup):
@@ -210,7 +215,8 @@ def main():
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         toks, used = generate(model, kv, torch.empty(0, dtype=torch.int32, device=dev), args.canvases,
-                              canvas_len=CANVAS, max_steps=48, seed=1, adaptive=True)
+                              canvas_len=CANVAS, max_steps=48, seed=1, adaptive=True,
+                              commit_rule=args.commit_rule, token_rule=args.token_rule, stop_rule=args.stop_rule)
         torch.cuda.synchronize()
         gt = time.perf_counter() - t1
         gen = {"canvases": args.canvases, "steps_per_canvas": used,
@@ -239,7 +245,9 @@ def main():
                                "layers, hidden 2816, 128 experts top-8 + shared (SwiGLU 704), vocab 262144, "
                                "256-token canvas after a 4096-token prompt",
                    "canvas": CANVAS, "committed_rows": P, "params": n_params, "adaptive_stop_in_timed_loop": False,
-                   "expert_weights": "fp8_e4m3 (row scales)" if fp8 else "bf16"},
+                   "expert_weights": "fp8_e4m3 (row scales)" if fp8 else "bf16",
+                   "sampler": {"commit_rule": args.commit_rule, "token_rule": args.token_rule,
+                               "stop_rule": args.stop_rule}},
         "eff_tok_s": eff, "tokens_per_forward": {"full_schedule": round(tpf_full, 3), "pages": 20},
         "commit_ms": round(commit, 3), "prefill_ms": round(prefill_ms, 1),
         "roofline": roof,
