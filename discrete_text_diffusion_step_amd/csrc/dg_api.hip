@@ -192,6 +192,13 @@ AttnPlan attn_plan(const dg_attn_cfg *c, int n) {
 struct AttnWs {
   void *h, *qkv, *v_rows, *o;
   float *o_part, *ml_part, *oproj_part, *qkv_part;
+  float2 *rope_tab;
+};
+
+// A rotation table made once for every layer of one type at one position.
+struct RopeTab {
+  const float2 *tab = nullptr;
+  int pos0 = -1;
 };
 
 AttnWs attn_carve(const dg_attn_cfg *c, const AttnPlan &p, Carve &cv) {
@@ -211,6 +218,7 @@ AttnWs attn_carve(const dg_attn_cfg *c, const AttnPlan &p, Carve &cv) {
   }
   w.oproj_part = p.oproj_ks > 1 ? cv.take<float>(p.oproj_ks * n * c->hidden) : nullptr;
   w.qkv_part = p.qkv_ks > 1 ? cv.take<float>(p.qkv_ks * n * p.Ntot) : nullptr;
+  w.rope_tab = cv.take<float2>(n * (c->head_dim / 2));
   return w;
 }
 
@@ -247,7 +255,8 @@ int rope_rot(const dg_attn_cfg *c) {
 
 // x <- x + Attention(x).  h_in, when given, already holds rms(x, w_in_norm).
 int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, int causal, void *x,
-              Carve &cv, hipStream_t s, const void *h_in = nullptr, NextNorm next = NextNorm()) {
+              Carve &cv, hipStream_t s, const void *h_in = nullptr, NextNorm next = NextNorm(),
+              RopeTab rt = RopeTab()) {
   const AttnPlan p = attn_plan(c, n);
   const AttnWs ws = attn_carve(c, p, cv);
   const int dt = c->dtype;
@@ -315,6 +324,12 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   if (DG_QKV_FUSED && p.qkv_wide && p.qkv_ks > 1) {
     nr.part = ws.qkv_part;
     nr.n_part = p.qkv_ks;
+  }
+  if (rt.tab && rt.pos0 == P) {
+    nr.rope_tab = rt.tab;
+  } else {
+    DG_HIP(launch_rope_table(P, n, dh, c->rope_base, rope_rot(c), ws.rope_tab, s));
+    nr.rope_tab = ws.rope_tab;
   }
   DG_HIP(launch_norm_rope(nr, dt, s));
   const long long vt_cache_hs = static_cast<long long>(dh) * kv->capacity;
@@ -746,6 +761,7 @@ size_t layer_ws_bytes(const dg_model_cfg *c, int n) {
 struct StepWs {
   void *x, *h, *g_sc;   // h: pre-norm activations handed from block to block
   float *logits, *rowstats;
+  float2 *tab[2];       // rotation tables of the sliding and the global layers
   void *rest;
 };
 
@@ -758,6 +774,8 @@ StepWs step_carve(const dg_model_cfg *c, int n, bool need_logits, Carve &cv) {
   w.g_sc = cv.bytes(static_cast<size_t>(n) * (c->sc_ffn > 0 ? c->sc_ffn : 1) * es);
   w.logits = need_logits ? cv.take<float>(static_cast<size_t>(n) * c->vocab) : nullptr;
   w.rowstats = cv.take<float>(static_cast<size_t>(n) * 2);
+  w.tab[0] = cv.take<float2>(static_cast<size_t>(n) * (c->sliding.head_dim / 2));
+  w.tab[1] = cv.take<float2>(static_cast<size_t>(n) * (c->global.head_dim / 2));
   size_t tail = layer_ws_bytes(c, n);
   {
     Carve t(nullptr);
@@ -772,6 +790,24 @@ StepWs step_carve(const dg_model_cfg *c, int n, bool need_logits, Carve &cv) {
   }
   w.rest = cv.bytes(tail + 256);
   return w;
+}
+
+// Rotation tables for the first layer of each type (every layer of a type
+// sits at the same position in a step); a layer at another position makes
+// its own.
+int make_rope_tabs(const dg_model_cfg *cfg, const dg_kv_cache *kv, int n, const StepWs &sw, RopeTab (&rt)[2],
+                   hipStream_t s) {
+  for (int t = 0; t < 2; ++t) {
+    for (int l = 0; l < cfg->n_layers; ++l) {
+      const dg_attn_cfg *ac = layer_cfg(cfg, l);
+      if ((ac == &cfg->global) != (t == 1)) continue;
+      rt[t].pos0 = kv->layer[l].kv_len;
+      rt[t].tab = sw.tab[t];
+      DG_HIP(launch_rope_table(rt[t].pos0, n, ac->head_dim, ac->rope_base, rope_rot(ac), sw.tab[t], s));
+      break;
+    }
+  }
+  return DG_OK;
 }
 
 }  // namespace
@@ -963,6 +999,8 @@ int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cac
   const int dt = cfg->dtype, D = cfg->sliding.hidden;
 
   DG_HIP(launch_embed(dt, st->tokens, n, D, cfg->vocab, w->embed, sw.x, s));
+  RopeTab rt[2];
+  DG_TRY(make_rope_tabs(cfg, kv, n, sw, rt, s));
   if (st->use_u && cfg->sc_ffn > 0) {
     GemmArgs g = dense_args(st->u, D, n, cfg->sc_ffn, D, sw.g_sc, cfg->sc_ffn);
     g.seg_B0[0] = w->sc_gate;
@@ -982,7 +1020,8 @@ int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cac
     to_moe.w = w->moe[l].w_in_norm;
     to_moe.eps = mc.rms_eps;
     const dg_attn_cfg *ac = layer_cfg(cfg, l);
-    DG_TRY(attn_impl(ac, &w->attn[l], &L, n, 0, sw.x, c1, s, l == 0 ? nullptr : sw.h, to_moe));
+    DG_TRY(attn_impl(ac, &w->attn[l], &L, n, 0, sw.x, c1, s, l == 0 ? nullptr : sw.h, to_moe,
+                     rt[ac == &cfg->global ? 1 : 0]));
     NextNorm to_attn;
     if (l + 1 < cfg->n_layers) {
       to_attn.h = sw.h;
@@ -1026,6 +1065,8 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int dt = cfg->dtype, D = cfg->sliding.hidden;
   DG_HIP(launch_embed(dt, tokens, n, D, cfg->vocab, w->embed, sw.x, s));
+  RopeTab rt[2];
+  DG_TRY(make_rope_tabs(cfg, kv, n, sw, rt, s));
   const int L = cfg->n_layers;
   for (int l = 0; l < L; ++l) {
     const dg_attn_cfg *ac = layer_cfg(cfg, l);
@@ -1073,6 +1114,13 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
       nr.eps = ac->rms_eps;
       nr.sqrt_dh = static_cast<float>(sqrt(static_cast<double>(ac->head_dim)));
       nr.v_unit_rms = ac->v_unit_rms;
+      const RopeTab &r = rt[ac == &cfg->global ? 1 : 0];
+      if (r.tab && r.pos0 == KL.kv_len) {
+        nr.rope_tab = r.tab;
+      } else {
+        DG_HIP(launch_rope_table(KL.kv_len, n, ac->head_dim, ac->rope_base, rope_rot(ac), aw.rope_tab, s));
+        nr.rope_tab = aw.rope_tab;
+      }
       DG_HIP(launch_norm_rope(nr, dt, s));
       DG_HIP(launch_v_transpose(dt, aw.v_rows, n, ac->n_kv_heads, ac->head_dim, KL.v,
                                 static_cast<long long>(ac->head_dim) * KL.capacity, KL.capacity, KL.kv_len, s));
@@ -1086,7 +1134,8 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
     to_moe.h = sw.h;
     to_moe.w = w->moe[l].w_in_norm;
     to_moe.eps = mc.rms_eps;
-    DG_TRY(attn_impl(ac, &w->attn[l], &KL, n, 1, sw.x, c1, s, l == 0 ? nullptr : sw.h, to_moe));
+    DG_TRY(attn_impl(ac, &w->attn[l], &KL, n, 1, sw.x, c1, s, l == 0 ? nullptr : sw.h, to_moe,
+                     rt[ac == &cfg->global ? 1 : 0]));
     NextNorm to_attn;   // the next layer (possibly the K/V-only last one) reads its pre-norm from sw.h
     to_attn.h = sw.h;
     to_attn.w = w->attn[l + 1].w_in_norm;

@@ -24,6 +24,8 @@ struct NormRopeArgs {
   // the pass sums them (split order) and rounds to the model dtype first.
   const float *part = nullptr;
   int n_part = 0;
+  // [n_tok][dh/2] (cos, sin) of the rotation angles (launch_rope_table)
+  const float2 *rope_tab = nullptr;
 };
 
 struct AttnArgs {
@@ -67,6 +69,8 @@ struct SampleArgs {
 constexpr int kSortedMaxRows = 4096;
 
 hipError_t launch_norm_rope(const NormRopeArgs &a, int dtype, hipStream_t s);
+// tab[j][t] = (cos, sin) of angle (pos0 + j) * base^(-2t/dh), fp64 angle; t >= n_rot: (1, 0)
+hipError_t launch_rope_table(int pos0, int n_tok, int dh, double base, int n_rot, float2 *tab, hipStream_t s);
 hipError_t launch_attention(const AttnArgs &a, int dtype, int dh, hipStream_t s);
 // dst[h][d][col0 + j] = src[h][j][d] for j < n (values to the transposed layout)
 hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh, void *dst, long long dst_hs,

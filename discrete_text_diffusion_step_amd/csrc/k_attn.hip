@@ -29,21 +29,29 @@ __device__ __forceinline__ float2 rope_angle(int pos, int t, int dh, double base
   return make_float2(static_cast<float>(cos(th)), static_cast<float>(sin(th)));
 }
 
+// tab[j][t] = (cos, sin) of the angle of position pos0 + j, frequency t
+__global__ __launch_bounds__(256) void rope_table_kernel(int pos0, int n_tok, int dh, double base, int n_rot,
+                                                         float2 *tab) {
+  const int half = dh >> 1;
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<long long>(n_tok) * half) return;
+  const int j = static_cast<int>(i / half), t = static_cast<int>(i - static_cast<long long>(j) * half);
+  tab[i] = rope_angle(pos0 + j, t, dh, base, n_rot);
+}
+
+// One wave per (token, head item): items are the q heads, then the k heads
+// (normed, rotated, written to the cache), then the v heads (unit-RMS in
+// global layers, written to the row buffer).  Angles come from the table.
 template <typename T>
 __global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
-  __shared__ float cs[256], sn[256];
   const int j = blockIdx.x;
   const int half = a.dh >> 1;
-  for (int t = threadIdx.x; t < half; t += blockDim.x) {
-    const float2 v = rope_angle(a.pos0 + j, t, a.dh, a.rope_base, a.n_rot);
-    cs[t] = v.x;
-    sn[t] = v.y;
-  }
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   T *row = static_cast<T *>(a.qkv) + static_cast<long long>(j) * a.ld;
+  const float2 *tab = a.rope_tab + static_cast<long long>(j) * half;
   const int items = a.Hq + 2 * a.Hkv;
-  for (int it = wave; it < items; it += 4) {
+  const int it = blockIdx.y * 4 + wave;
+  if (it < items) {
     const T *src;
     const T *w = nullptr;
     T *dst;
@@ -122,7 +130,8 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
           q *= to_f32<T>(w[t + half]);
         }
         if (rope) {
-          const float c = cs[t], sv = sn[t];
+          const float2 cs = tab[t];
+          const float c = cs.x, sv = cs.y;
           const float o0 = p * c - q * sv;
           const float o1 = q * c + p * sv;
           p = o0;
@@ -755,50 +764,96 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
   }
 }
 
-// Merge the key slices of one query row: weights w_s = exp(m_s - M) / L are
-// computed once per row, then every thread adds its columns.
+__device__ __forceinline__ void store4(bf16_t *p, const float *f) {
+  uint2 u;
+  u.x = static_cast<uint32_t>(f32_to_bf16(f[0])) | (static_cast<uint32_t>(f32_to_bf16(f[1])) << 16);
+  u.y = static_cast<uint32_t>(f32_to_bf16(f[2])) | (static_cast<uint32_t>(f32_to_bf16(f[3])) << 16);
+  *reinterpret_cast<uint2 *>(p) = u;
+}
+__device__ __forceinline__ void store4(float *p, const float *f) {
+  *reinterpret_cast<float4 *>(p) = make_float4(f[0], f[1], f[2], f[3]);
+}
+
+// Merge of the split-KV partials, one wave per (kv head, row): lane s reads
+// split s's (max, sum) and the wave forms w_s = exp(m_s - M) / sum_s l_s
+// exp(m_s - M) by reductions (no barrier); every lane then adds its four
+// columns over the splits in order.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a, int dh) {
-  __shared__ float ws[32];
   const int R = a.n_rep * a.n_tok;
-  const int idx = blockIdx.x;  // g * R + rr
-  const int g = idx / R, rr = idx % R;
   const long long rows = static_cast<long long>(a.Hkv) * R;
-  if (threadIdx.x == 0) {
-    float M = -1e30f;
-    for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, a.ml_part[(s * rows + idx) * 2]);
-    float L = 0.f;
-    for (int s = 0; s < a.n_split; ++s) {
-      const float *ml = a.ml_part + (s * rows + idx) * 2;
-      ws[s] = __expf(ml[0] - M);
-      L += ml[1] * ws[s];
-    }
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
-    for (int s = 0; s < a.n_split; ++s) ws[s] *= inv;
+  const int lane = threadIdx.x & 63;
+  const long long idx = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (idx >= rows) return;
+  // lane s holds split s (n_split <= 64): max and normaliser by wave reductions
+  const int ns = a.n_split;
+  float m = -1e30f, l = 0.f;
+  if (lane < ns) {
+    m = a.ml_part[(lane * rows + idx) * 2];
+    l = a.ml_part[(lane * rows + idx) * 2 + 1];
   }
-  __syncthreads();
+  const float M = wave_max(m);
+  const float e = lane < ns ? __expf(m - M) : 0.f;
+  const float L = wave_sum(l * e);
+  const float wl = L > 0.f ? e / L : 0.f;
+  const int g = static_cast<int>(idx / R), rr = static_cast<int>(idx % R);
   const int h = g * a.n_rep + rr / a.n_tok;
   const int j = rr % a.n_tok;
   T *op = static_cast<T *>(a.out) + static_cast<long long>(j) * a.out_ld + h * dh;
-  for (int d = threadIdx.x * 4; d < dh; d += blockDim.x * 4) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < a.n_split; ++s) {
+  for (int d = lane * 4; d < dh; d += 256) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s = 0; s < ns; ++s) {
+      const float w = __shfl(wl, s, 64);
       const float4 v = *reinterpret_cast<const float4 *>(a.o_part + (s * rows + idx) * dh + d);
-      const float w = ws[s];
-      acc.x += w * v.x;
-      acc.y += w * v.y;
-      acc.z += w * v.z;
-      acc.w += w * v.w;
+      acc[0] += w * v.x;
+      acc[1] += w * v.y;
+      acc[2] += w * v.z;
+      acc[3] += w * v.w;
     }
-    op[d] = from_f32<T>(acc.x);
-    op[d + 1] = from_f32<T>(acc.y);
-    op[d + 2] = from_f32<T>(acc.z);
-    op[d + 3] = from_f32<T>(acc.w);
+    store4(op + d, acc);
   }
 }
 
 // dst[h][d][col0 + j] = src[h][j][d]: values stored dimension-major (V^T)
 // through a 64 x 64 LDS tile.
+// bf16 with 8-aligned destination columns: 16-byte loads of token rows and
+// 16-byte stores of dimension rows, the tile transposed in LDS.
+__global__ __launch_bounds__(256) void v_transpose16_kernel(const bf16_t *src, int n, int dh, bf16_t *dst,
+                                                            long long dst_hs, int dst_ld, int col0) {
+  __shared__ bf16_t tile[64][72];   // [token][d], rows padded by 16 bytes
+  const int h = blockIdx.z;
+  const int j0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
+  const bf16_t *s = src + static_cast<long long>(h) * n * dh;
+  bf16_t *o = dst + h * dst_hs;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = tid + 256 * q;          // 512 chunks: 64 tokens x 8 chunks of 8 d
+    const int jj = c >> 3, dc = (c & 7) * 8;
+    const int j = j0 + jj, d = d0 + dc;
+    if (j < n && d < dh)
+      *reinterpret_cast<uint4 *>(&tile[jj][dc]) = *reinterpret_cast<const uint4 *>(s + static_cast<long long>(j) * dh + d);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = tid + 256 * q;          // 512 chunks: 64 d rows x 8 chunks of 8 tokens
+    const int dd = c >> 3, jc = (c & 7) * 8;
+    const int d = d0 + dd, j = j0 + jc;
+    if (d >= dh || j >= n) continue;
+    if (j + 8 <= n) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = static_cast<uint32_t>(tile[jc + 2 * e][dd]) | (static_cast<uint32_t>(tile[jc + 2 * e + 1][dd]) << 16);
+      *reinterpret_cast<uint4 *>(o + static_cast<long long>(d) * dst_ld + col0 + j) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      for (int e = 0; j + e < n; ++e) o[static_cast<long long>(d) * dst_ld + col0 + j + e] = tile[jc + e][dd];
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void v_transpose_kernel(const T *src, int n, int dh, T *dst, long long dst_hs,
                                                           int dst_ld, int col0) {
@@ -834,7 +889,7 @@ hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(a.Hkv * R), dim3(DH / 4 < 256 ? DH / 4 : 256), 0, s, a, DH);
+  hipLaunchKernelGGL(attn_combine_kernel<T>, dim3((a.Hkv * R + 3) / 4), dim3(256), 0, s, a, DH);
   return hipGetLastError();
 }
 
@@ -844,7 +899,11 @@ hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh
                               int dst_ld, int col0, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   dim3 grid((n + 63) / 64, (dh + 63) / 64, Hkv);
-  if (dtype == DG_BF16)
+  const bool vec = dtype == DG_BF16 && col0 % 8 == 0 && dst_ld % 8 == 0 && dst_hs % 8 == 0 && dh % 8 == 0;
+  if (vec)
+    hipLaunchKernelGGL(v_transpose16_kernel, grid, dim3(256), 0, s, static_cast<const bf16_t *>(src), n, dh,
+                       static_cast<bf16_t *>(dst), dst_hs, dst_ld, col0);
+  else if (dtype == DG_BF16)
     hipLaunchKernelGGL(v_transpose_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t *>(src), n, dh,
                        static_cast<bf16_t *>(dst), dst_hs, dst_ld, col0);
   else
@@ -897,10 +956,20 @@ hipError_t launch_attention(const AttnArgs &a, int dtype, int dh, hipStream_t s)
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_rope_table(int pos0, int n_tok, int dh, double base, int n_rot, float2 *tab, hipStream_t s) {
+  if (n_tok <= 0) return hipSuccess;
+  const long long n = static_cast<long long>(n_tok) * (dh / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, pos0, n_tok,
+                     dh, base, n_rot, tab);
+  return hipGetLastError();
+}
+
 hipError_t launch_norm_rope(const NormRopeArgs &a, int dtype, hipStream_t s) {
   if (a.n_tok <= 0) return hipSuccess;
-  if (dtype == DG_BF16) hipLaunchKernelGGL(norm_rope_kernel<bf16_t>, dim3(a.n_tok), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(norm_rope_kernel<float>, dim3(a.n_tok), dim3(256), 0, s, a);
+  if (!a.rope_tab) return hipErrorInvalidValue;
+  const dim3 grid(a.n_tok, (a.Hq + 2 * a.Hkv + 3) / 4);
+  if (dtype == DG_BF16) hipLaunchKernelGGL(norm_rope_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(norm_rope_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -51,33 +51,47 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const float *part
   T *xr = x + static_cast<long long>(row) * D;
   float v[MAXC][8];
   float ss = 0.f;
+  // the extra rows (routed experts, or split partials) are loaded eight at a
+  // time before they are summed, in row order
+  constexpr int KX = 8;
+  const int nx = COMBINE ? k : splits;
+  int src[KX];   // first batch of row indices, read once
+#pragma unroll
+  for (int j = 0; j < KX; ++j)
+    src[j] = j < nx ? (COMBINE ? pair_row[row * k + j] : j * n + row) : 0;
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int c = tid * 8 + 2048 * i;
     if (c >= D) break;
     float a[8], o[8];
     if constexpr (COMBINE) {
-      // Y rows: the shared expert's row is the token's own, then its k experts
+      // the shared expert's row is the token's own, then its k experts
       load8(part + static_cast<long long>(row) * D + c, a);
-      for (int j = 0; j < k; ++j) {
-        float t[8];
-        load8(part + static_cast<long long>(pair_row[row * k + j]) * D + c, t);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] += t[e];
-      }
-      load8(xr + c, o);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] = ls * (o[e] + a[e]);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) a[e] = 0.f;
-      for (int z = 0; z < splits; ++z) {
-        float t[8];
-        load8(part + (static_cast<long long>(z) * n + row) * D + c, t);
+    }
+    load8(xr + c, o);
+    for (int z0 = 0; z0 < nx; z0 += KX) {
+      float t[KX][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] += t[e];
-      }
-      load8(xr + c, o);
+      for (int j = 0; j < KX; ++j)
+        if (z0 + j < nx) {
+          const long long r = z0 == 0 ? src[j]
+                                      : (COMBINE ? pair_row[row * k + z0 + j] : static_cast<long long>(z0 + j) * n + row);
+          load8(part + r * D + c, t[j]);
+        }
+#pragma unroll
+      for (int j = 0; j < KX; ++j)
+        if (z0 + j < nx) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[e] += t[j][e];
+        }
+    }
+    if constexpr (COMBINE) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = ls * (o[e] + a[e]);
+    } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) a[e] += o[e];
     }
