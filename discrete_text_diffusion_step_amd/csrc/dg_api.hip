@@ -313,6 +313,7 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   nr.k_dst = kv->k;
   nr.k_head_stride = static_cast<long long>(kv->capacity) * dh;
   nr.k_row0 = P;
+  nr.k_ring = kv->ring ? kv->capacity : 0;
   nr.v_dst = ws.v_rows;
   nr.v_head_stride = static_cast<long long>(n) * dh;
   nr.pos0 = P;
@@ -333,7 +334,8 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   }
   DG_HIP(launch_norm_rope(nr, dt, s));
   const long long vt_cache_hs = static_cast<long long>(dh) * kv->capacity;
-  DG_HIP(launch_v_transpose(dt, ws.v_rows, n, Hkv, dh, kv->v, vt_cache_hs, kv->capacity, P, s));
+  DG_HIP(launch_v_transpose(dt, ws.v_rows, n, Hkv, dh, kv->v, vt_cache_hs, kv->capacity, P, s,
+                            kv->ring ? kv->capacity : 0));
 
   AttnArgs at;
   at.q = ws.qkv;
@@ -348,6 +350,7 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   at.Hkv = Hkv;
   at.n_rep = Hq / Hkv;
   at.kv_len = P;
+  at.ring = kv->ring ? kv->capacity : 0;
   at.sliding = c->layer_type == 0;
   at.window = c->window;
   at.key_lo = (at.sliding && !causal) ? (P > c->window ? P - c->window : 0) : 0;
@@ -392,17 +395,32 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
   return DG_OK;
 }
 
+// Room for this call's rows at positions [kv_len, kv_len + n): a plain
+// cache needs kv_len + n <= capacity; a ring (sliding layers) needs the
+// window and the new rows to fit at once.
+int check_kv_room(const dg_attn_cfg *c, const dg_kv_layer *kv, int n) {
+  if (kv->ring != 0 && kv->ring != 1) return DG_ERR_SHAPE;
+  if (kv->ring) {
+    if (c->layer_type != 0 || c->window <= 0 || kv->capacity % 32) return DG_ERR_UNSUPPORTED;
+    if (kv->capacity < c->window + n) return DG_ERR_CAPACITY;
+    return DG_OK;
+  }
+  if (kv->kv_len > kv->capacity) return DG_ERR_SHAPE;
+  if (kv->kv_len + n > kv->capacity) return DG_ERR_CAPACITY;   // this call's rows sit at [kv_len, kv_len + n)
+  return DG_OK;
+}
+
 int check_attn_call(const dg_attn_cfg *c, const dg_attn_w *w, const dg_kv_layer *kv, int n, int causal,
                     const void *x) {
   DG_TRY(check_attn_cfg(c));
   if (!w || !kv || !x) return DG_ERR_NULL;
   if (!w->w_in_norm || !w->w_q || !w->w_k || !w->w_o || !w->q_norm || !w->k_norm) return DG_ERR_NULL;
   if (!c->shared_kv && !w->w_v) return DG_ERR_NULL;
-  if (n < 0 || kv->kv_len < 0 || kv->capacity < 0 || kv->kv_len > kv->capacity) return DG_ERR_SHAPE;
+  if (n < 0 || kv->kv_len < 0 || kv->capacity < 0) return DG_ERR_SHAPE;
   if (kv->capacity % 8) return DG_ERR_SHAPE;
   if (n > 0 && (!kv->k || !kv->v)) return DG_ERR_NULL;
   if (causal != 0 && causal != 1) return DG_ERR_SHAPE;
-  if (kv->kv_len + n > kv->capacity) return DG_ERR_CAPACITY;   // this call's rows sit at [kv_len, kv_len + n)
+  DG_TRY(check_kv_room(c, kv, n));
   return DG_OK;
 }
 
@@ -973,7 +991,8 @@ static int check_kv(const dg_model_cfg *c, const dg_kv_cache *kv) {
   const int P = kv->layer[0].kv_len;
   for (int l = 0; l < c->n_layers; ++l) {
     const dg_kv_layer &L = kv->layer[l];
-    if (L.kv_len != P || L.kv_len < 0 || L.kv_len > L.capacity || L.capacity % 8) return DG_ERR_SHAPE;
+    if (L.kv_len != P || L.kv_len < 0 || L.capacity % 8) return DG_ERR_SHAPE;
+    if (!L.ring && L.kv_len > L.capacity) return DG_ERR_SHAPE;
     if (!L.k || !L.v) return DG_ERR_NULL;
   }
   return DG_OK;
@@ -990,7 +1009,7 @@ int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cac
   const int n = st->canvas_len;
   if (n <= 0) return DG_ERR_SHAPE;
   for (int l = 0; l < cfg->n_layers; ++l)
-    if (kv->layer[l].kv_len + n > kv->layer[l].capacity) return DG_ERR_CAPACITY;
+    DG_TRY(check_kv_room(layer_cfg(cfg, l), &kv->layer[l], n));
   if (!ws) return DG_ERR_NULL;
   Carve cv(ws);
   const StepWs sw = step_carve(cfg, n, st->logits == nullptr, cv);
@@ -1057,7 +1076,7 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
   if (n < 0) return DG_ERR_SHAPE;
   if (n == 0) return DG_OK;
   for (int l = 0; l < cfg->n_layers; ++l)
-    if (kv->layer[l].kv_len + n > kv->layer[l].capacity) return DG_ERR_CAPACITY;
+    DG_TRY(check_kv_room(layer_cfg(cfg, l), &kv->layer[l], n));
   if (!ws) return DG_ERR_NULL;
   Carve cv(ws);
   const StepWs sw = step_carve(cfg, n, false, cv);
@@ -1106,6 +1125,7 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
       nr.k_dst = KL.k;
       nr.k_head_stride = static_cast<long long>(KL.capacity) * ac->head_dim;
       nr.k_row0 = KL.kv_len;
+      nr.k_ring = KL.ring ? KL.capacity : 0;
       nr.v_dst = aw.v_rows;
       nr.v_head_stride = static_cast<long long>(n) * ac->head_dim;
       nr.pos0 = KL.kv_len;
@@ -1123,7 +1143,8 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
       }
       DG_HIP(launch_norm_rope(nr, dt, s));
       DG_HIP(launch_v_transpose(dt, aw.v_rows, n, ac->n_kv_heads, ac->head_dim, KL.v,
-                                static_cast<long long>(ac->head_dim) * KL.capacity, KL.capacity, KL.kv_len, s));
+                                static_cast<long long>(ac->head_dim) * KL.capacity, KL.capacity, KL.kv_len, s,
+                                KL.ring ? KL.capacity : 0));
       KL.kv_len += n;
       break;
     }

@@ -13,6 +13,7 @@ struct NormRopeArgs {
   void *k_dst;               // [Hkv][..][dh], row k_row0 + j
   long long k_head_stride;   // elements between heads
   int k_row0;
+  int k_ring = 0;            // > 0: row r of the cache lives at r mod k_ring
   void *v_dst;               // [Hkv][n_tok][dh], row j
   long long v_head_stride;
   int pos0;
@@ -40,6 +41,7 @@ struct AttnArgs {
   int kv_len, key_lo;
   int causal, sliding, window;
   int n_split;
+  int ring;                  // > 0: cache position m lives at row / column m mod ring
   float *o_part;             // [n_split][Hkv*R][dh]
   float *ml_part;            // [n_split][Hkv*R][2]
   void *out;                 // row (token j, head h) at out + j*out_ld + h*dh
@@ -72,9 +74,10 @@ hipError_t launch_norm_rope(const NormRopeArgs &a, int dtype, hipStream_t s);
 // tab[j][t] = (cos, sin) of angle (pos0 + j) * base^(-2t/dh), fp64 angle; t >= n_rot: (1, 0)
 hipError_t launch_rope_table(int pos0, int n_tok, int dh, double base, int n_rot, float2 *tab, hipStream_t s);
 hipError_t launch_attention(const AttnArgs &a, int dtype, int dh, hipStream_t s);
-// dst[h][d][col0 + j] = src[h][j][d] for j < n (values to the transposed layout)
+// dst[h][d][col0 + j] = src[h][j][d] for j < n (values to the transposed layout);
+// ring > 0: column (col0 + j) mod ring
 hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh, void *dst, long long dst_hs,
-                              int dst_ld, int col0, hipStream_t s);
+                              int dst_ld, int col0, hipStream_t s, int ring = 0);
 // Workgroups the split-KV attention grid aims for: kernels whose LDS tiles
 // exceed 80 KB run one workgroup per CU, the others two.
 #ifndef DG_ATTN_PAIR

@@ -63,7 +63,8 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
     } else if (it < a.Hq + a.Hkv) {
       const int h = it - a.Hq;
       src = row + a.k_off + h * a.dh;
-      dst = static_cast<T *>(a.k_dst) + h * a.k_head_stride + static_cast<long long>(a.k_row0 + j) * a.dh;
+      const int kr = a.k_ring ? (a.k_row0 + j) % a.k_ring : a.k_row0 + j;
+      dst = static_cast<T *>(a.k_dst) + h * a.k_head_stride + static_cast<long long>(kr) * a.dh;
       w = static_cast<const T *>(a.k_norm);
     } else {
       const int h = it - a.Hq - a.Hkv;
@@ -334,6 +335,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
       const int r = p / C::KCPR, c = (p % C::KCPR) ^ C::kswz(r);
       int m = t0 + r;
       m = m < k_lo ? k_lo : (m >= k_hi ? k_hi - 1 : m);
+      if (a.ring) m %= a.ring;
       const T *src = Kg + static_cast<long long>(m) * DH + c * C::VEC;
       __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(kb + blk * 64 * C::VEC), 16, 0, 0);
     }
@@ -343,7 +345,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
       const int p = blk * 64 + lane;
       const int d = p / C::VCPR, c = (p % C::VCPR) ^ C::vswz(d);
       int k0 = t0 + c * C::VEC;
-      k0 = k0 > vld - C::VEC ? vld - C::VEC : k0;
+      // ring: 32-key tiles start at multiples of 32 and the ring length is a
+      // multiple of 32, so a chunk of 8 keys never wraps
+      k0 = a.ring ? k0 % a.ring : (k0 > vld - C::VEC ? vld - C::VEC : k0);
       const T *src = Vg + static_cast<long long>(d) * vld + k0;
       __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(vb + blk * 64 * C::VEC), 16, 0, 0);
     }
@@ -597,6 +601,7 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
       const int r = p / C::KCPR, c = (p % C::KCPR) ^ C::kswz(r);
       int m = t0 + r;
       m = m < k_lo ? k_lo : (m >= k_hi ? k_hi - 1 : m);
+      if (a.ring) m %= a.ring;
       const T *src = Kg + static_cast<long long>(m) * DH + c * C::VEC;
       __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(kb + blk * 64 * C::VEC), 16, 0, 0);
     }
@@ -606,7 +611,9 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
       const int p = blk * 64 + lane;
       const int d = p / C::VCPR, c = (p % C::VCPR) ^ C::vswz(d);
       int k0 = t0 + c * C::VEC;
-      k0 = k0 > vld - C::VEC ? vld - C::VEC : k0;
+      // ring: 32-key tiles start at multiples of 32 and the ring length is a
+      // multiple of 32, so a chunk of 8 keys never wraps
+      k0 = a.ring ? k0 % a.ring : (k0 > vld - C::VEC ? vld - C::VEC : k0);
       const T *src = Vg + static_cast<long long>(d) * vld + k0;
       __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(vb + blk * 64 * C::VEC), 16, 0, 0);
     }
@@ -820,7 +827,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a, int
 // bf16 with 8-aligned destination columns: 16-byte loads of token rows and
 // 16-byte stores of dimension rows, the tile transposed in LDS.
 __global__ __launch_bounds__(256) void v_transpose16_kernel(const bf16_t *src, int n, int dh, bf16_t *dst,
-                                                            long long dst_hs, int dst_ld, int col0) {
+                                                            long long dst_hs, int dst_ld, int col0, int ring) {
   __shared__ bf16_t tile[64][72];   // [token][d], rows padded by 16 bytes
   const int h = blockIdx.z;
   const int j0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
@@ -843,20 +850,25 @@ __global__ __launch_bounds__(256) void v_transpose16_kernel(const bf16_t *src, i
     const int d = d0 + dd, j = j0 + jc;
     if (d >= dh || j >= n) continue;
     if (j + 8 <= n) {
+      // col0, j and the ring length are multiples of 8: the 8 columns never wrap
+      const int col = ring ? (col0 + j) % ring : col0 + j;
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         w[e] = static_cast<uint32_t>(tile[jc + 2 * e][dd]) | (static_cast<uint32_t>(tile[jc + 2 * e + 1][dd]) << 16);
-      *reinterpret_cast<uint4 *>(o + static_cast<long long>(d) * dst_ld + col0 + j) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4 *>(o + static_cast<long long>(d) * dst_ld + col) = make_uint4(w[0], w[1], w[2], w[3]);
     } else {
-      for (int e = 0; j + e < n; ++e) o[static_cast<long long>(d) * dst_ld + col0 + j + e] = tile[jc + e][dd];
+      for (int e = 0; j + e < n; ++e) {
+        const int col = ring ? (col0 + j + e) % ring : col0 + j + e;
+        o[static_cast<long long>(d) * dst_ld + col] = tile[jc + e][dd];
+      }
     }
   }
 }
 
 template <typename T>
 __global__ __launch_bounds__(256) void v_transpose_kernel(const T *src, int n, int dh, T *dst, long long dst_hs,
-                                                          int dst_ld, int col0) {
+                                                          int dst_ld, int col0, int ring) {
   __shared__ T tile[64][65];
   const int h = blockIdx.z;
   const int j0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
@@ -870,7 +882,7 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const T *src, int n, i
   __syncthreads();
   for (int i = ty; i < 64; i += 4) {
     const int d = d0 + i, j = j0 + tx;
-    if (j < n && d < dh) o[static_cast<long long>(d) * dst_ld + col0 + j] = tile[tx][i];
+    if (j < n && d < dh) o[static_cast<long long>(d) * dst_ld + (ring ? (col0 + j) % ring : col0 + j)] = tile[tx][i];
   }
 }
 
@@ -896,19 +908,20 @@ hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh, void *dst, long long dst_hs,
-                              int dst_ld, int col0, hipStream_t s) {
+                              int dst_ld, int col0, hipStream_t s, int ring) {
   if (n <= 0) return hipSuccess;
   dim3 grid((n + 63) / 64, (dh + 63) / 64, Hkv);
-  const bool vec = dtype == DG_BF16 && col0 % 8 == 0 && dst_ld % 8 == 0 && dst_hs % 8 == 0 && dh % 8 == 0;
+  const bool vec = dtype == DG_BF16 && col0 % 8 == 0 && dst_ld % 8 == 0 && dst_hs % 8 == 0 && dh % 8 == 0 &&
+                   ring % 8 == 0;
   if (vec)
     hipLaunchKernelGGL(v_transpose16_kernel, grid, dim3(256), 0, s, static_cast<const bf16_t *>(src), n, dh,
-                       static_cast<bf16_t *>(dst), dst_hs, dst_ld, col0);
+                       static_cast<bf16_t *>(dst), dst_hs, dst_ld, col0, ring);
   else if (dtype == DG_BF16)
     hipLaunchKernelGGL(v_transpose_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t *>(src), n, dh,
-                       static_cast<bf16_t *>(dst), dst_hs, dst_ld, col0);
+                       static_cast<bf16_t *>(dst), dst_hs, dst_ld, col0, ring);
   else
     hipLaunchKernelGGL(v_transpose_kernel<float>, grid, dim3(256), 0, s, static_cast<const float *>(src), n, dh,
-                       static_cast<float *>(dst), dst_hs, dst_ld, col0);
+                       static_cast<float *>(dst), dst_hs, dst_ld, col0, ring);
   return hipGetLastError();
 }
 

@@ -26,7 +26,10 @@ def generate(model, kv, prompt, n_canvases, canvas_len=256, max_steps=48, seed=1
     V = model.cfg["vocab"]
     tau = 0.5 * math.log(V) if tau is None else tau
     if prompt is not None and prompt.numel() > 0:
-        B.dg_commit_canvas(model, kv, prompt, stream=stream)
+        # a ring cache takes at most ring_tokens new positions per call
+        step = getattr(kv, "ring_tokens", 0) or prompt.numel()
+        for p0 in range(0, prompt.numel(), step):
+            B.dg_commit_canvas(model, kv, prompt[p0:p0 + step], stream=stream)
     out = torch.empty(n_canvases, canvas_len, dtype=torch.int32, device=prompt.device)
     steps_used = []
     canvas = B.Canvas(canvas_len, model.cfg["hidden"], model.cfg["dtype"], device=prompt.device)

@@ -107,6 +107,13 @@ typedef struct {
   void *v;
   int capacity;
   int kv_len;
+  int ring;            /* 0: position m at row m (kv_len + n_tok <= capacity).
+                        * 1 (sliding layers only): position m at row m mod
+                        * capacity, so the cache holds only the window and the
+                        * rows in flight: capacity a multiple of 32 and at least
+                        * window + n_tok; kv_len counts all committed positions
+                        * (aitrends glossary Sliding-window: only the last
+                        * window rows are ever read). */
 } dg_kv_layer;
 
 /* Workspace bytes for dg_attn_layer with at most n_tok tokens per call. */

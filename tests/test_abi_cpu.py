@@ -44,7 +44,7 @@ def _attn_c(**over):
 def test_attn_validation_codes():
     L = B.lib()
     w = B.AttnW(*(ctypes.c_void_p(256) for _ in range(7)))
-    kv = B.KVLayer(ctypes.c_void_p(256), ctypes.c_void_p(256), 4096, 2048)
+    kv = B.KVLayer(ctypes.c_void_p(256), ctypes.c_void_p(256), 4096, 2048, 0)
     x = ctypes.c_void_p(256)
     ws = ctypes.c_void_p(256)
     call = lambda c, n=256, causal=0, kvv=kv, wsb=1 << 40, xx=x, ww=w: L.dg_attn_layer(
@@ -57,7 +57,7 @@ def test_attn_validation_codes():
     assert call(_attn_c(), n=-1) == -2
     assert call(_attn_c(), causal=2) == -2
     assert call(_attn_c(), wsb=1024) == -4
-    full = B.KVLayer(ctypes.c_void_p(256), ctypes.c_void_p(256), 2104, 2048)
+    full = B.KVLayer(ctypes.c_void_p(256), ctypes.c_void_p(256), 2104, 2048, 0)
     assert call(_attn_c(), causal=1, kvv=full) == -7
     c = _attn_c()
     c.dtype = 7
@@ -152,3 +152,21 @@ def test_quantize_fp8_validation_codes():
     assert L.dg_quantize_fp8(1, p, 4, 0, p, p, None) == -2
     assert L.dg_quantize_fp8(1, None, 4, 64, p, p, None) == -1
     assert L.dg_quantize_fp8(1, p, 0, 64, None, None, None) == 0
+
+
+def test_ring_cache_validation_codes():
+    L = B.lib()
+    w = B.AttnW(*(ctypes.c_void_p(256) for _ in range(7)))
+    x = ctypes.c_void_p(256)
+    call = lambda c, kvv, n=256: L.dg_attn_layer(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kvv), n, 0, x,
+                                                 ctypes.c_void_p(256), 1 << 40, None)
+    ring = lambda cap, kvl: B.KVLayer(ctypes.c_void_p(256), ctypes.c_void_p(256), cap, kvl, 1)
+    # window 1024 + 256 tokens: 1280 rows; kv_len may run far past the ring
+    assert call(_attn_c(), ring(1280, 9000), n=0) == 0
+    assert call(_attn_c(), ring(1272, 100)) == -3              # not a multiple of 32
+    assert call(_attn_c(), ring(1248, 100)) == -7              # window + tokens do not fit
+    g = synth.global_cfg()
+    assert call(B.attn_cfg_c(g), ring(1280, 100)) == -3        # rings are for sliding layers
+    bad = ring(1280, 100)
+    bad.ring = 2
+    assert call(_attn_c(), bad) == -2
