@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--token-rule", choices=("argmax", "gumbel"), default="argmax")
     ap.add_argument("--stop-rule", choices=("renoised", "stable"), default="renoised",
                     help="adaptive stop of the generation run")
+    ap.add_argument("--ring", action="store_true",
+                    help="sliding layers keep a ring of window + 4096 rows; the prompt is committed in 4096-token chunks")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -158,15 +160,19 @@ def main():
         log("expert weights quantised to fp8 e4m3")
     model = B.Model(mcfg, w)
     cap = args.prompt + args.canvases * CANVAS
-    kv = B.KV(mcfg, cap, device=dev)
-    ws = torch.empty(B.dg_workspace_bytes(model.c_cfg, CANVAS, max(args.prompt, CANVAS)), dtype=torch.uint8,
-                     device=dev)
+    chunk = 4096 if args.ring else args.prompt
+    kv = B.KV(mcfg, cap, device=dev, ring_tokens=chunk if args.ring else 0)
+    kv_bytes = sum(t.numel() * t.element_size() for t in kv.k + kv.v)
+    log(f"kv cache: {kv_bytes / 1e9:.2f} GB ({'ring' if args.ring else 'plain'} sliding layers)")
+    ws = torch.empty(B.dg_workspace_bytes(model.c_cfg, CANVAS, max(min(args.prompt, chunk), CANVAS)),
+                     dtype=torch.uint8, device=dev)
     prompt = synth.tokens(args.prompt, V, synth.generator(2, dev), device=dev)
 
     # prompt prefill (causal encode of 4096 tokens)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    B.dg_commit_canvas(model, kv, prompt, ws=ws)
+    for p0 in range(0, args.prompt, chunk):
+        B.dg_commit_canvas(model, kv, prompt[p0:p0 + chunk], ws=ws)
     torch.cuda.synchronize()
     prefill_ms = (time.perf_counter() - t0) * 1e3
     P = kv.kv_len
@@ -246,6 +252,7 @@ def main():
                                "256-token canvas after a 4096-token prompt",
                    "canvas": CANVAS, "committed_rows": P, "params": n_params, "adaptive_stop_in_timed_loop": False,
                    "expert_weights": "fp8_e4m3 (row scales)" if fp8 else "bf16",
+                   "kv_cache": {"sliding": "ring" if args.ring else "plain", "bytes": kv_bytes},
                    "sampler": {"commit_rule": args.commit_rule, "token_rule": args.token_rule,
                                "stop_rule": args.stop_rule}},
         "eff_tok_s": eff, "tokens_per_forward": {"full_schedule": round(tpf_full, 3), "pages": 20},
