@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--token-rule", choices=("argmax", "gumbel"), default="argmax")
     ap.add_argument("--stop-rule", choices=("renoised", "stable"), default="renoised",
                     help="adaptive stop of the generation run")
+    ap.add_argument("--batch", type=int, default=1,
+                    help="canvases per forward (independent sequences, each with its own prompt and KV cache)")
     ap.add_argument("--ring", action="store_true",
                     help="sliding layers keep a ring of window + 4096 rows; the prompt is committed in 4096-token chunks")
     args = ap.parse_args()
@@ -161,30 +163,39 @@ def main():
     model = B.Model(mcfg, w)
     cap = args.prompt + args.canvases * CANVAS
     chunk = 4096 if args.ring else args.prompt
-    kv = B.KV(mcfg, cap, device=dev, ring_tokens=chunk if args.ring else 0)
-    kv_bytes = sum(t.numel() * t.element_size() for t in kv.k + kv.v)
-    log(f"kv cache: {kv_bytes / 1e9:.2f} GB ({'ring' if args.ring else 'plain'} sliding layers)")
-    ws = torch.empty(B.dg_workspace_bytes(model.c_cfg, CANVAS, max(min(args.prompt, chunk), CANVAS)),
+    NB = args.batch
+    kvs = [B.KV(mcfg, cap, device=dev, ring_tokens=chunk if args.ring else 0) for _ in range(NB)]
+    kv = kvs[0]
+    kv_bytes = sum(t.numel() * t.element_size() for k in kvs for t in k.k + k.v)
+    log(f"kv cache: {kv_bytes / 1e9:.2f} GB ({'ring' if args.ring else 'plain'} sliding layers, {NB} sequence(s))")
+    ws_step = (B.dg_workspace_bytes_batch(model.c_cfg, NB, CANVAS) if NB > 1
+               else B.dg_workspace_bytes(model.c_cfg, CANVAS, 0))
+    ws = torch.empty(max(ws_step, B.dg_workspace_bytes(model.c_cfg, CANVAS, max(min(args.prompt, chunk), CANVAS))),
                      dtype=torch.uint8, device=dev)
-    prompt = synth.tokens(args.prompt, V, synth.generator(2, dev), device=dev)
 
-    # prompt prefill (causal encode of 4096 tokens)
+    # prompt prefill (causal encode of 4096 tokens), one prompt per sequence
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for p0 in range(0, args.prompt, chunk):
-        B.dg_commit_canvas(model, kv, prompt[p0:p0 + chunk], ws=ws)
+    for b in range(NB):
+        prompt = synth.tokens(args.prompt, V, synth.generator(2 + b, dev), device=dev)
+        for p0 in range(0, args.prompt, chunk):
+            B.dg_commit_canvas(model, kvs[b], prompt[p0:p0 + chunk], ws=ws)
     torch.cuda.synchronize()
-    prefill_ms = (time.perf_counter() - t0) * 1e3
+    prefill_ms = (time.perf_counter() - t0) * 1e3 / NB
     P = kv.kv_len
-    log(f"prefill {args.prompt} tokens: {prefill_ms:.1f} ms, kv_len {P}")
+    log(f"prefill {args.prompt} tokens: {prefill_ms:.1f} ms per sequence, kv_len {P}")
 
-    canvas = B.Canvas(CANVAS, D, "bf16", device=dev)
-    canvas.tokens.copy_(B.dg_canvas_noise(CANVAS, V, 1, 0, device=dev))
+    canvas = B.Canvas(CANVAS, D, "bf16", device=dev, n_canvas=NB)
+    for b in range(NB):
+        canvas.tokens[b * CANVAS:(b + 1) * CANVAS].copy_(B.dg_canvas_noise(CANVAS, V, 1, b, device=dev))
 
     def step(i):
-        s = dict(synth.sampler_cfg(V, n_steps=48, step=i % 48, canvas_idx=0, final_step=(i % 48 == 47)),
-                 commit_rule=args.commit_rule, token_rule=args.token_rule)
-        B.dg_canvas_step(model, kv, canvas, s, ws=ws)
+        scs = [dict(synth.sampler_cfg(V, n_steps=48, step=i % 48, canvas_idx=b, final_step=(i % 48 == 47)),
+                    commit_rule=args.commit_rule, token_rule=args.token_rule) for b in range(NB)]
+        if NB > 1:
+            B.dg_canvas_step_batch(model, kvs, canvas, scs, ws=ws)
+        else:
+            B.dg_canvas_step(model, kv, canvas, scs[0], ws=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -209,14 +220,14 @@ def main():
     for _ in range(3):
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        B.dg_commit_canvas(model, kv, canvas.tokens, ws=ws)
+        B.dg_commit_canvas(model, kv, canvas.tokens[:CANVAS], ws=ws)
         torch.cuda.synchronize()
         commit_ms.append((time.perf_counter() - t1) * 1e3)
         kv.set_len(P)   # rewind: the rows appended are scratch here
     commit = sorted(commit_ms)[1]
 
     gen = None
-    if not args.no_generate:
+    if not args.no_generate and NB == 1:
         kv.set_len(P)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
@@ -230,7 +241,7 @@ def main():
         log(f"adaptive generation: {gen}")
 
     avg_ms = sum(durs) / len(durs)
-    bytes_launch = gateup_bytes(mcfg, CANVAS)
+    bytes_launch = gateup_bytes(mcfg, CANVAS * NB)
     achieved = bytes_launch / (avg_ms * 1e-3) / 1e9
     kname = ("moe expert gate/up (grouped MFMA GEMM + SwiGLU, fp8 e4m3 weights widened to bf16)" if fp8 else
              "moe expert gate/up (grouped MFMA GEMM + SwiGLU)")
@@ -240,17 +251,19 @@ def main():
             "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": bytes_launch, "launches": len(durs)}
 
     tpf_full = CANVAS / 48.0
-    eff = {"tpf_5.33_incl_commit": round(CANVAS / (48 * ms_step + commit) * 1e3, 1),
-           "tpf_20": round(20.0 / ms_step * 1e3, 1)}
+    # per forward of NB canvases: 48 steps then NB commits of 256 positions
+    eff = {"tpf_5.33_incl_commit": round(NB * CANVAS / (48 * ms_step + NB * commit) * 1e3, 1),
+           "tpf_20": round(NB * 20.0 / ms_step * 1e3, 1)}
     result = {
         "metric": "canvas denoise steps/s (256-tok canvas) + eff. tok/s; % of MFMA/HBM roofline",
-        "value": round(K / elapsed, 3), "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "value": round(NB * K / elapsed, 3), "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded random-init weights and tokens)",
         "config": {"workload": "30-layer DiffusionGemma-style canvas denoise step: 25 sliding (W 1024) + 5 global "
                                "layers, hidden 2816, 128 experts top-8 + shared (SwiGLU 704), vocab 262144, "
                                "256-token canvas after a 4096-token prompt",
                    "canvas": CANVAS, "committed_rows": P, "params": n_params, "adaptive_stop_in_timed_loop": False,
+                   "canvases_per_forward": NB,
                    "expert_weights": "fp8_e4m3 (row scales)" if fp8 else "bf16",
                    "kv_cache": {"sliding": "ring" if args.ring else "plain", "bytes": kv_bytes},
                    "sampler": {"commit_rule": args.commit_rule, "token_rule": args.token_rule,

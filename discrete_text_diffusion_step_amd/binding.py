@@ -133,6 +133,9 @@ def lib(path=None):
             "dg_workspace_bytes": (c_size, [P(ModelCfg), c_int, c_int]),
             "dg_canvas_step": (c_int, [P(ModelCfg), P(ModelW), P(KVCache), P(CanvasState), P(SamplerCfg),
                                        c_void, c_size, c_void]),
+            "dg_canvas_step_batch": (c_int, [P(ModelCfg), P(ModelW), P(KVCache), P(CanvasState), P(SamplerCfg),
+                                             c_int, c_void, c_size, c_void]),
+            "dg_workspace_bytes_batch": (c_size, [P(ModelCfg), c_int, c_int]),
             "dg_commit_canvas": (c_int, [P(ModelCfg), P(ModelW), P(KVCache), c_void, c_int, c_void, c_size,
                                          c_void]),
             "dg_rmsnorm": (c_int, [c_int, c_int, c_float, c_int, c_void, c_void, c_void, c_void]),
@@ -414,23 +417,30 @@ def dg_workspace_bytes(mcfg_c, max_canvas, max_commit):
     return lib().dg_workspace_bytes(ctypes.byref(mcfg_c), max_canvas, max_commit)
 
 
-class Canvas:
-    """Device state of one canvas carried across denoising steps."""
+def dg_workspace_bytes_batch(mcfg_c, n_canvas, canvas_len):
+    return lib().dg_workspace_bytes_batch(ctypes.byref(mcfg_c), n_canvas, canvas_len)
 
-    def __init__(self, n, hidden, dtype, device="cuda", keep_logits_vocab=0):
+
+class Canvas:
+    """Device state carried across denoising steps for n_canvas canvases of n
+    positions, stored back to back (one canvas by default)."""
+
+    def __init__(self, n, hidden, dtype, device="cuda", keep_logits_vocab=0, n_canvas=1):
         dt = torch.bfloat16 if dtype == "bf16" else torch.float32
-        self.tokens = torch.zeros(n, dtype=torch.int32, device=device)
-        self.u = torch.zeros(n, hidden, dtype=dt, device=device)
-        self.commit = torch.zeros(n, dtype=torch.uint8, device=device)
-        self.entropy = torch.zeros(n, dtype=torch.float32, device=device)
-        self.n_renoised = torch.zeros(1, dtype=torch.int32, device=device)
-        self.logits = (torch.empty(n, keep_logits_vocab, dtype=torch.float32, device=device)
+        m = n * n_canvas
+        self.tokens = torch.zeros(m, dtype=torch.int32, device=device)
+        self.u = torch.zeros(m, hidden, dtype=dt, device=device)
+        self.commit = torch.zeros(m, dtype=torch.uint8, device=device)
+        self.entropy = torch.zeros(m, dtype=torch.float32, device=device)
+        self.n_renoised = torch.zeros(n_canvas, dtype=torch.int32, device=device)
+        self.logits = (torch.empty(m, keep_logits_vocab, dtype=torch.float32, device=device)
                        if keep_logits_vocab else None)
         self.use_u = 0
         self.n = n
+        self.n_canvas = n_canvas
         # proposals of the previous step (-1: none yet) and how many changed
-        self.pred = torch.full((n,), -1, dtype=torch.int32, device=device)
-        self.n_changed = torch.zeros(1, dtype=torch.int32, device=device)
+        self.pred = torch.full((m,), -1, dtype=torch.int32, device=device)
+        self.n_changed = torch.zeros(n_canvas, dtype=torch.int32, device=device)
 
     def c_state(self):
         return CanvasState(ptr(self.tokens), ptr(self.u), self.use_u, ptr(self.commit), ptr(self.entropy),
@@ -446,6 +456,22 @@ def dg_canvas_step(model, kv, canvas, scfg, ws=None, stream=None):
     check(L.dg_canvas_step(ctypes.byref(model.c_cfg), ctypes.byref(model.c_w), ctypes.byref(kv.c),
                            ctypes.byref(st), ctypes.byref(c), ptr(ws), ws.numel(), stream_handle(stream)),
           "dg_canvas_step")
+    canvas.use_u = 1 if model.cfg["sc_ffn"] > 0 else 0
+
+
+def dg_canvas_step_batch(model, kvs, canvas, scfgs, ws=None, stream=None):
+    """One step of canvas.n_canvas canvases in one forward; kvs[b] and
+    scfgs[b] belong to canvas b."""
+    L = lib()
+    B = canvas.n_canvas
+    assert len(kvs) == B and len(scfgs) == B
+    st = canvas.c_state()
+    cs = (SamplerCfg * B)(*[sampler_cfg_c(c) for c in scfgs])
+    ks = (KVCache * B)(*[kv.c for kv in kvs])
+    if ws is None:
+        ws = workspace(L.dg_workspace_bytes_batch(ctypes.byref(model.c_cfg), B, canvas.n), canvas.tokens.device)
+    check(L.dg_canvas_step_batch(ctypes.byref(model.c_cfg), ctypes.byref(model.c_w), ks, ctypes.byref(st), cs, B,
+                                 ptr(ws), ws.numel(), stream_handle(stream)), "dg_canvas_step_batch")
     canvas.use_u = 1 if model.cfg["sc_ffn"] > 0 else 0
 
 

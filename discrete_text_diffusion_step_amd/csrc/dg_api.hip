@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <vector>
+
 #include "dg_launch.h"
 
 
@@ -201,18 +203,19 @@ struct RopeTab {
   int pos0 = -1;
 };
 
-AttnWs attn_carve(const dg_attn_cfg *c, const AttnPlan &p, Carve &cv) {
+// p: the projections over all rows; pa: the attention of one canvas
+AttnWs attn_carve(const dg_attn_cfg *c, const AttnPlan &p, const AttnPlan &pa, Carve &cv) {
   const size_t es = esize(c->dtype);
   AttnWs w;
   const size_t n = static_cast<size_t>(p.n);
   w.h = cv.bytes(n * c->hidden * es);
   w.qkv = cv.bytes(n * p.Ntot * es);
-  w.v_rows = cv.bytes(n * p.Nk * es);   // [Hkv][n][dh] from the norm pass
+  w.v_rows = cv.bytes(n * p.Nk * es);   // per canvas [Hkv][C][dh] from the norm pass
   w.o = cv.bytes(n * p.Nq * es);
-  const size_t rows = static_cast<size_t>(c->n_kv_heads) * p.R;
-  if (p.n_split_max > 1) {
-    w.o_part = cv.take<float>(p.n_split_max * rows * c->head_dim);
-    w.ml_part = cv.take<float>(p.n_split_max * rows * 2);
+  const size_t rows = static_cast<size_t>(c->n_kv_heads) * pa.R;
+  if (pa.n_split_max > 1) {
+    w.o_part = cv.take<float>(pa.n_split_max * rows * c->head_dim);
+    w.ml_part = cv.take<float>(pa.n_split_max * rows * 2);
   } else {
     w.o_part = w.ml_part = nullptr;
   }
@@ -253,15 +256,19 @@ int rope_rot(const dg_attn_cfg *c) {
   return static_cast<int>(floor(rf * (c->head_dim / 2) + 0.5));
 }
 
-// x <- x + Attention(x).  h_in, when given, already holds rms(x, w_in_norm).
-int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, int causal, void *x,
-              Carve &cv, hipStream_t s, const void *h_in = nullptr, NextNorm next = NextNorm(),
-              RopeTab rt = RopeTab()) {
+// x <- x + Attention(x) for B canvases of C rows each (x holds them back to
+// back), canvas b attending over its own cache kvs[b].  The projections run
+// over all B*C rows at once; norm/RoPE, the cache writes and attention run
+// per canvas.  h_in, when given, already holds rms(x, w_in_norm); rts[b]
+// (optional) is canvas b's rotation table.
+int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *const *kvs, int B, int C, int causal,
+              void *x, Carve &cv, hipStream_t s, const void *h_in, NextNorm next, const RopeTab *rts) {
+  const int n = B * C;
   const AttnPlan p = attn_plan(c, n);
-  const AttnWs ws = attn_carve(c, p, cv);
+  const AttnPlan pa = B == 1 ? p : attn_plan(c, C);
+  const AttnWs ws = attn_carve(c, p, pa, cv);
   const int dt = c->dtype;
   const int D = c->hidden, dh = c->head_dim, Hq = c->n_q_heads, Hkv = c->n_kv_heads;
-  const int P = kv->kv_len;
 
   const void *h = h_in;
   if (!h) {
@@ -294,81 +301,88 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
     }
   }
 
-  NormRopeArgs nr;
-  nr.qkv = ws.qkv;
-  nr.ld = p.Ntot;
-  nr.n_tok = n;
-  nr.Hq = Hq;
-  nr.Hkv = Hkv;
-  nr.dh = dh;
-  nr.q_off = 0;
-  nr.k_off = p.Nq;
-  nr.v_off = c->shared_kv ? p.Nq : p.Nq + p.Nk;
-  nr.q_norm = w->q_norm;
-  nr.k_norm = w->k_norm;
-  // This call's K rows go to the cache at rows [P, P + n); its V rows go to
-  // the workspace and are then written transposed into cache columns
-  // [P, P + n).  Decode uses those rows as scratch (kv_len stays P); encode
-  // keeps them and advances kv_len.
-  nr.k_dst = kv->k;
-  nr.k_head_stride = static_cast<long long>(kv->capacity) * dh;
-  nr.k_row0 = P;
-  nr.k_ring = kv->ring ? kv->capacity : 0;
-  nr.v_dst = ws.v_rows;
-  nr.v_head_stride = static_cast<long long>(n) * dh;
-  nr.pos0 = P;
-  nr.rope_base = c->rope_base;
-  nr.n_rot = rope_rot(c);
-  nr.eps = c->rms_eps;
-  nr.sqrt_dh = static_cast<float>(sqrt(static_cast<double>(dh)));
-  nr.v_unit_rms = c->v_unit_rms;
-  if (DG_QKV_FUSED && p.qkv_wide && p.qkv_ks > 1) {
-    nr.part = ws.qkv_part;
-    nr.n_part = p.qkv_ks;
-  }
-  if (rt.tab && rt.pos0 == P) {
-    nr.rope_tab = rt.tab;
-  } else {
-    DG_HIP(launch_rope_table(P, n, dh, c->rope_base, rope_rot(c), ws.rope_tab, s));
-    nr.rope_tab = ws.rope_tab;
-  }
-  DG_HIP(launch_norm_rope(nr, dt, s));
-  const long long vt_cache_hs = static_cast<long long>(dh) * kv->capacity;
-  DG_HIP(launch_v_transpose(dt, ws.v_rows, n, Hkv, dh, kv->v, vt_cache_hs, kv->capacity, P, s,
-                            kv->ring ? kv->capacity : 0));
+  for (int b = 0; b < B; ++b) {
+    dg_kv_layer *kv = kvs[b];
+    const int P = kv->kv_len;
+    void *qkv_b = static_cast<char *>(ws.qkv) + static_cast<size_t>(b) * C * p.Ntot * esize(dt);
+    void *vrows_b = static_cast<char *>(ws.v_rows) + static_cast<size_t>(b) * C * p.Nk * esize(dt);
+    NormRopeArgs nr;
+    nr.qkv = qkv_b;
+    nr.ld = p.Ntot;
+    nr.n_tok = C;
+    nr.Hq = Hq;
+    nr.Hkv = Hkv;
+    nr.dh = dh;
+    nr.q_off = 0;
+    nr.k_off = p.Nq;
+    nr.v_off = c->shared_kv ? p.Nq : p.Nq + p.Nk;
+    nr.q_norm = w->q_norm;
+    nr.k_norm = w->k_norm;
+    // This call's K rows go to the cache at rows [P, P + C); its V rows go to
+    // the workspace and are then written transposed into cache columns
+    // [P, P + C).  Decode uses those rows as scratch (kv_len stays P); encode
+    // keeps them and advances kv_len.
+    nr.k_dst = kv->k;
+    nr.k_head_stride = static_cast<long long>(kv->capacity) * dh;
+    nr.k_row0 = P;
+    nr.k_ring = kv->ring ? kv->capacity : 0;
+    nr.v_dst = vrows_b;
+    nr.v_head_stride = static_cast<long long>(C) * dh;
+    nr.pos0 = P;
+    nr.rope_base = c->rope_base;
+    nr.n_rot = rope_rot(c);
+    nr.eps = c->rms_eps;
+    nr.sqrt_dh = static_cast<float>(sqrt(static_cast<double>(dh)));
+    nr.v_unit_rms = c->v_unit_rms;
+    if (B == 1 && DG_QKV_FUSED && p.qkv_wide && p.qkv_ks > 1) {
+      nr.part = ws.qkv_part;
+      nr.n_part = p.qkv_ks;
+    }
+    if (rts && rts[b].tab && rts[b].pos0 == P) {
+      nr.rope_tab = rts[b].tab;
+    } else {
+      float2 *tab = ws.rope_tab + static_cast<size_t>(b) * C * (dh / 2);
+      DG_HIP(launch_rope_table(P, C, dh, c->rope_base, rope_rot(c), tab, s));
+      nr.rope_tab = tab;
+    }
+    DG_HIP(launch_norm_rope(nr, dt, s));
+    const long long vt_cache_hs = static_cast<long long>(dh) * kv->capacity;
+    DG_HIP(launch_v_transpose(dt, vrows_b, C, Hkv, dh, kv->v, vt_cache_hs, kv->capacity, P, s,
+                              kv->ring ? kv->capacity : 0));
 
-  AttnArgs at;
-  at.q = ws.qkv;
-  at.q_ld = p.Ntot;
-  at.k_cache = kv->k;
-  at.cache_hs = static_cast<long long>(kv->capacity) * dh;
-  at.v_cache = kv->v;
-  at.vcache_hs = vt_cache_hs;
-  at.vcache_ld = kv->capacity;
-  at.n_tok = n;
-  at.Hq = Hq;
-  at.Hkv = Hkv;
-  at.n_rep = Hq / Hkv;
-  at.kv_len = P;
-  at.ring = kv->ring ? kv->capacity : 0;
-  at.sliding = c->layer_type == 0;
-  at.window = c->window;
-  at.key_lo = (at.sliding && !causal) ? (P > c->window ? P - c->window : 0) : 0;
-  at.causal = causal;
-  // split the keys so the grid covers the chip, at least 64 keys per slice
-  const int n_keys = P + n - at.key_lo;
-  int ns = p.n_split_max;
-  const int max_by_keys = (n_keys + 63) / 64;
-  if (ns > max_by_keys) ns = max_by_keys;
-  if (ns < 1) ns = 1;
-  at.n_split = ns;
-  at.o_part = ws.o_part;
-  at.ml_part = ws.ml_part;
-  at.out = ws.o;
-  at.out_ld = p.Nq;
-  {
-    TimedLaunch tl(DG_KT_ATTN, s);
-    DG_HIP(launch_attention(at, dt, dh, s));
+    AttnArgs at;
+    at.q = qkv_b;
+    at.q_ld = p.Ntot;
+    at.k_cache = kv->k;
+    at.cache_hs = static_cast<long long>(kv->capacity) * dh;
+    at.v_cache = kv->v;
+    at.vcache_hs = vt_cache_hs;
+    at.vcache_ld = kv->capacity;
+    at.n_tok = C;
+    at.Hq = Hq;
+    at.Hkv = Hkv;
+    at.n_rep = Hq / Hkv;
+    at.kv_len = P;
+    at.ring = kv->ring ? kv->capacity : 0;
+    at.sliding = c->layer_type == 0;
+    at.window = c->window;
+    at.key_lo = (at.sliding && !causal) ? (P > c->window ? P - c->window : 0) : 0;
+    at.causal = causal;
+    // split the keys so the grid covers the chip, at least 64 keys per slice
+    const int n_keys = P + C - at.key_lo;
+    int ns = pa.n_split_max;
+    const int max_by_keys = (n_keys + 63) / 64;
+    if (ns > max_by_keys) ns = max_by_keys;
+    if (ns < 1) ns = 1;
+    at.n_split = ns;
+    at.o_part = ws.o_part;
+    at.ml_part = ws.ml_part;
+    at.out = static_cast<char *>(ws.o) + static_cast<size_t>(b) * C * p.Nq * esize(dt);
+    at.out_ld = p.Nq;
+    {
+      TimedLaunch tl(DG_KT_ATTN, s);
+      DG_HIP(launch_attention(at, dt, dh, s));
+    }
   }
 
   // x += o W_o^T
@@ -391,8 +405,15 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
     }
   }
   if (next.h) DG_HIP(launch_rmsnorm(dt, n, D, next.eps, x, next.w, next.h, s));
-  if (causal) kv->kv_len = P + n;
+  if (causal)
+    for (int b = 0; b < B; ++b) kvs[b]->kv_len += C;
   return DG_OK;
+}
+
+int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, int causal, void *x, Carve &cv,
+              hipStream_t s, const void *h_in = nullptr, NextNorm next = NextNorm(), RopeTab rt = RopeTab()) {
+  dg_kv_layer *k1[1] = {kv};
+  return attn_impl(c, w, k1, 1, n, causal, x, cv, s, h_in, next, &rt);
 }
 
 // Room for this call's rows at positions [kv_len, kv_len + n): a plain
@@ -424,9 +445,10 @@ int check_attn_call(const dg_attn_cfg *c, const dg_attn_w *w, const dg_kv_layer 
   return DG_OK;
 }
 
-size_t attn_ws_bytes(const dg_attn_cfg *c, int n) {
+size_t attn_ws_bytes(const dg_attn_cfg *c, int n, int C = 0) {
   Carve cv(nullptr);
-  attn_carve(c, attn_plan(c, n), cv);
+  const AttnPlan p = attn_plan(c, n);
+  attn_carve(c, p, C > 0 && C != n ? attn_plan(c, C) : p, cv);
   return cv.off + 256;
 }
 
@@ -508,9 +530,13 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   DG_HIP(launch_router_topk(rl, n, E, k, c->route_scale, idx, tw, s));
   const int rows_per_expert = (n * k + E - 1) / E;
   const int mtile = rows_per_expert > 48 ? 4 : DG_MOE_MT;   // 64-row tiles for long groups
+  const bool fp8 = c->expert_format == DG_EXPERTS_FP8_E4M3;
+  // long groups (several canvases, prompt commits): 256-row wide tiles, so
+  // each expert's weights are streamed once for all of its rows
+  const bool wide_l = !fp8 && dt == DG_BF16 && rows_per_expert > DG_WIDE_EXPERTS_L;
   // the shared expert's rows are cut into chunks of one row tile, so its
   // workgroups run side by side with the routed experts' instead of looping
-  const int chunk = 16 * mtile;
+  const int chunk = wide_l ? 256 : 16 * mtile;
   const int n_x = (n + chunk - 1) / chunk;
   DG_HIP(launch_moe_permute(idx, tw, n, k, E, chunk, ws.g_off, ws.row_token, ws.row_weight, ws.pair_row, s));
 
@@ -539,7 +565,6 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   gu.C = ws.H;
   gu.ldc = fmax;
   const long long moe_rows = static_cast<long long>(n) * (k + 1);
-  const bool fp8 = c->expert_format == DG_EXPERTS_FP8_E4M3;
   gu.bs0 = w->s_gate;
   gu.bs1 = w->s_up;
   gu.bxs0 = w->ss_gate;
@@ -549,6 +574,8 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   {
     TimedLaunch tl(DG_KT_MOE_GATEUP, s);
     if (fp8) DG_HIP(launch_gemm_f8_grouped(gu, EPI_SWIGLU, mtile, s));
+    else if (wide_l && wide_ok(dt, gu, WIDE_EXPERT_GU_L, moe_rows))
+      DG_HIP(launch_gemm_wide(gu, EPI_SWIGLU, WIDE_EXPERT_GU_L, s));
     else if (wide) DG_HIP(launch_gemm_wide(gu, EPI_SWIGLU, WIDE_EXPERT_GU, s));
     else DG_HIP(sgemm(dt, gu, EPI_SWIGLU, mtile, DG_MOE_NT_GU, s));
   }
@@ -580,6 +607,8 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   {
     TimedLaunch tl(DG_KT_MOE_DOWN, s);
     if (fp8) DG_HIP(launch_gemm_f8_grouped(dn, EPI_ROWSCALE_F32, mtile, s));
+    else if (wide_l && wide_ok(dt, dn, WIDE_EXPERT_DN_L, moe_rows))
+      DG_HIP(launch_gemm_wide(dn, EPI_ROWSCALE_F32, WIDE_EXPERT_DN_L, s));
     else if (wide && wide_ok(dt, dn, WIDE_EXPERT_DN, moe_rows))
       DG_HIP(launch_gemm_wide(dn, EPI_ROWSCALE_F32, WIDE_EXPERT_DN, s));
     else if (DG_DOWN_COLS && mtile == DG_MOE_MT && wide_ok(dt, dn, WIDE_EXPERT_DN, moe_rows))
@@ -715,12 +744,18 @@ SoftWs soft_carve(int n, int D, int V, int dtype, Carve &cv) {
   return w;
 }
 
+// u = P E for n rows; the probabilities of canvas b (rows [b*C, (b+1)*C))
+// are tempered with sc[b]'s temperature (B = 1, C = n: one canvas).
 int soft_embed_impl(const dg_sampler_cfg *sc, int n, int D, int dt, const float *logits, const float *rowstats,
-                    const void *embed_t, void *u, Carve &cv, hipStream_t s) {
+                    const void *embed_t, void *u, Carve &cv, hipStream_t s, int B = 1) {
   const int V = sc->vocab;
   const SoftWs ws = soft_carve(n, D, V, dt, cv);
   if (n == 0) return DG_OK;
-  DG_HIP(launch_probs(dt, logits, rowstats, n, V, static_cast<float>(1.0 / temperature(sc)), ws.P, s));
+  const int C = n / B;
+  for (int b = 0; b < B; ++b)
+    DG_HIP(launch_probs(dt, logits + static_cast<size_t>(b) * C * V, rowstats + static_cast<size_t>(b) * C * 2, C, V,
+                        static_cast<float>(1.0 / temperature(&sc[b])),
+                        static_cast<char *>(ws.P) + static_cast<size_t>(b) * C * V * esize(dt), s));
   const SoftPlan pl = softembed_plan(dt, n, D, V);
   {
     GemmArgs g = dense_args(ws.P, V, n, D, V, u, D);
@@ -768,9 +803,10 @@ const dg_attn_cfg *layer_cfg(const dg_model_cfg *c, int l) {
   return (l % c->global_every) == c->global_every - 1 ? &c->global : &c->sliding;
 }
 
-size_t layer_ws_bytes(const dg_model_cfg *c, int n) {
+// n rows in canvases of C rows (C = n: one canvas)
+size_t layer_ws_bytes(const dg_model_cfg *c, int n, int C) {
   size_t m = moe_ws_bytes(&c->moe, n);
-  const size_t a0 = attn_ws_bytes(&c->sliding, n), a1 = attn_ws_bytes(&c->global, n);
+  const size_t a0 = attn_ws_bytes(&c->sliding, n, C), a1 = attn_ws_bytes(&c->global, n, C);
   if (a0 > m) m = a0;
   if (a1 > m) m = a1;
   return m;
@@ -783,7 +819,7 @@ struct StepWs {
   void *rest;
 };
 
-StepWs step_carve(const dg_model_cfg *c, int n, bool need_logits, Carve &cv) {
+StepWs step_carve(const dg_model_cfg *c, int n, bool need_logits, Carve &cv, int C = 0) {
   const size_t es = esize(c->dtype);
   const int D = c->sliding.hidden;
   StepWs w;
@@ -794,7 +830,7 @@ StepWs step_carve(const dg_model_cfg *c, int n, bool need_logits, Carve &cv) {
   w.rowstats = cv.take<float>(static_cast<size_t>(n) * 2);
   w.tab[0] = cv.take<float2>(static_cast<size_t>(n) * (c->sliding.head_dim / 2));
   w.tab[1] = cv.take<float2>(static_cast<size_t>(n) * (c->global.head_dim / 2));
-  size_t tail = layer_ws_bytes(c, n);
+  size_t tail = layer_ws_bytes(c, n, C > 0 ? C : n);
   {
     Carve t(nullptr);
     t.bytes(static_cast<size_t>(n) * D * es);
@@ -810,18 +846,23 @@ StepWs step_carve(const dg_model_cfg *c, int n, bool need_logits, Carve &cv) {
   return w;
 }
 
-// Rotation tables for the first layer of each type (every layer of a type
-// sits at the same position in a step); a layer at another position makes
-// its own.
-int make_rope_tabs(const dg_model_cfg *cfg, const dg_kv_cache *kv, int n, const StepWs &sw, RopeTab (&rt)[2],
+// Rotation tables of every canvas for the first layer of each type (every
+// layer of a type sits at the same position in a step); rt[2*b + t] is
+// canvas b's table for type t (0 sliding, 1 global).  A layer at another
+// position makes its own.
+int make_rope_tabs(const dg_model_cfg *cfg, const dg_kv_cache *kv, int B, int C, const StepWs &sw, RopeTab *rt,
                    hipStream_t s) {
   for (int t = 0; t < 2; ++t) {
     for (int l = 0; l < cfg->n_layers; ++l) {
       const dg_attn_cfg *ac = layer_cfg(cfg, l);
       if ((ac == &cfg->global) != (t == 1)) continue;
-      rt[t].pos0 = kv->layer[l].kv_len;
-      rt[t].tab = sw.tab[t];
-      DG_HIP(launch_rope_table(rt[t].pos0, n, ac->head_dim, ac->rope_base, rope_rot(ac), sw.tab[t], s));
+      for (int b = 0; b < B; ++b) {
+        RopeTab &r = rt[2 * b + t];
+        r.pos0 = kv[b].layer[l].kv_len;
+        r.tab = sw.tab[t] + static_cast<size_t>(b) * C * (ac->head_dim / 2);
+        DG_HIP(launch_rope_table(r.pos0, C, ac->head_dim, ac->rope_base, rope_rot(ac), sw.tab[t] +
+                                 static_cast<size_t>(b) * C * (ac->head_dim / 2), s));
+      }
       break;
     }
   }
@@ -998,28 +1039,38 @@ static int check_kv(const dg_model_cfg *c, const dg_kv_cache *kv) {
   return DG_OK;
 }
 
-int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cache *kv, dg_canvas_state *st,
-                   const dg_sampler_cfg *scfg, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// One denoising step of B canvases of C rows (st's buffers hold them back to
+// back; kv[b] and scfg[b] are canvas b's).
+int step_impl(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cache *kv, dg_canvas_state *st,
+              const dg_sampler_cfg *scfg, int B, void *ws, size_t ws_bytes, hipStream_t s) {
   DG_TRY(check_model(cfg));
-  DG_TRY(check_sampler_cfg(scfg));
   DG_TRY(check_model_w(cfg, w, true));
-  DG_TRY(check_kv(cfg, kv));
+  if (!kv || !scfg) return DG_ERR_NULL;
+  if (B <= 0) return DG_ERR_SHAPE;
   if (!st || !st->tokens || !st->u || !st->commit || !st->entropy || !st->n_renoised) return DG_ERR_NULL;
-  if (scfg->vocab != cfg->vocab) return DG_ERR_SHAPE;
-  const int n = st->canvas_len;
-  if (n <= 0) return DG_ERR_SHAPE;
-  for (int l = 0; l < cfg->n_layers; ++l)
-    DG_TRY(check_kv_room(layer_cfg(cfg, l), &kv->layer[l], n));
+  const int C = st->canvas_len;
+  if (C <= 0) return DG_ERR_SHAPE;
+  for (int b = 0; b < B; ++b) {
+    DG_TRY(check_sampler_cfg(&scfg[b]));
+    if (scfg[b].vocab != cfg->vocab) return DG_ERR_SHAPE;
+    if (scfg[b].commit_rule == DG_COMMIT_SORTED_CUMULATIVE && C > kSortedMaxRows) return DG_ERR_SHAPE;
+    DG_TRY(check_kv(cfg, &kv[b]));
+    for (int l = 0; l < cfg->n_layers; ++l) DG_TRY(check_kv_room(layer_cfg(cfg, l), &kv[b].layer[l], C));
+  }
+  const int n = B * C;
   if (!ws) return DG_ERR_NULL;
   Carve cv(ws);
-  const StepWs sw = step_carve(cfg, n, st->logits == nullptr, cv);
+  const StepWs sw = step_carve(cfg, n, st->logits == nullptr, cv, C);
   if (ws_bytes < cv.off) return DG_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int dt = cfg->dtype, D = cfg->sliding.hidden;
+  const int dt = cfg->dtype, D = cfg->sliding.hidden, V = cfg->vocab;
 
-  DG_HIP(launch_embed(dt, st->tokens, n, D, cfg->vocab, w->embed, sw.x, s));
-  RopeTab rt[2];
-  DG_TRY(make_rope_tabs(cfg, kv, n, sw, rt, s));
+  DG_HIP(launch_embed(dt, st->tokens, n, D, V, w->embed, sw.x, s));
+  std::vector<RopeTab> rt(2 * B);
+  DG_TRY(make_rope_tabs(cfg, kv, B, C, sw, rt.data(), s));
   if (st->use_u && cfg->sc_ffn > 0) {
     GemmArgs g = dense_args(st->u, D, n, cfg->sc_ffn, D, sw.g_sc, cfg->sc_ffn);
     g.seg_B0[0] = w->sc_gate;
@@ -1029,18 +1080,25 @@ int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cac
     d.seg_B0[0] = w->sc_down;
     DG_HIP(sgemm(dt, d, EPI_ADD, DG_DENSE_MT, DG_DENSE_NT, s));
   }
+  std::vector<dg_kv_layer> Ls(B);
+  std::vector<dg_kv_layer *> Lp(B);
+  std::vector<RopeTab> rl(B);
   for (int l = 0; l < cfg->n_layers; ++l) {
     Carve c1(sw.rest);
-    dg_kv_layer L = kv->layer[l];
+    const dg_attn_cfg *ac = layer_cfg(cfg, l);
+    const int t = ac == &cfg->global ? 1 : 0;
+    for (int b = 0; b < B; ++b) {
+      Ls[b] = kv[b].layer[l];   // decode: the caller's kv_len stays as it is
+      Lp[b] = &Ls[b];
+      rl[b] = rt[2 * b + t];
+    }
     dg_moe_cfg mc = cfg->moe;
     mc.layer_scalar = w->layer_scalar[l];
     NextNorm to_moe;
     to_moe.h = sw.h;
     to_moe.w = w->moe[l].w_in_norm;
     to_moe.eps = mc.rms_eps;
-    const dg_attn_cfg *ac = layer_cfg(cfg, l);
-    DG_TRY(attn_impl(ac, &w->attn[l], &L, n, 0, sw.x, c1, s, l == 0 ? nullptr : sw.h, to_moe,
-                     rt[ac == &cfg->global ? 1 : 0]));
+    DG_TRY(attn_impl(ac, &w->attn[l], Lp.data(), B, C, 0, sw.x, c1, s, l == 0 ? nullptr : sw.h, to_moe, rl.data()));
     NextNorm to_attn;
     if (l + 1 < cfg->n_layers) {
       to_attn.h = sw.h;
@@ -1053,18 +1111,41 @@ int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cac
   float *logits = st->logits ? st->logits : sw.logits;
   {
     Carve c(sw.rest);
-    DG_TRY(lm_head_impl(n, D, cfg->vocab, cfg->rms_eps, dt, sw.x, w->w_final_norm, w->embed, logits, c, s));
+    DG_TRY(lm_head_impl(n, D, V, cfg->rms_eps, dt, sw.x, w->w_final_norm, w->embed, logits, c, s));
   }
-  {
+  for (int b = 0; b < B; ++b) {
     Carve c(sw.rest);
-    DG_TRY(sample_impl(scfg, n, logits, DG_F32, st->tokens, st->commit, st->entropy, sw.rowstats, st->n_renoised,
-                       st->pred, st->n_changed, c, s));
+    const size_t r0 = static_cast<size_t>(b) * C;
+    DG_TRY(sample_impl(&scfg[b], C, logits + r0 * V, DG_F32, st->tokens + r0, st->commit + r0, st->entropy + r0,
+                       sw.rowstats + 2 * r0, st->n_renoised + b, st->pred ? st->pred + r0 : nullptr,
+                       st->n_changed ? st->n_changed + b : nullptr, c, s));
   }
   if (cfg->sc_ffn > 0) {
     Carve c(sw.rest);
-    DG_TRY(soft_embed_impl(scfg, n, D, dt, logits, sw.rowstats, w->embed_t, st->u, c, s));
+    DG_TRY(soft_embed_impl(scfg, n, D, dt, logits, sw.rowstats, w->embed_t, st->u, c, s, B));
   }
   return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cache *kv, dg_canvas_state *st,
+                   const dg_sampler_cfg *scfg, void *ws, size_t ws_bytes, void *stream) {
+  return step_impl(cfg, w, kv, st, scfg, 1, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int dg_canvas_step_batch(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cache *kv, dg_canvas_state *st,
+                         const dg_sampler_cfg *scfg, int n_canvas, void *ws, size_t ws_bytes, void *stream) {
+  return step_impl(cfg, w, kv, st, scfg, n_canvas, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t dg_workspace_bytes_batch(const dg_model_cfg *cfg, int n_canvas, int canvas_len) {
+  if (!cfg || n_canvas <= 0 || canvas_len <= 0) return 0;
+  Carve a(nullptr);
+  step_carve(cfg, n_canvas * canvas_len, true, a, canvas_len);
+  return a.off + 256;
 }
 
 int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *kv, const int32_t *tokens, int n,
@@ -1085,7 +1166,7 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
   const int dt = cfg->dtype, D = cfg->sliding.hidden;
   DG_HIP(launch_embed(dt, tokens, n, D, cfg->vocab, w->embed, sw.x, s));
   RopeTab rt[2];
-  DG_TRY(make_rope_tabs(cfg, kv, n, sw, rt, s));
+  DG_TRY(make_rope_tabs(cfg, kv, 1, n, sw, rt, s));
   const int L = cfg->n_layers;
   for (int l = 0; l < L; ++l) {
     const dg_attn_cfg *ac = layer_cfg(cfg, l);
@@ -1094,7 +1175,7 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
       // last layer: only its K/V are needed (pre-norm, projections, norm/RoPE, append)
       Carve c1(sw.rest);
       const AttnPlan p = attn_plan(ac, n);
-      const AttnWs aw = attn_carve(ac, p, c1);
+      const AttnWs aw = attn_carve(ac, p, p, c1);
       const void *hA = sw.h;   // written by the previous MoE block
       if (l == 0) {
         DG_HIP(launch_rmsnorm(dt, n, D, ac->rms_eps, sw.x, w->attn[l].w_in_norm, aw.h, s));

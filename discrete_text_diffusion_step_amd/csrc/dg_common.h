@@ -284,6 +284,8 @@ enum WideCfg {
   WIDE_ROWS256_N128 = 1,  // 256 x 128 tile, 8 waves x 16 columns
   WIDE_EXPERT_GU = 2,     // expert gate/up: 16*DG_WMOE_MT rows x 64 columns (x2 matrices), 4 waves
   WIDE_EXPERT_DN = 3,     // expert down: 16*DG_WMOE_MT rows x 128 columns, 4 waves
+  WIDE_EXPERT_GU_L = 4,   // expert gate/up, long groups: 256 rows x 128 columns (x2 matrices), 8 waves
+  WIDE_EXPERT_DN_L = 5,   // expert down, long groups: 256 rows x 128 columns, 8 waves
   // every configuration walks k in stages of 64
 };
 #ifndef DG_WIDE_P
@@ -319,12 +321,18 @@ enum WideCfg {
 #ifndef DG_WMOE_MT
 #define DG_WMOE_MT 2
 #endif
+// expert groups averaging more rows than this use the 256-row configurations
+#ifndef DG_WIDE_EXPERTS_L
+#define DG_WIDE_EXPERTS_L 48
+#endif
 #ifndef DG_WMOE_P
 #define DG_WMOE_P 3
 #endif
 // column tile width and k-stage depth of each wide configuration
 inline int wide_bn(int cfg) { return cfg == WIDE_ROWS256_N256 ? 256 : (cfg == WIDE_EXPERT_GU ? 64 : 128); }
-inline int wide_bm(int cfg) { return cfg <= WIDE_ROWS256_N128 ? 256 : 16 * DG_WMOE_MT; }
+inline int wide_bm(int cfg) {
+  return (cfg <= WIDE_ROWS256_N128 || cfg >= WIDE_EXPERT_GU_L) ? 256 : 16 * DG_WMOE_MT;
+}
 inline int wide_kstage(int) { return 64; }
 hipError_t launch_gemm_wide(const GemmArgs &a, int mode, int cfg, hipStream_t s);
 // Column-split bf16 streaming product (waves own adjacent 16*nt-column slices,

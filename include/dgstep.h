@@ -345,6 +345,22 @@ int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cac
                    dg_canvas_state *state, const dg_sampler_cfg *scfg, void *ws, size_t ws_bytes,
                    void *stream);
 
+/* n_canvas independent canvases (separate sequences, each with its own KV
+ * cache) in one forward: the projections, experts, head and P.E run over all
+ * n_canvas * canvas_len rows at once, so every weight is streamed once for
+ * all of them; norm/RoPE, the cache writes, attention and the sampler run
+ * per canvas.  kv[b] and scfg[b] belong to canvas b (arrays of n_canvas);
+ * the buffers of st hold the canvases back to back (tokens, commit,
+ * entropy, pred: [n_canvas * canvas_len]; u: [n_canvas * canvas_len, D];
+ * logits: [n_canvas * canvas_len, vocab]; n_renoised, n_changed:
+ * [n_canvas]); st->canvas_len is one canvas's length.  Each canvas's result
+ * is the one dg_canvas_step gives for it alone.  Workspace:
+ * dg_workspace_bytes_batch. */
+int dg_canvas_step_batch(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cache *kv,
+                         dg_canvas_state *st, const dg_sampler_cfg *scfg, int n_canvas, void *ws, size_t ws_bytes,
+                         void *stream);
+size_t dg_workspace_bytes_batch(const dg_model_cfg *cfg, int n_canvas, int canvas_len);
+
 /* Commit (encode): run the n_tok final tokens causally through the stack and
  * append every layer's K/V at [kv_len, kv_len + n_tok); the last layer stops
  * after its K/V (aitrends attention paragraph: work after the last layer is

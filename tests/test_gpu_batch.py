@@ -1,0 +1,112 @@
+"""Several canvases in one forward (dg_canvas_step_batch) against each canvas
+stepped alone (dg_canvas_step, itself checked against the oracle), and one
+batched canvas against the oracle directly.
+
+The batched products run over more rows, so their tiling and split-K may
+differ from the single-canvas run: logits and u are compared at the fp32
+bar; tokens and commits bit for bit where the oracle-side entropy is more
+than 1e-3 nats from the bound.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from discrete_text_diffusion_step_amd import binding as B
+from discrete_text_diffusion_step_amd import synth
+from oracle import dg_oracle as O
+from tests.helpers import assert_close, np64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _lib(gpu_lib):
+    torch.manual_seed(0)
+    yield
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def test_batch_equals_single_canvases():
+    from tests.test_gpu_parity import gpu_weights, oracle_weights, tiny_model
+    mcfg, w = tiny_model("f32")
+    model = B.Model(mcfg, gpu_weights(w))
+    V, C, D = mcfg["vocab"], 32, mcfg["hidden"]
+    prompts = [synth.tokens(n, V, synth.generator(10 + i)).cuda() for i, n in enumerate((64, 32, 96))]
+    nb = len(prompts)
+
+    def fresh_caches():
+        kvs = []
+        for p in prompts:
+            kv = B.KV(mcfg, 160)
+            B.dg_commit_canvas(model, kv, p)
+            kvs.append(kv)
+        return kvs
+
+    def scfg(b, step):
+        t = (2.0, 1.0, 0.7)[b]
+        return synth.sampler_cfg(V, t_max=t, t_min=0.5, n_steps=4, step=step, canvas_idx=b)
+
+    # batched
+    kvs = fresh_caches()
+    batch = B.Canvas(C, D, "f32", keep_logits_vocab=V, n_canvas=nb)
+    for b in range(nb):
+        batch.tokens[b * C:(b + 1) * C].copy_(B.dg_canvas_noise(C, V, 1, b))
+    got = []
+    for step in range(2):
+        B.dg_canvas_step_batch(model, kvs, batch, [scfg(b, step) for b in range(nb)])
+        sync()
+        got.append(dict(logits=batch.logits.clone(), tokens=batch.tokens.clone(), u=batch.u.clone(),
+                        entropy=batch.entropy.clone(), n_renoised=batch.n_renoised.clone()))
+    assert [kv.kv_len for kv in kvs] == [64, 32, 96]     # decode leaves the caches as they were
+
+    # each canvas alone
+    kvs1 = fresh_caches()
+    for b in range(nb):
+        one = B.Canvas(C, D, "f32", keep_logits_vocab=V)
+        one.tokens.copy_(B.dg_canvas_noise(C, V, 1, b))
+        for step in range(2):
+            B.dg_canvas_step(model, kvs1[b], one, scfg(b, step))
+            sync()
+            g = got[step]
+            rows = slice(b * C, (b + 1) * C)
+            assert_close(np64(g["logits"][rows]), np64(one.logits), "f32", f"canvas {b} step {step} logits")
+            assert_close(np64(g["u"][rows]), np64(one.u), "f32", f"canvas {b} step {step} u")
+            H = np64(one.entropy)
+            clear = np.abs(H - scfg(b, step)["tau"]) > 1e-3
+            np.testing.assert_array_equal(g["tokens"][rows].cpu().numpy()[clear], one.tokens.cpu().numpy()[clear])
+            if clear.all():
+                assert int(g["n_renoised"][b].item()) == int(one.n_renoised.item())
+            # continue the single run from the batched tokens, so both see the same canvas
+            one.tokens.copy_(g["tokens"][rows])
+            one.u.copy_(g["u"][rows])
+
+    # canvas 2 of the first batched step against the oracle
+    wn = oracle_weights(w)
+    rkv = dict(k=[np.zeros((2, 160, 64)) for _ in range(2)], v=[np.zeros((2, 160, 64)) for _ in range(2)],
+               kv_len=0)
+    kn, vn = O.commit_canvas(mcfg, wn, rkv, prompts[2].cpu().numpy(), "f32")
+    for l in range(2):
+        rkv["k"][l][:, :96], rkv["v"][l][:, :96] = kn[l], vn[l]
+    rkv["kv_len"] = 96
+    ref = O.canvas_step(mcfg, wn, rkv, dict(tokens=O.canvas_noise(C, V, 1, 2), u=None), scfg(2, 0), "f32")
+    assert_close(np64(got[0]["logits"][2 * C:3 * C]), ref["logits"], "f32", "batched canvas 2 vs oracle")
+    assert np.max(np.abs(np64(got[0]["entropy"][2 * C:3 * C]) - ref["entropy"])) < 1e-4 * math.log(V)
+
+
+def test_batch_validation():
+    from tests.test_gpu_parity import gpu_weights, tiny_model
+    mcfg, w = tiny_model("f32")
+    model = B.Model(mcfg, gpu_weights(w))
+    V, C = mcfg["vocab"], 32
+    kv = B.KV(mcfg, 64)
+    batch = B.Canvas(C, mcfg["hidden"], "f32", n_canvas=2)
+    full = B.KV(mcfg, 64)
+    full.set_len(48)                       # 48 + 32 rows do not fit 64
+    with pytest.raises(B.DGError) as e:
+        B.dg_canvas_step_batch(model, [kv, full], batch, [synth.sampler_cfg(V)] * 2)
+    assert e.value.status == -7
