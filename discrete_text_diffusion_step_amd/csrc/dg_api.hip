@@ -468,7 +468,11 @@ struct MoeWs {
 bool router_small_tiles(const dg_moe_cfg *c) { return c->dtype == DG_BF16 && c->hidden % 64 == 0; }
 
 int router_ksplit(const dg_moe_cfg *c, int n) {
-  if (router_small_tiles(c)) return 1;
+  if (router_small_tiles(c)) {
+    int ks = DG_ROUTER_KS;
+    while (ks > 1 && c->hidden % (64 * ks)) ks >>= 1;
+    return ks;
+  }
   return choose_ksplit(n, c->n_experts, c->hidden, 16 * DG_DENSE_MT, 16 * DG_DENSE_NT, 256, 16);
 }
 
@@ -518,16 +522,26 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
     h = ws.h;
   }
   const float *rl = rl_in;
+  int n_rparts = 1;
   if (!rl) {
     GemmArgs g = dense_args(h, D, n, E, D, ws.rl, E);
     g.seg_B0[0] = w->w_router;
-    if (router_small_tiles(c)) DG_HIP(sgemm(dt, g, EPI_STORE_F32, 1, 1, s));
-    else DG_HIP(dense_product(dt, g, EPI_STORE_F32, ws.rpart, router_ksplit(c, n), s));
-    rl = ws.rl;
+    if (router_small_tiles(c)) {
+      // 16 x 16 tiles, split-K partials [ks][n][E]; the top-k pass adds them
+      g.C = ws.rpart;
+      g.ldc = E;
+      g.k_splits = router_ksplit(c, n);
+      DG_HIP(sgemm(dt, g, g.k_splits > 1 ? EPI_PARTIAL_F32 : EPI_STORE_F32, 1, 1, s));
+      n_rparts = g.k_splits;
+      rl = ws.rpart;
+    } else {
+      DG_HIP(dense_product(dt, g, EPI_STORE_F32, ws.rpart, router_ksplit(c, n), s));
+      rl = ws.rl;
+    }
   }
   int32_t *idx = idx_out ? idx_out : ws.idx;
   float *tw = w_out ? w_out : ws.tw;
-  DG_HIP(launch_router_topk(rl, n, E, k, c->route_scale, idx, tw, s));
+  DG_HIP(launch_router_topk(rl, n_rparts, n, E, k, c->route_scale, idx, tw, s));
   const int rows_per_expert = (n * k + E - 1) / E;
   const int mtile = rows_per_expert > 48 ? 4 : DG_MOE_MT;   // 64-row tiles for long groups
   const bool fp8 = c->expert_format == DG_EXPERTS_FP8_E4M3;

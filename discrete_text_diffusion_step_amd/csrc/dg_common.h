@@ -322,6 +322,10 @@ enum WideCfg {
 #define DG_WMOE_MT 2
 #endif
 // expert groups averaging more rows than this use the 256-row configurations
+// router product: split-K partials, summed in split order by the top-k pass
+#ifndef DG_ROUTER_KS
+#define DG_ROUTER_KS 4
+#endif
 #ifndef DG_WIDE_EXPERTS_L
 #define DG_WIDE_EXPERTS_L 48
 #endif

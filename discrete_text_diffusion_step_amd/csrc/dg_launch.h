@@ -91,8 +91,9 @@ hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh
 #endif
 int attn_target_workgroups(int dtype, int dh);
 int attn_block_rows(int dtype, int dh);
-hipError_t launch_router_topk(const float *logits, int n_tok, int E, int k, float scale, int32_t *idx, float *w,
-                              hipStream_t s);
+// logits: n_parts partial sums [n_parts][n_tok][E], added in order
+hipError_t launch_router_topk(const float *logits, int n_parts, int n_tok, int E, int k, float scale, int32_t *idx,
+                              float *w, hipStream_t s);
 hipError_t launch_moe_permute(const int32_t *idx, const float *w, int n_tok, int k, int E, int chunk, int *g_off,
                               int *row_token, float *row_weight, int *pair_row, hipStream_t s);
 hipError_t launch_moe_combine(int dtype, void *x, const float *Y, const int *pair_row, int n_tok, int k, int D,

@@ -1445,7 +1445,8 @@ hipError_t launch_gemm_stream(const GemmArgs &a, int mode, int mt, int nt, hipSt
   DG_STREAM_CASE(DG_DENSE_MT, DG_DENSE_NT, 1, EPI_STORE_F32, DG_DENSE_S)
   DG_STREAM_CASE(DG_DENSE_MT, DG_DENSE_NT, 1, EPI_ADD, DG_DENSE_S)
   DG_STREAM_CASE(DG_DENSE_MT, DG_DENSE_NT, 1, EPI_PARTIAL_F32, DG_DENSE_S)
-  DG_STREAM_CASE(1, 1, 1, EPI_STORE_F32, 3)   // router logits: 16 x 16 tiles, whole depth
+  DG_STREAM_CASE(1, 1, 1, EPI_STORE_F32, 3)     // router logits: 16 x 16 tiles, whole depth
+  DG_STREAM_CASE(1, 1, 1, EPI_PARTIAL_F32, 3)   // router logits as split-K partials
   DG_STREAM_CASE(DG_MOE_MT, DG_MOE_NT_GU, 2, EPI_SWIGLU, DG_GU_S)
   DG_STREAM_CASE(DG_DN_MT, DG_MOE_NT_DN, 1, EPI_ROWSCALE_F32, DG_MOE_S)
   DG_STREAM_CASE(DG_MOE_MT, DG_MOE_NT_DN, 1, EPI_ROWSCALE_F32, DG_MOE_S)

@@ -59,17 +59,24 @@ __device__ __forceinline__ void wave_max64(uint32_t &hi, uint32_t &lo) {
 // complemented expert id), so k rounds of a wave maximum pick the experts in
 // order.  Weights are the softmax restricted to the chosen experts (the
 // full-softmax denominator cancels in the renormalisation) times route_scale.
-__global__ __launch_bounds__(256) void router_topk_kernel(const float *logits, int n_tok, int E, int k,
-                                                          float scale, int32_t *idx_out, float *w_out) {
+__global__ __launch_bounds__(256) void router_topk_kernel(const float *logits, int n_parts, int n_tok, int E,
+                                                          int k, float scale, int32_t *idx_out, float *w_out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= n_tok) return;
+  const long long part_stride = static_cast<long long>(n_tok) * E;
   const float *r = logits + static_cast<long long>(t) * E;
   uint32_t kh[4], kl[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    kh[i] = e < E ? float_key(r[e]) : 0u;
+    float v = 0.f;
+    if (e < E) {
+      // the logit is the sum of the split-K partials, in split order
+      v = r[e];
+      for (int p = 1; p < n_parts; ++p) v += r[p * part_stride + e];
+    }
+    kh[i] = e < E ? float_key(v) : 0u;
     kl[i] = e < E ? 0xffffffffu - static_cast<uint32_t>(e) : 0u;
   }
   float chosen_v[8];
@@ -253,10 +260,11 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(T *x, const float *Y, 
 
 }  // namespace
 
-hipError_t launch_router_topk(const float *logits, int n_tok, int E, int k, float scale, int32_t *idx,
+hipError_t launch_router_topk(const float *logits, int n_parts, int n_tok, int E, int k, float scale, int32_t *idx,
                               float *w, hipStream_t s) {
   if (n_tok <= 0) return hipSuccess;
-  hipLaunchKernelGGL(router_topk_kernel, dim3((n_tok + 3) / 4), dim3(256), 0, s, logits, n_tok, E, k, scale, idx, w);
+  hipLaunchKernelGGL(router_topk_kernel, dim3((n_tok + 3) / 4), dim3(256), 0, s, logits, n_parts, n_tok, E, k, scale,
+                     idx, w);
   return hipGetLastError();
 }
 

@@ -295,6 +295,26 @@ def test_moe_bf16_full_injected():
     assert_delta_close(np64(xd), ref, np64(x), "bf16", "moe delta")
 
 
+def test_moe_bf16_router_computed():
+    """Full-size block with the router product on the device (split-K partials
+    summed by the top-k pass): indices bit-exact where the oracle's 8th/9th
+    logit gap exceeds 1e-3, outputs on those tokens at the bf16 bar."""
+    cfg = synth.moe_cfg(2816, 128, 8, 704, 704)
+    g = synth.generator(59)
+    w = synth.moe_weights(cfg, g, with_router=True)
+    x = synth.hidden_states(256, cfg["hidden"], g, "bf16")
+    xd = x.clone().cuda()
+    idx, wts = B.dg_moe_block(cfg, cuda(w), xd, None, want_topk=True)
+    sync()
+    ref, ridx, rw, r = O.moe_block_grouped(cfg, npw(w), np64(x), "bf16")
+    srt = -np.sort(-r, axis=1)
+    clear = (srt[:, 7] - srt[:, 8]) > 1e-3
+    assert clear.mean() > 0.9
+    np.testing.assert_array_equal(idx.cpu().numpy()[clear], ridx[clear])
+    assert rel_err(wts.cpu().numpy()[clear], rw[clear]) < 1e-2
+    assert_delta_close(np64(xd)[clear], ref[clear], np64(x)[clear], "bf16", "moe (router computed) delta")
+
+
 def test_moe_bf16_ragged_groups():
     """45 tokens over 16 experts (top-4): short groups, ragged column tiles
     (ffn 192, shared 128, hidden 320)."""
