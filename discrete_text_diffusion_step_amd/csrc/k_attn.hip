@@ -509,6 +509,13 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
 // P V for its half of the output.  Grid, query blocks, key slices and the
 // split partials are those of attn_fwd_kernel.
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory loads are in flight
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <int DH>
 __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
@@ -517,6 +524,7 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
   constexpr int QT = C::QT;
   constexpr int HALF = DH / 2, DSH = HALF / 32, DTH = HALF / 16;
   static_assert(C::KINS % 8 == 0 && C::VINS % 8 == 0, "eight waves share each tile");
+  constexpr int kNK = C::KINS / 8, kNV = C::VINS / 8;   // loads per wave per K / V^T tile
   __shared__ __attribute__((aligned(16))) T sK0[C::KCH * C::VEC];
   __shared__ __attribute__((aligned(16))) T sK1[C::KCH * C::VEC];
   __shared__ __attribute__((aligned(16))) T sV0[C::VCH * C::VEC];
@@ -593,7 +601,7 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
   const T *Vg = static_cast<const T *>(a.v_cache) + g * a.vcache_hs;
   const int vld = a.vcache_ld;
 
-  auto issue = [&](int t0, T *kb, T *vb) {
+  auto issue_k = [&](int t0, T *kb) {
 #pragma unroll
     for (int j = 0; j < C::KINS / 8; ++j) {
       const int blk = wave + 8 * j;
@@ -605,6 +613,8 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
       const T *src = Kg + static_cast<long long>(m) * DH + c * C::VEC;
       __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(kb + blk * 64 * C::VEC), 16, 0, 0);
     }
+  };
+  auto issue_v = [&](int t0, T *vb) {
 #pragma unroll
     for (int j = 0; j < C::VINS / 8; ++j) {
       const int blk = wave + 8 * j;
@@ -619,7 +629,18 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
     }
   };
 
-  auto compute = [&](int t0, const T *kb, const T *vb) {
+  // One 32-key tile.  Loads run two deep per operand: K(i+2) is issued once
+  // every wave has read K(i) (after the score exchange), V(i+1) once every
+  // wave has finished P V on tile i-1 (after the barrier that opens tile i).
+  // The DMA queue per wave is therefore K0 V0 K1 V1 K2 ..., and the waits
+  // count loads issued after the one needed: K(i) is followed by V(i) and
+  // K(i+1); V(i) by K(i+1), V(i+1) and K(i+2), each present if that tile is.
+  auto tile = [&](int ti, T *kb, const T *vb, T *vb_next) {
+    const int t0 = t_first + ti * kBKV;
+    if (ti + 1 < n_tiles) wait_vm<kNV + kNK>();
+    else wait_vm<kNV>();
+    __syncthreads();
+    if (ti + 1 < n_tiles) issue_v(t0 + kBKV, vb_next);
     // ---- partial S^T = K Q^T over this wave's half of the head dimension
     f32x4 st[2][QT];
 #pragma unroll
@@ -655,6 +676,7 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[kt][qt][i] += xs[wave ^ 1][(kt * QT + qt) * 4 + i][lane];
+    if (ti + 2 < n_tiles) issue_k(t0 + 2 * kBKV, kb);
     // ---- mask, online softmax (identical in both waves of the pair)
     Frag<T> pf[QT];
 #pragma unroll
@@ -711,6 +733,10 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
         vm[e >> 1] |= ok ? ((e & 1) ? 0xffff0000u : 0x0000ffffu) : 0u;
       }
     }
+    if (ti + 2 < n_tiles) wait_vm<2 * kNK + kNV>();
+    else if (ti + 1 < n_tiles) wait_vm<kNK + kNV>();
+    else wait_vm<0>();
+    __syncthreads();
     Frag<T> vf[2];
     load_v_frag<T, DH>(vf[0], vb, hf * HALF + l16, lg);
 #pragma unroll
@@ -723,20 +749,15 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
     }
   };
 
-  if (n_tiles > 0) issue(t_first, sK0, sV0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  if (n_tiles > 0) {
+    issue_k(t_first, sK0);
+    issue_v(t_first, sV0);
+  }
+  if (n_tiles > 1) issue_k(t_first + kBKV, sK1);
   for (int it = 0; it < n_tiles; it += 2) {
-    const int t0 = t_first + it * kBKV;
-    if (it + 1 < n_tiles) issue(t0 + kBKV, sK1, sV1);
-    compute(t0, sK0, sV0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    tile(it, sK0, sV0, sV1);
     if (it + 1 >= n_tiles) break;
-    if (it + 2 < n_tiles) issue(t0 + 2 * kBKV, sK0, sV0);
-    compute(t0 + kBKV, sK1, sV1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    tile(it + 1, sK1, sV1, sV0);
   }
 
   // ---- finish: lanes sharing a query (same l16) hold partial sums of l
