@@ -509,6 +509,23 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
 // P V for its half of the output.  Grid, query blocks, key slices and the
 // split partials are those of attn_fwd_kernel.
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;   // nats a score may exceed the reference max by
+
+// P to bf16: gfx950 packs two floats with round-to-nearest-even in one
+// instruction (the same rounding as f32_to_bf16 on the finite values P holds)
+__device__ __forceinline__ void p_to_bf16(Frag<bf16_t> &f, const float *s) {
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f2_t x = {s[2 * j], s[2 * j + 1]};
+    w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf2_t));
+  }
+  f.v = *reinterpret_cast<bf16x8 *>(w);
+}
+
 // Wait until at most N of this wave's vector-memory loads are in flight
 // (they complete in issue order).
 template <int N>
@@ -601,9 +618,67 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
   const T *Vg = static_cast<const T *>(a.v_cache) + g * a.vcache_hs;
   const int vld = a.vcache_ld;
 
-  auto issue_k = [&](int t0, T *kb) {
+  // A tile that lies wholly inside [k_lo, k_hi) is fetched with buffer loads
+  // into LDS: a 32-bit per-lane offset inside the tile plus a scalar tile
+  // offset, over buffer resources whose extent is this kv head's K rows /
+  // V^T columns (every such tile lies inside it).  A tile never wraps the ring
+  // (tiles start at multiples of 32 and the ring length is a multiple of 32).
+  // Other tiles take the general path, which clamps each key.
+  static_assert(C::VCPR == 4, "V^T chunk swizzle below assumes four 16-byte chunks per row");
+  // K: with 64 chunks per row (d_h 512) load j of a wave covers row
+  // wave + 8j, so its lane offset is (lane ^ swizzle) * 16, formed in the
+  // loop from the lane index rather than held in registers (the d_h 512
+  // kernel has none to spare); narrower rows keep precomputed offsets.
+  constexpr bool kRowPerLoad = C::KCPR == 64;
+  uint32_t koff[kRowPerLoad ? 1 : kNK] = {};
+  if constexpr (!kRowPerLoad) {
 #pragma unroll
-    for (int j = 0; j < C::KINS / 8; ++j) {
+    for (int j = 0; j < kNK; ++j) {
+      const int p = (wave + 8 * j) * 64 + lane;
+      const int r = p / C::KCPR, c = (p % C::KCPR) ^ C::kswz(r);
+      koff[j] = static_cast<uint32_t>((r * DH + c * C::VEC) * sizeof(T));
+    }
+  }
+  // V^T chunk (wave + 8j)*64 + lane is row d = (wave + 8j)*16 + lane/4; its
+  // swizzle (d/4) % 4 = (lane/16) % 4 is the same for every j
+  const uint32_t voff = static_cast<uint32_t>(
+      ((lane >> 2) * vld + (((lane & 3) ^ ((lane >> 4) & 3)) * C::VEC)) * sizeof(T));
+  const long long k_bytes = static_cast<long long>(a.ring ? a.ring : k_hi) * DH * sizeof(T);
+  const long long v_bytes = static_cast<long long>(DH) * vld * sizeof(T);
+  const bool buf_ok = k_bytes < (1ll << 31) && v_bytes < (1ll << 31);
+  constexpr int kRawBufferFlags = 0x00020000;   // resource word 3 on gfx9: 32-bit data format
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(Kg), 0, buf_ok ? static_cast<int>(k_bytes) : 0,
+                                        kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(Vg), 0, buf_ok ? static_cast<int>(v_bytes) : 0,
+                                        kRawBufferFlags);
+
+  auto issue_k = [&](int t0, T *kb) {
+    if (buf_ok && t0 >= k_lo && t0 + kBKV <= k_hi) {
+      const int row0 = a.ring ? t0 % a.ring : t0;
+      const int soff = row0 * DH * static_cast<int>(sizeof(T));
+      if constexpr (kRowPerLoad) {
+        uint32_t ln;   // lane index, recomputed here (not hoisted, not spilled)
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        const uint32_t l16 = ln << 4;
+#pragma unroll
+        for (int j = 0; j < kNK; ++j) {
+          const int r = wave + 8 * j;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void_t *)(kb + r * 64 * C::VEC), 16,
+                                                   static_cast<int>(l16 ^ (C::kswz(r) * 16)),
+                                                   soff + r * DH * static_cast<int>(sizeof(T)), 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kNK; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void_t *)(kb + (wave + 8 * j) * 64 * C::VEC), 16,
+                                                   static_cast<int>(koff[j]), soff, 0, 0);
+      }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < kNK; ++j) {
       const int blk = wave + 8 * j;
       const int p = blk * 64 + lane;
       const int r = p / C::KCPR, c = (p % C::KCPR) ^ C::kswz(r);
@@ -615,19 +690,44 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
     }
   };
   auto issue_v = [&](int t0, T *vb) {
+    if (buf_ok && (a.ring || t0 + kBKV <= vld)) {
+      const int col0 = a.ring ? t0 % a.ring : t0;
 #pragma unroll
-    for (int j = 0; j < C::VINS / 8; ++j) {
+      for (int j = 0; j < kNV; ++j) {
+        const int soff = (col0 + (wave + 8 * j) * 16 * vld) * static_cast<int>(sizeof(T));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void_t *)(vb + (wave + 8 * j) * 64 * C::VEC), 16,
+                                                 static_cast<int>(voff), soff, 0, 0);
+      }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < kNV; ++j) {
       const int blk = wave + 8 * j;
       const int p = blk * 64 + lane;
       const int d = p / C::VCPR, c = (p % C::VCPR) ^ C::vswz(d);
       int k0 = t0 + c * C::VEC;
-      // ring: 32-key tiles start at multiples of 32 and the ring length is a
-      // multiple of 32, so a chunk of 8 keys never wraps
+      // ring: a chunk of 8 keys never wraps (see above)
       k0 = a.ring ? k0 % a.ring : (k0 > vld - C::VEC ? vld - C::VEC : k0);
       const T *src = Vg + static_cast<long long>(d) * vld + k0;
       __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(vb + blk * 64 * C::VEC), 16, 0, 0);
     }
   };
+
+  // Wave-uniform bounds of this wave's query positions: a tile needs no
+  // per-score mask when every key in it is visible to every query here.
+  int pq_min = qpos[0], pq_max = qpos[0];
+#pragma unroll
+  for (int qt = 1; qt < QT; ++qt) {
+    pq_min = min(pq_min, qpos[qt]);
+    pq_max = max(pq_max, qpos[qt]);
+  }
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) {
+    pq_min = min(pq_min, __shfl_xor(pq_min, sh, 64));
+    pq_max = max(pq_max, __shfl_xor(pq_max, sh, 64));
+  }
+  pq_min = __builtin_amdgcn_readfirstlane(pq_min);
+  pq_max = __builtin_amdgcn_readfirstlane(pq_max);
 
   // One 32-key tile.  Loads run two deep per operand: K(i+2) is issued once
   // every wave has read K(i) (after the score exchange), V(i+1) once every
@@ -637,6 +737,9 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
   // K(i+1); V(i) by K(i+1), V(i+1) and K(i+2), each present if that tile is.
   auto tile = [&](int ti, T *kb, const T *vb, T *vb_next) {
     const int t0 = t_first + ti * kBKV;
+    const bool in_range = t0 >= k_lo && t0 + kBKV <= k_hi;
+    const bool unmasked = in_range && (!a.causal || (t0 + kBKV - 1 <= pq_min &&
+                                                     (!a.sliding || t0 > pq_max - a.window)));
     if (ti + 1 < n_tiles) wait_vm<kNV + kNK>();
     else wait_vm<kNV>();
     __syncthreads();
@@ -677,54 +780,91 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[kt][qt][i] += xs[wave ^ 1][(kt * QT + qt) * 4 + i][lane];
     if (ti + 2 < n_tiles) issue_k(t0 + 2 * kBKV, kb);
-    // ---- mask, online softmax (identical in both waves of the pair)
+    // ---- mask (tiles cut by the key range, the causal diagonal or the
+    // window only), online softmax (identical in both waves of the pair)
+    if (!unmasked) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = t0 + lg * 8 + kt * 4 + i;
+            bool ok = m >= k_lo && m < k_hi;
+            if (a.causal) {
+              const int pq = qpos[qt];
+              ok = ok && (m <= pq) && (!a.sliding || m > pq - a.window);
+            }
+            if (!ok) st[kt][qt][i] = -INFINITY;
+          }
+    }
     Frag<T> pf[QT];
+    float corr[QT];
+    bool grow = false;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      float sv[8];
       float mt = -1e30f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) mt = fmaxf(mt, fmaxf(fmaxf(st[kt][qt][0], st[kt][qt][1]),
+                                                          fmaxf(st[kt][qt][2], st[kt][qt][3])));
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      corr[qt] = mt;
+      grow = grow || mt > m_run[qt] + kRescaleSlack;
+    }
+    // The reference maximum moves only when a score exceeds it by more than
+    // kRescaleSlack (then for every query of the wave, so the O rescale is
+    // one uniform branch); until then exp(s - m) <= e^kRescaleSlack, and
+    // O / l is the same quotient.
+    if (__ballot(grow) != 0ull) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float m_new = fmaxf(m_run[qt], corr[qt]);
+        const float c = __builtin_amdgcn_exp2f((m_run[qt] - m_new) * kLog2e);
+        m_run[qt] = m_new;
+        l_run[qt] *= c;
+#pragma unroll
+        for (int dt = 0; dt < DTH; ++dt) {
+          o[dt][qt][0] *= c;
+          o[dt][qt][1] *= c;
+          o[dt][qt][2] *= c;
+          o[dt][qt][3] *= c;
+        }
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float nm = -m_run[qt] * kLog2e;
+      float sv[8];
+      float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = t0 + lg * 8 + kt * 4 + i;
-          bool ok = m >= k_lo && m < k_hi;
-          if (a.causal) {
-            const int pq = qpos[qt];
-            ok = ok && (m <= pq) && (!a.sliding || m > pq - a.window);
-          }
-          const float v = ok ? st[kt][qt][i] : -INFINITY;
-          sv[kt * 4 + i] = v;
-          mt = fmaxf(mt, v);
+          const float e = __builtin_amdgcn_exp2f(fmaf(st[kt][qt][i], kLog2e, nm));
+          sv[kt * 4 + i] = e;
+          psum += e;
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run[qt], mt);
-      const float corr = __expf(m_run[qt] - m_new);
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sv[e] = __expf(sv[e] - m_new);
-        psum += sv[e];
-      }
-      l_run[qt] = l_run[qt] * corr + psum;
-      m_run[qt] = m_new;
-      if (__ballot(corr != 1.0f) != 0ull) {
-#pragma unroll
-        for (int dt = 0; dt < DTH; ++dt) {
-          o[dt][qt][0] *= corr;
-          o[dt][qt][1] *= corr;
-          o[dt][qt][2] *= corr;
-          o[dt][qt][3] *= corr;
-        }
-      }
-      pf[qt].from_floats(sv);
+      l_run[qt] += psum;
+      p_to_bf16(pf[qt], sv);
     }
-    // ---- O^T += V^T P^T over this wave's half (edge tiles: values of keys
-    // outside the range are zeroed)
-    const bool edge = (t0 < k_lo) || (t0 + kBKV > k_hi);
-    uint32_t vm[4];
-    if (edge) {
+    // ---- O^T += V^T P^T over this wave's half (tiles cut by the key range:
+    // values of keys outside it are zeroed, as the cache holds anything there)
+    if (ti + 2 < n_tiles) wait_vm<2 * kNK + kNV>();
+    else if (ti + 1 < n_tiles) wait_vm<kNK + kNV>();
+    else wait_vm<0>();
+    __syncthreads();
+    Frag<T> vf[2];
+    load_v_frag<T, DH>(vf[0], vb, hf * HALF + l16, lg);
+    if (in_range) {
+#pragma unroll
+      for (int dt = 0; dt < DTH; ++dt) {
+        if (dt + 1 < DTH) load_v_frag<T, DH>(vf[(dt + 1) & 1], vb, hf * HALF + (dt + 1) * 16 + l16, lg);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) mma(o[dt][qt], vf[dt & 1], pf[qt]);
+      }
+    } else {
+      uint32_t vm[4];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int m = t0 + lg * 8 + e;
@@ -732,20 +872,14 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
         if ((e & 1) == 0) vm[e >> 1] = 0;
         vm[e >> 1] |= ok ? ((e & 1) ? 0xffff0000u : 0x0000ffffu) : 0u;
       }
-    }
-    if (ti + 2 < n_tiles) wait_vm<2 * kNK + kNV>();
-    else if (ti + 1 < n_tiles) wait_vm<kNK + kNV>();
-    else wait_vm<0>();
-    __syncthreads();
-    Frag<T> vf[2];
-    load_v_frag<T, DH>(vf[0], vb, hf * HALF + l16, lg);
 #pragma unroll
-    for (int dt = 0; dt < DTH; ++dt) {
-      if (dt + 1 < DTH) load_v_frag<T, DH>(vf[(dt + 1) & 1], vb, hf * HALF + (dt + 1) * 16 + l16, lg);
-      Frag<T> v = vf[dt & 1];
-      if (edge) mask_frag(v, vm);
+      for (int dt = 0; dt < DTH; ++dt) {
+        if (dt + 1 < DTH) load_v_frag<T, DH>(vf[(dt + 1) & 1], vb, hf * HALF + (dt + 1) * 16 + l16, lg);
+        Frag<T> v = vf[dt & 1];
+        mask_frag(v, vm);
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) mma(o[dt][qt], v, pf[qt]);
+        for (int qt = 0; qt < QT; ++qt) mma(o[dt][qt], v, pf[qt]);
+      }
     }
   };
 
