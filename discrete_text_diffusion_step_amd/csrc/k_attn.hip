@@ -526,6 +526,33 @@ __device__ __forceinline__ void p_to_bf16(Frag<bf16_t> &f, const float *s) {
   f.v = *reinterpret_cast<bf16x8 *>(w);
 }
 
+// Raw buffer resource (gfx9 layout: 48-bit base, stride 0, byte extent,
+// word 3 = 32-bit data format), wave-uniform.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p)));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(p >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r.w = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from (resource + soff + voff) into LDS at lds + 16*lane
+// (lds wave-uniform).  Issued through inline asm, so the compiler sees no
+// LDS write and adds no waits of its own for it (it cannot tell these tiles
+// from the other LDS data and would wait for every transfer in flight): the
+// caller waits with vmcnt and synchronises before any wave reads the data.
+// The instruction writes no register; M0 carries the LDS address (one wait
+// state between writing M0 and the load) and is declared clobbered.
+__device__ __forceinline__ void dma16(const i32x4_t &rsrc, uint32_t voff, int soff, const void *lds) {
+  const uint32_t m0 = static_cast<uint32_t>((uintptr_t)((lds_void_t *)(const_cast<void *>(lds))));
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               ::"v"(voff), "s"(rsrc), "s"(soff), "s"(__builtin_amdgcn_readfirstlane(static_cast<int>(m0)))
+               : "memory", "m0");
+}
+
 // Wait until at most N of this wave's vector-memory loads are in flight
 // (they complete in issue order).
 template <int N>
@@ -601,6 +628,13 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
       else qf[qt][s].zero();
     }
   }
+  // Consume the Q fragments here, so the compiler waits for their loads once
+  // before the tile loop; otherwise it waits (vmcnt(0): every K/V DMA in
+  // flight as well) at their first use inside the loop, on every tile.
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int s = 0; s < DSH; ++s) asm volatile("" ::"v"(qf[qt][s].v));
 
   f32x4 o[DTH][QT];
 #pragma unroll
@@ -618,12 +652,12 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
   const T *Vg = static_cast<const T *>(a.v_cache) + g * a.vcache_hs;
   const int vld = a.vcache_ld;
 
-  // A tile that lies wholly inside [k_lo, k_hi) is fetched with buffer loads
-  // into LDS: a 32-bit per-lane offset inside the tile plus a scalar tile
-  // offset, over buffer resources whose extent is this kv head's K rows /
-  // V^T columns (every such tile lies inside it).  A tile never wraps the ring
-  // (tiles start at multiples of 32 and the ring length is a multiple of 32).
-  // Other tiles take the general path, which clamps each key.
+  // Tiles move by buffer loads into LDS (dma16) over resources spanning this
+  // kv head's K rows / V^T columns.  A tile that lies wholly inside
+  // [k_lo, k_hi) uses a 32-bit per-lane offset inside the tile plus a scalar
+  // tile offset; a tile never wraps the ring (tiles start at multiples of 32
+  // and the ring length is a multiple of 32).  Other tiles take the general
+  // path, whose per-lane offsets clamp each key.
   static_assert(C::VCPR == 4, "V^T chunk swizzle below assumes four 16-byte chunks per row");
   // K: with 64 chunks per row (d_h 512) load j of a wave covers row
   // wave + 8j, so its lane offset is (lane ^ swizzle) * 16, formed in the
@@ -643,19 +677,12 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
   // swizzle (d/4) % 4 = (lane/16) % 4 is the same for every j
   const uint32_t voff = static_cast<uint32_t>(
       ((lane >> 2) * vld + (((lane & 3) ^ ((lane >> 4) & 3)) * C::VEC)) * sizeof(T));
-  const long long k_bytes = static_cast<long long>(a.ring ? a.ring : k_hi) * DH * sizeof(T);
-  const long long v_bytes = static_cast<long long>(DH) * vld * sizeof(T);
-  const bool buf_ok = k_bytes < (1ll << 31) && v_bytes < (1ll << 31);
-  constexpr int kRawBufferFlags = 0x00020000;   // resource word 3 on gfx9: 32-bit data format
-  const __amdgpu_buffer_rsrc_t k_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(Kg), 0, buf_ok ? static_cast<int>(k_bytes) : 0,
-                                        kRawBufferFlags);
-  const __amdgpu_buffer_rsrc_t v_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(Vg), 0, buf_ok ? static_cast<int>(v_bytes) : 0,
-                                        kRawBufferFlags);
+  // byte extents below 2^31 (the launcher sends larger caches to attn_fwd_kernel)
+  const i32x4_t k_rsrc = buffer_rsrc(Kg, static_cast<uint32_t>((a.ring ? a.ring : k_hi) * DH * sizeof(T)));
+  const i32x4_t v_rsrc = buffer_rsrc(Vg, static_cast<uint32_t>(DH * vld * sizeof(T)));
 
   auto issue_k = [&](int t0, T *kb) {
-    if (buf_ok && t0 >= k_lo && t0 + kBKV <= k_hi) {
+    if (t0 >= k_lo && t0 + kBKV <= k_hi) {
       const int row0 = a.ring ? t0 % a.ring : t0;
       const int soff = row0 * DH * static_cast<int>(sizeof(T));
       if constexpr (kRowPerLoad) {
@@ -665,15 +692,12 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < kNK; ++j) {
           const int r = wave + 8 * j;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void_t *)(kb + r * 64 * C::VEC), 16,
-                                                   static_cast<int>(l16 ^ (C::kswz(r) * 16)),
-                                                   soff + r * DH * static_cast<int>(sizeof(T)), 0, 0);
+          dma16(k_rsrc, l16 ^ static_cast<uint32_t>(C::kswz(r) * 16), soff + r * DH * static_cast<int>(sizeof(T)),
+                kb + r * 64 * C::VEC);
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < kNK; ++j)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void_t *)(kb + (wave + 8 * j) * 64 * C::VEC), 16,
-                                                   static_cast<int>(koff[j]), soff, 0, 0);
+        for (int j = 0; j < kNK; ++j) dma16(k_rsrc, koff[j], soff, kb + (wave + 8 * j) * 64 * C::VEC);
       }
       return;
     }
@@ -685,19 +709,16 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
       int m = t0 + r;
       m = m < k_lo ? k_lo : (m >= k_hi ? k_hi - 1 : m);
       if (a.ring) m %= a.ring;
-      const T *src = Kg + static_cast<long long>(m) * DH + c * C::VEC;
-      __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(kb + blk * 64 * C::VEC), 16, 0, 0);
+      dma16(k_rsrc, static_cast<uint32_t>((m * DH + c * C::VEC) * sizeof(T)), 0, kb + blk * 64 * C::VEC);
     }
   };
   auto issue_v = [&](int t0, T *vb) {
-    if (buf_ok && (a.ring || t0 + kBKV <= vld)) {
+    if (a.ring || t0 + kBKV <= vld) {
       const int col0 = a.ring ? t0 % a.ring : t0;
 #pragma unroll
-      for (int j = 0; j < kNV; ++j) {
-        const int soff = (col0 + (wave + 8 * j) * 16 * vld) * static_cast<int>(sizeof(T));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void_t *)(vb + (wave + 8 * j) * 64 * C::VEC), 16,
-                                                 static_cast<int>(voff), soff, 0, 0);
-      }
+      for (int j = 0; j < kNV; ++j)
+        dma16(v_rsrc, voff, (col0 + (wave + 8 * j) * 16 * vld) * static_cast<int>(sizeof(T)),
+              vb + (wave + 8 * j) * 64 * C::VEC);
       return;
     }
 #pragma unroll
@@ -708,8 +729,7 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
       int k0 = t0 + c * C::VEC;
       // ring: a chunk of 8 keys never wraps (see above)
       k0 = a.ring ? k0 % a.ring : (k0 > vld - C::VEC ? vld - C::VEC : k0);
-      const T *src = Vg + static_cast<long long>(d) * vld + k0;
-      __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)(vb + blk * 64 * C::VEC), 16, 0, 0);
+      dma16(v_rsrc, static_cast<uint32_t>((d * vld + k0) * sizeof(T)), 0, vb + blk * 64 * C::VEC);
     }
   };
 
@@ -742,7 +762,7 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
                                                      (!a.sliding || t0 > pq_max - a.window)));
     if (ti + 1 < n_tiles) wait_vm<kNV + kNK>();
     else wait_vm<kNV>();
-    __syncthreads();
+    lds_sync();   // not __syncthreads(): its fence would wait for every DMA in flight
     if (ti + 1 < n_tiles) issue_v(t0 + kBKV, vb_next);
     // ---- partial S^T = K Q^T over this wave's half of the head dimension
     f32x4 st[2][QT];
@@ -853,7 +873,7 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
     if (ti + 2 < n_tiles) wait_vm<2 * kNK + kNV>();
     else if (ti + 1 < n_tiles) wait_vm<kNK + kNV>();
     else wait_vm<0>();
-    __syncthreads();
+    lds_sync();
     Frag<T> vf[2];
     load_v_frag<T, DH>(vf[0], vb, hf * HALF + l16, lg);
     if (in_range) {
@@ -1047,7 +1067,8 @@ hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
   const int R = a.n_rep * a.n_tok;
   const int qblocks = (R + C::BQ - 1) / C::BQ;
   if constexpr (sizeof(T) == 2 && (DH == 256 || DH == 512)) {
-    if (DG_ATTN_PAIR)
+    // the pair form addresses a head's cache with 32-bit byte offsets
+    if (DG_ATTN_PAIR && static_cast<long long>(a.vcache_ld) * DH * static_cast<long long>(sizeof(T)) < (1ll << 31))
       hipLaunchKernelGGL((attn_pair_kernel<DH>), dim3(a.Hkv * qblocks, a.n_split), dim3(512), 0, s, a);
     else
       hipLaunchKernelGGL((attn_fwd_kernel<T, DH>), dim3(a.Hkv * qblocks, a.n_split), dim3(256), 0, s, a);
