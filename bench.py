@@ -203,7 +203,9 @@ def main():
     log(f"warmup {args.warmup} steps done")
 
     K = args.steps
-    timer = B.kernel_timer("moe_gateup", capacity=K * mcfg["n_layers"] + 8)
+    # every 7th gate/up launch (30 layers a step: the sample rotates through
+    # them); timing all of them would add a few microseconds per event
+    timer = B.kernel_timer("moe_gateup", capacity=K * mcfg["n_layers"] // 7 + 8, every=7)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with timer:

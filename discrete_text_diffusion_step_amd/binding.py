@@ -91,7 +91,7 @@ class CanvasState(ctypes.Structure):
 
 class KernelTimer(ctypes.Structure):
     _fields_ = [("start", ctypes.POINTER(c_void)), ("stop", ctypes.POINTER(c_void)), ("capacity", c_int),
-                ("count", c_int), ("kernel", c_int)]
+                ("count", c_int), ("kernel", c_int), ("every", c_int), ("seen", c_int)]
 
 
 DG_KT = {"moe_gateup": 1, "moe_down": 2, "lm_head": 3, "attn": 4, "soft_embed": 5, "qkv": 6, "oproj": 7}
@@ -485,10 +485,11 @@ def dg_commit_canvas(model, kv, tokens, ws=None, stream=None):
 
 
 class kernel_timer:
-    """Context manager timing every launch of one kernel class with HIP events
-    recorded by the library on the launching stream."""
+    """Context manager timing launches of one kernel class with HIP events
+    recorded by the library on the launching stream: every `every`-th launch
+    (each event adds a few microseconds between kernels)."""
 
-    def __init__(self, kind, capacity=4096):
+    def __init__(self, kind, capacity=4096, every=1):
         self.kind = DG_KT[kind]
         self.cap = capacity
         self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -499,7 +500,7 @@ class kernel_timer:
         torch.cuda.synchronize()
         self._start = (c_void * capacity)(*[a.cuda_event for a, _ in self.ev])
         self._stop = (c_void * capacity)(*[b.cuda_event for _, b in self.ev])
-        self.t = KernelTimer(self._start, self._stop, capacity, 0, self.kind)
+        self.t = KernelTimer(self._start, self._stop, capacity, 0, self.kind, every, 0)
 
     def __enter__(self):
         lib().dg_set_kernel_timer(ctypes.byref(self.t))

@@ -51,10 +51,13 @@ struct TimedLaunch {
   hipStream_t s;
   int slot;
   TimedLaunch(int kt, hipStream_t st) : t(nullptr), s(st), slot(-1) {
-    if (g_timer && g_timer->kernel == kt && g_timer->count < g_timer->capacity) {
-      t = g_timer;
-      slot = t->count++;
-      hipEventRecord(static_cast<hipEvent_t>(t->start[slot]), s);
+    if (g_timer && g_timer->kernel == kt) {
+      const int every = g_timer->every > 1 ? g_timer->every : 1;
+      if (g_timer->seen++ % every == 0 && g_timer->count < g_timer->capacity) {
+        t = g_timer;
+        slot = t->count++;
+        hipEventRecord(static_cast<hipEvent_t>(t->start[slot]), s);
+      }
     }
   }
   ~TimedLaunch() {

@@ -372,10 +372,14 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
 
 /* Optional kernel timer.  The caller creates `capacity` pairs of hipEvent_t
  * and attaches the record with dg_set_kernel_timer; while attached, the
- * library records start[i] / stop[i] on the launching stream around each
- * launch of the selected kernel class and increments `count` (launches past
- * `capacity` are not timed).  The attachment is per host thread; NULL
- * detaches.  This pointer is the library's only state and is off by default. */
+ * library records start[i] / stop[i] on the launching stream around every
+ * `every`-th launch of the selected kernel class (0 or 1: each launch) and
+ * increments `count` (launches past `capacity` are not timed).  `seen`
+ * counts the launches of the class since it was set (the caller sets it to
+ * 0).  Each recorded event adds a few microseconds between kernels, so a
+ * caller timing a whole step samples launches.  The attachment is per host
+ * thread; NULL detaches.  This pointer is the library's only state and is
+ * off by default. */
 enum {
   DG_KT_NONE = 0,
   DG_KT_MOE_GATEUP = 1,  /* grouped expert gate/up product with the SwiGLU epilogue */
@@ -392,6 +396,8 @@ typedef struct {
   int capacity;
   int count;
   int kernel;     /* DG_KT_* */
+  int every;      /* record every `every`-th launch (0 or 1: each) */
+  int seen;       /* launches of the class seen while attached */
 } dg_kernel_timer;
 
 void dg_set_kernel_timer(dg_kernel_timer *timer);
