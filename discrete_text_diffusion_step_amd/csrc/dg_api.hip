@@ -291,13 +291,7 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *const *kvs,
   g.seg_start[g.nseg] = p.Ntot;
   {
     TimedLaunch tl(DG_KT_QKV, s);
-    if (DG_QKV_FUSED && p.qkv_wide && p.qkv_ks > 1) {
-      // split-K partials; the norm/RoPE pass below sums them
-      g.C = ws.qkv_part;
-      g.ldc = p.Ntot;
-      g.k_splits = p.qkv_ks;
-      DG_HIP(launch_gemm_wide(g, EPI_PARTIAL_F32, DG_PROJ_CFG, s));
-    } else if (p.qkv_wide) {
+    if (p.qkv_wide) {
       DG_HIP(wide_product(g, EPI_STORE, DG_PROJ_CFG, ws.qkv_part, p.qkv_ks, s));
     } else {
       DG_HIP(sgemm(dt, g, EPI_STORE, DG_DENSE_MT, DG_DENSE_NT, s));
@@ -337,10 +331,6 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *const *kvs,
     nr.eps = c->rms_eps;
     nr.sqrt_dh = static_cast<float>(sqrt(static_cast<double>(dh)));
     nr.v_unit_rms = c->v_unit_rms;
-    if (B == 1 && DG_QKV_FUSED && p.qkv_wide && p.qkv_ks > 1) {
-      nr.part = ws.qkv_part;
-      nr.n_part = p.qkv_ks;
-    }
     if (rts && rts[b].tab && rts[b].pos0 == P) {
       nr.rope_tab = rts[b].tab;
     } else {
@@ -628,8 +618,6 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
       DG_HIP(launch_gemm_wide(dn, EPI_ROWSCALE_F32, WIDE_EXPERT_DN_L, s));
     else if (wide && wide_ok(dt, dn, WIDE_EXPERT_DN, moe_rows))
       DG_HIP(launch_gemm_wide(dn, EPI_ROWSCALE_F32, WIDE_EXPERT_DN, s));
-    else if (DG_DOWN_COLS && mtile == DG_MOE_MT && wide_ok(dt, dn, WIDE_EXPERT_DN, moe_rows))
-      DG_HIP(launch_gemm_cols(dn, EPI_ROWSCALE_F32, DG_MOE_MT, DG_COLS_NT, s));   // k = ffn is short
     else DG_HIP(sgemm(dt, dn, EPI_ROWSCALE_F32, mtile == DG_MOE_MT ? DG_DN_MT : mtile, DG_MOE_NT_DN, s));
   }
 

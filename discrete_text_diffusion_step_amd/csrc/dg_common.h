@@ -312,9 +312,6 @@ enum WideCfg {
 #ifndef DG_PROJ_TARGET
 #define DG_PROJ_TARGET 256
 #endif
-#ifndef DG_QKV_FUSED
-#define DG_QKV_FUSED 0
-#endif
 #ifndef DG_WIDE_EXPERTS
 #define DG_WIDE_EXPERTS 0
 #endif
@@ -339,18 +336,6 @@ inline int wide_bm(int cfg) {
 }
 inline int wide_kstage(int) { return 64; }
 hipError_t launch_gemm_wide(const GemmArgs &a, int mode, int cfg, hipStream_t s);
-// Column-split bf16 streaming product (waves own adjacent 16*nt-column slices,
-// whole k each); tile (16*mt) x (64*nt).  Needs every k range in whole 64-deep stages.
-#ifndef DG_COLS_NT
-#define DG_COLS_NT 2
-#endif
-#ifndef DG_COLS_S
-#define DG_COLS_S 3
-#endif
-#ifndef DG_DOWN_COLS
-#define DG_DOWN_COLS 0
-#endif
-hipError_t launch_gemm_cols(const GemmArgs &a, int mode, int mt, int nt, hipStream_t s);
 
 template <typename T>
 hipError_t launch_splitk_reduce(const float *part, int splits, int M, int N, long long ldc,

@@ -21,10 +21,6 @@ struct NormRopeArgs {
   int n_rot;                 // frequencies kept (the rest are zero)
   float eps, sqrt_dh;
   int v_unit_rms;
-  // Optional: the projections still as split-K fp32 partials [n_part][n_tok][ld];
-  // the pass sums them (split order) and rounds to the model dtype first.
-  const float *part = nullptr;
-  int n_part = 0;
   // [n_tok][dh/2] (cos, sin) of the rotation angles (launch_rope_table)
   const float2 *rope_tab = nullptr;
 };

@@ -74,31 +74,18 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
       norm = a.v_unit_rms != 0;
     }
     // lane handles the 4 consecutive pair indices t0 = 4*lane + 256*i (t0 < half)
-    // and their partners t0 + half; the sources are the stored projections,
-    // or the sum of the split-K partials rounded to the model dtype
-    const long long col0 = src - row;
+    // and their partners t0 + half
     auto load4 = [&](int t, float *o) {
-      if (!a.part) {
-        if constexpr (sizeof(T) == 2) {
-          const uint2 u = *reinterpret_cast<const uint2 *>(src + t);
-          o[0] = __uint_as_float(u.x << 16);
-          o[1] = __uint_as_float(u.x & 0xffff0000u);
-          o[2] = __uint_as_float(u.y << 16);
-          o[3] = __uint_as_float(u.y & 0xffff0000u);
-        } else {
-          const float4 f = *reinterpret_cast<const float4 *>(src + t);
-          o[0] = f.x; o[1] = f.y; o[2] = f.z; o[3] = f.w;
-        }
-        return;
+      if constexpr (sizeof(T) == 2) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(src + t);
+        o[0] = __uint_as_float(u.x << 16);
+        o[1] = __uint_as_float(u.x & 0xffff0000u);
+        o[2] = __uint_as_float(u.y << 16);
+        o[3] = __uint_as_float(u.y & 0xffff0000u);
+      } else {
+        const float4 f = *reinterpret_cast<const float4 *>(src + t);
+        o[0] = f.x; o[1] = f.y; o[2] = f.z; o[3] = f.w;
       }
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int z = 0; z < a.n_part; ++z) {
-        const float4 f = *reinterpret_cast<const float4 *>(a.part + (static_cast<long long>(z) * a.n_tok + j) * a.ld +
-                                                           col0 + t);
-        acc[0] += f.x; acc[1] += f.y; acc[2] += f.z; acc[3] += f.w;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = to_f32<T>(from_f32<T>(acc[e]));
     };
     float x0[2][4], x1[2][4];
     float ss = 0.f;

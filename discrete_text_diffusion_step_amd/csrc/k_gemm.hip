@@ -858,205 +858,6 @@ hipError_t launch_f8_one(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Column-split form for short depths (the expert down projection, k = 704):
-// the four waves of a workgroup own adjacent 16*NT-column slices of the
-// tile and each walks the whole k range, so a wave has the full k loop to
-// keep loads in flight, and writes its outputs straight from its
-// accumulators (no cross-wave reduction).  Row-contiguous loads as above.
-template <int MT, int NT, int NB, int MODE, int S>
-__device__ __forceinline__ void cols_tile(const GemmArgs &a, int row_begin, int rows, const bf16_t *const *Bp,
-                                          int n0, int ncols, int kb, int ke, int split) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cr = contig_row(lane), cc = contig_chunk(lane);
-  const int l16 = lane & 15, lg = lane >> 4;
-  const int c0 = wave * NT * 16;   // this wave's first column inside the tile
-
-  uint32_t ao[MT][2];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = mt * 16 + h * 8 + cr;
-      int pr = row_begin + (r < rows ? r : 0);
-      if (a.a_rows) pr = a.a_rows[pr];
-      ao[mt][h] = (static_cast<uint32_t>(pr) * static_cast<uint32_t>(a.lda) + cc * 8) * 2u;
-    }
-  uint32_t bo[NT][2];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = c0 + nt * 16 + h * 8 + cr;
-      bo[nt][h] = (static_cast<uint32_t>(c < ncols ? c : 0) * static_cast<uint32_t>(a.ldb) + cc * 8) * 2u;
-    }
-  const char *Ab = static_cast<const char *>(a.A);
-  const char *B0 = reinterpret_cast<const char *>(Bp[0]);
-  const char *B1 = reinterpret_cast<const char *>(Bp[NB - 1]);
-
-  f32x4 acc[NB][MT][NT];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nb][mt][nt] = zero4();
-
-  const int my = (ke - kb) / 64;
-  bf16x8 xa[S][MT][2];
-  bf16x8 xb[S][NB][NT][2];
-  auto load = [&](int it, bf16x8(&ya)[MT][2], bf16x8(&yb)[NB][NT][2]) {
-    const uint32_t kbyte = static_cast<uint32_t>(kb + it * 64) * 2u;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          yb[nb][nt][h] = *reinterpret_cast<const bf16x8 *>((nb == 0 ? B0 : B1) + (bo[nt][h] + kbyte));
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) ya[mt][h] = *reinterpret_cast<const bf16x8 *>(Ab + (ao[mt][h] + kbyte));
-  };
-  auto compute = [&](const bf16x8(&ya)[MT][2], const bf16x8(&yb)[NB][NT][2]) {
-    Frag<bf16_t> fb[NB][NT][2];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) contig_to_frags(yb[nb][nt][0], yb[nb][nt][1], fb[nb][nt][0].v, fb[nb][nt][1].v);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      Frag<bf16_t> fa[2];
-      contig_to_frags(ya[mt][0], ya[mt][1], fa[0].v, fa[1].v);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) mma(acc[nb][mt][nt], fa[ks], fb[nb][nt][ks]);
-    }
-  };
-#pragma unroll
-  for (int r = 0; r < S - 1; ++r)
-    if (r < my) load(r, xa[r], xb[r]);
-  for (int i = 0; i < my; i += S) {
-#pragma unroll
-    for (int r = 0; r < S; ++r) {
-      const int it = i + r;
-      if (it < my) {
-        if (it + S - 1 < my) load(it + S - 1, xa[(r + S - 1) % S], xb[(r + S - 1) % S]);
-        compute(xa[r], xb[r]);
-      }
-    }
-  }
-
-  // lane holds rows 4*lg + i, column l16 of each 16x16 sub-tile
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int c = c0 + nt * 16 + l16;
-    if (c >= ncols) continue;
-    const int col = n0 + c;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + lg * 4 + i;
-        if (r >= rows) continue;
-        const long long row = row_begin + r;
-        const float v = acc[0][mt][nt][i];
-        if constexpr (MODE == EPI_STORE) {
-          static_cast<bf16_t *>(a.C)[row * a.ldc + col] = f32_to_bf16(v);
-        } else if constexpr (MODE == EPI_STORE_F32) {
-          static_cast<float *>(a.C)[row * a.ldc + col] = v;
-        } else if constexpr (MODE == EPI_ADD) {
-          bf16_t *cp = static_cast<bf16_t *>(a.C) + row * a.ldc + col;
-          *cp = f32_to_bf16(bf16_to_f32(*cp) + v);
-        } else if constexpr (MODE == EPI_SWIGLU) {
-          static_cast<bf16_t *>(a.C)[row * a.ldc + col] = f32_to_bf16(silu_f(v) * acc[NB - 1][mt][nt][i]);
-        } else if constexpr (MODE == EPI_ROWSCALE_F32) {
-          static_cast<float *>(a.C)[row * a.ldc + col] = v * a.rowscale[row];
-        } else if constexpr (MODE == EPI_PARTIAL_F32) {
-          static_cast<float *>(a.C)[(static_cast<long long>(split) * a.M + row) * a.ldc + col] = v;
-        }
-      }
-  }
-}
-
-template <int MT, int NT, int NB, int MODE, int S>
-__global__ __launch_bounds__(256) void gemm_cols_kernel(const GemmArgs a) {
-  constexpr int BM = MT * 16, BN = 4 * NT * 16;
-  if (a.g_off == nullptr) {
-    int L = blockIdx.x;
-    const int total = gridDim.x;
-    if ((total & 7) == 0) {
-      const int per = total >> 3;
-      L = (L & 7) * per + (L >> 3);
-    }
-    const int m_tiles = (a.M + BM - 1) / BM;
-    const int n_tiles = (a.N + BN - 1) / BN;
-    int m_tile, n_tile, split;
-    if (a.tile_order == 0) {
-      m_tile = L % m_tiles;
-      const int r = L / m_tiles;
-      n_tile = r % n_tiles;
-      split = r / n_tiles;
-    } else {
-      n_tile = L % n_tiles;
-      const int r = L / n_tiles;
-      m_tile = r % m_tiles;
-      split = r / m_tiles;
-    }
-    const int n0 = n_tile * BN;
-    int s = 0;
-    while (s + 1 < a.nseg && n0 >= a.seg_start[s + 1]) ++s;
-    const bf16_t *Bp[NB];
-    Bp[0] = static_cast<const bf16_t *>(a.seg_B0[s]) + static_cast<long long>(n0 - a.seg_start[s]) * a.ldb;
-    if (NB > 1)
-      Bp[NB - 1] = static_cast<const bf16_t *>(a.seg_B1[s]) + static_cast<long long>(n0 - a.seg_start[s]) * a.ldb;
-    const int kper = a.K / a.k_splits;
-    const int row0 = m_tile * BM;
-    cols_tile<MT, NT, NB, MODE, S>(a, row0, min(BM, a.M - row0), Bp, n0, min(BN, a.seg_start[s + 1] - n0),
-                                   split * kper, (split + 1) * kper, split);
-  } else {
-    const int g = blockIdx.y;
-    const int n0 = blockIdx.x * BN;
-    const int Ng = (g < a.n_xgroups) ? a.N_x : a.N;
-    if (n0 >= Ng) return;
-    const bf16_t *Bp[NB];
-    GemmArgs ga = a;
-    if (g < a.n_xgroups) {
-      ga.K = a.K_x;
-      ga.ldb = a.ldb_x;
-      Bp[0] = static_cast<const bf16_t *>(a.Bx0) + static_cast<long long>(n0) * a.ldb_x;
-      if (NB > 1) Bp[NB - 1] = static_cast<const bf16_t *>(a.Bx1) + static_cast<long long>(n0) * a.ldb_x;
-    } else {
-      const long long off = static_cast<long long>(g - a.n_xgroups) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
-      Bp[0] = static_cast<const bf16_t *>(a.seg_B0[0]) + off;
-      if (NB > 1) Bp[NB - 1] = static_cast<const bf16_t *>(a.seg_B1[0]) + off;
-    }
-    const int r0 = a.g_off[g], r1 = a.g_off[g + 1];
-    for (int rb = r0; rb < r1; rb += BM)
-      cols_tile<MT, NT, NB, MODE, S>(ga, rb, min(BM, r1 - rb), Bp, n0, min(BN, Ng - n0), 0, ga.K, 0);
-  }
-}
-
-template <int MT, int NT, int NB, int MODE, int S>
-hipError_t launch_cols_one(const GemmArgs &a, hipStream_t s) {
-  constexpr int BM = MT * 16, BN = 4 * NT * 16;
-  dim3 grid;
-  if (a.g_off) {
-    const int nmax = a.N > a.N_x ? a.N : a.N_x;
-    grid = dim3((nmax + BN - 1) / BN, a.n_groups);
-  } else {
-    const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
-    grid = dim3(mt * nt * a.k_splits, 1);
-  }
-  if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_cols_kernel<MT, NT, NB, MODE, S>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
 // Tile body of the streaming kernel: the row-contiguous bf16 form when every
 // k range of the launch is a whole number of 64-deep stages (CONTIG).
 template <typename T, int MT, int NT, int NB, int MODE, int S, bool CONTIG>
@@ -1465,14 +1266,6 @@ hipError_t launch_gemm_f8_grouped(const GemmArgs &a, int mode, int mt, hipStream
   DG_F8_CASE(EPI_SWIGLU, 4, DG_F8_NT_GU, 2, DG_F8_S)
   DG_F8_CASE(EPI_ROWSCALE_F32, 4, DG_F8_NT_DN, 1, DG_F8_S)
 #undef DG_F8_CASE
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_gemm_cols(const GemmArgs &a, int mode, int mt, int nt, hipStream_t s) {
-#define DG_COLS_CASE(MT_, NT_, NB_, MODE_, S_) \
-  if (mt == MT_ && nt == NT_ && mode == MODE_) return launch_cols_one<MT_, NT_, NB_, MODE_, S_>(a, s);
-  DG_COLS_CASE(DG_MOE_MT, DG_COLS_NT, 1, EPI_ROWSCALE_F32, DG_COLS_S)
-#undef DG_COLS_CASE
   return hipErrorInvalidValue;
 }
 
