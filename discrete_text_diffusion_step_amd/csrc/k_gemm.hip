@@ -567,6 +567,14 @@ __device__ __forceinline__ void stream_epilogue(const GemmArgs &a, float *red, c
   }
 }
 
+// Weight (streamed) operand loads are non-temporal: each weight byte is read
+// once per product, and marking it so keeps the L2 for the activation rows
+// that every column tile of the product re-reads (measured on the expert
+// gate/up product: HBM fetch 1.085x -> 1.026x of the algorithmic bytes).
+__device__ __forceinline__ bf16x8 ld_stream(const char *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(p));
+}
+
 // bf16 form with row-contiguous loads: 64-deep k stages (wave w takes
 // stages w, w+4, ...), each 16-row block of A and B fetched as two loads of
 // 8 whole rows and turned into the two fragments of the stage with DPP row
@@ -624,7 +632,7 @@ __device__ __forceinline__ void stream_tile_c(const GemmArgs &a, float *red, int
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          yb[nb][nt][h] = *reinterpret_cast<const bf16x8 *>((nb == 0 ? B0 : B1) + (bo[nt][h] + kbyte));
+          yb[nb][nt][h] = ld_stream((nb == 0 ? B0 : B1) + (bo[nt][h] + kbyte));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -754,7 +762,7 @@ __device__ __forceinline__ void stream_tile_f8(const GemmArgs &a, float *red, in
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          yb[nb][nt][h] = *reinterpret_cast<const bf16x8 *>((nb == 0 ? B0 : B1) + (bo[nt][h] + kb));
+          yb[nb][nt][h] = ld_stream((nb == 0 ? B0 : B1) + (bo[nt][h] + kb));
 #pragma unroll
     for (int jh = 0; jh < 2; ++jh) {
       const uint32_t ka = (static_cast<uint32_t>(st) * 128u + (half ? 0u : 64u * jh)) * 2u;
@@ -1046,7 +1054,7 @@ __device__ __forceinline__ void wide_tile(const GemmArgs &a, bf16_t *lds, bf16_t
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int j = 0; j < DB; ++j) xb[nb][j].load(reinterpret_cast<const bf16_t *>(Bb[nb] + (bo[j] + kbyte)));
+      for (int j = 0; j < DB; ++j) xb[nb][j].v = ld_stream(Bb[nb] + (bo[j] + kbyte));
   };
   auto stage_a = [&](int buf, const Frag<bf16_t>(&xa)[D]) {
 #pragma unroll
