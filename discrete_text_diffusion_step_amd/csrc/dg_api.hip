@@ -618,7 +618,13 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
       DG_HIP(launch_gemm_wide(dn, EPI_ROWSCALE_F32, WIDE_EXPERT_DN_L, s));
     else if (wide && wide_ok(dt, dn, WIDE_EXPERT_DN, moe_rows))
       DG_HIP(launch_gemm_wide(dn, EPI_ROWSCALE_F32, WIDE_EXPERT_DN, s));
-    else DG_HIP(sgemm(dt, dn, EPI_ROWSCALE_F32, mtile == DG_MOE_MT ? DG_DN_MT : mtile, DG_MOE_NT_DN, s));
+    else {
+      const int dmt = mtile == DG_MOE_MT ? DG_DN_MT : mtile;
+      hipError_t e = hipErrorNotSupported;
+      if (DG_DN_RING && dt == DG_BF16) e = launch_gemm_down_ring(dn, dmt, s);
+      if (e == hipErrorNotSupported) e = sgemm(dt, dn, EPI_ROWSCALE_F32, dmt, DG_MOE_NT_DN, s);
+      DG_HIP(e);
+    }
   }
 
   if (next.h && fused_norm_ok(D)) {

@@ -1225,6 +1225,264 @@ hipError_t launch_wide_one(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ----------------------------------------------------------------------------
+// Grouped product of short depth (the expert down projection, k = F) with
+// several work items per workgroup and each wave's load ring carried from one
+// item to the next.
+//
+// A work item is one 16*NT-column tile of one group for one block of 16*MT
+// rows.  At k = 704 a wave owns only three 64-deep stages of an item, so with
+// one item per workgroup every wave first waits a whole HBM latency for its
+// first stage and has no loads in flight while the workgroup reduces and
+// stores.  Here workgroup b walks a contiguous range of items (row blocks
+// innermost, so a group's column tile is re-read from L2 by its next row
+// block), and a wave issues the loads of the next item's stage s as soon as
+// it has consumed stage s of the current one: the next item's weights stream
+// in during the rest of the current item, its reduction and its stores.
+//
+// Wave w owns stages w, w+4, ...  Its ring holds exactly its stages of one
+// item, so ring slots are compile-time constants.  Every load is issued
+// unconditionally (after the last item they re-read one 16-byte chunk of the
+// activation rows), and the routing weights of an item are loaded before the
+// next item's stages, so the compiler's wait counts never drain the ring.
+// The cross-wave reduction alternates between two LDS buffers behind one
+// LDS-only barrier per item.
+constexpr int kDnMaxGroups = 1024;
+// LDS pitch (floats) of one accumulator element's 64 lanes in the reduction
+// buffer: 4 extra floats spread the row-major reads over the banks
+constexpr int kDnPitch = 68;
+
+struct DnItem {
+  const char *B;    // first weight row of the column tile
+  long long ldb;    // weight row stride (elements)
+  int row0, rows;   // logical rows [row0, row0 + rows)
+  int n0, ncols;    // output columns [n0, n0 + ncols)
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ DnItem dn_decode(const GemmArgs &a, const int *pre, const int *goff, int ng, int item) {
+  // group g with pre[g] <= item < pre[g + 1] (groups without items have pre[g] == pre[g + 1])
+  int lo = 0, hi = ng;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (__builtin_amdgcn_readfirstlane(pre[mid]) <= item) lo = mid;
+    else hi = mid;
+  }
+  const int g = lo;
+  const int r0 = __builtin_amdgcn_readfirstlane(goff[g]);
+  const int r1 = __builtin_amdgcn_readfirstlane(goff[g + 1]);
+  const int nrb = (r1 - r0 + BM - 1) / BM;
+  const int local = item - __builtin_amdgcn_readfirstlane(pre[g]);
+  const int ct = local / nrb, rb = local - ct * nrb;
+  DnItem it;
+  it.n0 = ct * BN;
+  it.row0 = r0 + rb * BM;
+  it.rows = min(BM, r1 - it.row0);
+  if (g < a.n_xgroups) {
+    it.ncols = min(BN, a.N_x - it.n0);
+    it.ldb = a.ldb_x;
+    it.B = static_cast<const char *>(a.Bx0) + static_cast<long long>(it.n0) * a.ldb_x * 2;
+  } else {
+    it.ncols = min(BN, a.N - it.n0);
+    it.ldb = a.ldb;
+    it.B = static_cast<const char *>(a.seg_B0[0]) +
+           (static_cast<long long>(g - a.n_xgroups) * a.b_gstride + static_cast<long long>(it.n0) * a.ldb) * 2;
+  }
+  return it;
+}
+
+template <int MT, int NT, int SW, int MODE>
+__device__ __forceinline__ void dn_walk(const GemmArgs &a, float *red, const int *pre, const int *goff, int ng,
+                                        int total) {
+  constexpr int BM = MT * 16, BN = NT * 16, EL = MT * NT * 4;
+  constexpr int NQ = EL * 16 / 256;   // epilogue quads per thread
+  static_assert(EL * 16 % 256 == 0, "epilogue quads must divide among the workgroup");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cr = contig_row(lane), cc = contig_chunk(lane);
+  const char *Ab = static_cast<const char *>(a.A);
+
+  uint32_t ao[MT][2], bo[NT][2];
+  const char *Bn;
+  auto point_at = [&](const DnItem &it) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = mt * 16 + h * 8 + cr;
+        ao[mt][h] = (static_cast<uint32_t>(it.row0 + (r < it.rows ? r : 0)) * static_cast<uint32_t>(a.lda) + cc * 8) * 2u;
+      }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = nt * 16 + h * 8 + cr;
+        bo[nt][h] = (static_cast<uint32_t>(c < it.ncols ? c : 0) * static_cast<uint32_t>(it.ldb) + cc * 8) * 2u;
+      }
+    Bn = it.B;
+  };
+  auto point_idle = [&]() {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) ao[mt][0] = ao[mt][1] = 0u;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bo[nt][0] = bo[nt][1] = 0u;
+    Bn = Ab;
+  };
+
+  bf16x8 xa[SW][MT][2];
+  bf16x8 xb[SW][NT][2];
+  auto load = [&](int st, bf16x8(&ya)[MT][2], bf16x8(&yb)[NT][2]) {
+    const uint32_t kbyte = static_cast<uint32_t>(wave + 4 * st) * 128u;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) yb[nt][h] = ld_stream(Bn + (bo[nt][h] + kbyte));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) ya[mt][h] = *reinterpret_cast<const bf16x8 *>(Ab + (ao[mt][h] + kbyte));
+  };
+  f32x4 acc[MT][NT];
+  auto compute = [&](const bf16x8(&ya)[MT][2], const bf16x8(&yb)[NT][2]) {
+    Frag<bf16_t> fb[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) contig_to_frags(yb[nt][0], yb[nt][1], fb[nt][0].v, fb[nt][1].v);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      Frag<bf16_t> fa[2];
+      contig_to_frags(ya[mt][0], ya[mt][1], fa[0].v, fa[1].v);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) mma(acc[mt][nt], fa[ks], fb[nt][ks]);
+    }
+  };
+
+  // item j of this workgroup: runs of R adjacent items, run r at (b + r G) R
+  constexpr int R = DG_DN_RING_RUN;
+  auto item_of = [&](int j) { return (static_cast<int>(blockIdx.x) + (j / R) * static_cast<int>(gridDim.x)) * R + j % R; };
+  DnItem cur = dn_decode<BM, BN>(a, pre, goff, ng, item_of(0));
+  point_at(cur);
+#pragma unroll
+  for (int st = 0; st < SW; ++st) {
+    load(st, xa[st], xb[st]);
+    __builtin_amdgcn_sched_barrier(0);   // stages in order: the loop waits on them oldest first
+  }
+
+  for (int j = 0, buf = 0; item_of(j) < total; ++j, buf ^= 1) {
+    // rows this thread stores in the epilogue, and their routing weights
+    // (loaded ahead of the next item's stages; see above)
+    float rs[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int r = (tid + 256 * j) / (BN / 4);
+      rs[j] = MODE == EPI_ROWSCALE_F32 ? a.rowscale[cur.row0 + (r < cur.rows ? r : 0)] : 1.f;
+    }
+    // keep these loads ahead of the stage loads below, and each stage's
+    // fragment moves after the wait for that stage only
+    __builtin_amdgcn_sched_barrier(0);
+    DnItem nxt = cur;
+    if (item_of(j + 1) < total) {
+      nxt = dn_decode<BM, BN>(a, pre, goff, ng, item_of(j + 1));
+      point_at(nxt);
+    } else {
+      point_idle();
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
+#pragma unroll
+    for (int st = 0; st < SW; ++st) {
+      compute(xa[st], xb[st]);
+      load(st, xa[st], xb[st]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    float *rbuf = red + buf * (4 * EL * kDnPitch);
+    {
+      float *dst = rbuf + wave * EL * kDnPitch;
+      int e = 0;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int k = 0; k < 4; ++k, ++e) dst[e * kDnPitch + lane] = acc[mt][nt][k];
+    }
+    lds_barrier();
+    // each thread adds up, over the 4 waves, 4 consecutive columns of one row
+    // (4 neighbouring lanes of one accumulator element); a wave covers whole
+    // rows of the tile, so each store instruction writes whole cache lines
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int q = tid + 256 * j, r = q / (BN / 4), c = (q % (BN / 4)) * 4;
+      const int e = ((r >> 4) * NT + (c >> 4)) * 4 + (r & 3);
+      const int l4 = ((r & 15) >> 2) * 16 + (c & 15);
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float4 t = *reinterpret_cast<const float4 *>(rbuf + (w * EL + e) * kDnPitch + l4);
+        v[0] += t.x; v[1] += t.y; v[2] += t.z; v[3] += t.w;
+      }
+      if (r < cur.rows && c < cur.ncols) {
+        const long long off = static_cast<long long>(cur.row0 + r) * a.ldc + cur.n0 + c;
+        float *cp = static_cast<float *>(a.C) + off;
+        const int nv = cur.ncols - c < 4 ? cur.ncols - c : 4;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] *= rs[j];
+        if (nv == 4 && (off & 3) == 0) {
+          // non-temporal: the rows are read once, by the combine pass
+          const f32x4 q4 = {v[0], v[1], v[2], v[3]};
+          __builtin_nontemporal_store(q4, reinterpret_cast<f32x4 *>(cp));
+        } else {
+          for (int u = 0; u < nv; ++u) cp[u] = v[u];
+        }
+      }
+    }
+    cur = nxt;
+  }
+}
+
+template <int MT, int NT, int SPW, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 3 : 2, NT <= 2 ? 3 : 2))) void gemm_down_ring_kernel(const GemmArgs a) {
+  constexpr int BM = MT * 16, BN = NT * 16, EL = MT * NT * 4;
+  __shared__ __attribute__((aligned(16))) float red[2 * 4 * EL * kDnPitch];
+  __shared__ int pre[kDnMaxGroups + 1], goff[kDnMaxGroups + 1];
+  const int ng = a.n_groups, tid = threadIdx.x;
+  for (int g = tid; g <= ng; g += 256) goff[g] = a.g_off[g];
+  __syncthreads();
+  // items per group, then their running sum (wave 0, 64 groups at a time)
+  for (int g = tid; g < ng; g += 256) {
+    const int Ng = g < a.n_xgroups ? a.N_x : a.N;
+    pre[g + 1] = ((goff[g + 1] - goff[g] + BM - 1) / BM) * ((Ng + BN - 1) / BN);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int carry = 0;
+    for (int base = 1; base <= ng; base += 64) {
+      const int idx = base + tid;
+      int v = idx <= ng ? pre[idx] : 0;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off, 64);
+        if (tid >= off) v += t;
+      }
+      if (idx <= ng) pre[idx] = v + carry;
+      carry += __shfl(v, 63, 64);
+    }
+    if (tid == 0) pre[0] = 0;
+  }
+  __syncthreads();
+  const int total = pre[ng];
+  if (static_cast<int>(blockIdx.x) * DG_DN_RING_RUN >= total) return;
+  // a wave owns (nsteps - wave + 3) / 4 stages: SPW or SPW - 1 (checked on the host)
+  const int nsteps = a.K / 64;
+  const int wave = tid >> 6;
+  if ((nsteps - wave + 3) / 4 == SPW) dn_walk<MT, NT, SPW, MODE>(a, red, pre, goff, ng, total);
+  else dn_walk<MT, NT, SPW - 1, MODE>(a, red, pre, goff, ng, total);
+}
+
 }  // namespace
 
 template <typename T>
@@ -1294,6 +1552,25 @@ hipError_t launch_gemm_wide(const GemmArgs &a, int mode, int cfg, hipStream_t s)
   DG_WIDE_CASE(WIDE_EXPERT_DN_L, 16, 1, 1, 8, 2, DG_WIDE_P, EPI_ROWSCALE_F32)
 #undef DG_WIDE_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_down_ring(const GemmArgs &a, int mt, hipStream_t s) {
+  constexpr int MT = DG_DN_MT, NT = DG_DN_RING_NT;
+  if (mt != MT || !a.g_off || a.a_rows || a.K != a.K_x || a.K % 64 || a.n_groups < 1 || a.n_groups > kDnMaxGroups ||
+      a.lda % 8 || a.ldb % 8 || a.ldb_x % 8 || a.ldc % 4 || !a.rowscale)
+    return hipErrorNotSupported;
+  // 32-bit lane offsets: every activation row and every weight tile
+  if (static_cast<long long>(a.M) * a.lda * 2 >= (1ll << 31) || 16ll * NT * (a.ldb > a.ldb_x ? a.ldb : a.ldb_x) * 2 >= (1ll << 31))
+    return hipErrorNotSupported;
+  const int nsteps = a.K / 64, spw = (nsteps + 3) / 4;
+  const dim3 grid(DG_DN_RING_WG);
+  if (spw == 3 && nsteps > 8)
+    hipLaunchKernelGGL((gemm_down_ring_kernel<MT, NT, 3, EPI_ROWSCALE_F32>), grid, dim3(256), 0, s, a);
+  else if (spw == 2 && nsteps > 4)
+    hipLaunchKernelGGL((gemm_down_ring_kernel<MT, NT, 2, EPI_ROWSCALE_F32>), grid, dim3(256), 0, s, a);
+  else
+    return hipErrorNotSupported;
+  return hipGetLastError();
 }
 
 template <typename T>

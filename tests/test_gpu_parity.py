@@ -332,6 +332,31 @@ def test_moe_bf16_ragged_groups():
     assert_delta_close(np64(xd), ref, np64(x), "bf16", "moe ragged delta")
 
 
+@pytest.mark.parametrize("D,E,k,F,n", [(2752, 16, 4, 704, 45), (320, 16, 4, 320, 45), (256, 8, 2, 512, 100)])
+def test_moe_bf16_down_ring_groups(D, E, k, F, n):
+    """Expert down product with several (expert, column tile, row block)
+    items per workgroup: skewed router logits leave experts 0-2 without rows
+    and give expert 5 most tokens (several row blocks); D = 2784 ends in a
+    half column tile; ffn 704 / 320 / 512 give waves 3 / 2 / 1 and 2 / 1
+    stages of 64 per item."""
+    cfg = synth.moe_cfg(D, E, k, F, F, dtype="bf16")
+    g = synth.generator(61)
+    w = synth.moe_weights(cfg, g)
+    x = synth.hidden_states(n, D, g, "bf16")
+    rl = synth.router_logits(n, E, g)
+    rl[:, :3] -= 20.0
+    rl[:, 5] += 4.0
+    xd = x.clone().cuda()
+    idx, _ = B.dg_moe_block(cfg, cuda(w), xd, rl.cuda(), want_topk=True)
+    sync()
+    ref, ridx, _, _ = O.moe_block_grouped(cfg, npw(w), np64(x), "bf16", router_logits=np64(rl))
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    counts = np.bincount(ridx.ravel(), minlength=E)
+    assert counts[:3].sum() == 0 and counts[5] > 32
+    assert_close(np64(xd), ref, "bf16", "moe x")
+    assert_delta_close(np64(xd), ref, np64(x), "bf16", "moe down-ring delta")
+
+
 def test_moe_bf16_prefill_rows():
     """2048 tokens: ~128 rows per expert exercises the 128-row tiles."""
     cfg = synth.moe_cfg(256, 16, 8, 128, 128, dtype="bf16")
