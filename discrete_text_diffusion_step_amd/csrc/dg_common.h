@@ -279,19 +279,13 @@ hipError_t launch_gemm_f8_grouped(const GemmArgs &a, int mode, int mt, hipStream
 // workgroup and the load ring carried across items: bf16, grouped mode,
 // mt == DG_DN_MT, K == K_x with 5..12 stages of 64.  Returns
 // hipErrorNotSupported for other shapes (the caller then uses the streaming
-// kernel).  DG_DN_RING_WG workgroups, each taking a contiguous item range.
+// kernel).  DG_DN_RING_WG resident workgroups stride through the items.
 hipError_t launch_gemm_down_ring(const GemmArgs &a, int mt, hipStream_t s);
 #ifndef DG_DN_RING
 #define DG_DN_RING 1
 #endif
 #ifndef DG_DN_RING_WG
 #define DG_DN_RING_WG 512
-#endif
-#ifndef DG_DN_RING_RUN
-#define DG_DN_RING_RUN 1
-#endif
-#ifndef DG_DN_RING_NT
-#define DG_DN_RING_NT DG_MOE_NT_DN
 #endif
 // streaming variant: tile (16*mt) x (16*nt), waves split k (K per split a multiple of 32)
 template <typename T>
