@@ -246,7 +246,7 @@ def main():
     bytes_launch = gateup_bytes(mcfg, CANVAS * NB)
     achieved = bytes_launch / (avg_ms * 1e-3) / 1e9
     kname = ("moe expert gate/up (grouped MFMA GEMM + SwiGLU, fp8 e4m3 weights widened to bf16)" if fp8 else
-             "moe expert gate/up (grouped MFMA GEMM + SwiGLU)")
+             "moe expert gate/up (grouped wide-tile MFMA GEMM + SwiGLU)")
     roof = {"kernel": kname, "bound": "hbm",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiling.read_traffic(fp8=fp8),

@@ -576,14 +576,17 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   gu.bs1 = w->s_up;
   gu.bxs0 = w->ss_gate;
   gu.bxs1 = w->ss_up;
-  // the wide-tile kernel measured slower than the streaming one on expert groups
-  const bool wide = !fp8 && DG_WIDE_EXPERTS && rows_per_expert <= 48 && wide_ok(dt, gu, WIDE_EXPERT_GU, n);
+  // gate/up of short groups: the wide-tile kernel (activation stages shared
+  // through LDS by four waves of 16 columns each); down: the carried-ring
+  // kernel below, unless the wide form is asked for
+  const bool wide_gu = !fp8 && DG_WIDE_EXPERTS_GU && rows_per_expert <= 48 && wide_ok(dt, gu, WIDE_EXPERT_GU, n);
+  const bool wide = !fp8 && DG_WIDE_EXPERTS && rows_per_expert <= 48;
   {
     TimedLaunch tl(DG_KT_MOE_GATEUP, s);
     if (fp8) DG_HIP(launch_gemm_f8_grouped(gu, EPI_SWIGLU, mtile, s));
     else if (wide_l && wide_ok(dt, gu, WIDE_EXPERT_GU_L, moe_rows))
       DG_HIP(launch_gemm_wide(gu, EPI_SWIGLU, WIDE_EXPERT_GU_L, s));
-    else if (wide) DG_HIP(launch_gemm_wide(gu, EPI_SWIGLU, WIDE_EXPERT_GU, s));
+    else if (wide_gu) DG_HIP(launch_gemm_wide(gu, EPI_SWIGLU, WIDE_EXPERT_GU, s));
     else DG_HIP(sgemm(dt, gu, EPI_SWIGLU, mtile, DG_MOE_NT_GU, s));
   }
 

@@ -327,6 +327,9 @@ enum WideCfg {
 #ifndef DG_WIDE_EXPERTS
 #define DG_WIDE_EXPERTS 0
 #endif
+#ifndef DG_WIDE_EXPERTS_GU
+#define DG_WIDE_EXPERTS_GU 1
+#endif
 #ifndef DG_WMOE_MT
 #define DG_WMOE_MT 2
 #endif

@@ -17,7 +17,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 COPY_BYTES = 1 << 30
-GATEUP_KERNEL = "gemm_stream_kernel<unsigned short, 2, 2, 2, 3, 3, true>"   # expert gate/up (SwiGLU)
+GATEUP_KERNEL = "gemm_wide_kernel<2, 1, 2, 4, 2, 3, 3>"                     # expert gate/up (SwiGLU)
 GATEUP_KERNEL_FP8 = "gemm_f8_grouped_kernel<2, 2, 2, 3, 2>"                  # the same with e4m3 weights
 COPY_KERNEL = "copyBuffer"
 GEMM_SOURCES = ("csrc/k_gemm.hip", "csrc/dg_common.h")   # the GEMM kernels and their tile settings
