@@ -34,36 +34,34 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int n, int D, float eps, f
   }
 }
 
-// Residual update fused with the next block's RMSNorm, one workgroup per
-// row (rows up to 256 * 8 * MAXC wide, held in registers between the passes).
-// The stored row is rounded to T first and the norm is taken over the
-// stored values (fp32 sum of squares, block reduction).
+// Residual update fused with the next block's RMSNorm, one workgroup of 512
+// threads per row (rows up to 512 * 8 wide): each thread owns 8 consecutive
+// elements and issues the loads of every extra row at once (up to 16 at a
+// time), so a row costs one round of memory latency instead of one per batch.
+// The stored row is rounded to T first and the norm is taken over the stored
+// values (fp32 sum of squares, block reduction).
 //   reduce_add: x <- T(x + sum_s part[s])      (split-K partials, s ascending)
 //   combine:    x <- T(ls * (x + Y[t] + sum_j Y[pair_row[t*k+j]]))
 //   then        h <- T(w * x * sqrt(D) / (||x||_2 + eps))
-template <typename T, int MAXC, bool COMBINE>
-__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const float *part, int splits, const int *pair_row,
-                                                               int k, float ls, int n, int D, T *x, const T *w,
-                                                               float eps, float sqrt_d, T *h) {
-  __shared__ float red[4];
+constexpr int kResThreads = 512;
+template <typename T, bool COMBINE>
+__global__ __launch_bounds__(kResThreads) void residual_rmsnorm_kernel(const float *part, int splits,
+                                                                       const int *pair_row, int k, float ls, int n,
+                                                                       int D, T *x, const T *w, float eps,
+                                                                       float sqrt_d, T *h) {
+  __shared__ float red[kResThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;
   T *xr = x + static_cast<long long>(row) * D;
-  float v[MAXC][8];
-  float ss = 0.f;
-  // the extra rows (routed experts, or split partials) are loaded eight at a
-  // time before they are summed, in row order
-  constexpr int KX = 8;
+  const int c = tid * 8;
+  const bool active = c < D;
+  constexpr int KX = 16;
   const int nx = COMBINE ? k : splits;
-  int src[KX];   // first batch of row indices, read once
-#pragma unroll
-  for (int j = 0; j < KX; ++j)
-    src[j] = j < nx ? (COMBINE ? pair_row[row * k + j] : j * n + row) : 0;
-#pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
-    const int c = tid * 8 + 2048 * i;
-    if (c >= D) break;
+  float v[8], g[8];
+  float ss = 0.f;
+  if (active) {
     float a[8], o[8];
+    load8(w + c, g);
     if constexpr (COMBINE) {
       // the shared expert's row is the token's own, then its k experts
       load8(part + static_cast<long long>(row) * D + c, a);
@@ -77,8 +75,7 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const float *part
 #pragma unroll
       for (int j = 0; j < KX; ++j)
         if (z0 + j < nx) {
-          const long long r = z0 == 0 ? src[j]
-                                      : (COMBINE ? pair_row[row * k + z0 + j] : static_cast<long long>(z0 + j) * n + row);
+          const long long r = COMBINE ? pair_row[row * k + z0 + j] : static_cast<long long>(z0 + j) * n + row;
           load8(part + r * D + c, t[j]);
         }
 #pragma unroll
@@ -97,26 +94,23 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const float *part
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      v[i][e] = to_f32<T>(from_f32<T>(a[e]));
-      ss += v[i][e] * v[i][e];
+      v[e] = to_f32<T>(from_f32<T>(a[e]));
+      ss += v[e] * v[e];
     }
-    store8(xr + c, v[i]);
+    store8(xr + c, v);
   }
   ss = wave_sum(ss);
   if (lane == 0) red[wave] = ss;
   __syncthreads();
-  ss = (red[0] + red[1]) + (red[2] + red[3]);
+  ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kResThreads / 64; ++i) ss += red[i];
   const float scale = sqrt_d / (sqrtf(ss) + eps);
-  T *hr = h + static_cast<long long>(row) * D;
+  if (active) {
+    float o[8];
 #pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
-    const int c = tid * 8 + 2048 * i;
-    if (c >= D) break;
-    float g[8], o[8];
-    load8(w + c, g);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = g[e] * v[i][e] * scale;
-    store8(hr + c, o);
+    for (int e = 0; e < 8; ++e) o[e] = g[e] * v[e] * scale;
+    store8(h + static_cast<long long>(row) * D + c, o);
   }
 }
 
@@ -229,7 +223,7 @@ hipError_t launch_transpose(int dtype, int rows, int cols, const void *in, void 
 }
 
 
-int residual_norm_max_width() { return 256 * 8 * 2; }
+int residual_norm_max_width() { return kResThreads * 8; }
 
 hipError_t launch_reduce_add_rmsnorm(int dtype, const float *part, int splits, int n, int D, void *x, const void *w,
                                      float eps, void *h, hipStream_t s) {
@@ -238,11 +232,11 @@ hipError_t launch_reduce_add_rmsnorm(int dtype, const float *part, int splits, i
   const float sq = static_cast<float>(__builtin_sqrt(static_cast<double>(D)));   // as launch_rmsnorm
   const dim3 grid(n);
   if (dtype == DG_BF16)
-    hipLaunchKernelGGL((residual_rmsnorm_kernel<bf16_t, 2, false>), grid, dim3(256), 0, s, part, splits, nullptr, 0,
+    hipLaunchKernelGGL((residual_rmsnorm_kernel<bf16_t, false>), grid, dim3(kResThreads), 0, s, part, splits, nullptr, 0,
                        1.0f, n, D, static_cast<bf16_t *>(x), static_cast<const bf16_t *>(w), eps, sq,
                        static_cast<bf16_t *>(h));
   else
-    hipLaunchKernelGGL((residual_rmsnorm_kernel<float, 2, false>), grid, dim3(256), 0, s, part, splits, nullptr, 0,
+    hipLaunchKernelGGL((residual_rmsnorm_kernel<float, false>), grid, dim3(kResThreads), 0, s, part, splits, nullptr, 0,
                        1.0f, n, D, static_cast<float *>(x), static_cast<const float *>(w), eps, sq,
                        static_cast<float *>(h));
   return hipGetLastError();
@@ -255,11 +249,11 @@ hipError_t launch_combine_rmsnorm(int dtype, void *x, const float *Y, const int 
   const float sq = static_cast<float>(__builtin_sqrt(static_cast<double>(D)));   // as launch_rmsnorm
   const dim3 grid(n);
   if (dtype == DG_BF16)
-    hipLaunchKernelGGL((residual_rmsnorm_kernel<bf16_t, 2, true>), grid, dim3(256), 0, s, Y, 0, pair_row, k,
+    hipLaunchKernelGGL((residual_rmsnorm_kernel<bf16_t, true>), grid, dim3(kResThreads), 0, s, Y, 0, pair_row, k,
                        layer_scalar, n, D, static_cast<bf16_t *>(x), static_cast<const bf16_t *>(w), eps, sq,
                        static_cast<bf16_t *>(h));
   else
-    hipLaunchKernelGGL((residual_rmsnorm_kernel<float, 2, true>), grid, dim3(256), 0, s, Y, 0, pair_row, k,
+    hipLaunchKernelGGL((residual_rmsnorm_kernel<float, true>), grid, dim3(kResThreads), 0, s, Y, 0, pair_row, k,
                        layer_scalar, n, D, static_cast<float *>(x), static_cast<const float *>(w), eps, sq,
                        static_cast<float *>(h));
   return hipGetLastError();
