@@ -74,27 +74,49 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
       norm = a.v_unit_rms != 0;
     }
     // lane handles the 4 consecutive pair indices t0 = 4*lane + 256*i (t0 < half)
-    // and their partners t0 + half
-    auto load4 = [&](int t, float *o) {
+    // and their partners t0 + half.  Every load is issued before any value is
+    // unpacked, so the wave waits for memory once.
+    using Raw = typename std::conditional<sizeof(T) == 2, uint2, float4>::type;
+    auto unpack = [](const Raw &r, float *o) {
       if constexpr (sizeof(T) == 2) {
-        const uint2 u = *reinterpret_cast<const uint2 *>(src + t);
-        o[0] = __uint_as_float(u.x << 16);
-        o[1] = __uint_as_float(u.x & 0xffff0000u);
-        o[2] = __uint_as_float(u.y << 16);
-        o[3] = __uint_as_float(u.y & 0xffff0000u);
+        o[0] = __uint_as_float(r.x << 16);
+        o[1] = __uint_as_float(r.x & 0xffff0000u);
+        o[2] = __uint_as_float(r.y << 16);
+        o[3] = __uint_as_float(r.y & 0xffff0000u);
       } else {
-        const float4 f = *reinterpret_cast<const float4 *>(src + t);
-        o[0] = f.x; o[1] = f.y; o[2] = f.z; o[3] = f.w;
+        o[0] = r.x; o[1] = r.y; o[2] = r.z; o[3] = r.w;
       }
     };
-    float x0[2][4], x1[2][4];
+    Raw rx0[2], rx1[2], rw0[2], rw1[2];
+    float4 rcs[2][2];   // (cos, sin) of pairs t0, t0+1 and t0+2, t0+3
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t0 = 4 * lane + 256 * i;
+      if (t0 < half) {
+        rx0[i] = *reinterpret_cast<const Raw *>(src + t0);
+        rx1[i] = *reinterpret_cast<const Raw *>(src + t0 + half);
+        if (w) {
+          rw0[i] = *reinterpret_cast<const Raw *>(w + t0);
+          rw1[i] = *reinterpret_cast<const Raw *>(w + t0 + half);
+        }
+        if (rope) {
+          rcs[i][0] = *reinterpret_cast<const float4 *>(tab + t0);
+          rcs[i][1] = *reinterpret_cast<const float4 *>(tab + t0 + 2);
+        }
+      }
+    }
+    float x0[2][4], x1[2][4], wp[2][4], wq[2][4];
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int t0 = 4 * lane + 256 * i;
       if (t0 < half) {
-        load4(t0, x0[i]);
-        load4(t0 + half, x1[i]);
+        unpack(rx0[i], x0[i]);
+        unpack(rx1[i], x1[i]);
+        if (w) {
+          unpack(rw0[i], wp[i]);
+          unpack(rw1[i], wq[i]);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) ss += x0[i][e] * x0[i][e] + x1[i][e] * x1[i][e];
       }
@@ -114,12 +136,12 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
         const int t = t0 + e;
         float p = x0[i][e] * scale, q = x1[i][e] * scale;
         if (w) {
-          p *= to_f32<T>(w[t]);
-          q *= to_f32<T>(w[t + half]);
+          p *= wp[i][e];
+          q *= wq[i][e];
         }
         if (rope) {
-          const float2 cs = tab[t];
-          const float c = cs.x, sv = cs.y;
+          const float4 cs = rcs[i][e >> 1];
+          const float c = (e & 1) ? cs.z : cs.x, sv = (e & 1) ? cs.w : cs.y;
           const float o0 = p * c - q * sv;
           const float o1 = q * c + p * sv;
           p = o0;
