@@ -62,19 +62,36 @@ __device__ __forceinline__ void wave_max64(uint32_t &hi, uint32_t &lo) {
 __global__ __launch_bounds__(256) void router_topk_kernel(const float *logits, int n_parts, int n_tok, int E,
                                                           int k, float scale, int32_t *idx_out, float *w_out) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform token: the row base lives in scalar registers, so each load
+  // needs only a per-lane offset
+  const int t = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x * 4 + (threadIdx.x >> 6)));
   if (t >= n_tok) return;
   const long long part_stride = static_cast<long long>(n_tok) * E;
   const float *r = logits + static_cast<long long>(t) * E;
+  // the logit is the sum of the split-K partials, in split order; the first
+  // kMaxParts partials of all four experts are loaded before any is added,
+  // so the wave waits for memory once
+  constexpr int kMaxParts = 8;
+  float pv[4][kMaxParts];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+#pragma unroll
+    for (int p = 0; p < kMaxParts; ++p)
+      if (e < E && p < n_parts)
+        pv[i][p] = logits[static_cast<uint32_t>(p * part_stride + static_cast<long long>(t) * E + e)];
+  }
   uint32_t kh[4], kl[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
     float v = 0.f;
     if (e < E) {
-      // the logit is the sum of the split-K partials, in split order
-      v = r[e];
-      for (int p = 1; p < n_parts; ++p) v += r[p * part_stride + e];
+      v = pv[i][0];
+#pragma unroll
+      for (int p = 1; p < kMaxParts; ++p)
+        if (p < n_parts) v += pv[i][p];
+      for (int p = kMaxParts; p < n_parts; ++p) v += r[p * part_stride + e];
     }
     kh[i] = e < E ? float_key(v) : 0u;
     kl[i] = e < E ? 0xffffffffu - static_cast<uint32_t>(e) : 0u;
