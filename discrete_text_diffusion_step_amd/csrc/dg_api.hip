@@ -616,7 +616,12 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   dn.bxs0 = w->ss_down;
   {
     TimedLaunch tl(DG_KT_MOE_DOWN, s);
-    if (fp8) DG_HIP(launch_gemm_f8_grouped(dn, EPI_ROWSCALE_F32, mtile, s));
+    if (fp8) {
+      hipError_t e = hipErrorNotSupported;
+      if (DG_DN_RING) e = launch_gemm_down_ring(dn, mtile == DG_MOE_MT ? DG_DN_MT : mtile, true, s);
+      if (e == hipErrorNotSupported) e = launch_gemm_f8_grouped(dn, EPI_ROWSCALE_F32, mtile, s);
+      DG_HIP(e);
+    }
     else if (wide_l && wide_ok(dt, dn, WIDE_EXPERT_DN_L, moe_rows))
       DG_HIP(launch_gemm_wide(dn, EPI_ROWSCALE_F32, WIDE_EXPERT_DN_L, s));
     else if (wide && wide_ok(dt, dn, WIDE_EXPERT_DN, moe_rows))
@@ -624,7 +629,7 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
     else {
       const int dmt = mtile == DG_MOE_MT ? DG_DN_MT : mtile;
       hipError_t e = hipErrorNotSupported;
-      if (DG_DN_RING && dt == DG_BF16) e = launch_gemm_down_ring(dn, dmt, s);
+      if (DG_DN_RING && dt == DG_BF16) e = launch_gemm_down_ring(dn, dmt, false, s);
       if (e == hipErrorNotSupported) e = sgemm(dt, dn, EPI_ROWSCALE_F32, dmt, DG_MOE_NT_DN, s);
       DG_HIP(e);
     }

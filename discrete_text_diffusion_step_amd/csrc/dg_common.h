@@ -276,11 +276,13 @@ hipError_t launch_gemm_f8_grouped(const GemmArgs &a, int mode, int mt, hipStream
 #endif
 
 // Expert down product with several (group, column tile, row block) items per
-// workgroup and the load ring carried across items: bf16, grouped mode,
-// mt == DG_DN_MT, K == K_x with 5..12 stages of 64.  Returns
-// hipErrorNotSupported for other shapes (the caller then uses the streaming
-// kernel).  DG_DN_RING_WG resident workgroups stride through the items.
-hipError_t launch_gemm_down_ring(const GemmArgs &a, int mt, hipStream_t s);
+// workgroup and the load ring carried across items: bf16 weights (5..12
+// stages of 64) or E4M3 weights with per-row scales (fp8: 5..8 stages of
+// 128, the last one possibly 64 deep), grouped mode, mt == DG_DN_MT,
+// K == K_x.  Returns hipErrorNotSupported for other shapes (the caller then
+// uses the streaming kernel).  DG_DN_RING_WG resident workgroups stride
+// through the items.
+hipError_t launch_gemm_down_ring(const GemmArgs &a, int mt, bool fp8, hipStream_t s);
 #ifndef DG_DN_RING
 #define DG_DN_RING 1
 #endif

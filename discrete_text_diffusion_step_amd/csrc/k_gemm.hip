@@ -1255,12 +1255,14 @@ constexpr int kDnPitch = 68;
 
 struct DnItem {
   const char *B;    // first weight row of the column tile
+  const float *S;   // its per-row weight scales (fp8 weights only)
   long long ldb;    // weight row stride (elements)
   int row0, rows;   // logical rows [row0, row0 + rows)
   int n0, ncols;    // output columns [n0, n0 + ncols)
 };
 
-template <int BM, int BN>
+// ESZ: bytes per weight element (2: bf16, 1: fp8 e4m3 with per-row scales)
+template <int BM, int BN, int ESZ>
 __device__ __forceinline__ DnItem dn_decode(const GemmArgs &a, const int *pre, const int *goff, int ng, int item) {
   // group g with pre[g] <= item < pre[g + 1] (groups without items have pre[g] == pre[g + 1])
   int lo = 0, hi = ng;
@@ -1282,25 +1284,39 @@ __device__ __forceinline__ DnItem dn_decode(const GemmArgs &a, const int *pre, c
   if (g < a.n_xgroups) {
     it.ncols = min(BN, a.N_x - it.n0);
     it.ldb = a.ldb_x;
-    it.B = static_cast<const char *>(a.Bx0) + static_cast<long long>(it.n0) * a.ldb_x * 2;
+    it.B = static_cast<const char *>(a.Bx0) + static_cast<long long>(it.n0) * a.ldb_x * ESZ;
+    it.S = ESZ == 1 ? a.bxs0 + it.n0 : nullptr;
   } else {
+    const int e = g - a.n_xgroups;
     it.ncols = min(BN, a.N - it.n0);
     it.ldb = a.ldb;
     it.B = static_cast<const char *>(a.seg_B0[0]) +
-           (static_cast<long long>(g - a.n_xgroups) * a.b_gstride + static_cast<long long>(it.n0) * a.ldb) * 2;
+           (static_cast<long long>(e) * a.b_gstride + static_cast<long long>(it.n0) * a.ldb) * ESZ;
+    it.S = ESZ == 1 ? a.bs0 + static_cast<long long>(e) * a.N + it.n0 : nullptr;
   }
   return it;
 }
 
-template <int MT, int NT, int SW, int MODE>
+// F8: OCP E4M3 weights with one fp32 scale per weight row, widened to bf16
+// in registers.  A stage is then 128 deep (128 weight bytes per row, as in
+// stream_tile_f8): its activation rows are two 64-deep halves, and with
+// k % 128 == 64 the last stage is 64 deep (its second-half weight loads
+// re-read the first half and the second-half activation fragments are
+// zeroed).  The scales are applied per column in the epilogue, before the
+// routing weight.
+template <int MT, int NT, int SW, int MODE, bool F8>
 __device__ __forceinline__ void dn_walk(const GemmArgs &a, float *red, const int *pre, const int *goff, int ng,
                                         int total) {
   constexpr int BM = MT * 16, BN = NT * 16, EL = MT * NT * 4;
+  constexpr int JH = F8 ? 2 : 1;         // activation halves per stage
+  constexpr int ESZ = F8 ? 1 : 2;        // weight bytes per element
   constexpr int NQ = EL * 16 / 256;   // epilogue quads per thread
   static_assert(EL * 16 % 256 == 0, "epilogue quads must divide among the workgroup");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cr = contig_row(lane), cc = contig_chunk(lane);
+  const int hb = (lane & 15) >> 3, lg = lane >> 4;
+  const int ca = F8 ? 2 * lg + hb : cc;   // activation chunk (8 elements) inside a 64-deep block
   const char *Ab = static_cast<const char *>(a.A);
 
   uint32_t ao[MT][2], bo[NT][2];
@@ -1311,14 +1327,15 @@ __device__ __forceinline__ void dn_walk(const GemmArgs &a, float *red, const int
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int r = mt * 16 + h * 8 + cr;
-        ao[mt][h] = (static_cast<uint32_t>(it.row0 + (r < it.rows ? r : 0)) * static_cast<uint32_t>(a.lda) + cc * 8) * 2u;
+        ao[mt][h] = (static_cast<uint32_t>(it.row0 + (r < it.rows ? r : 0)) * static_cast<uint32_t>(a.lda) + ca * 8) * 2u;
       }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int c = nt * 16 + h * 8 + cr;
-        bo[nt][h] = (static_cast<uint32_t>(c < it.ncols ? c : 0) * static_cast<uint32_t>(it.ldb) + cc * 8) * 2u;
+        bo[nt][h] = F8 ? static_cast<uint32_t>(c < it.ncols ? c : 0) * static_cast<uint32_t>(it.ldb) + cc * 16
+                       : (static_cast<uint32_t>(c < it.ncols ? c : 0) * static_cast<uint32_t>(it.ldb) + cc * 8) * 2u;
       }
     Bn = it.B;
   };
@@ -1330,39 +1347,84 @@ __device__ __forceinline__ void dn_walk(const GemmArgs &a, float *red, const int
     Bn = Ab;
   };
 
-  bf16x8 xa[SW][MT][2];
+  bf16x8 xa[SW][MT][JH][2];
   bf16x8 xb[SW][NT][2];
-  auto load = [&](int st, bf16x8(&ya)[MT][2], bf16x8(&yb)[NT][2]) {
-    const uint32_t kbyte = static_cast<uint32_t>(wave + 4 * st) * 128u;
+  auto load = [&](int st, bf16x8(&ya)[MT][JH][2], bf16x8(&yb)[NT][2]) {
+    const int sg = wave + 4 * st;   // stage of the item
+    if constexpr (F8) {
+      const bool half = (sg + 1) * 128 > a.K;
+      const uint32_t kb = static_cast<uint32_t>(sg) * 128u - ((half && hb) ? 64u : 0u);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) yb[nt][h] = ld_stream(Bn + (bo[nt][h] + kbyte));
+        for (int h = 0; h < 2; ++h) yb[nt][h] = ld_stream(Bn + (bo[nt][h] + kb));
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int jh = 0; jh < 2; ++jh) {
+        const uint32_t ka = (static_cast<uint32_t>(sg) * 128u + (half ? 0u : 64u * jh)) * 2u;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) ya[mt][h] = *reinterpret_cast<const bf16x8 *>(Ab + (ao[mt][h] + kbyte));
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) ya[mt][jh][h] = *reinterpret_cast<const bf16x8 *>(Ab + (ao[mt][h] + ka));
+      }
+    } else {
+      const uint32_t kbyte = static_cast<uint32_t>(sg) * 128u;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) yb[nt][h] = ld_stream(Bn + (bo[nt][h] + kbyte));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) ya[mt][0][h] = *reinterpret_cast<const bf16x8 *>(Ab + (ao[mt][h] + kbyte));
+    }
   };
   f32x4 acc[MT][NT];
-  auto compute = [&](const bf16x8(&ya)[MT][2], const bf16x8(&yb)[NT][2]) {
-    Frag<bf16_t> fb[NT][2];
+  auto compute = [&](int st, const bf16x8(&ya)[MT][JH][2], const bf16x8(&yb)[NT][2]) {
+    if constexpr (F8) {
+      const bool half = (wave + 4 * st + 1) * 128 > a.K;
+      Frag<bf16_t> fa[MT][4];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) contig_to_frags(yb[nt][0], yb[nt][1], fb[nt][0].v, fb[nt][1].v);
+      for (int mt = 0; mt < MT; ++mt) {
+        contig_to_frags(ya[mt][0][0], ya[mt][0][1], fa[mt][0].v, fa[mt][1].v);
+        contig_to_frags(ya[mt][1][0], ya[mt][1][1], fa[mt][2].v, fa[mt][3].v);
+        if (half) {
+          fa[mt][2].v = bf16x8{};
+          fa[mt][3].v = bf16x8{};
+        }
+      }
+      // weight fragments are widened one 16-column block at a time
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      Frag<bf16_t> fa[2];
-      contig_to_frags(ya[mt][0], ya[mt][1], fa[0].v, fa[1].v);
+      for (int nt = 0; nt < NT; ++nt) {
+        bf16x8 f0, f1;
+        contig_to_frags(yb[nt][0], yb[nt][1], f0, f1);
+        Frag<bf16_t> fb[4];
+        e4m3x16_to_bf16(f0, fb[0].v, fb[1].v);
+        e4m3x16_to_bf16(f1, fb[2].v, fb[3].v);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) mma(acc[mt][nt], fa[ks], fb[nt][ks]);
+          for (int mt = 0; mt < MT; ++mt) mma(acc[mt][nt], fa[mt][ks], fb[ks]);
+      }
+    } else {
+      Frag<bf16_t> fb[NT][2];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) contig_to_frags(yb[nt][0], yb[nt][1], fb[nt][0].v, fb[nt][1].v);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        Frag<bf16_t> fa[2];
+        contig_to_frags(ya[mt][0][0], ya[mt][0][1], fa[0].v, fa[1].v);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) mma(acc[mt][nt], fa[ks], fb[nt][ks]);
+      }
     }
   };
 
   // item j of this workgroup: b + j G (the live workgroups sweep the weights
   // together; contiguous item ranges per workgroup measured 13% slower)
   auto item_of = [&](int j) { return static_cast<int>(blockIdx.x) + j * static_cast<int>(gridDim.x); };
-  DnItem cur = dn_decode<BM, BN>(a, pre, goff, ng, item_of(0));
+  DnItem cur = dn_decode<BM, BN, ESZ>(a, pre, goff, ng, item_of(0));
   point_at(cur);
 #pragma unroll
   for (int st = 0; st < SW; ++st) {
@@ -1374,9 +1436,14 @@ __device__ __forceinline__ void dn_walk(const GemmArgs &a, float *red, const int
     // rows this thread stores in the epilogue, and their routing weights
     // (loaded ahead of the next item's stages; see above)
     float rs[NQ];
+    float4 sc[NQ];   // weight scales of the 4 columns (fp8)
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const int r = (tid + 256 * j) / (BN / 4);
+      if constexpr (F8) {
+        const int c = ((tid + 256 * j) % (BN / 4)) * 4;
+        sc[j] = *reinterpret_cast<const float4 *>(cur.S + (c + 4 <= cur.ncols ? c : 0));
+      }
       rs[j] = MODE == EPI_ROWSCALE_F32 ? a.rowscale[cur.row0 + (r < cur.rows ? r : 0)] : 1.f;
     }
     // keep these loads ahead of the stage loads below, and each stage's
@@ -1384,7 +1451,7 @@ __device__ __forceinline__ void dn_walk(const GemmArgs &a, float *red, const int
     __builtin_amdgcn_sched_barrier(0);
     DnItem nxt = cur;
     if (item_of(j + 1) < total) {
-      nxt = dn_decode<BM, BN>(a, pre, goff, ng, item_of(j + 1));
+      nxt = dn_decode<BM, BN, ESZ>(a, pre, goff, ng, item_of(j + 1));
       point_at(nxt);
     } else {
       point_idle();
@@ -1395,7 +1462,7 @@ __device__ __forceinline__ void dn_walk(const GemmArgs &a, float *red, const int
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
 #pragma unroll
     for (int st = 0; st < SW; ++st) {
-      compute(xa[st], xb[st]);
+      compute(st, xa[st], xb[st]);
       load(st, xa[st], xb[st]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1430,6 +1497,12 @@ __device__ __forceinline__ void dn_walk(const GemmArgs &a, float *red, const int
         const long long off = static_cast<long long>(cur.row0 + r) * a.ldc + cur.n0 + c;
         float *cp = static_cast<float *>(a.C) + off;
         const int nv = cur.ncols - c < 4 ? cur.ncols - c : 4;
+        if constexpr (F8) {
+          v[0] *= sc[j].x;
+          v[1] *= sc[j].y;
+          v[2] *= sc[j].z;
+          v[3] *= sc[j].w;
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) v[u] *= rs[j];
         if (nv == 4 && (off & 3) == 0) {
@@ -1445,7 +1518,7 @@ __device__ __forceinline__ void dn_walk(const GemmArgs &a, float *red, const int
   }
 }
 
-template <int MT, int NT, int SPW, int MODE>
+template <int MT, int NT, int SPW, int MODE, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_down_ring_kernel(const GemmArgs a) {
   constexpr int BM = MT * 16, BN = NT * 16, EL = MT * NT * 4;
   __shared__ __attribute__((aligned(16))) float red[2 * 4 * EL * kDnPitch];
@@ -1478,10 +1551,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int total = pre[ng];
   if (static_cast<int>(blockIdx.x) >= total) return;
   // a wave owns (nsteps - wave + 3) / 4 stages: SPW or SPW - 1 (checked on the host)
-  const int nsteps = a.K / 64;
+  const int nsteps = F8 ? (a.K + 127) / 128 : a.K / 64;
   const int wave = tid >> 6;
-  if ((nsteps - wave + 3) / 4 == SPW) dn_walk<MT, NT, SPW, MODE>(a, red, pre, goff, ng, total);
-  else dn_walk<MT, NT, SPW - 1, MODE>(a, red, pre, goff, ng, total);
+  if ((nsteps - wave + 3) / 4 == SPW) dn_walk<MT, NT, SPW, MODE, F8>(a, red, pre, goff, ng, total);
+  else dn_walk<MT, NT, SPW - 1, MODE, F8>(a, red, pre, goff, ng, total);
 }
 
 }  // namespace
@@ -1555,22 +1628,27 @@ hipError_t launch_gemm_wide(const GemmArgs &a, int mode, int cfg, hipStream_t s)
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_down_ring(const GemmArgs &a, int mt, hipStream_t s) {
+hipError_t launch_gemm_down_ring(const GemmArgs &a, int mt, bool fp8, hipStream_t s) {
   constexpr int MT = DG_DN_MT, NT = DG_MOE_NT_DN;
   if (mt != MT || !a.g_off || a.a_rows || a.K != a.K_x || a.K % 64 || a.n_groups < 1 || a.n_groups > kDnMaxGroups ||
       a.lda % 8 || a.ldb % 8 || a.ldb_x % 8 || a.ldc % 4 || !a.rowscale)
     return hipErrorNotSupported;
+  // fp8 rows are read 16 bytes at a time and scaled per row
+  if (fp8 && (a.ldb % 16 || a.ldb_x % 16 || !a.bs0 || !a.bxs0)) return hipErrorNotSupported;
   // 32-bit lane offsets: every activation row and every weight tile
   if (static_cast<long long>(a.M) * a.lda * 2 >= (1ll << 31) || 16ll * NT * (a.ldb > a.ldb_x ? a.ldb : a.ldb_x) * 2 >= (1ll << 31))
     return hipErrorNotSupported;
-  const int nsteps = a.K / 64, spw = (nsteps + 3) / 4;
+  const int nsteps = fp8 ? (a.K + 127) / 128 : a.K / 64, spw = (nsteps + 3) / 4;
   const dim3 grid(DG_DN_RING_WG);
-  if (spw == 3 && nsteps > 8)
-    hipLaunchKernelGGL((gemm_down_ring_kernel<MT, NT, 3, EPI_ROWSCALE_F32>), grid, dim3(256), 0, s, a);
-  else if (spw == 2 && nsteps > 4)
-    hipLaunchKernelGGL((gemm_down_ring_kernel<MT, NT, 2, EPI_ROWSCALE_F32>), grid, dim3(256), 0, s, a);
-  else
+  // (the fp8 form with three stages per wave does not fit the registers)
+  if (spw == 3 && nsteps > 8 && !fp8) {
+    hipLaunchKernelGGL((gemm_down_ring_kernel<MT, NT, 3, EPI_ROWSCALE_F32, false>), grid, dim3(256), 0, s, a);
+  } else if (spw == 2 && nsteps > 4) {
+    if (fp8) hipLaunchKernelGGL((gemm_down_ring_kernel<MT, NT, 2, EPI_ROWSCALE_F32, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_down_ring_kernel<MT, NT, 2, EPI_ROWSCALE_F32, false>), grid, dim3(256), 0, s, a);
+  } else {
     return hipErrorNotSupported;
+  }
   return hipGetLastError();
 }
 

@@ -92,6 +92,32 @@ def test_moe_fp8_small(D, E, k, F, Fs, n, seed):
     assert_delta_close(np64(xd), ref, np64(x), "bf16", "fp8 moe delta")
 
 
+@pytest.mark.parametrize("D,E,k,F,n", [(2752, 16, 4, 704, 45), (320, 16, 4, 576, 45), (256, 8, 2, 640, 100)])
+def test_moe_fp8_down_ring_groups(D, E, k, F, n):
+    """fp8 down product with several (expert, column tile, row block) items per
+    workgroup: skewed router logits leave experts 0-2 without rows and give
+    expert 5 most tokens (several row blocks); ffn 704 and 576 end on a
+    64-deep half stage (held by wave 1 and by wave 0), 640 on whole stages;
+    the waves own 2/2/1/1, 2/1/1/1 and 2/1/1/1 stages of 128 per item."""
+    cfg = synth.moe_cfg(D, E, k, F, F, dtype="bf16")
+    g = synth.generator(63)
+    w = synth.moe_weights(cfg, g, with_router=False)
+    x = synth.hidden_states(n, D, g, "bf16")
+    rl = synth.router_logits(n, E, g)
+    rl[:, :3] -= 20.0
+    rl[:, 5] += 4.0
+    wq, xd, idx = _run_gpu(cfg, w, x, rl)
+    codes, scales, deq = F8.quantize_experts(npw(w))
+    wn = npw(w)
+    wn.update(deq)
+    ref, ridx, _, _ = O.moe_block_grouped(cfg, wn, np64(x), "bf16", router_logits=np64(rl))
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    counts = np.bincount(ridx.ravel(), minlength=E)
+    assert counts[:3].sum() == 0 and counts[5] > 32
+    assert_close(np64(xd), ref, "bf16", "fp8 moe x")
+    assert_delta_close(np64(xd), ref, np64(x), "bf16", "fp8 moe down-ring delta")
+
+
 class _LazyDeq:
     """Expert e of a stacked matrix, quantised and dequantised by the oracle
     on first use (so a token sample touches only its own experts)."""
