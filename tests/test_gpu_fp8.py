@@ -118,6 +118,23 @@ def test_moe_fp8_down_ring_groups(D, E, k, F, n):
     assert_delta_close(np64(xd), ref, np64(x), "bf16", "fp8 moe down-ring delta")
 
 
+def test_moe_fp8_single_token():
+    """One token: fewer down-product items than resident workgroups."""
+    cfg = synth.moe_cfg(2816, 16, 4, 704, 704, dtype="bf16")
+    g = synth.generator(69)
+    w = synth.moe_weights(cfg, g, with_router=False)
+    x = synth.hidden_states(1, 2816, g, "bf16")
+    rl = synth.router_logits(1, 16, g)
+    wq, xd, idx = _run_gpu(cfg, w, x, rl)
+    codes, scales, deq = F8.quantize_experts(npw(w))
+    wn = npw(w)
+    wn.update(deq)
+    ref, ridx, _, _ = O.moe_block_grouped(cfg, wn, np64(x), "bf16", router_logits=np64(rl))
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    assert_close(np64(xd), ref, "bf16", "fp8 moe x")
+    assert_delta_close(np64(xd), ref, np64(x), "bf16", "fp8 moe single-token delta")
+
+
 class _LazyDeq:
     """Expert e of a stacked matrix, quantised and dequantised by the oracle
     on first use (so a token sample touches only its own experts)."""

@@ -357,6 +357,24 @@ def test_moe_bf16_down_ring_groups(D, E, k, F, n):
     assert_delta_close(np64(xd), ref, np64(x), "bf16", "moe down-ring delta")
 
 
+@pytest.mark.parametrize("n", [1, 3])
+def test_moe_bf16_few_tokens(n):
+    """A handful of tokens: fewer (expert, column tile, row block) items than
+    resident workgroups in the down product, so most workgroups have none."""
+    cfg = synth.moe_cfg(2816, 16, 4, 704, 704, dtype="bf16")
+    g = synth.generator(67 + n)
+    w = synth.moe_weights(cfg, g)
+    x = synth.hidden_states(n, 2816, g, "bf16")
+    rl = synth.router_logits(n, 16, g)
+    xd = x.clone().cuda()
+    idx, _ = B.dg_moe_block(cfg, cuda(w), xd, rl.cuda(), want_topk=True)
+    sync()
+    ref, ridx, _, _ = O.moe_block_grouped(cfg, npw(w), np64(x), "bf16", router_logits=np64(rl))
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    assert_close(np64(xd), ref, "bf16", "moe x")
+    assert_delta_close(np64(xd), ref, np64(x), "bf16", "moe few-token delta")
+
+
 def test_moe_bf16_prefill_rows():
     """2048 tokens: ~128 rows per expert exercises the 128-row tiles."""
     cfg = synth.moe_cfg(256, 16, 8, 128, 128, dtype="bf16")
