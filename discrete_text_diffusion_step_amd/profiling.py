@@ -19,6 +19,8 @@ ROOT = os.path.dirname(HERE)
 COPY_BYTES = 1 << 30
 GATEUP_KERNEL = "gemm_wide_kernel<2, 1, 2, 4, 2, 3, 3>"                     # expert gate/up (SwiGLU)
 GATEUP_KERNEL_FP8 = "gemm_f8_grouped_kernel<2, 2, 2, 3, 2>"                  # the same with e4m3 weights
+DOWN_KERNEL = "gemm_down_ring_kernel<2, 4, 3, 4, false>"                    # expert down (routing-weight row scale)
+DOWN_KERNEL_FP8 = "gemm_down_ring_kernel<2, 4, 2, 4, true>"                 # the same with e4m3 weights
 COPY_KERNEL = "copyBuffer"
 GEMM_SOURCES = ("csrc/k_gemm.hip", "csrc/dg_common.h")   # the GEMM kernels and their tile settings
 
@@ -76,8 +78,11 @@ def _per_dispatch(rows, name_part, counter):
     return sum(v) / len(v), len(v)
 
 
-def summarize_traffic(fetch_csv, write_csv, command, algorithmic_bytes, fp8=False):
-    kern = GATEUP_KERNEL_FP8 if fp8 else GATEUP_KERNEL
+def summarize_traffic(fetch_csv, write_csv, command, algorithmic_bytes, fp8=False, product="gate/up"):
+    if product == "down":
+        kern = DOWN_KERNEL_FP8 if fp8 else DOWN_KERNEL
+    else:
+        kern = GATEUP_KERNEL_FP8 if fp8 else GATEUP_KERNEL
     fr, wr = _rows(fetch_csv), _rows(write_csv)
     cf, ncf = _per_dispatch(fr, COPY_KERNEL, "FETCH_SIZE")
     cw, ncw = _per_dispatch(wr, COPY_KERNEL, "WRITE_SIZE")
@@ -88,15 +93,15 @@ def summarize_traffic(fetch_csv, write_csv, command, algorithmic_bytes, fp8=Fals
     fetch_b = gf * ff * 1024.0
     write_b = gw * fw * 1024.0
     lines = [
-        "# HBM traffic of the expert gate/up launch (MoE layer, 256-token canvas, 128 experts top-8 + shared"
+        f"# HBM traffic of the expert {product} launch (MoE layer, 256-token canvas, 128 experts top-8 + shared"
         + (", fp8 e4m3 weights)" if fp8 else ")"),
         f"kernel: {kern}",
         f"command: {command}",
         f"gemm_source_hash: {gemm_source_hash()}",
         f"copy calibration: {COPY_BYTES} B device copy; FETCH_SIZE {cf:.0f} KiB ({ncf} dispatches), "
         f"WRITE_SIZE {cw:.0f} KiB ({ncw}); factors fetch {ff:.4f}, write {fw:.4f}",
-        f"gate/up raw: FETCH_SIZE {gf:.0f} KiB ({ngf} dispatches), WRITE_SIZE {gw:.0f} KiB ({ngw})",
-        f"gate/up scaled: fetch_bytes {fetch_b:.0f}, write_bytes {write_b:.0f}",
+        f"{product} raw: FETCH_SIZE {gf:.0f} KiB ({ngf} dispatches), WRITE_SIZE {gw:.0f} KiB ({ngw})",
+        f"{product} scaled: fetch_bytes {fetch_b:.0f}, write_bytes {write_b:.0f}",
         f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
         f"algorithmic_bytes_per_launch: {algorithmic_bytes}",
         f"traffic / algorithmic: {(fetch_b + write_b) / algorithmic_bytes:.3f}",
@@ -171,7 +176,8 @@ if __name__ == "__main__":
     if what == "traffic":
         fetch_csv, write_csv, command, alg = sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5])
         fp8 = len(sys.argv) > 6 and sys.argv[6] == "fp8"
-        sys.stdout.write(summarize_traffic(fetch_csv, write_csv, command, alg, fp8=fp8))
+        product = sys.argv[7] if len(sys.argv) > 7 else "gate/up"
+        sys.stdout.write(summarize_traffic(fetch_csv, write_csv, command, alg, fp8=fp8, product=product))
     elif what == "stats":
         sys.stdout.write(summarize_stats(sys.argv[2], sys.argv[3]))
         if len(sys.argv) > 4:
