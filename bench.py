@@ -203,9 +203,10 @@ def main():
     log(f"warmup {args.warmup} steps done")
 
     K = args.steps
-    # every 7th gate/up launch (30 layers a step: the sample rotates through
-    # them); timing all of them would add a few microseconds per event
-    timer = B.kernel_timer("moe_gateup", capacity=K * mcfg["n_layers"] // 7 + 8, every=7)
+    # every 31st gate/up launch (30 layers a step: 31 is prime to 30, so the
+    # sample rotates through the layers; each event costs a few us between
+    # two kernels, so fewer of them disturb the timed step less)
+    timer = B.kernel_timer("moe_gateup", capacity=K * mcfg["n_layers"] // 31 + 8, every=31)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with timer:
