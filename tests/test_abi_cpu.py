@@ -3,6 +3,8 @@ entry point, and rejects bad arguments on the host before any HIP call."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -27,6 +29,38 @@ def test_library_exports_every_declared_entry_point():
         assert n in names
     for n in names:
         assert hasattr(L, n), n
+
+
+STRUCTS = {
+    "dg_attn_cfg": B.AttnCfg, "dg_attn_w": B.AttnW, "dg_kv_layer": B.KVLayer, "dg_moe_cfg": B.MoeCfg,
+    "dg_moe_w": B.MoeW, "dg_sampler_cfg": B.SamplerCfg, "dg_model_cfg": B.ModelCfg, "dg_model_w": B.ModelW,
+    "dg_kv_cache": B.KVCache, "dg_canvas_state": B.CanvasState, "dg_kernel_timer": B.KernelTimer,
+}
+C_NAME = {"global_": "global"}   # binding field names that differ from the header's
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """Every ctypes mirror of a header struct has the header's size and field
+    offsets, as a C compiler lays them out (the header is compiled as C)."""
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "dgstep.h"', "int main(void) {"]
+    for cname, py in STRUCTS.items():
+        lines.append(f'  printf("{cname} . %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {C_NAME.get(f, f)}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {(a, b): int(c) for a, b, c in (ln.split() for ln in out if ln)}
+    for cname, py in STRUCTS.items():
+        assert got[(cname, ".")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
 
 
 def test_status_strings():
