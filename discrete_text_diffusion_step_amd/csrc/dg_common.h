@@ -346,6 +346,10 @@ enum WideCfg {
 #ifndef DG_WMOE_P
 #define DG_WMOE_P 3
 #endif
+// activation prefetch depth (stages) of the expert gate/up configuration
+#ifndef DG_WMOE_PA
+#define DG_WMOE_PA 2
+#endif
 // column tile width and k-stage depth of each wide configuration
 inline int wide_bn(int cfg) { return cfg == WIDE_ROWS256_N256 ? 256 : (cfg == WIDE_EXPERT_GU ? 64 : 128); }
 inline int wide_bm(int cfg) {

@@ -987,8 +987,12 @@ __device__ __forceinline__ void wide_tile(const GemmArgs &a, bf16_t *lds, bf16_t
                                           int split) {
   static_assert(KSUB == 2, "stages are 64 deep (128 bytes per A row)");
   // A is fetched PA stages ahead (ring of PA register slots); PA = 2 needs
-  // an even ring length R so slot parity is fixed inside the unrolled body
-  constexpr int PA = ((P + 1) % 2 == 0) ? DG_WIDE_PA : 1;
+  // an even ring length R so slot parity is fixed inside the unrolled body.
+  // The expert gate/up configuration (two products, short row tiles) takes
+  // its own depth: two stages measured faster there, slower for the
+  // 256-row projections.
+  constexpr int PA_WANT = (NB == 2 && MT <= 4) ? DG_WMOE_PA : DG_WIDE_PA;
+  constexpr int PA = ((P + 1) % 2 == 0) ? PA_WANT : 1;
   constexpr int BM = MT * 16;
   constexpr int D = BM / 8 / NW;         // A load instructions per wave per stage
   static_assert(D * 8 * NW == BM, "A rows must split evenly over the waves");
