@@ -188,8 +188,8 @@ AttnPlan attn_plan(const dg_attn_cfg *c, int n) {
   p.qkv_wide = DG_PROJ_WIDE && wide_ok(c->dtype, gq, DG_PROJ_CFG, n);
   p.qkv_ks = p.qkv_wide ? wide_ksplit(gq, DG_PROJ_CFG, DG_PROJ_TARGET) : 1;
   const GemmArgs go = dense_args(nullptr, p.Nq, n, c->hidden, p.Nq, nullptr, c->hidden);
-  p.oproj_wide = DG_PROJ_WIDE && wide_ok(c->dtype, go, DG_PROJ_CFG, n);
-  p.oproj_ks = p.oproj_wide ? wide_ksplit(go, DG_PROJ_CFG, DG_PROJ_TARGET)
+  p.oproj_wide = DG_PROJ_WIDE && wide_ok(c->dtype, go, WIDE_ROWS256_N128_OP, n);
+  p.oproj_ks = p.oproj_wide ? wide_ksplit(go, WIDE_ROWS256_N128_OP, DG_PROJ_TARGET)
                             : choose_ksplit(n, c->hidden, p.Nq, 16 * DG_DENSE_MT, 16 * DG_DENSE_NT, 512, 8);
   return p;
 }
@@ -388,11 +388,11 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *const *kvs,
       o.C = ws.oproj_part;
       o.ldc = D;
       o.k_splits = p.oproj_ks;
-      DG_HIP(launch_gemm_wide(o, EPI_PARTIAL_F32, DG_PROJ_CFG, s));
+      DG_HIP(launch_gemm_wide(o, EPI_PARTIAL_F32, WIDE_ROWS256_N128_OP, s));
       DG_HIP(launch_reduce_add_rmsnorm(dt, ws.oproj_part, p.oproj_ks, n, D, x, next.w, next.eps, next.h, s));
       next.h = nullptr;
     } else if (p.oproj_wide) {
-      DG_HIP(wide_product(o, EPI_ADD, DG_PROJ_CFG, ws.oproj_part, p.oproj_ks, s));
+      DG_HIP(wide_product(o, EPI_ADD, WIDE_ROWS256_N128_OP, ws.oproj_part, p.oproj_ks, s));
     } else {
       DG_HIP(dense_product(dt, o, EPI_ADD, ws.oproj_part, p.oproj_ks, s));
     }

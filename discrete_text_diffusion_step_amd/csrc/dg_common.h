@@ -300,6 +300,7 @@ enum WideCfg {
   WIDE_EXPERT_DN = 3,     // expert down: 16*DG_WMOE_MT rows x 128 columns, 4 waves
   WIDE_EXPERT_GU_L = 4,   // expert gate/up, long groups: 256 rows x 128 columns (x2 matrices), 8 waves
   WIDE_EXPERT_DN_L = 5,   // expert down, long groups: 256 rows x 128 columns, 8 waves
+  WIDE_ROWS256_N128_OP = 6,  // the 256 x 128 form with DG_OPROJ_P weight stages ahead (output projection)
   // every configuration walks k in stages of 64
 };
 #ifndef DG_WIDE_P
@@ -307,6 +308,11 @@ enum WideCfg {
 #endif
 #ifndef DG_WIDE_PA
 #define DG_WIDE_PA 1
+#endif
+// weight stages in flight for the output projection (deeper rings measured
+// faster for Q|K|V, slower for O-proj)
+#ifndef DG_OPROJ_P
+#define DG_OPROJ_P 2
 #endif
 #ifndef DG_WIDE256_P
 #define DG_WIDE256_P 2
@@ -353,7 +359,7 @@ enum WideCfg {
 // column tile width and k-stage depth of each wide configuration
 inline int wide_bn(int cfg) { return cfg == WIDE_ROWS256_N256 ? 256 : (cfg == WIDE_EXPERT_GU ? 64 : 128); }
 inline int wide_bm(int cfg) {
-  return (cfg <= WIDE_ROWS256_N128 || cfg >= WIDE_EXPERT_GU_L) ? 256 : 16 * DG_WMOE_MT;
+  return (cfg <= WIDE_ROWS256_N128 || cfg >= WIDE_EXPERT_GU_L) ? 256 : 16 * DG_WMOE_MT;   // _N128_OP too
 }
 inline int wide_kstage(int) { return 64; }
 hipError_t launch_gemm_wide(const GemmArgs &a, int mode, int cfg, hipStream_t s);

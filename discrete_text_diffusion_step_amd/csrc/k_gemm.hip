@@ -1624,6 +1624,8 @@ hipError_t launch_gemm_wide(const GemmArgs &a, int mode, int cfg, hipStream_t s)
   DG_WIDE_CASE(WIDE_ROWS256_N128, 16, 1, 1, 8, 2, DG_WIDE_P, EPI_PARTIAL_F32)
   DG_WIDE_CASE(WIDE_ROWS256_N128, 16, 1, 1, 8, 2, DG_WIDE_P, EPI_STORE_F32)
   DG_WIDE_CASE(WIDE_ROWS256_N128, 16, 1, 1, 8, 2, DG_WIDE_P, EPI_ADD)
+  DG_WIDE_CASE(WIDE_ROWS256_N128_OP, 16, 1, 1, 8, 2, DG_OPROJ_P, EPI_PARTIAL_F32)
+  DG_WIDE_CASE(WIDE_ROWS256_N128_OP, 16, 1, 1, 8, 2, DG_OPROJ_P, EPI_ADD)
   DG_WIDE_CASE(WIDE_EXPERT_GU, DG_WMOE_MT, 1, 2, 4, 2, DG_WMOE_P, EPI_SWIGLU)
   DG_WIDE_CASE(WIDE_EXPERT_DN, DG_WMOE_MT, 2, 1, 4, 2, DG_WMOE_P, EPI_ROWSCALE_F32)
   DG_WIDE_CASE(WIDE_EXPERT_GU_L, 16, 1, 2, 8, 2, DG_WIDE_P, EPI_SWIGLU)
