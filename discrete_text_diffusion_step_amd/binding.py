@@ -86,7 +86,7 @@ class KVCache(ctypes.Structure):
 class CanvasState(ctypes.Structure):
     _fields_ = [("tokens", c_void), ("u", c_void), ("use_u", c_int), ("commit", c_void),
                 ("entropy", c_void), ("n_renoised", c_void), ("logits", c_void), ("canvas_len", c_int),
-                ("pred", c_void), ("n_changed", c_void)]
+                ("pred", c_void), ("n_changed", c_void), ("n_nonfinite", c_void)]
 
 
 class KernelTimer(ctypes.Structure):
@@ -121,7 +121,7 @@ def lib(path=None):
             "dg_quantize_fp8": (c_int, [c_int, c_void, ctypes.c_longlong, c_int, c_void, c_void, c_void]),
             "dg_sample_workspace_bytes": (c_size, [c_int, c_int]),
             "dg_sample_renoise": (c_int, [P(SamplerCfg), c_int, c_void, c_int, c_void, c_void, c_void, c_void,
-                                          c_void, c_void, c_void, c_void, c_size, c_void]),
+                                          c_void, c_void, c_void, c_void, c_void, c_size, c_void]),
             "dg_canvas_noise": (c_int, [c_int, c_int, ctypes.c_uint64, ctypes.c_uint32, c_void, c_void]),
             "dg_lm_head_workspace_bytes": (c_size, [c_int, c_int, c_int]),
             "dg_lm_head": (c_int, [c_int, c_int, c_int, c_float, c_int, c_void, c_void, c_void, c_void, c_void,
@@ -284,7 +284,7 @@ def quantize_moe_weights(w, stream=None):
 def dg_sample_renoise(scfg, logits, want_rowstats=True, pred=None, stream=None):
     """Sampler outputs; pred (optional int32 [n], -1 before the first step)
     holds the previous proposals and receives this step's, and the result
-    then carries n_changed."""
+    then carries n_changed.  n_nonfinite counts rows holding a NaN or +-inf."""
     L = lib()
     n, V = logits.shape
     dev = logits.device
@@ -293,13 +293,15 @@ def dg_sample_renoise(scfg, logits, want_rowstats=True, pred=None, stream=None):
                entropy=torch.empty(n, dtype=torch.float32, device=dev),
                n_renoised=torch.empty(1, dtype=torch.int32, device=dev),
                rowstats=torch.empty(n, 2, dtype=torch.float32, device=dev) if want_rowstats else None,
-               n_changed=torch.empty(1, dtype=torch.int32, device=dev) if pred is not None else None)
+               n_changed=torch.empty(1, dtype=torch.int32, device=dev) if pred is not None else None,
+               n_nonfinite=torch.empty(1, dtype=torch.int32, device=dev))
     c = sampler_cfg_c(scfg)
     ws = workspace(L.dg_sample_workspace_bytes(n, V), dev)
     ldt = DG_BF16 if logits.dtype == torch.bfloat16 else DG_F32
     check(L.dg_sample_renoise(ctypes.byref(c), n, ptr(logits), ldt, ptr(out["tokens"]), ptr(out["commit"]),
                               ptr(out["entropy"]), ptr(out["rowstats"]), ptr(out["n_renoised"]), ptr(pred),
-                              ptr(out["n_changed"]), ptr(ws), ws.numel(), stream_handle(stream)),
+                              ptr(out["n_changed"]), ptr(out["n_nonfinite"]), ptr(ws), ws.numel(),
+                              stream_handle(stream)),
           "dg_sample_renoise")
     return out
 
@@ -441,10 +443,13 @@ class Canvas:
         # proposals of the previous step (-1: none yet) and how many changed
         self.pred = torch.full((m,), -1, dtype=torch.int32, device=device)
         self.n_changed = torch.zeros(n_canvas, dtype=torch.int32, device=device)
+        # positions whose logits held a NaN or +-inf in the last step
+        self.n_nonfinite = torch.zeros(n_canvas, dtype=torch.int32, device=device)
 
     def c_state(self):
         return CanvasState(ptr(self.tokens), ptr(self.u), self.use_u, ptr(self.commit), ptr(self.entropy),
-                           ptr(self.n_renoised), ptr(self.logits), self.n, ptr(self.pred), ptr(self.n_changed))
+                           ptr(self.n_renoised), ptr(self.logits), self.n, ptr(self.pred), ptr(self.n_changed),
+                           ptr(self.n_nonfinite))
 
 
 def dg_canvas_step(model, kv, canvas, scfg, ws=None, stream=None):

@@ -673,7 +673,7 @@ int sample_chunks(int vocab) {
 
 struct SampleWs {
   float *part;
-  int *part_idx;
+  int *part_idx, *part_nf;
 };
 
 SampleWs sample_carve(int n, int vocab, Carve &cv) {
@@ -681,6 +681,7 @@ SampleWs sample_carve(int n, int vocab, Carve &cv) {
   SampleWs w;
   w.part = cv.take<float>(static_cast<size_t>(n) * nc * 4);
   w.part_idx = cv.take<int>(static_cast<size_t>(n) * nc);
+  w.part_nf = cv.take<int>(static_cast<size_t>(n) * nc);
   return w;
 }
 
@@ -701,8 +702,8 @@ int check_sampler_cfg(const dg_sampler_cfg *c) {
 }
 
 int sample_impl(const dg_sampler_cfg *c, int n, const void *logits, int ldt, int32_t *tok, uint8_t *commit,
-                float *ent, float *rowstats, int32_t *nre, int32_t *pred, int32_t *n_changed, Carve &cv,
-                hipStream_t s) {
+                float *ent, float *rowstats, int32_t *nre, int32_t *pred, int32_t *n_changed, int32_t *n_nonfinite,
+                Carve &cv, hipStream_t s) {
   const SampleWs ws = sample_carve(n, c->vocab, cv);
   if (c->commit_rule == DG_COMMIT_SORTED_CUMULATIVE && n > kSortedMaxRows) return DG_ERR_SHAPE;
   SampleArgs a;
@@ -720,6 +721,8 @@ int sample_impl(const dg_sampler_cfg *c, int n, const void *logits, int ldt, int
   a.key1 = static_cast<uint32_t>(c->seed >> 32);
   a.part = ws.part;
   a.part_idx = ws.part_idx;
+  a.part_nf = ws.part_nf;
+  a.n_nonfinite = n_nonfinite;
   a.tokens = tok;
   a.commit = commit;
   a.entropy = ent;
@@ -959,15 +962,15 @@ size_t dg_sample_workspace_bytes(int n_pos, int vocab) {
 
 int dg_sample_renoise(const dg_sampler_cfg *cfg, int n_pos, const void *logits, int logits_dtype, int32_t *tok,
                       uint8_t *commit, float *ent, float *rowstats, int32_t *nre, int32_t *pred,
-                      int32_t *n_changed, void *ws, size_t ws_bytes, void *stream) {
+                      int32_t *n_changed, int32_t *n_nonfinite, void *ws, size_t ws_bytes, void *stream) {
   DG_TRY(check_sampler_cfg(cfg));
   if (!dtype_ok(logits_dtype)) return DG_ERR_DTYPE;
   if (n_pos < 0) return DG_ERR_SHAPE;
   if (!logits || !tok || !commit || !ent || !nre || !ws) return DG_ERR_NULL;
   if (ws_bytes < dg_sample_workspace_bytes(n_pos, cfg->vocab)) return DG_ERR_WORKSPACE;
   Carve cv(ws);
-  return sample_impl(cfg, n_pos, logits, logits_dtype, tok, commit, ent, rowstats, nre, pred, n_changed, cv,
-                     static_cast<hipStream_t>(stream));
+  return sample_impl(cfg, n_pos, logits, logits_dtype, tok, commit, ent, rowstats, nre, pred, n_changed,
+                     n_nonfinite, cv, static_cast<hipStream_t>(stream));
 }
 
 int dg_canvas_noise(int n_pos, int vocab, uint64_t seed, uint32_t canvas_idx, int32_t *tokens, void *stream) {
@@ -1137,7 +1140,8 @@ int step_impl(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cache *k
     const size_t r0 = static_cast<size_t>(b) * C;
     DG_TRY(sample_impl(&scfg[b], C, logits + r0 * V, DG_F32, st->tokens + r0, st->commit + r0, st->entropy + r0,
                        sw.rowstats + 2 * r0, st->n_renoised + b, st->pred ? st->pred + r0 : nullptr,
-                       st->n_changed ? st->n_changed + b : nullptr, c, s));
+                       st->n_changed ? st->n_changed + b : nullptr,
+                       st->n_nonfinite ? st->n_nonfinite + b : nullptr, c, s));
   }
   if (cfg->sc_ffn > 0) {
     Carve c(sw.rest);

@@ -53,6 +53,7 @@ struct SampleArgs {
   uint32_t step, canvas_idx, key0, key1;
   float *part;          // [n_pos][n_chunks][4]: m, Z, S, best value
   int *part_idx;        // [n_pos][n_chunks]: argmax index
+  int *part_nf;         // [n_pos][n_chunks]: non-finite logits in the slice
   int32_t *tokens;
   uint8_t *commit;
   float *entropy;
@@ -62,6 +63,7 @@ struct SampleArgs {
   int token_rule;       // 0: argmax, 1: Gumbel-max draw
   int32_t *pred;        // optional [n_pos] proposals in/out
   int32_t *n_changed;   // optional [1] (with pred)
+  int32_t *n_nonfinite; // optional [1]: rows holding a NaN or +-inf logit
 };
 // rows the sorted cumulative commit rule handles (one workgroup, LDS)
 constexpr int kSortedMaxRows = 4096;

@@ -96,11 +96,13 @@ __global__ __launch_bounds__(256) void rowstats_partial_kernel(const SampleArgs 
   const int clen = a.vocab / a.n_chunks;
   const long long base = static_cast<long long>(row) * a.vocab + static_cast<long long>(chunk) * clen;
   float m = -INFINITY, Z = 0.f, S = 0.f, bv = -INFINITY;
-  int bi = 0x7fffffff;
+  int bi = 0x7fffffff, nf = 0;
   for (int c = threadIdx.x * 8; c < clen; c += 256 * 8) {
     float l[8];
     load_logits8(a.logits, a.logits_bf16, base + c, l);
     float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) nf += !isfinite(l[j]);
     if constexpr (GUMBEL) {
       // proposal score l/t + g, noise words for v = v0 .. v0+7 (v0 % 8 == 0)
       const uint32_t v0 = static_cast<uint32_t>(chunk * clen + c);
@@ -153,7 +155,9 @@ __global__ __launch_bounds__(256) void rowstats_partial_kernel(const SampleArgs 
       }
     }
     better(bv, bi, bv2, bi2);
+    nf += __shfl_xor(nf, o, 64);
   }
+  __shared__ int snf[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     sm[wave][0] = m;
@@ -161,6 +165,7 @@ __global__ __launch_bounds__(256) void rowstats_partial_kernel(const SampleArgs 
     sm[wave][2] = S;
     sm[wave][3] = bv;
     si[wave] = bi;
+    snf[wave] = nf;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -184,6 +189,7 @@ __global__ __launch_bounds__(256) void rowstats_partial_kernel(const SampleArgs 
     p[2] = SS;
     p[3] = BV;
     a.part_idx[static_cast<long long>(row) * a.n_chunks + chunk] = BI;
+    a.part_nf[static_cast<long long>(row) * a.n_chunks + chunk] = snf[0] + snf[1] + snf[2] + snf[3];
   }
 }
 
@@ -204,16 +210,21 @@ __global__ __launch_bounds__(256) void sample_finalize_kernel(const SampleArgs a
   __shared__ float sH[kSortedMaxRows];
   __shared__ int sP[kSortedMaxRows];
   const bool sorted = a.commit_rule == 1;
-  int renoised = 0, changed = 0;
+  int renoised = 0, changed = 0, nonfinite = 0;
   for (int row = threadIdx.x; row < a.n_pos; row += 256) {
     const float *p = a.part + static_cast<long long>(row) * a.n_chunks * 4;
     const int *pi = a.part_idx + static_cast<long long>(row) * a.n_chunks;
+    const int *pnf = a.part_nf + static_cast<long long>(row) * a.n_chunks;
     float M = p[0], Z = p[1], S = p[2], bv = p[3];
-    int bi = pi[0];
+    int bi = pi[0], nf = pnf[0];
     for (int c = 1; c < a.n_chunks; ++c) {
       merge_stats(M, Z, S, p[c * 4], p[c * 4 + 1], p[c * 4 + 2]);
       better(bv, bi, p[c * 4 + 3], pi[c]);
+      nf += pnf[c];
     }
+    nonfinite += nf > 0;
+    // NaN logits are never a candidate; a row of NaN only proposes token 0
+    if (bi < 0 || bi >= a.vocab) bi = 0;
     const float H = __logf(Z) - S / Z;
     if (a.pred) {
       changed += a.pred[row] != bi;
@@ -265,6 +276,10 @@ __global__ __launch_bounds__(256) void sample_finalize_kernel(const SampleArgs a
   if (a.pred && a.n_changed) {
     const int nch = block_sum(changed, red);
     if (threadIdx.x == 0) *a.n_changed = nch;
+  }
+  if (a.n_nonfinite) {
+    const int nnf = block_sum(nonfinite, red);
+    if (threadIdx.x == 0) *a.n_nonfinite = nnf;
   }
   if (threadIdx.x == 0) *a.n_renoised = nre;
 }

@@ -253,11 +253,16 @@ size_t dg_sample_workspace_bytes(int n_pos, int vocab);
  * pred_inout: optional [n_pos] int32: in, the previous step's proposals (-1
  *   before the first step); out, this step's.  n_changed_out: optional [1]
  *   int32, the number of positions whose proposal changed (read only with
- *   pred_inout): the output-stability signal for adaptive stop. */
+ *   pred_inout): the output-stability signal for adaptive stop.
+ * n_nonfinite_out: optional [1] int32, the number of rows holding at least
+ *   one NaN or +-inf logit (failure detection).  Such a row's entropy is NaN,
+ *   so it is re-noised unless final_step; a NaN logit is never proposed, and a
+ *   row with no number at all proposes token 0. */
 int dg_sample_renoise(const dg_sampler_cfg *cfg, int n_pos, const void *logits, int logits_dtype,
                       int32_t *tokens_out, uint8_t *commit_out, float *entropy_out,
                       float *rowstats_out, int32_t *n_renoised_out, int32_t *pred_inout,
-                      int32_t *n_changed_out, void *ws, size_t ws_bytes, void *stream);
+                      int32_t *n_changed_out, int32_t *n_nonfinite_out, void *ws, size_t ws_bytes,
+                      void *stream);
 
 /* Initial canvas: n_pos uniform random tokens (counter step word 0xFFFFFFFF;
  * aibars text-diffusion paragraph: generation starts from a noise block). */
@@ -266,8 +271,15 @@ int dg_canvas_noise(int n_pos, int vocab, uint64_t seed, uint32_t canvas_idx, in
 
 /* ------------------------------------------------- tied head, self-condition */
 
-/* logits = rms(x, w_final_norm) E^T with the head tied to the embedding table.
- * x [n_pos, D] and embed [vocab, D] in `dtype`; logits_out [n_pos, vocab] fp32. */
+/* Tied LM head: logits = rms(x, w_final_norm) E^T, the output head sharing
+ * the embedding table (aitrends notebook summary, details paragraphs: tied
+ * embedding; thakicloud Architecture: vocabulary 262,144).  Reading: a final
+ * RMSNorm precedes the head and no soft-cap follows it (the pages name the
+ * norm helper for the block inputs only).
+ * x [n_pos, D] and embed [vocab, D] in `dtype` (device); w_final_norm [D];
+ * logits_out [n_pos, vocab] fp32 (device, caller-owned); ws holds the normed
+ * rows.  hidden a multiple of 64, vocab of 8; DG_ERR_SHAPE / DG_ERR_NULL /
+ * DG_ERR_WORKSPACE before any launch. */
 size_t dg_lm_head_workspace_bytes(int n_pos, int hidden, int dtype);
 int dg_lm_head(int n_pos, int hidden, int vocab, float rms_eps, int dtype, const void *x,
                const void *w_final_norm, const void *embed, float *logits_out, void *ws,
@@ -330,6 +342,7 @@ typedef struct {
   int canvas_len;
   int32_t *pred;       /* optional [canvas_len]: proposals in/out, as dg_sample_renoise's pred_inout */
   int32_t *n_changed;  /* optional [1] out: proposals changed this step (needs pred) */
+  int32_t *n_nonfinite; /* optional [1] out: positions whose logits hold a NaN or +-inf */
 } dg_canvas_state;
 
 /* Workspace bytes for dg_canvas_step with canvases of up to max_canvas_tokens
@@ -337,10 +350,18 @@ typedef struct {
  * max_commit_tokens tokens per call (e.g. a prompt). */
 size_t dg_workspace_bytes(const dg_model_cfg *cfg, int max_canvas_tokens, int max_commit_tokens);
 
-/* One denoising step: x = E[tokens] + MLP_sc(u); every layer in decode mode
- * (attention then MoE); final norm + tied head; sampler; u <- P.E for the next
- * step.  Committed rows are only read; cache rows [kv_len, kv_len +
- * canvas_len) are scratch.  No device-to-host transfer. */
+/* One denoising step over the canvas (DiffusionGemma Technical Report review,
+ * section 1 Canvas: every position of the block is predicted in parallel at
+ * each step; aitrends notebook summary, attention paragraph: decode attends
+ * over [committed cache | canvas] without a causal mask; sampler paragraph:
+ * the entropy bound fixes confident positions and re-noises the rest; velog
+ * Self-conditioning: the previous step's expected embedding feeds the next).
+ * x = E[tokens] + MLP_sc(u); every layer in decode mode (attention then MoE,
+ * x <- layer_scalar * (x + y)); final norm + tied head; sampler; u <- P.E for
+ * the next step.  Committed rows are only read; cache rows [kv_len, kv_len +
+ * canvas_len) are scratch.  No device-to-host transfer: n_renoised (and
+ * n_changed, n_nonfinite) stay on the device.  Every layer's kv_len must be
+ * equal; the capacity must hold kv_len + canvas_len (DG_ERR_CAPACITY). */
 int dg_canvas_step(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cache *kv,
                    dg_canvas_state *state, const dg_sampler_cfg *scfg, void *ws, size_t ws_bytes,
                    void *stream);

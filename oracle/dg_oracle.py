@@ -369,11 +369,28 @@ def temperature(t_max, t_min, step, n_steps):
     return float(t_max) + (float(t_min) - float(t_max)) * step / (n_steps - 1)
 
 
+def first_argmax(s):
+    """Per row, the index of the largest entry that is a number (lowest id on
+    ties).  Reading for non-finite logits, which the pages never meet: a NaN
+    is never a candidate, -inf is an ordinary (smallest) value, and a row with
+    no number at all proposes token 0."""
+    s = np.asarray(s, dtype=np.float64)
+    nan = np.isnan(s)
+    filled = np.where(nan, -np.inf, s)
+    idx = np.argmax(filled, axis=1)
+    for r in np.nonzero(np.isneginf(filled[np.arange(len(s)), idx]))[0]:
+        cand = np.nonzero(~nan[r])[0]
+        idx[r] = cand[0] if len(cand) else 0
+    return idx
+
+
 def row_stats(logits, t):
     """Per row of l/t: max m, Z = sum e^d, S = sum e^d d (d = l/t - m), entropy H.
 
     H = ln Z - S/Z equals -sum p ln p for p = softmax(l/t), in nats.
-    Also the argmax of the raw logits, lowest id on ties.
+    Also the argmax of the raw logits, lowest id on ties (first_argmax).
+    A row holding a NaN or +-inf has a NaN entropy (so it never commits on
+    its own).
     """
     l = np.asarray(logits, dtype=np.float64) / t
     m = l.max(axis=1, keepdims=True)
@@ -382,7 +399,9 @@ def row_stats(logits, t):
     Z = e.sum(axis=1)
     S = (e * d).sum(axis=1)
     H = np.log(Z) - S / Z
-    amax = np.argmax(np.asarray(logits, dtype=np.float64), axis=1)  # first max
+    with np.errstate(invalid="ignore"):
+        H = np.where(np.isfinite(np.asarray(logits, np.float64)).all(axis=1), H, np.nan)
+    amax = first_argmax(logits)
     return m[:, 0], Z, S, H, amax
 
 
@@ -488,7 +507,7 @@ def sample_renoise(logits, scfg, pred_prev=None):
     if scfg.get("token_rule", "argmax") == "gumbel":
         sc = np.asarray(logits, dtype=np.float64) / t + gumbel_noise(
             np.arange(n), scfg["vocab"], scfg["seed"], scfg["step"], scfg["canvas_idx"])
-        pred = np.argmax(sc, axis=1)
+        pred = first_argmax(sc)
         top2 = -np.sort(-sc, axis=1)[:, :2]
         margin = top2[:, 0] - top2[:, 1]
     else:
@@ -503,8 +522,9 @@ def sample_renoise(logits, scfg, pred_prev=None):
     noise = renoise_tokens(n, scfg["vocab"], scfg["seed"], scfg["step"], scfg["canvas_idx"])
     tokens = np.where(commit, pred, noise)
     n_changed = None if pred_prev is None else int(np.sum(np.asarray(pred_prev) != pred))
+    n_nonfinite = int(np.sum(~np.isfinite(np.asarray(logits, np.float64)).all(axis=1)))
     return dict(tokens=tokens.astype(np.int64), commit=commit, entropy=H,
-                n_renoised=int(np.sum(~commit)), argmax=amax, pred=pred.astype(np.int64),
+                n_renoised=int(np.sum(~commit)), n_nonfinite=n_nonfinite, argmax=amax, pred=pred.astype(np.int64),
                 n_changed=n_changed, gumbel_margin=margin, prior_sum=prior, row_max=m,
                 row_z=Z, temperature=t)
 

@@ -120,12 +120,12 @@ def test_sampler_validation_codes():
     L = B.lib()
     p = ctypes.c_void_p(256)
     call = lambda s, n=256, ldt=0, wsb=1 << 30: L.dg_sample_renoise(
-        ctypes.byref(s), n, p, ldt, p, p, p, None, p, None, None, p, wsb, None)
+        ctypes.byref(s), n, p, ldt, p, p, p, None, p, None, None, None, p, wsb, None)
     assert call(B.sampler_cfg_c(synth.sampler_cfg(262144, t_max=0.0))) == -2
     assert call(B.sampler_cfg_c(synth.sampler_cfg(262143))) == -2
     assert call(B.sampler_cfg_c(synth.sampler_cfg(262144)), ldt=3) == -5
     assert call(B.sampler_cfg_c(synth.sampler_cfg(262144)), wsb=8) == -4
-    assert L.dg_sample_renoise(None, 1, p, 0, p, p, p, None, p, None, None, p, 1 << 30, None) == -1
+    assert L.dg_sample_renoise(None, 1, p, 0, p, p, p, None, p, None, None, None, p, 1 << 30, None) == -1
     bad = B.sampler_cfg_c(synth.sampler_cfg(262144))
     bad.commit_rule = 2
     assert call(bad) == -3

@@ -313,6 +313,79 @@ def test_shared_kv_projection_global_layer():
                                gk ** 2 * (v[..., :h] ** 2 + v[..., h:] ** 2), rtol=1e-10)
 
 
+def _rms_by_hand(vec, w, eps):
+    """w_t * x_t * sqrt(d) / (||x|| + eps) written as scalar loops."""
+    d = len(vec)
+    nrm = math.sqrt(sum(float(a) * float(a) for a in vec))
+    return [float(w[t]) * float(vec[t]) * math.sqrt(d) / (nrm + eps) for t in range(d)]
+
+
+@pytest.mark.parametrize("layer_type", [0, 1])
+def test_head_major_split_by_hand(layer_type):
+    """[AIT] projection code: the projection output is split 'l (n h) -> n l h',
+    so head n owns columns [n*d_h, (n+1)*d_h), i.e. rows [n*d_h, (n+1)*d_h) of
+    W_q (W_k for kv head g).  Each head is rebuilt here from those weight rows
+    with the pre-norm, QK-norm and split-half rotation as scalar loops; a
+    split taking columns n, n+H, n+2H, ... (the '(h n)' order) fails."""
+    cfg, w, g = tiny_layer(layer_type)
+    x = np64(synth.hidden_states(3, cfg["hidden"], g, "f32"))
+    pos0 = 37
+    q, k, v = O.project_qkv(cfg, w, x, pos0, "f32")
+    dh, half, eps = cfg["head_dim"], cfg["head_dim"] // 2, cfg["rms_eps"]
+    rf = cfg["rotary_factor"] if layer_type == 1 else 1.0
+    n_keep = int(round(rf * half))
+
+    def head(W, gamma, n, j):
+        h = _rms_by_hand(x[j], w["w_in_norm"], eps)
+        raw = [sum(h[d] * float(W[n * dh + t, d]) for d in range(len(h))) for t in range(dh)]
+        nr = _rms_by_hand(raw, gamma, eps)
+        out = list(nr)
+        p = pos0 + j
+        for t in range(half):
+            f = cfg["rope_base"] ** (-2.0 * t / dh) if t < n_keep else 0.0
+            c, s = math.cos(p * f), math.sin(p * f)
+            out[t] = nr[t] * c - nr[t + half] * s
+            out[t + half] = nr[t + half] * c + nr[t] * s
+        return np.array(out), np.array(raw)
+
+    for n, j in ((0, 0), (cfg["n_q_heads"] - 1, 2), (1, 1)):
+        ref, _ = head(w["w_q"], w["q_norm"], n, j)
+        np.testing.assert_allclose(q[n, j], ref, rtol=1e-10, atol=1e-12)
+    for gi, j in ((0, 1), (cfg["n_kv_heads"] - 1, 2)):
+        ref, raw = head(w["w_k"], w["k_norm"], gi, j)
+        np.testing.assert_allclose(k[gi, j], ref, rtol=1e-10, atol=1e-12)
+        if layer_type == 1:
+            # shared projection: the value is the raw key of the same head at unit RMS
+            np.testing.assert_allclose(v[gi, j], _rms_by_hand(raw, np.ones(dh), eps), rtol=1e-10,
+                                       atol=1e-12)
+
+
+def test_selfcond_adds_swiglu_of_u_by_hand():
+    """[AIT] glossary "Self-conditioning"; [VLG] soft embedding: the expected
+    embedding u passes through the small MLP and is ADDED to the token
+    embedding (x_j = E[c_j] + MLP_sc(u_j), no sqrt(D) scale).  The MLP
+    (bias-free SwiGLU) is evaluated here with scalar loops for u != 0, so
+    'replace' instead of 'add', a dropped gate, or a swapped gate/up fails."""
+    D, V, F = 12, 40, 5
+    g = synth.generator(12)
+    E = np64(synth.embed_table(V, D, g, "f32"))
+    sc = {k: v * 10.0 for k, v in npw(synth.selfcond_weights(D, F, g, "f32")).items()}
+    u = np64(synth.hidden_states(3, D, g, "f32"))
+    tok = np.array([5, 39, 0])
+    x = O.embed_selfcond(tok, E, u, sc, "f32")
+    for j in range(3):
+        a = []
+        for f in range(F):
+            zg = sum(float(sc["sc_gate"][f, d]) * float(u[j, d]) for d in range(D))
+            zu = sum(float(sc["sc_up"][f, d]) * float(u[j, d]) for d in range(D))
+            a.append(zg / (1.0 + math.exp(-zg)) * zu)
+        for d in range(D):
+            mlp = sum(float(sc["sc_down"][d, f]) * a[f] for f in range(F))
+            assert abs(x[j, d] - (E[tok[j], d] + mlp)) <= 1e-12 * (1.0 + abs(E[tok[j], d]))
+    # the MLP term is not negligible here: replacing instead of adding would fail
+    assert np.max(np.abs(x - E[tok])) > 1e-2
+
+
 # ----------------------------------------------------------------------------
 # MoE
 # ----------------------------------------------------------------------------
@@ -434,6 +507,30 @@ def test_entropy_matches_library_and_commit_sets():
         # probabilities from the row statistics are the tempered softmax
         pr = O.probs(logits, out["row_max"], out["row_z"], out["temperature"])
         np.testing.assert_allclose(pr, p, rtol=1e-10, atol=1e-300)
+
+
+def test_nonfinite_rows_counted_and_proposals_skip_nan():
+    """Failure detection (a reading: the pages never meet non-finite logits).
+    Rows with a NaN or +-inf are counted, their entropy is NaN so they are
+    re-noised, a NaN is never proposed, and an all-NaN row proposes 0."""
+    V = 64
+    lg = np.zeros((5, V))
+    lg[0, 10] = 5.0                          # ordinary peaked row
+    lg[1, 0] = np.nan
+    lg[1, 7] = 9.0                           # NaN ignored: 7 is the argmax
+    lg[2, :] = np.nan                        # no number at all
+    lg[3, 3] = np.inf
+    lg[4, :] = -np.inf
+    lg[4, 0] = np.nan                        # -inf is a value: first -inf after the NaN
+    with np.errstate(invalid="ignore"):
+        out = O.sample_renoise(lg, scfg(V, final_step=False))
+        fin = O.sample_renoise(lg, scfg(V, final_step=True))
+    assert out["n_nonfinite"] == 4
+    np.testing.assert_array_equal(fin["tokens"], [10, 7, 0, 3, 1])
+    assert np.isfinite(out["entropy"][0]) and np.isnan(out["entropy"][1:]).all()
+    noise = O.renoise_tokens(5, V, 1, 0, 0)
+    np.testing.assert_array_equal(out["tokens"][1:], noise[1:])
+    assert out["commit"][0] and out["n_renoised"] == 4
 
 
 def test_final_step_commits_everything():
