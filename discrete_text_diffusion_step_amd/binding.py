@@ -76,7 +76,8 @@ class ModelCfg(ctypes.Structure):
 class ModelW(ctypes.Structure):
     _fields_ = [("embed", c_void), ("embed_t", c_void), ("w_final_norm", c_void), ("sc_gate", c_void),
                 ("sc_up", c_void), ("sc_down", c_void), ("attn", ctypes.POINTER(AttnW)),
-                ("moe", ctypes.POINTER(MoeW)), ("layer_scalar", ctypes.POINTER(c_float))]
+                ("moe", ctypes.POINTER(MoeW)), ("layer_scalar", ctypes.POINTER(c_float)),
+                ("router_logits", ctypes.POINTER(c_void))]
 
 
 class KVCache(ctypes.Structure):
@@ -370,7 +371,21 @@ class Model:
         sc = weights.get("sc") or {}
         self.c_w = ModelW(ptr(weights["embed"]), ptr(weights["embed_t"]), ptr(weights["w_final_norm"]),
                           ptr(sc.get("sc_gate")), ptr(sc.get("sc_up")), ptr(sc.get("sc_down")),
-                          self._attn, self._moe, self._ls)
+                          self._attn, self._moe, self._ls, None)
+        self._rl = None
+
+    def set_router_logits(self, logits):
+        """Per-layer fp32 router logits [rows, n_experts] (device tensors, one
+        per layer, None entries computed) used instead of the router product
+        by the next calls; None restores the router product everywhere."""
+        if logits is None:
+            self._rl = None
+            self.c_w.router_logits = None
+            return
+        assert len(logits) == self.cfg["n_layers"]
+        self._rl_t = [None if t is None else t.contiguous() for t in logits]
+        self._rl = (c_void * len(logits))(*[None if t is None else t.data_ptr() for t in self._rl_t])
+        self.c_w.router_logits = ctypes.cast(self._rl, ctypes.POINTER(c_void))
 
 
 def ring_capacity(window, max_tokens):

@@ -1043,6 +1043,20 @@ size_t dg_workspace_bytes(const dg_model_cfg *cfg, int max_canvas_tokens, int ma
 
 static int check_model_w(const dg_model_cfg *c, const dg_model_w *w, bool need_head) {
   if (!w || !w->embed || !w->attn || !w->moe || !w->layer_scalar) return DG_ERR_NULL;
+  for (int l = 0; l < c->n_layers; ++l) {
+    const dg_attn_cfg *ac = (l % c->global_every) == c->global_every - 1 ? &c->global : &c->sliding;
+    const dg_attn_w &a = w->attn[l];
+    if (!a.w_in_norm || !a.w_q || !a.w_k || !a.w_o || !a.q_norm || !a.k_norm) return DG_ERR_NULL;
+    if (!ac->shared_kv && !a.w_v) return DG_ERR_NULL;
+    const dg_moe_w &m = w->moe[l];
+    if (!m.w_in_norm || !m.w_gate || !m.w_up || !m.w_down || !m.ws_gate || !m.ws_up || !m.ws_down)
+      return DG_ERR_NULL;
+    if (c->moe.expert_format == DG_EXPERTS_FP8_E4M3 &&
+        (!m.s_gate || !m.s_up || !m.s_down || !m.ss_gate || !m.ss_up || !m.ss_down))
+      return DG_ERR_NULL;
+    const bool router = m.w_router || (w->router_logits && w->router_logits[l]);
+    if (!router) return DG_ERR_NULL;
+  }
   if (need_head && (!w->w_final_norm || !w->embed_t)) return DG_ERR_NULL;
   if (c->sc_ffn > 0 && need_head && (!w->sc_gate || !w->sc_up || !w->sc_down)) return DG_ERR_NULL;
   return DG_OK;
@@ -1128,7 +1142,8 @@ int step_impl(const dg_model_cfg *cfg, const dg_model_w *w, const dg_kv_cache *k
       to_attn.eps = layer_cfg(cfg, l + 1)->rms_eps;
     }
     Carve c2(sw.rest);
-    DG_TRY(moe_impl(&mc, &w->moe[l], n, sw.x, nullptr, nullptr, nullptr, c2, s, sw.h, to_attn));
+    DG_TRY(moe_impl(&mc, &w->moe[l], n, sw.x, w->router_logits ? w->router_logits[l] : nullptr, nullptr, nullptr, c2,
+                    s, sw.h, to_attn));
   }
   float *logits = st->logits ? st->logits : sw.logits;
   {
@@ -1266,7 +1281,8 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
     to_attn.w = w->attn[l + 1].w_in_norm;
     to_attn.eps = layer_cfg(cfg, l + 1)->rms_eps;
     Carve c2(sw.rest);
-    DG_TRY(moe_impl(&mc, &w->moe[l], n, sw.x, nullptr, nullptr, nullptr, c2, s, sw.h, to_attn));
+    DG_TRY(moe_impl(&mc, &w->moe[l], n, sw.x, w->router_logits ? w->router_logits[l] : nullptr, nullptr, nullptr, c2,
+                    s, sw.h, to_attn));
   }
   return DG_OK;
 }

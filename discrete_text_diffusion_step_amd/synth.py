@@ -219,8 +219,10 @@ def sampler_logits(n, vocab, gen, s_max=7.0, n_flat=4, n_peaked=4, device="cpu")
     return out
 
 
-def model_weights(mcfg, seed, device="cpu", std=0.02, layer_seed_base=1000):
-    """Weights for a whole stack; layer l draws from seed layer_seed_base + l."""
+def model_weights(mcfg, seed, device="cpu", std=0.02, layer_seed_base=1000, gamma_range=None):
+    """Weights for a whole stack; layer l draws from seed layer_seed_base + l.
+    gamma_range=(lo, hi): the constant QK-norm gains of layer l are drawn
+    from U[lo, hi] (seed 2000 + l) instead of U[0.5, 1.5]."""
     dt = mcfg["dtype"]
     D, V = mcfg["hidden"], mcfg["vocab"]
     g = generator(seed, device)
@@ -232,7 +234,12 @@ def model_weights(mcfg, seed, device="cpu", std=0.02, layer_seed_base=1000):
         gl = generator(layer_seed_base + l, device)
         glob = (l % mcfg["global_every"]) == mcfg["global_every"] - 1
         acfg = mcfg["global"] if glob else mcfg["sliding"]
-        w["attn"].append(attn_weights(acfg, gl, std, device))
+        gamma = None
+        if gamma_range is not None:
+            gg = generator(2000 + l)
+            gamma = tuple(float(v) for v in torch.rand(2, generator=gg) * (gamma_range[1] - gamma_range[0])
+                          + gamma_range[0])
+        w["attn"].append(attn_weights(acfg, gl, std, device, gamma=gamma))
         w["moe"].append(moe_weights(mcfg["moe"], gl, std, device))
         w["layer_scalar"].append(1.0)
     return w

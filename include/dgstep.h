@@ -323,6 +323,13 @@ typedef struct {
   const dg_attn_w *attn;     /* host array [n_layers] */
   const dg_moe_w *moe;       /* host array [n_layers] */
   const float *layer_scalar; /* host array [n_layers] */
+  /* Optional (NULL: the router product runs).  Host array [n_layers] of
+   * device pointers, each [rows, n_experts] fp32 router logits used by that
+   * layer's MoE block in place of rms(x) W_router^T, rows = the tokens of
+   * the call (all canvases of a batch, back to back).  A NULL entry computes
+   * that layer's logits.  Lets a caller feed the device and a reference the
+   * same routing (as dg_moe_block's router_logits_in). */
+  const float *const *router_logits;
 } dg_model_w;
 
 typedef struct {

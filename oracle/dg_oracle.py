@@ -557,7 +557,7 @@ def embed_selfcond(tokens, embed, u, sc, dtype):
     sc = None disables self-conditioning.
     Storage points: the MLP hidden activation and x.
     """
-    x = np.asarray(embed, np.float64)[np.asarray(tokens)]
+    x = np.asarray(np.asarray(embed)[np.asarray(tokens)], np.float64)   # gather, then widen
     if sc is None or u is None:
         return store(x, dtype)
     add = swiglu_ffn(np.asarray(u, np.float64), sc["sc_gate"], sc["sc_up"], sc["sc_down"], dtype)
@@ -574,12 +574,19 @@ def layer_type(l, global_every):
     return 1 if (l % global_every) == global_every - 1 else 0
 
 
+def _injected(weights, l):
+    rl = weights.get("router_logits")
+    return None if rl is None else rl[l]
+
+
 def canvas_step(model, weights, kv, state, scfg, dtype):
     """One denoising step over the canvas (decode mode through every layer).
 
     model: dict(n_layers, global_every, sliding=cfg, global=cfg, moe=cfg,
                 rms_eps, vocab).
-    weights: dict(embed, w_final_norm, sc (or None), attn[l], moe[l]).
+    weights: dict(embed, w_final_norm, sc (or None), attn[l], moe[l],
+    layer_scalar[l], optionally router_logits[l]: injected router logits of
+    layer l used in place of the router product, None entries computed).
     kv: dict(k[l], v[l], kv_len).  state: dict(tokens, u (or None)).
     Returns dict(sample outputs, logits, u_next, x_final).
     """
@@ -590,7 +597,7 @@ def canvas_step(model, weights, kv, state, scfg, dtype):
         acfg = model["global"] if layer_type(l, model["global_every"]) else model["sliding"]
         x, _, _ = attn_layer(acfg, weights["attn"][l], kv["k"][l], kv["v"][l], P, x, 0, dtype)
         x, _, _, _ = moe_block_grouped(dict(model["moe"], layer_scalar=weights["layer_scalar"][l]),
-                                       weights["moe"][l], x, dtype)
+                                       weights["moe"][l], x, dtype, router_logits=_injected(weights, l))
     logits = lm_head(x, weights["w_final_norm"], weights["embed"], model["rms_eps"], dtype)
     out = sample_renoise(logits, scfg)
     p = probs(logits, out["row_max"], out["row_z"], out["temperature"])
@@ -622,7 +629,7 @@ def commit_canvas(model, weights, kv, tokens, dtype):
         else:
             x, k, v = attn_layer(acfg, weights["attn"][l], kv["k"][l], kv["v"][l], P, x, 1, dtype)
             x, _, _, _ = moe_block_grouped(dict(model["moe"], layer_scalar=weights["layer_scalar"][l]),
-                                           weights["moe"][l], x, dtype)
+                                           weights["moe"][l], x, dtype, router_logits=_injected(weights, l))
         k_new.append(k)
         v_new.append(v)
     return k_new, v_new
@@ -650,3 +657,66 @@ def param_count(D, n_layers, global_every, sliding, glob, n_experts, top_k, ffn,
         total += a + router + experts + shared + D
         active += a + router + top_k * 3 * ffn * D + shared + D
     return total, active
+
+
+def generate(model, weights, kv, prompt, n_canvases, canvas_len, max_steps, seed, t_max, t_min, tau, dtype,
+             stop_rule="renoised"):
+    """Block-autoregressive generation from the step and commit above.
+
+    [ABN] block-autoregressive denoising: the prompt is committed, then each
+    block of canvas_len positions starts from uniform noise, is denoised, and
+    is committed to the KV cache before the next block.  [REV] section 1
+    (Adaptive Stopping): the loop stops early once the prediction settles.
+    stop_rule "renoised": stop after a step that re-noised no position.
+    stop_rule "stable": from the second step on, stop once no position's
+    proposal changed since the previous step; the canvas then takes the
+    proposals everywhere.  The last allowed step commits every position.
+    kv: dict(k[l], v[l], kv_len) with room for the prompt and the canvases;
+    it is copied, not modified.
+    Returns dict(tokens [n_canvases, canvas_len], steps [n_canvases],
+    min_entropy_gap: the smallest |H - tau| met, min_lead: the smallest
+    argmax lead met on any position, kv: the cache after the last commit).
+    """
+    kv = dict(k=[np.array(a, np.float64) for a in kv["k"]], v=[np.array(a, np.float64) for a in kv["v"]],
+              kv_len=kv["kv_len"])
+    V = model["vocab"]
+
+    def append(tok):
+        k_new, v_new = commit_canvas(model, weights, kv, tok, dtype)
+        P, n = kv["kv_len"], len(tok)
+        for l in range(model["n_layers"]):
+            kv["k"][l][:, P:P + n] = k_new[l]
+            kv["v"][l][:, P:P + n] = v_new[l]
+        kv["kv_len"] = P + n
+
+    if prompt is not None and len(prompt):
+        append(np.asarray(prompt))
+    out, steps = [], []
+    gap, lead = np.inf, np.inf
+    for c in range(n_canvases):
+        tokens, u, pred_prev = canvas_noise(canvas_len, V, seed, c), None, None
+        used = 0
+        for i in range(max_steps):
+            final = i == max_steps - 1
+            s = dict(vocab=V, tau=tau, t_max=t_max, t_min=t_min, n_steps=max_steps, step=i, canvas_idx=c,
+                     seed=seed, final_step=final)
+            r = canvas_step(model, weights, kv, dict(tokens=tokens, u=u), s, dtype)
+            used += 1
+            gap = min(gap, float(np.min(np.abs(r["entropy"] - tau))))
+            top = -np.partition(-r["logits"], 1, axis=1)[:, :2]
+            lead = min(lead, float(np.min(top[:, 0] - top[:, 1])))
+            tokens, u = r["tokens"], r["u_next"]
+            if final:
+                break
+            if stop_rule == "stable":
+                changed = None if pred_prev is None else int(np.sum(r["pred"] != pred_prev))
+                pred_prev = r["pred"]
+                if changed == 0:
+                    tokens = r["pred"]
+                    break
+            elif r["n_renoised"] == 0:
+                break
+        out.append(tokens)
+        steps.append(used)
+        append(tokens)
+    return dict(tokens=np.array(out), steps=steps, min_entropy_gap=gap, min_lead=lead, kv=kv)

@@ -135,45 +135,39 @@ def test_moe_fp8_single_token():
     assert_delta_close(np64(xd), ref, np64(x), "bf16", "fp8 moe single-token delta")
 
 
-class _LazyDeq:
-    """Expert e of a stacked matrix, quantised and dequantised by the oracle
-    on first use (so a token sample touches only its own experts)."""
-
-    def __init__(self, stack):
-        self.stack, self.cache = stack, {}
-
-    def __getitem__(self, e):
-        e = int(e)
-        if e not in self.cache:
-            q, s = F8.quantize_rows(np64(self.stack[e]))
-            self.cache[e] = (q, s, F8.dequantize_rows(q, s))
-        return self.cache[e][2]
+def _quantize_stack(stack, ex):
+    """The oracle's codes, scales and dequantised values of an expert stack
+    [E, N, K] (bf16 tensor), one expert per task."""
+    res = list(ex.map(lambda e: F8.quantize_rows(np64(stack[e])), range(stack.shape[0])))
+    q = np.stack([r[0] for r in res])
+    sc = np.stack([r[1] for r in res])
+    deq = np.stack(list(ex.map(lambda e: F8.dequantize_rows(q[e], sc[e]), range(stack.shape[0]))))
+    return q, sc, deq
 
 
-def test_moe_fp8_full_sampled_tokens():
-    """128 experts top-8 + shared at the canvas shape (256 tokens) on the GPU;
-    the oracle recomputes a sample of tokens one by one."""
+def test_moe_fp8_full_all_tokens():
+    """128 experts top-8 + shared at the canvas shape (256 tokens): codes and
+    scales of every expert bit-exact, and every token's output against the
+    oracle's MoE on the oracle's own dequantised weights."""
+    from concurrent.futures import ThreadPoolExecutor
     cfg = synth.moe_cfg(2816, 128, 8, 704, 704)
     g = synth.generator(53)
     w = synth.moe_weights(cfg, g, with_router=False)
     x = synth.hidden_states(256, cfg["hidden"], g, "bf16")
     rl = synth.router_logits(256, 128, g)
     wq, xd, idx = _run_gpu(cfg, w, x, rl)
-    sample = [0, 1, 97, 200, 255]
     wn = {"w_in_norm": np64(w["w_in_norm"])}
-    for n in ("w_gate", "w_up", "w_down"):
-        wn[n] = _LazyDeq(w[n])
+    with ThreadPoolExecutor(16) as ex:
+        for n in ("w_gate", "w_up", "w_down"):
+            q, sc, wn[n] = _quantize_stack(w[n], ex)
+            np.testing.assert_array_equal(wq[n].cpu().numpy(), q)
+            np.testing.assert_array_equal(wq[SCALE_NAME[n]].cpu().numpy(), sc)
     for n in ("ws_gate", "ws_up", "ws_down"):
-        q, s = F8.quantize_rows(np64(w[n]))
+        q, sc = F8.quantize_rows(np64(w[n]))
         np.testing.assert_array_equal(wq[n].cpu().numpy(), q)
-        np.testing.assert_array_equal(wq[SCALE_NAME[n]].cpu().numpy(), s)
-        wn[n] = F8.dequantize_rows(q, s)
-    ref, ridx, _, _ = O.moe_block(cfg, wn, np64(x)[sample], "bf16", router_logits=np64(rl)[sample])
-    np.testing.assert_array_equal(idx.cpu().numpy()[sample], ridx)
-    for n in ("w_gate", "w_up", "w_down"):
-        for e, (q, s, _) in wn[n].cache.items():
-            np.testing.assert_array_equal(wq[n][e].cpu().numpy(), q)
-            np.testing.assert_array_equal(wq[SCALE_NAME[n]][e].cpu().numpy(), s)
-    got = np64(xd)[sample]
-    assert_close(got, ref, "bf16", "fp8 moe x (sampled tokens)")
-    assert_delta_close(got, ref, np64(x)[sample], "bf16", "fp8 moe delta (sampled tokens)")
+        np.testing.assert_array_equal(wq[SCALE_NAME[n]].cpu().numpy(), sc)
+        wn[n] = F8.dequantize_rows(q, sc)
+    ref, ridx, _, _ = O.moe_block_grouped(cfg, wn, np64(x), "bf16", router_logits=np64(rl))
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    assert_close(np64(xd), ref, "bf16", "fp8 moe x (all tokens)")
+    assert_delta_close(np64(xd), ref, np64(x), "bf16", "fp8 moe delta (all tokens)")

@@ -14,7 +14,8 @@ import torch
 from discrete_text_diffusion_step_amd import binding as B
 from discrete_text_diffusion_step_amd import synth
 from oracle import dg_oracle as O
-from tests.helpers import assert_close, assert_delta_close, cuda, np64, npw, rel_err
+from tests.helpers import (assert_close, assert_delta_close, check_router_sets, check_sampler_outputs, cuda, np64,
+                           npw, rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -119,10 +120,9 @@ def test_lm_head(dtype, n, D, V):
     wn = synth._uniform(g, (D,), 0.5, 1.5, dtype, "cpu")
     lg = B.dg_lm_head(x.cuda(), wn.cuda(), E.cuda(), 1e-6)
     sync()
-    cols = np.arange(V) if V <= 8192 else np.sort(np.random.default_rng(0).choice(V, 4096, replace=False))
-    h = O.store(O.rms(np64(x), np64(wn), 1e-6), dtype)
-    ref = h @ np64(E[torch.from_numpy(cols)]).T
-    assert_close(lg.cpu().numpy()[:, cols], ref, "f32" if dtype == "f32" else "bf16", "logits")
+    # every column (the oracle slices the vocabulary, never a sum)
+    ref = O.lm_head(np64(x), np64(wn), E.float().numpy(), 1e-6, dtype)
+    assert_close(lg.cpu().numpy(), ref, "f32" if dtype == "f32" else "bf16", "logits")
 
 
 @pytest.mark.parametrize("dtype,n,D,V", [("f32", 32, 256, 4096), ("bf16", 45, 320, 8000),
@@ -138,10 +138,8 @@ def test_soft_embed(dtype, n, D, V):
     sync()
     ref = O.sample_renoise(np64(lg), s)
     p = O.probs(np64(lg), ref["row_max"], ref["row_z"], ref["temperature"])
-    cols = np.arange(D) if D <= 512 else np.sort(np.random.default_rng(1).choice(D, 256, replace=False))
-    Pq = O.store(p, dtype)
-    uref = O.store(Pq @ np64(E[:, torch.from_numpy(cols)]), dtype)
-    assert_close(np64(u)[:, cols], uref, dtype, "u = P.E")
+    uref = O.soft_embed(p, E.float().numpy(), dtype)      # every column
+    assert_close(np64(u), uref, dtype, "u = P.E")
 
 
 def test_embed_transpose():
@@ -269,17 +267,18 @@ def test_moe_tiny_f32(n, inject):
     idx, wts = B.dg_moe_block(cfg, cuda(w), xd, None if rl is None else rl.cuda(), want_topk=True)
     sync()
     ref, ridx, rw, r = O.moe_block(cfg, npw(w), np64(x), "f32", router_logits=None if rl is None else np64(rl))
-    # indices bit-exact where the k-th / (k+1)-th logit gap is clear
-    srt = -np.sort(-r, axis=1)
-    clear = (srt[:, cfg["top_k"] - 1] - srt[:, cfg["top_k"]]) > 1e-3
-    np.testing.assert_array_equal(idx.cpu().numpy()[clear], ridx[clear])
+    # indices bit-exact where the k-th / (k+1)-th logit gap is clear, valid inside the band
+    clear = check_router_sets(idx.cpu().numpy(), ridx, r, cfg["top_k"])
     assert rel_err(wts.cpu().numpy()[clear], rw[clear]) < 1e-5
     assert_close(np64(xd), ref, "f32", "moe x")
 
 
-def test_moe_bf16_full_injected():
-    """128 experts top-8 + shared at the canvas shape, router logits N(0,1)."""
-    cfg = synth.moe_cfg(2816, 128, 8, 704, 704)
+@pytest.mark.parametrize("layer_scalar,route_scale", [(1.0, 1.0), (1.15, 1.3), (0.85, 0.7)])
+def test_moe_bf16_full_injected(layer_scalar, route_scale):
+    """128 experts top-8 + shared at the canvas shape, router logits N(0,1);
+    the layer scalar rescales x + y and the route scale the routed weights
+    (aitrends glossary "Layer Scalar", "MoE")."""
+    cfg = synth.moe_cfg(2816, 128, 8, 704, 704, layer_scalar=layer_scalar, route_scale=route_scale)
     g = synth.generator(53)
     w = synth.moe_weights(cfg, g, with_router=False)
     x = synth.hidden_states(256, cfg["hidden"], g, "bf16")
@@ -307,10 +306,10 @@ def test_moe_bf16_router_computed():
     idx, wts = B.dg_moe_block(cfg, cuda(w), xd, None, want_topk=True)
     sync()
     ref, ridx, rw, r = O.moe_block_grouped(cfg, npw(w), np64(x), "bf16")
-    srt = -np.sort(-r, axis=1)
-    clear = (srt[:, 7] - srt[:, 8]) > 1e-3
+    # exact where the 8th/9th logit gap is clear; inside the band the sets may
+    # differ only by experts within 1e-3 of the oracle's 8th logit
+    clear = check_router_sets(idx.cpu().numpy(), ridx, r, 8)
     assert clear.mean() > 0.9
-    np.testing.assert_array_equal(idx.cpu().numpy()[clear], ridx[clear])
     assert rel_err(wts.cpu().numpy()[clear], rw[clear]) < 1e-2
     assert_delta_close(np64(xd)[clear], ref[clear], np64(x)[clear], "bf16", "moe (router computed) delta")
 
@@ -442,9 +441,9 @@ def test_tiny_commit_then_two_steps():
         ref = O.canvas_step(mcfg, wn, rkv, dict(tokens=tokens, u=u), s, "f32")
         assert_close(canvas.logits.cpu().numpy(), ref["logits"], "f32", f"step {step} logits")
         assert np.max(np.abs(canvas.entropy.cpu().numpy() - ref["entropy"])) < 1e-4 * math.log(V)
-        H = ref["entropy"]
-        clear = np.abs(H - s["tau"]) > 1e-3
-        np.testing.assert_array_equal(canvas.commit.cpu().numpy().astype(bool)[clear], ref["commit"][clear])
-        np.testing.assert_array_equal(canvas.tokens.cpu().numpy()[clear], ref["tokens"][clear])
+        noise = O.renoise_tokens(C, V, s["seed"], s["step"], s["canvas_idx"])
+        dl = float(np.max(np.abs(canvas.logits.cpu().numpy() - ref["logits"])))
+        check_sampler_outputs(canvas.tokens.cpu().numpy(), canvas.commit.cpu().numpy(), ref, ref["logits"], noise,
+                              s["tau"], band_logit=max(2 * dl, 1e-6), band_h=1e-3)
         assert_close(np64(canvas.u), ref["u_next"], "f32", f"step {step} u")
         tokens, u = ref["tokens"], ref["u_next"]   # each side continues from its own state
