@@ -123,6 +123,9 @@ def lib(path=None):
             "dg_sample_workspace_bytes": (c_size, [c_int, c_int]),
             "dg_sample_renoise": (c_int, [P(SamplerCfg), c_int, c_void, c_int, c_void, c_void, c_void, c_void,
                                           c_void, c_void, c_void, c_void, c_void, c_size, c_void]),
+            "dg_sample_noalloc_max_bytes": (c_size, []),
+            "dg_sample_renoise_noalloc": (c_int, [P(SamplerCfg), c_int, c_void, c_int, c_void, c_void, c_void,
+                                                  c_void, c_void, c_void, c_void, c_void, c_void]),
             "dg_canvas_noise": (c_int, [c_int, c_int, ctypes.c_uint64, ctypes.c_uint32, c_void, c_void]),
             "dg_lm_head_workspace_bytes": (c_size, [c_int, c_int, c_int]),
             "dg_lm_head": (c_int, [c_int, c_int, c_int, c_float, c_int, c_void, c_void, c_void, c_void, c_void,
@@ -304,6 +307,28 @@ def dg_sample_renoise(scfg, logits, want_rowstats=True, pred=None, stream=None):
                               ptr(out["n_changed"]), ptr(out["n_nonfinite"]), ptr(ws), ws.numel(),
                               stream_handle(stream)),
           "dg_sample_renoise")
+    return out
+
+
+def dg_sample_renoise_noalloc(scfg, logits, want_rowstats=True, pred=None, stream=None):
+    """dg_sample_renoise on the library's built-in scratch (no workspace);
+    the outputs are allocated here, by the caller's side."""
+    L = lib()
+    n, V = logits.shape
+    dev = logits.device
+    out = dict(tokens=torch.empty(n, dtype=torch.int32, device=dev),
+               commit=torch.empty(n, dtype=torch.uint8, device=dev),
+               entropy=torch.empty(n, dtype=torch.float32, device=dev),
+               n_renoised=torch.empty(1, dtype=torch.int32, device=dev),
+               rowstats=torch.empty(n, 2, dtype=torch.float32, device=dev) if want_rowstats else None,
+               n_changed=torch.empty(1, dtype=torch.int32, device=dev) if pred is not None else None,
+               n_nonfinite=torch.empty(1, dtype=torch.int32, device=dev))
+    c = sampler_cfg_c(scfg)
+    ldt = DG_BF16 if logits.dtype == torch.bfloat16 else DG_F32
+    check(L.dg_sample_renoise_noalloc(ctypes.byref(c), n, ptr(logits), ldt, ptr(out["tokens"]), ptr(out["commit"]),
+                                      ptr(out["entropy"]), ptr(out["rowstats"]), ptr(out["n_renoised"]), ptr(pred),
+                                      ptr(out["n_changed"]), ptr(out["n_nonfinite"]), stream_handle(stream)),
+          "dg_sample_renoise_noalloc")
     return out
 
 

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "dg_launch.h"
@@ -893,6 +894,38 @@ int make_rope_tabs(const dg_model_cfg *cfg, const dg_kv_cache *kv, int B, int C,
 
 }  // namespace
 
+// Built-in scratch of dg_sample_renoise_noalloc: the sampler's per-row,
+// per-vocabulary-slice partial statistics for up to kNoAllocSlots
+// (row, slice) pairs.  Each GPU holds its own copy for the life of the
+// process.  Host code never passes the array's name to a kernel (on the host
+// it is only a stand-in); it uses the device address taken once per device.
+namespace {
+constexpr size_t kNoAllocSlots = 8192 * 16;   // e.g. 8192 rows x 16 slices
+constexpr size_t kNoAllocScratchBytes = kNoAllocSlots * (4 * sizeof(float) + 2 * sizeof(int)) + 3 * 256;
+constexpr int kMaxDevices = 64;
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+void *g_scratch_dev[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, taken on the first call on
+// that device (hipGetSymbolAddress with the device current); nullptr if it
+// cannot be taken.
+void *scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_dev[dev] = p;
+  }
+  return g_scratch_dev[dev];
+}
+}  // namespace
+
 // ====================================================================== ABI
 
 extern "C" {
@@ -968,6 +1001,24 @@ int dg_sample_renoise(const dg_sampler_cfg *cfg, int n_pos, const void *logits, 
   if (n_pos < 0) return DG_ERR_SHAPE;
   if (!logits || !tok || !commit || !ent || !nre || !ws) return DG_ERR_NULL;
   if (ws_bytes < dg_sample_workspace_bytes(n_pos, cfg->vocab)) return DG_ERR_WORKSPACE;
+  Carve cv(ws);
+  return sample_impl(cfg, n_pos, logits, logits_dtype, tok, commit, ent, rowstats, nre, pred, n_changed,
+                     n_nonfinite, cv, static_cast<hipStream_t>(stream));
+}
+
+size_t dg_sample_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+int dg_sample_renoise_noalloc(const dg_sampler_cfg *cfg, int n_pos, const void *logits, int logits_dtype,
+                              int32_t *tok, uint8_t *commit, float *ent, float *rowstats, int32_t *nre,
+                              int32_t *pred, int32_t *n_changed, int32_t *n_nonfinite, void *stream) {
+  DG_TRY(check_sampler_cfg(cfg));
+  if (!dtype_ok(logits_dtype)) return DG_ERR_DTYPE;
+  if (n_pos < 0) return DG_ERR_SHAPE;
+  if (!logits || !tok || !commit || !ent || !nre) return DG_ERR_NULL;
+  // the partial statistics must fit the built-in scratch
+  if (dg_sample_workspace_bytes(n_pos, cfg->vocab) > kNoAllocScratchBytes) return DG_ERR_WORKSPACE;
+  void *ws = scratch_address();
+  if (!ws) return DG_ERR_HIP;
   Carve cv(ws);
   return sample_impl(cfg, n_pos, logits, logits_dtype, tok, commit, ent, rowstats, nre, pred, n_changed,
                      n_nonfinite, cv, static_cast<hipStream_t>(stream));

@@ -20,7 +20,9 @@
  *     the arrays of per-layer records are HOST memory.  The library never
  *     allocates or frees device memory and keeps no mutable global state;
  *     scratch memory is the caller's workspace `ws` of `ws_bytes` bytes,
- *     256-byte aligned, sized by the matching *_workspace_bytes query.
+ *     256-byte aligned, sized by the matching *_workspace_bytes query (the
+ *     one exception, dg_sample_renoise_noalloc, uses a built-in per-GPU
+ *     scratch array instead).
  *   - `stream` is a hipStream_t (NULL = the null stream).  All device work is
  *     enqueued asynchronously on it; nothing synchronises with the host.
  *   - Arguments are validated on the host before any HIP call; a failed
@@ -263,6 +265,24 @@ int dg_sample_renoise(const dg_sampler_cfg *cfg, int n_pos, const void *logits, 
                       float *rowstats_out, int32_t *n_renoised_out, int32_t *pred_inout,
                       int32_t *n_changed_out, int32_t *n_nonfinite_out, void *ws, size_t ws_bytes,
                       void *stream);
+
+/* dg_sample_renoise without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and results as
+ * dg_sample_renoise (the same kernels); the partial statistics live in a
+ * scratch array built into the library, one per GPU, held until the process
+ * ends: at most dg_sample_noalloc_max_bytes() bytes, which covers
+ * n_pos * (vocabulary slices) <= 131072 (8192 positions at any vocabulary).
+ * Larger calls return DG_ERR_WORKSPACE before any HIP call.  Nothing is
+ * allocated: the scratch address is taken once per device on the first call
+ * there (DG_ERR_HIP if that fails).  Every call on one GPU uses the same
+ * scratch, so calls that overlap on one GPU (several streams or threads at
+ * once) race; serialise them. */
+size_t dg_sample_noalloc_max_bytes(void);
+int dg_sample_renoise_noalloc(const dg_sampler_cfg *cfg, int n_pos, const void *logits, int logits_dtype,
+                              int32_t *tokens_out, uint8_t *commit_out, float *entropy_out,
+                              float *rowstats_out, int32_t *n_renoised_out, int32_t *pred_inout,
+                              int32_t *n_changed_out, int32_t *n_nonfinite_out, void *stream);
 
 /* Initial canvas: n_pos uniform random tokens (counter step word 0xFFFFFFFF;
  * aibars text-diffusion paragraph: generation starts from a noise block). */

@@ -137,6 +137,26 @@ def test_sampler_validation_codes():
     assert call(big, n=4097) == -2
 
 
+def test_sampler_noalloc_validation_codes():
+    """The allocation-free sampler rejects what the built-in scratch cannot
+    hold (and bad arguments) on the host, before any HIP call."""
+    L = B.lib()
+    p = ctypes.c_void_p(256)
+    cap = L.dg_sample_noalloc_max_bytes()
+    assert 0 < cap <= 8 << 20
+    call = lambda s, n, ldt=0: L.dg_sample_renoise_noalloc(ctypes.byref(s), n, p, ldt, p, p, p, None, p, None,
+                                                          None, None, None)
+    s = B.sampler_cfg_c(synth.sampler_cfg(262144))
+    # 16 vocabulary slices per row at V = 262144: 8192 rows fit, 8193 do not
+    assert L.dg_sample_workspace_bytes(8192, 262144) <= cap < L.dg_sample_workspace_bytes(8193, 262144)
+    assert call(s, 8193) == -4
+    assert call(s, 100000) == -4
+    assert call(s, 8, ldt=3) == -5
+    assert call(s, -1) == -2
+    assert L.dg_sample_renoise_noalloc(None, 1, p, 0, p, p, p, None, p, None, None, None, None) == -1
+    assert L.dg_sample_renoise_noalloc(ctypes.byref(s), 1, None, 0, p, p, p, None, p, None, None, None, None) == -1
+
+
 def test_workspace_queries_grow_with_tokens():
     L = B.lib()
     c = _attn_c()
