@@ -50,6 +50,32 @@ def build(verbose=False, out=OUT, defines=(), build_dir=BUILD):
     return out
 
 
+def build_host_sanitized(out_dir):
+    """A library for checking the host code: dg_api.hip (argument checks,
+    workspace carving, launch order) compiled with AddressSanitizer and
+    UndefinedBehaviorSanitizer on its host side only, linked with the kernel
+    objects of the regular build.  Returns the library path; a program that
+    loads it must itself be linked with the same sanitizers (clang)."""
+    os.makedirs(out_dir, exist_ok=True)
+    if not all(os.path.exists(os.path.join(BUILD, f + ".o")) for f in os.listdir(CSRC) if f.endswith(".hip")):
+        build()
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+    obj = os.path.join(out_dir, "dg_api_san.o")
+    cmd = [HIPCC] + FLAGS + san + ["-c", os.path.join(CSRC, "dg_api.hip"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized compile failed:\n" + r.stderr)
+    kernels = [os.path.join(BUILD, f + ".o") for f in sorted(os.listdir(CSRC))
+               if f.endswith(".hip") and f != "dg_api.hip"]
+    out = os.path.join(out_dir, "libdgstep_san.so")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out, obj] + kernels
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized link failed:\n" + r.stderr)
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)
