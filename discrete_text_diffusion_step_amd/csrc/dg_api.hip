@@ -702,17 +702,12 @@ int check_sampler_cfg(const dg_sampler_cfg *c) {
   return DG_OK;
 }
 
-int sample_impl(const dg_sampler_cfg *c, int n, const void *logits, int ldt, int32_t *tok, uint8_t *commit,
-                float *ent, float *rowstats, int32_t *nre, int32_t *pred, int32_t *n_changed, int32_t *n_nonfinite,
-                Carve &cv, hipStream_t s) {
-  const SampleWs ws = sample_carve(n, c->vocab, cv);
-  if (c->commit_rule == DG_COMMIT_SORTED_CUMULATIVE && n > kSortedMaxRows) return DG_ERR_SHAPE;
+SampleArgs sample_args(const dg_sampler_cfg *c, int n, int32_t *tok, uint8_t *commit, float *ent, float *rowstats,
+                       int32_t *nre, int32_t *pred, int32_t *n_changed, int32_t *n_nonfinite) {
   SampleArgs a;
-  a.logits = logits;
-  a.logits_bf16 = ldt == DG_BF16;
+  memset(&a, 0, sizeof(a));
   a.n_pos = n;
   a.vocab = c->vocab;
-  a.n_chunks = sample_chunks(c->vocab);
   a.inv_t = static_cast<float>(1.0 / temperature(c));
   a.tau = c->tau;
   a.final_step = c->final_step;
@@ -720,10 +715,6 @@ int sample_impl(const dg_sampler_cfg *c, int n, const void *logits, int ldt, int
   a.canvas_idx = c->canvas_idx;
   a.key0 = static_cast<uint32_t>(c->seed & 0xffffffffull);
   a.key1 = static_cast<uint32_t>(c->seed >> 32);
-  a.part = ws.part;
-  a.part_idx = ws.part_idx;
-  a.part_nf = ws.part_nf;
-  a.n_nonfinite = n_nonfinite;
   a.tokens = tok;
   a.commit = commit;
   a.entropy = ent;
@@ -733,6 +724,22 @@ int sample_impl(const dg_sampler_cfg *c, int n, const void *logits, int ldt, int
   a.token_rule = c->token_rule;
   a.pred = pred;
   a.n_changed = pred ? n_changed : nullptr;
+  a.n_nonfinite = n_nonfinite;
+  return a;
+}
+
+int sample_impl(const dg_sampler_cfg *c, int n, const void *logits, int ldt, int32_t *tok, uint8_t *commit,
+                float *ent, float *rowstats, int32_t *nre, int32_t *pred, int32_t *n_changed, int32_t *n_nonfinite,
+                Carve &cv, hipStream_t s) {
+  const SampleWs ws = sample_carve(n, c->vocab, cv);
+  if (c->commit_rule == DG_COMMIT_SORTED_CUMULATIVE && n > kSortedMaxRows) return DG_ERR_SHAPE;
+  SampleArgs a = sample_args(c, n, tok, commit, ent, rowstats, nre, pred, n_changed, n_nonfinite);
+  a.logits = logits;
+  a.logits_bf16 = ldt == DG_BF16;
+  a.n_chunks = sample_chunks(c->vocab);
+  a.part = ws.part;
+  a.part_idx = ws.part_idx;
+  a.part_nf = ws.part_nf;
   DG_HIP(launch_sampler(a, s));
   return DG_OK;
 }

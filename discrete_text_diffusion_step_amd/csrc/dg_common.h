@@ -178,6 +178,37 @@ __device__ __forceinline__ void store8(float *p, const float *f) {
   reinterpret_cast<float4 *>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
 }
 
+
+// Online softmax statistics of a set of values x (x = logit / t): m = max x,
+// Z = sum exp(x - m), S = sum exp(x - m) (x - m).  merge_row_stats folds
+// (m2, Z2, S2) into (m, Z, S); a side whose m is -inf holds no value yet.
+__device__ __forceinline__ void merge_row_stats(float &m, float &Z, float &S, float m2, float Z2, float S2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    Z = Z2;
+    S = S2;
+    return;
+  }
+  if (m2 > m) {
+    const float sc = __expf(m - m2);
+    S = sc * (S + (m - m2) * Z) + S2;
+    Z = sc * Z + Z2;
+    m = m2;
+  } else {
+    const float sc = __expf(m2 - m);
+    S = S + sc * (S2 + (m2 - m) * Z2);
+    Z = Z + sc * Z2;
+  }
+}
+
+// Keep the larger value, the lower index on ties (a NaN is never taken).
+__device__ __forceinline__ void better_of(float &bv, int &bi, float v, int i) {
+  const bool take = v > bv || (v == bv && i < bi);
+  bv = take ? v : bv;
+  bi = take ? i : bi;
+}
+
 }  // namespace dg
 
 // ------------------------------------------------------------ host launchers

@@ -64,26 +64,7 @@ __device__ __forceinline__ int32_t uniform_token(uint32_t x0, int vocab) {
   return static_cast<int32_t>((static_cast<uint64_t>(x0) * static_cast<uint64_t>(vocab)) >> 32);
 }
 
-// merge (m2, Z2, S2) into (m, Z, S); S is taken relative to each own max
-__device__ __forceinline__ void merge_stats(float &m, float &Z, float &S, float m2, float Z2, float S2) {
-  if (m2 > m) {
-    const float sc = __expf(m - m2);
-    S = sc * (S + (m - m2) * Z) + S2;
-    Z = sc * Z + Z2;
-    m = m2;
-  } else {
-    const float sc = __expf(m2 - m);
-    S = S + sc * (S2 + (m2 - m) * Z2);
-    Z = Z + sc * Z2;
-  }
-}
-
-__device__ __forceinline__ void better(float &bv, int &bi, float v, int i) {
-  if (v > bv || (v == bv && i < bi)) {
-    bv = v;
-    bi = i;
-  }
-}
+__device__ __forceinline__ void better(float &bv, int &bi, float v, int i) { better_of(bv, bi, v, i); }
 
 __device__ __forceinline__ void load_logits8(const void *p, int bf16, long long off, float *f) {
   if (bf16) load8(static_cast<const bf16_t *>(p) + off, f);
@@ -145,15 +126,7 @@ __global__ __launch_bounds__(256) void rowstats_partial_kernel(const SampleArgs 
     const float m2 = __shfl_xor(m, o, 64), Z2 = __shfl_xor(Z, o, 64), S2 = __shfl_xor(S, o, 64);
     const float bv2 = __shfl_xor(bv, o, 64);
     const int bi2 = __shfl_xor(bi, o, 64);
-    if (m2 != -INFINITY) {
-      if (m == -INFINITY) {
-        m = m2;
-        Z = Z2;
-        S = S2;
-      } else {
-        merge_stats(m, Z, S, m2, Z2, S2);
-      }
-    }
+    merge_row_stats(m, Z, S, m2, Z2, S2);
     better(bv, bi, bv2, bi2);
     nf += __shfl_xor(nf, o, 64);
   }
@@ -172,15 +145,7 @@ __global__ __launch_bounds__(256) void rowstats_partial_kernel(const SampleArgs 
     float M = sm[0][0], ZZ = sm[0][1], SS = sm[0][2], BV = sm[0][3];
     int BI = si[0];
     for (int w = 1; w < 4; ++w) {
-      if (sm[w][0] != -INFINITY) {
-        if (M == -INFINITY) {
-          M = sm[w][0];
-          ZZ = sm[w][1];
-          SS = sm[w][2];
-        } else {
-          merge_stats(M, ZZ, SS, sm[w][0], sm[w][1], sm[w][2]);
-        }
-      }
+      merge_row_stats(M, ZZ, SS, sm[w][0], sm[w][1], sm[w][2]);
       better(BV, BI, sm[w][3], si[w]);
     }
     float *p = a.part + (static_cast<long long>(row) * a.n_chunks + chunk) * 4;
@@ -218,14 +183,15 @@ __global__ __launch_bounds__(256) void sample_finalize_kernel(const SampleArgs a
     float M = p[0], Z = p[1], S = p[2], bv = p[3];
     int bi = pi[0], nf = pnf[0];
     for (int c = 1; c < a.n_chunks; ++c) {
-      merge_stats(M, Z, S, p[c * 4], p[c * 4 + 1], p[c * 4 + 2]);
+      merge_row_stats(M, Z, S, p[c * 4], p[c * 4 + 1], p[c * 4 + 2]);
       better(bv, bi, p[c * 4 + 3], pi[c]);
       nf += pnf[c];
     }
     nonfinite += nf > 0;
     // NaN logits are never a candidate; a row of NaN only proposes token 0
     if (bi < 0 || bi >= a.vocab) bi = 0;
-    const float H = __logf(Z) - S / Z;
+    // a row holding a NaN or +-inf has no defined entropy (never committed on its own)
+    const float H = nf > 0 ? NAN : __logf(Z) - S / Z;
     if (a.pred) {
       changed += a.pred[row] != bi;
       a.pred[row] = bi;
