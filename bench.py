@@ -125,6 +125,8 @@ def main():
                     help="temperature at the first step of the adaptive generation run")
     ap.add_argument("--gen-t-min", type=float, default=1.0,
                     help="temperature at the last step of the adaptive generation run")
+    ap.add_argument("--v-only", action="store_true",
+                    help="global layers keep only V (keys rebuilt from it every call; one shared key scratch)")
     ap.add_argument("--ring", action="store_true",
                     help="sliding layers keep a ring of window + 4096 rows; the prompt is committed in 4096-token chunks")
     args = ap.parse_args()
@@ -168,9 +170,11 @@ def main():
     cap = args.prompt + args.canvases * CANVAS
     chunk = 4096 if args.ring else args.prompt
     NB = args.batch
-    kvs = [B.KV(mcfg, cap, device=dev, ring_tokens=chunk if args.ring else 0) for _ in range(NB)]
+    kvs = [B.KV(mcfg, cap, device=dev, ring_tokens=chunk if args.ring else 0, v_only_global=args.v_only)
+           for _ in range(NB)]
     kv = kvs[0]
-    kv_bytes = sum(t.numel() * t.element_size() for k in kvs for t in k.k + k.v)
+    kv_bytes = sum(t.numel() * t.element_size() for k in kvs
+                   for t in {id(x): x for x in k.k + k.v}.values())   # a shared key scratch counts once
     log(f"kv cache: {kv_bytes / 1e9:.2f} GB ({'ring' if args.ring else 'plain'} sliding layers, {NB} sequence(s))")
     ws_step = (B.dg_workspace_bytes_batch(model.c_cfg, NB, CANVAS) if NB > 1
                else B.dg_workspace_bytes(model.c_cfg, CANVAS, 0))
@@ -281,7 +285,8 @@ def main():
                    "canvas": CANVAS, "committed_rows": P, "params": n_params, "adaptive_stop_in_timed_loop": False,
                    "canvases_per_forward": NB,
                    "expert_weights": "fp8_e4m3 (row scales)" if fp8 else "bf16",
-                   "kv_cache": {"sliding": "ring" if args.ring else "plain", "bytes": kv_bytes},
+                   "kv_cache": {"sliding": "ring" if args.ring else "plain",
+                                "global": "v-only" if args.v_only else "plain", "bytes": kv_bytes},
                    "sampler": {"commit_rule": args.commit_rule, "token_rule": args.token_rule,
                                "stop_rule": args.stop_rule}},
         "eff_tok_s": eff, "tokens_per_forward": {"full_schedule": round(tpf_full, 3), "pages": 20},

@@ -38,7 +38,8 @@ class AttnW(ctypes.Structure):
 
 
 class KVLayer(ctypes.Structure):
-    _fields_ = [("k", c_void), ("v", c_void), ("capacity", c_int), ("kv_len", c_int), ("ring", c_int)]
+    _fields_ = [("k", c_void), ("v", c_void), ("capacity", c_int), ("kv_len", c_int), ("ring", c_int),
+                ("v_only", c_int)]
 
 
 class MoeCfg(ctypes.Structure):
@@ -221,15 +222,16 @@ def dg_status_string(status):
     return lib().dg_status_string(status).decode()
 
 
-def dg_attn_layer(cfg, w, k_cache, v_cache, kv_len, x, causal, stream=None, ring=False):
+def dg_attn_layer(cfg, w, k_cache, v_cache, kv_len, x, causal, stream=None, ring=False, v_only=False):
     """x <- x + Attention(x) in place; returns the new committed length.
     k_cache [Hkv][capacity][d_h]; v_cache transposed, [Hkv][d_h][capacity];
-    ring: position m at row m mod capacity (sliding layers)."""
+    ring: position m at row m mod capacity (sliding layers); v_only: the
+    keys of the committed positions are rebuilt from v_cache into k_cache."""
     L = lib()
     c = attn_cfg_c(cfg)
     n = x.shape[0]
     kv = KVLayer(ptr(k_cache), ptr(v_cache), k_cache.shape[1] if k_cache is not None else 0, kv_len,
-                 1 if ring else 0)
+                 1 if ring else 0, 1 if v_only else 0)
     nb = L.dg_attn_workspace_bytes(ctypes.byref(c), n)
     ws = workspace(nb, x.device)
     check(L.dg_attn_layer(ctypes.byref(c), ctypes.byref(attn_w_c(w)), ctypes.byref(kv), n, int(causal), ptr(x),
@@ -422,12 +424,15 @@ class KV:
     """Per-layer caches, K [Hkv][capacity][d_h] and V transposed [Hkv][d_h][capacity],
     and the C record over them.  ring_tokens > 0 gives the sliding layers a
     ring of ring_capacity(window, ring_tokens) rows instead of `capacity`
-    (every call then adds at most ring_tokens positions)."""
+    (every call then adds at most ring_tokens positions).  v_only_global:
+    the global layers keep only V; one K scratch is shared by all of them
+    (their keys are rebuilt from V by every call)."""
 
-    def __init__(self, mcfg, capacity, device="cuda", tensors=None, ring_tokens=0):
+    def __init__(self, mcfg, capacity, device="cuda", tensors=None, ring_tokens=0, v_only_global=False):
         L = mcfg["n_layers"]
         dt = torch.bfloat16 if mcfg["dtype"] == "bf16" else torch.float32
-        self.k, self.v, caps, rings = [], [], [], []
+        self.k, self.v, caps, rings, vonly = [], [], [], [], []
+        k_scratch = None
         for l in range(L):
             glob = (l % mcfg["global_every"]) == mcfg["global_every"] - 1
             c = mcfg["global"] if glob else mcfg["sliding"]
@@ -435,13 +440,20 @@ class KV:
             cap = ring_capacity(c["window"], ring_tokens) if ring else capacity
             caps.append(cap)
             rings.append(1 if ring else 0)
+            vo = bool(v_only_global) and glob
+            vonly.append(1 if vo else 0)
             if tensors is not None:
                 self.k.append(tensors[0][l])
                 self.v.append(tensors[1][l])
             else:
-                self.k.append(torch.zeros(c["n_kv_heads"], cap, c["head_dim"], dtype=dt, device=device))
+                if vo:
+                    if k_scratch is None:
+                        k_scratch = torch.zeros(c["n_kv_heads"], cap, c["head_dim"], dtype=dt, device=device)
+                    self.k.append(k_scratch)
+                else:
+                    self.k.append(torch.zeros(c["n_kv_heads"], cap, c["head_dim"], dtype=dt, device=device))
                 self.v.append(torch.zeros(c["n_kv_heads"], c["head_dim"], cap, dtype=dt, device=device))
-        self._layers = (KVLayer * L)(*[KVLayer(ptr(self.k[l]), ptr(self.v[l]), caps[l], 0, rings[l])
+        self._layers = (KVLayer * L)(*[KVLayer(ptr(self.k[l]), ptr(self.v[l]), caps[l], 0, rings[l], vonly[l])
                                        for l in range(L)])
         self.c = KVCache(self._layers, L)
         self.ring_tokens = ring_tokens

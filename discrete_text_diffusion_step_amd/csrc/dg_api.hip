@@ -332,6 +332,10 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *const *kvs,
     nr.eps = c->rms_eps;
     nr.sqrt_dh = static_cast<float>(sqrt(static_cast<double>(dh)));
     nr.v_unit_rms = c->v_unit_rms;
+    if (kv->v_only)   // the committed keys, rebuilt from the committed values into the k scratch
+      DG_HIP(launch_k_rebuild(dt, kv->v, static_cast<long long>(dh) * kv->capacity, kv->capacity, P, Hkv, dh,
+                              w->k_norm, c->rope_base, rope_rot(c), kv->k, static_cast<long long>(kv->capacity) * dh,
+                              s));
     if (rts && rts[b].tab && rts[b].pos0 == P) {
       nr.rope_tab = rts[b].tab;
     } else {
@@ -415,6 +419,9 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *kv, int n, 
 // window and the new rows to fit at once.
 int check_kv_room(const dg_attn_cfg *c, const dg_kv_layer *kv, int n) {
   if (kv->ring != 0 && kv->ring != 1) return DG_ERR_SHAPE;
+  if (kv->v_only != 0 && kv->v_only != 1) return DG_ERR_SHAPE;
+  // keys rebuilt from values: only where K = RoPE(k_norm * V) holds
+  if (kv->v_only && (kv->ring || c->layer_type != 1 || !c->shared_kv || !c->v_unit_rms)) return DG_ERR_UNSUPPORTED;
   if (kv->ring) {
     if (c->layer_type != 0 || c->window <= 0 || kv->capacity % 32) return DG_ERR_UNSUPPORTED;
     if (kv->capacity < c->window + n) return DG_ERR_CAPACITY;

@@ -72,6 +72,12 @@ hipError_t launch_norm_rope(const NormRopeArgs &a, int dtype, hipStream_t s);
 // tab[j][t] = (cos, sin) of angle (pos0 + j) * base^(-2t/dh), fp64 angle; t >= n_rot: (1, 0)
 hipError_t launch_rope_table(int pos0, int n_tok, int dh, double base, int n_rot, float2 *tab, hipStream_t s);
 hipError_t launch_attention(const AttnArgs &a, int dtype, int dh, hipStream_t s);
+// k[h][m][:] = RoPE_m(k_norm * V[h][m][:]) for positions m < n_pos, read from
+// the transposed value cache vt[h][d][m] (vt_hs elements between heads, row
+// pitch vt_ld); split-half rotation of the first n_rot frequencies, angles in
+// fp64 as in launch_rope_table.
+hipError_t launch_k_rebuild(int dtype, const void *vt, long long vt_hs, int vt_ld, int n_pos, int Hkv, int dh,
+                            const void *k_norm, double base, int n_rot, void *k, long long k_hs, hipStream_t s);
 // dst[h][d][col0 + j] = src[h][j][d] for j < n (values to the transposed layout);
 // ring > 0: column (col0 + j) mod ring
 hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh, void *dst, long long dst_hs,

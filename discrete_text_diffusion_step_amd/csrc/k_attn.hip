@@ -1110,6 +1110,137 @@ hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh
   return hipGetLastError();
 }
 
+// cos/sin of angle th >= 0: reduced modulo 2 pi in fp64 (at th < 2^20 the
+// reduction error is below 1e-9 rad), then fp32 sincos on [-pi, pi].
+__device__ __forceinline__ float2 cos_sin_reduced(double th) {
+  const double q = rint(th * 0.15915494309189535);   // th / (2 pi)
+  const float r = static_cast<float>(fma(-q, 6.283185307179586, th));
+  float s, c;
+  sincosf(r, &s, &c);
+  return make_float2(c, s);
+}
+
+// Keys rebuilt from the transposed value cache (layers whose keys and values
+// share one projection): K[m] = RoPE_m(gamma * V[m]).  A workgroup takes 64
+// positions of one head and walks the frequency pairs 64 at a time: the
+// value columns t and t + d/2 of its positions go through LDS (coalesced
+// reads of the transposed rows), then each thread writes 8 consecutive key
+// elements of one position and both halves.  The block's frequencies are
+// computed once (fp64) and each angle p * f_t is reduced in fp64 before an
+// fp32 sincos, so the pass stays bound by its memory traffic.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rebuild_kernel(const T *vt, long long vt_hs, int vt_ld, int n_pos, int dh,
+                                                        const T *gamma, double base, int n_rot, T *k, long long k_hs) {
+  constexpr int NP = 64, NT = 64;
+  __shared__ float tile[2][NT][NP + 1];   // [half][t][position]
+  __shared__ double freq[NT];
+  const int h = blockIdx.y, m0 = blockIdx.x * NP, half = dh >> 1;
+  const T *v = vt + h * vt_hs;
+  T *kh = k + h * k_hs;
+  const int tid = threadIdx.x;
+  for (int t0 = 0; t0 < half; t0 += NT) {
+    if (tid < NT) freq[tid] = pow(base, -2.0 * static_cast<double>(t0 + tid) / static_cast<double>(dh));
+    // columns t0.. t0+NT-1 and their partners, 64 positions each
+    for (int e = tid; e < 2 * NT * NP; e += 256) {
+      const int hf = e / (NT * NP), r = e % (NT * NP), t = r / NP, p = r % NP;
+      const int m = m0 + p, d = t0 + t + hf * half;
+      tile[hf][t][p] = (m < n_pos && t0 + t < half) ? to_f32<T>(v[static_cast<long long>(d) * vt_ld + m]) : 0.f;
+    }
+    __syncthreads();
+    // thread: position p, 8 consecutive t of the block
+    for (int e = tid; e < NP * (NT / 8); e += 256) {
+      const int p = e / (NT / 8), tb = (e % (NT / 8)) * 8;
+      const int m = m0 + p;
+      if (m < n_pos && t0 + tb < half) {
+        float lo[8], hi[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = t0 + tb + j;
+          float a = tile[0][tb + j][p] * to_f32<T>(gamma[t]);
+          float b = tile[1][tb + j][p] * to_f32<T>(gamma[t + half]);
+          if (t < n_rot) {
+            const float2 cs = cos_sin_reduced(static_cast<double>(m) * freq[tb + j]);
+            const float o0 = a * cs.x - b * cs.y, o1 = b * cs.x + a * cs.y;
+            a = o0;
+            b = o1;
+          }
+          lo[j] = a;
+          hi[j] = b;
+        }
+        T *row = kh + static_cast<long long>(m) * dh;
+        if constexpr (sizeof(T) == 2) {
+          store8(row + t0 + tb, lo);
+          store8(row + t0 + tb + half, hi);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            row[t0 + tb + j] = lo[j];
+            row[t0 + tb + j + half] = hi[j];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// bf16 form for d_h = 512 (the global layers): a workgroup issues every
+// 16-byte load of its 64 positions (512 value rows x 128 bytes) before it
+// stores any to LDS, so it waits on memory once, then each thread writes
+// 16-byte chunks of key rows.  Positions past n_pos in the last block are
+// read as a clamped in-range column and not written.
+constexpr int kRebuildDh = 512;
+__global__ __launch_bounds__(256) void k_rebuild16_kernel(const bf16_t *vt, long long vt_hs, int vt_ld, int n_pos,
+                                                          const bf16_t *gamma, double base, int n_rot, bf16_t *k,
+                                                          long long k_hs) {
+  constexpr int NP = 64, DH = kRebuildDh, HALF = DH / 2, PITCH = NP + 8;   // 16 bytes of padding per row
+  __shared__ __attribute__((aligned(16))) bf16_t tile[DH][PITCH];          // [d][position]
+  __shared__ double freq[HALF];
+  const int h = blockIdx.y, m0 = blockIdx.x * NP, tid = threadIdx.x;
+  const bf16_t *v = vt + h * vt_hs;
+  // 512 rows x 8 chunks of 8 positions: 16 loads per thread, all in flight at once
+  uint4 r[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = tid + 256 * i, d = c >> 3, p0 = (c & 7) * 8;
+    const int m = m0 + p0 < n_pos ? m0 + p0 : 0;   // n_pos, m0 and p0 are multiples of 8 or clamped in range
+    r[i] = *reinterpret_cast<const uint4 *>(v + static_cast<long long>(d) * vt_ld + m);
+  }
+  for (int t = tid; t < HALF; t += 256)
+    freq[t] = t < n_rot ? pow(base, -2.0 * static_cast<double>(t) / static_cast<double>(DH)) : 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = tid + 256 * i, d = c >> 3, p0 = (c & 7) * 8;
+    *reinterpret_cast<uint4 *>(&tile[d][p0]) = r[i];
+  }
+  __syncthreads();
+  // thread: one position, 8 consecutive t of a 64-wide t block, both halves
+  bf16_t *kh = k + h * k_hs;
+  for (int e = tid; e < NP * (HALF / 8); e += 256) {
+    const int p = e & (NP - 1), tb = (e >> 6) * 8;
+    const int m = m0 + p;
+    if (m >= n_pos) continue;
+    float lo[8], hi[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = tb + j;
+      float a = bf16_to_f32(tile[t][p]) * bf16_to_f32(gamma[t]);
+      float b = bf16_to_f32(tile[t + HALF][p]) * bf16_to_f32(gamma[t + HALF]);
+      if (t < n_rot) {
+        const float2 cs = cos_sin_reduced(static_cast<double>(m) * freq[t]);
+        const float o0 = a * cs.x - b * cs.y, o1 = b * cs.x + a * cs.y;
+        a = o0;
+        b = o1;
+      }
+      lo[j] = a;
+      hi[j] = b;
+    }
+    bf16_t *row = kh + static_cast<long long>(m) * DH;
+    store8(row + tb, lo);
+    store8(row + tb + HALF, hi);
+  }
+}
+
 // Workgroups that fill the chip once: one per CU where the double-buffered
 // 512-wide tiles take most of the LDS, two per CU otherwise.
 int attn_target_workgroups(int dtype, int dh) {
@@ -1159,6 +1290,25 @@ hipError_t launch_rope_table(int pos0, int n_tok, int dh, double base, int n_rot
   const long long n = static_cast<long long>(n_tok) * (dh / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, pos0, n_tok,
                      dh, base, n_rot, tab);
+  return hipGetLastError();
+}
+
+hipError_t launch_k_rebuild(int dtype, const void *vt, long long vt_hs, int vt_ld, int n_pos, int Hkv, int dh,
+                            const void *k_norm, double base, int n_rot, void *k, long long k_hs, hipStream_t s) {
+  if (n_pos <= 0) return hipSuccess;
+  if (dh % 16) return hipErrorInvalidValue;   // 8-element stores in each half
+  const dim3 grid((n_pos + 63) / 64, Hkv);
+  if (dtype == DG_BF16 && dh == kRebuildDh && vt_ld % 8 == 0 && vt_hs % 8 == 0) {
+    hipLaunchKernelGGL(k_rebuild16_kernel, grid, dim3(256), 0, s, static_cast<const bf16_t *>(vt), vt_hs, vt_ld, n_pos,
+                       static_cast<const bf16_t *>(k_norm), base, n_rot, static_cast<bf16_t *>(k), k_hs);
+    return hipGetLastError();
+  }
+  if (dtype == DG_BF16)
+    hipLaunchKernelGGL(k_rebuild_kernel<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t *>(vt), vt_hs, vt_ld,
+                       n_pos, dh, static_cast<const bf16_t *>(k_norm), base, n_rot, static_cast<bf16_t *>(k), k_hs);
+  else
+    hipLaunchKernelGGL(k_rebuild_kernel<float>, grid, dim3(256), 0, s, static_cast<const float *>(vt), vt_hs, vt_ld,
+                       n_pos, dh, static_cast<const float *>(k_norm), base, n_rot, static_cast<float *>(k), k_hs);
   return hipGetLastError();
 }
 

@@ -116,6 +116,15 @@ typedef struct {
                         * window + n_tok; kv_len counts all committed positions
                         * (aitrends glossary Sliding-window: only the last
                         * window rows are ever read). */
+  int v_only;          /* 0: k holds the layer's keys.  1 (global layers with
+                        * shared_kv and v_unit_rms only; not with ring): only
+                        * v is kept.  Since W_v = W_k, the stored value is the
+                        * unit-RMS raw key and K = RoPE_p(k_norm * V) (aitrends
+                        * attention paragraph: KV cache saving / reconstruction
+                        * with W_v = W_k), so every call rebuilds the keys of
+                        * positions [0, kv_len) from v into k, which is then
+                        * scratch of the same [Hkv][capacity][d_h] shape that
+                        * all v_only layers of a stack may share. */
 } dg_kv_layer;
 
 /* Workspace bytes for dg_attn_layer with at most n_tok tokens per call. */

@@ -96,6 +96,14 @@ def test_attn_validation_codes():
     c = _attn_c()
     c.dtype = 7
     assert call(c) == -5
+    # keys rebuilt from values only where W_v = W_k and V is unit-RMS (global layers), never in a ring
+    vo = B.KVLayer(ctypes.c_void_p(256), ctypes.c_void_p(256), 4096, 2048, 0, 1)
+    assert call(_attn_c(), kvv=vo) == -3
+    g = B.attn_cfg_c(synth.global_cfg())
+    vo_ring = B.KVLayer(ctypes.c_void_p(256), ctypes.c_void_p(256), 4096, 2048, 1, 1)
+    assert call(g, kvv=vo_ring) == -3
+    bad = B.KVLayer(ctypes.c_void_p(256), ctypes.c_void_p(256), 4096, 2048, 0, 2)
+    assert call(g, kvv=bad) == -2
     # zero tokens is a no-op
     assert call(_attn_c(), n=0) == 0
 

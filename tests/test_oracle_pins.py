@@ -386,6 +386,28 @@ def test_selfcond_adds_swiglu_of_u_by_hand():
     assert np.max(np.abs(x - E[tok])) > 1e-2
 
 
+def test_shared_kv_keys_are_rotated_scaled_values():
+    """The identity behind a value-only cache in W_v = W_k layers ([AIT]
+    attention paragraph: KV saving / reconstruction): the stored key equals
+    the split-half rotation, at the key's own position, of gamma_k times the
+    stored value, on every dim (float64, no rounding)."""
+    cfg, w, g = tiny_layer(1)
+    x = np64(synth.hidden_states(9, cfg["hidden"], g, "f32"))
+    pos0 = 1234
+    _, k, v = O.project_qkv(cfg, w, x, pos0, "f32")
+    dh, half = cfg["head_dim"], cfg["head_dim"] // 2
+    keep = int(round(cfg["rotary_factor"] * half))
+    for j in range(9):
+        p = pos0 + j
+        for t in range(half):
+            f = cfg["rope_base"] ** (-2.0 * t / dh) if t < keep else 0.0
+            c, s_ = math.cos(p * f), math.sin(p * f)
+            a = w["k_norm"][t] * v[:, j, t]
+            b = w["k_norm"][t + half] * v[:, j, t + half]
+            np.testing.assert_allclose(k[:, j, t], a * c - b * s_, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(k[:, j, t + half], b * c + a * s_, rtol=1e-12, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------
 # MoE
 # ----------------------------------------------------------------------------
