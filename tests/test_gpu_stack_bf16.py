@@ -88,6 +88,7 @@ class HostLayers:
         return len(self.layers)
 
     def __getitem__(self, l):
+        say(f"[stack]   oracle reads layer {l}")   # a progress line per layer of the float64 oracle
         return {k: (v.float().numpy() if isinstance(v, torch.Tensor) else v) for k, v in self.layers[l].items()}
 
 
