@@ -102,6 +102,88 @@ def cpu_baseline(mcfg, P, budget_note):
             "seconds_measured": round(4 * times["sliding"] + 2 * times["global"] + times["head"], 2)}
 
 
+def variants(args, mcfg, w, model, kv, P, cap, ws, K=20, warmup=2):
+    """The default run's extra lines, timed like the main one (warmup, then K
+    steps between synchronisations): the same step with 8 canvases per
+    forward (8 sequences, each with its own prompt and KV cache), then with
+    the expert weights quantised to OCP e4m3 in place (the bf16 expert
+    weights are released; run last)."""
+    import copy
+
+    import torch
+
+    from discrete_text_diffusion_step_amd import binding as B
+    from discrete_text_diffusion_step_amd import profiling
+    from discrete_text_diffusion_step_amd import synth
+    dev = "cuda"
+    V, D = mcfg["vocab"], mcfg["hidden"]
+    out = {}
+
+    def timed(fn, timer=None):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        if timer is not None:
+            timer.__enter__()
+        t0 = time.perf_counter()
+        for i in range(K):
+            fn(i)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if timer is not None:
+            timer.__exit__(None, None, None)
+        return el
+
+    def scfg(i, b):
+        return dict(synth.sampler_cfg(V, n_steps=48, step=i % 48, canvas_idx=b, final_step=(i % 48 == 47)),
+                    commit_rule=args.commit_rule, token_rule=args.token_rule)
+
+    # 8 canvases per forward
+    NB = 8
+    kv.set_len(P)
+    kvs = [kv] + [B.KV(mcfg, cap, device=dev) for _ in range(NB - 1)]
+    for b in range(1, NB):
+        B.dg_commit_canvas(model, kvs[b], synth.tokens(P, V, synth.generator(2 + b, dev), device=dev), ws=ws)
+    wsb = torch.empty(B.dg_workspace_bytes_batch(model.c_cfg, NB, CANVAS), dtype=torch.uint8, device=dev)
+    canvas = B.Canvas(CANVAS, D, "bf16", device=dev, n_canvas=NB)
+    for b in range(NB):
+        canvas.tokens[b * CANVAS:(b + 1) * CANVAS].copy_(B.dg_canvas_noise(CANVAS, V, 1, b, device=dev))
+    el = timed(lambda i: B.dg_canvas_step_batch(model, kvs, canvas, [scfg(i, b) for b in range(NB)], ws=wsb))
+    out["canvases_8"] = {"canvas_steps_per_s": round(NB * K / el, 2), "ms_per_forward": round(el * 1e3 / K, 3),
+                         "steps": K, "warmup": warmup, "committed_rows": P,
+                         "note": "one forward denoises 8 canvases of 256 tokens (8 sequences, 8 KV caches)"}
+    log(f"8 canvases per forward: {out['canvases_8']}")
+    del kvs, wsb, canvas
+    torch.cuda.empty_cache()
+
+    # fp8 e4m3 expert weights (row scales), one canvas per forward
+    mc8 = copy.deepcopy(mcfg)
+    mc8["moe"]["expert_format"] = "fp8_e4m3"
+    for l in range(len(w["moe"])):
+        w["moe"][l] = B.quantize_moe_weights(w["moe"][l])
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    model8 = B.Model(mc8, w)
+    kv.set_len(P)
+    canvas = B.Canvas(CANVAS, D, "bf16", device=dev)
+    canvas.tokens.copy_(B.dg_canvas_noise(CANVAS, V, 1, 0, device=dev))
+    timer = B.kernel_timer("moe_gateup", capacity=K * mcfg["n_layers"] // 31 + 8, every=31)
+    el = timed(lambda i: B.dg_canvas_step(model8, kv, canvas, scfg(i, 0), ws=ws), timer)
+    durs = timer.durations_ms()
+    avg_ms = sum(durs) / len(durs)
+    nbytes = gateup_bytes(mc8, CANVAS)
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    out["fp8_experts"] = {
+        "steps_per_s": round(K / el, 3), "ms_per_step": round(el * 1e3 / K, 4), "steps": K, "warmup": warmup,
+        "expert_weights": "fp8_e4m3 (row scales), widened to bf16 in registers",
+        "roofline": {"kernel": "moe expert gate/up (grouped MFMA GEMM + SwiGLU, fp8 e4m3 weights widened to bf16)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiling.read_traffic(fp8=True),
+                     "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": nbytes, "launches": len(durs)}}
+    log(f"fp8 expert weights: {out['fp8_experts']}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,13 +209,15 @@ def main():
                     help="temperature at the last step of the adaptive generation run")
     ap.add_argument("--v-only", action="store_true",
                     help="global layers keep only V (keys rebuilt from it every call; one shared key scratch)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the extra measurements of the default run (8 canvases per forward; fp8 expert weights)")
     ap.add_argument("--ring", action="store_true",
                     help="sliding layers keep a ring of window + 4096 rows; the prompt is committed in 4096-token chunks")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "multi-GPU runs are not part of this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the canvas step has no multi-GPU form", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -294,6 +378,8 @@ def main():
         "roofline": roof,
         "generation": gen,
     }
+    if not args.no_variants and NB == 1 and not fp8 and not args.ring and not args.v_only:
+        result["variants"] = variants(args, mcfg, w, model, kv, P, cap, ws)
     if not args.no_cpu_baseline and not fp8:
         log("cpu baseline (oracle sample)...")
         result["cpu_baseline"] = cpu_baseline(mcfg, P, "about 10-30 s of CPU work")

@@ -316,16 +316,21 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *const *kvs,
     nr.v_off = c->shared_kv ? p.Nq : p.Nq + p.Nk;
     nr.q_norm = w->q_norm;
     nr.k_norm = w->k_norm;
-    // This call's K rows go to the cache at rows [P, P + C); its V rows go to
-    // the workspace and are then written transposed into cache columns
-    // [P, P + C).  Decode uses those rows as scratch (kv_len stays P); encode
-    // keeps them and advances kv_len.
+    // This call's K rows go to the cache at rows [P, P + C), its V rows
+    // transposed into cache columns [P, P + C).  Decode uses those rows as
+    // scratch (kv_len stays P); encode keeps them and advances kv_len.
     nr.k_dst = kv->k;
     nr.k_head_stride = static_cast<long long>(kv->capacity) * dh;
     nr.k_row0 = P;
     nr.k_ring = kv->ring ? kv->capacity : 0;
     nr.v_dst = vrows_b;
     nr.v_head_stride = static_cast<long long>(C) * dh;
+    const long long vt_cache_hs = static_cast<long long>(dh) * kv->capacity;
+    nr.vt_dst = kv->v;
+    nr.vt_hs = vt_cache_hs;
+    nr.vt_ld = kv->capacity;
+    nr.vt_col0 = P;
+    nr.vt_ring = kv->ring ? kv->capacity : 0;
     nr.pos0 = P;
     nr.rope_base = c->rope_base;
     nr.n_rot = rope_rot(c);
@@ -344,9 +349,6 @@ int attn_impl(const dg_attn_cfg *c, const dg_attn_w *w, dg_kv_layer *const *kvs,
       nr.rope_tab = tab;
     }
     DG_HIP(launch_norm_rope(nr, dt, s));
-    const long long vt_cache_hs = static_cast<long long>(dh) * kv->capacity;
-    DG_HIP(launch_v_transpose(dt, vrows_b, C, Hkv, dh, kv->v, vt_cache_hs, kv->capacity, P, s,
-                              kv->ring ? kv->capacity : 0));
 
     AttnArgs at;
     at.q = qkv_b;
@@ -1312,6 +1314,11 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
       nr.k_ring = KL.ring ? KL.capacity : 0;
       nr.v_dst = aw.v_rows;
       nr.v_head_stride = static_cast<long long>(n) * ac->head_dim;
+      nr.vt_dst = KL.v;
+      nr.vt_hs = static_cast<long long>(ac->head_dim) * KL.capacity;
+      nr.vt_ld = KL.capacity;
+      nr.vt_col0 = KL.kv_len;
+      nr.vt_ring = KL.ring ? KL.capacity : 0;
       nr.pos0 = KL.kv_len;
       nr.rope_base = ac->rope_base;
       nr.n_rot = rope_rot(ac);
@@ -1326,9 +1333,6 @@ int dg_commit_canvas(const dg_model_cfg *cfg, const dg_model_w *w, dg_kv_cache *
         nr.rope_tab = aw.rope_tab;
       }
       DG_HIP(launch_norm_rope(nr, dt, s));
-      DG_HIP(launch_v_transpose(dt, aw.v_rows, n, ac->n_kv_heads, ac->head_dim, KL.v,
-                                static_cast<long long>(ac->head_dim) * KL.capacity, KL.capacity, KL.kv_len, s,
-                                KL.ring ? KL.capacity : 0));
       KL.kv_len += n;
       break;
     }

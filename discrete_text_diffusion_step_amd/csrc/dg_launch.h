@@ -23,6 +23,13 @@ struct NormRopeArgs {
   int v_unit_rms;
   // [n_tok][dh/2] (cos, sin) of the rotation angles (launch_rope_table)
   const float2 *rope_tab = nullptr;
+  // the transposed value cache vt[h][d][col] (vt_hs elements between heads,
+  // row pitch vt_ld): token j goes to column vt_col0 + j (mod vt_ring when
+  // vt_ring > 0).  launch_norm_rope writes the V heads there, straight from
+  // the projection where the shapes allow it, else through v_dst.
+  void *vt_dst = nullptr;
+  long long vt_hs = 0;
+  int vt_ld = 0, vt_col0 = 0, vt_ring = 0;
 };
 
 struct AttnArgs {
@@ -68,6 +75,9 @@ struct SampleArgs {
 // rows the sorted cumulative commit rule handles (one workgroup, LDS)
 constexpr int kSortedMaxRows = 4096;
 
+// q heads normed and rotated in place, k heads to the key cache, v heads to
+// the transposed value cache (vt_dst; v_dst is the row buffer of the
+// two-pass form taken when the fused one does not apply)
 hipError_t launch_norm_rope(const NormRopeArgs &a, int dtype, hipStream_t s);
 // tab[j][t] = (cos, sin) of angle (pos0 + j) * base^(-2t/dh), fp64 angle; t >= n_rot: (1, 0)
 hipError_t launch_rope_table(int pos0, int n_tok, int dh, double base, int n_rot, float2 *tab, hipStream_t s);
@@ -82,6 +92,11 @@ hipError_t launch_k_rebuild(int dtype, const void *vt, long long vt_hs, int vt_l
 // ring > 0: column (col0 + j) mod ring
 hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh, void *dst, long long dst_hs,
                               int dst_ld, int col0, hipStream_t s, int ring = 0);
+// 1: the V heads go from the projection to the transposed cache inside the
+// norm/RoPE launch (0: through the row buffer and a transpose launch)
+#ifndef DG_NORM_ROPE_VT
+#define DG_NORM_ROPE_VT 1
+#endif
 // Workgroups the split-KV attention grid aims for: kernels whose LDS tiles
 // exceed 80 KB run one workgroup per CU, the others two.
 #ifndef DG_ATTN_PAIR

@@ -42,15 +42,12 @@ __global__ __launch_bounds__(256) void rope_table_kernel(int pos0, int n_tok, in
 // One wave per (token, head item): items are the q heads, then the k heads
 // (normed, rotated, written to the cache), then the v heads (unit-RMS in
 // global layers, written to the row buffer).  Angles come from the table.
+// Items at or past `items` are left alone.
 template <typename T>
-__global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
-  const int j = blockIdx.x;
+__device__ __forceinline__ void norm_rope_item(const NormRopeArgs &a, int j, int it, int items, int lane) {
   const int half = a.dh >> 1;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   T *row = static_cast<T *>(a.qkv) + static_cast<long long>(j) * a.ld;
   const float2 *tab = a.rope_tab + static_cast<long long>(j) * half;
-  const int items = a.Hq + 2 * a.Hkv;
-  const int it = blockIdx.y * 4 + wave;
   if (it < items) {
     const T *src;
     const T *w = nullptr;
@@ -164,6 +161,118 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
       }
     }
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void norm_rope_kernel(const NormRopeArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  norm_rope_item<T>(a, blockIdx.x, blockIdx.y * 4 + wave, a.Hq + 2 * a.Hkv, threadIdx.x & 63);
+}
+
+// V heads straight to the transposed cache: one workgroup per (kv head,
+// token tile of 32*RH tokens).  All DH/64 column blocks of the tile's rows
+// are loaded first (8 lanes per 128-byte row segment, rows t/8 + 32r), the
+// unit-RMS scale of each row (global layers) comes from an 8-lane sum, and
+// each 64-wide column block is turned around in an LDS tile (two buffers,
+// one barrier per block) and stored as 64 dimension rows of 32*RH tokens
+// (16-byte stores).  RH * NQ = 8 keeps the rows in 32 registers a thread.
+// vt_col0, vt_ld, vt_hs and vt_ring are multiples of 8, so an 8-token chunk
+// never wraps the ring.
+template <int NQ, int RH>
+__device__ __forceinline__ void v_tile_to_cache(const NormRopeArgs &a, int h, int j0, bf16_t (*tile)[64][72]) {
+  constexpr int DH = 64 * NQ, TJ = 32 * RH, CH = TJ / 8;   // tokens per tile, 8-token chunks per dimension row
+  const int tid = threadIdx.x;
+  const int lr = tid >> 3, lc = tid & 7;     // row lr (+32r), 16-byte chunk lc of each 64-wide block
+  const bf16_t *base = static_cast<const bf16_t *>(a.qkv) + a.v_off + h * DH;
+  uint4 x[RH][NQ];
+#pragma unroll
+  for (int r = 0; r < RH; ++r) {
+    const int j = j0 + lr + 32 * r;
+    const bf16_t *src = base + static_cast<long long>(j < a.n_tok ? j : j0) * a.ld + lc * 8;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) x[r][q] = *reinterpret_cast<const uint4 *>(src + 64 * q);
+  }
+  float scale[RH];
+#pragma unroll
+  for (int r = 0; r < RH; ++r) scale[r] = 1.0f;
+  if (a.v_unit_rms) {
+#pragma unroll
+    for (int r = 0; r < RH; ++r) {
+      float ss = 0.f;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const uint32_t u[4] = {x[r][q].x, x[r][q].y, x[r][q].z, x[r][q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __uint_as_float(u[e] << 16), hi = __uint_as_float(u[e] & 0xffff0000u);
+          ss += lo * lo + hi * hi;
+        }
+      }
+      ss += __shfl_xor(ss, 1, 64);
+      ss += __shfl_xor(ss, 2, 64);
+      ss += __shfl_xor(ss, 4, 64);
+      scale[r] = a.sqrt_dh / (sqrtf(ss) + a.eps);
+    }
+  }
+  bf16_t *o = static_cast<bf16_t *>(a.vt_dst) + h * a.vt_hs;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    bf16_t (*tl)[72] = tile[q & 1];
+#pragma unroll
+    for (int r = 0; r < RH; ++r) {
+      uint4 v = x[r][q];
+      if (a.v_unit_rms) {
+        uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __uint_as_float(u[e] << 16) * scale[r];
+          const float hi = __uint_as_float(u[e] & 0xffff0000u) * scale[r];
+          u[e] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+        }
+        v = make_uint4(u[0], u[1], u[2], u[3]);
+      }
+      *reinterpret_cast<uint4 *>(&tl[lr + 32 * r][lc * 8]) = v;
+    }
+    __syncthreads();   // this block's tile written; the block before last (other buffer) is read out
+#pragma unroll
+    for (int i = 0; i < RH; ++i) {
+      const int c = tid + 256 * i;          // 64 * CH chunks: 64 d rows x CH chunks of 8 tokens
+      const int dd = c / CH, jc = (c % CH) * 8;
+      const int j = j0 + jc;
+      if (j >= a.n_tok) continue;
+      const long long orow = static_cast<long long>(64 * q + dd) * a.vt_ld;
+      if (j + 8 <= a.n_tok) {
+        const int col = a.vt_ring ? (a.vt_col0 + j) % a.vt_ring : a.vt_col0 + j;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = static_cast<uint32_t>(tl[jc + 2 * e][dd]) | (static_cast<uint32_t>(tl[jc + 2 * e + 1][dd]) << 16);
+        *reinterpret_cast<uint4 *>(o + orow + col) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        for (int e = 0; j + e < a.n_tok; ++e) {
+          const int col = a.vt_ring ? (a.vt_col0 + j + e) % a.vt_ring : a.vt_col0 + j + e;
+          o[orow + col] = tl[jc + e][dd];
+        }
+      }
+    }
+  }
+}
+
+// q and k items of norm_rope_item, with the V heads of the same call handled
+// by v_tile_to_cache: the first Hkv * ceil(n_tok / (32 * RH)) workgroups take
+// the V tiles, the rest (n_tok per group of four q/k items) one wave per item.
+template <int NQ, int RH>
+__global__ __launch_bounds__(256) void norm_rope_vt_kernel(const NormRopeArgs a, int n_vt) {
+  __shared__ __attribute__((aligned(16))) bf16_t tile[2][64][72];
+  const int b = blockIdx.x;
+  if (b < n_vt) {
+    const int ntj = (a.n_tok + 32 * RH - 1) / (32 * RH);
+    v_tile_to_cache<NQ, RH>(a, b / ntj, (b % ntj) * 32 * RH, tile);
+    return;
+  }
+  const int bq = b - n_vt;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  norm_rope_item<bf16_t>(a, bq % a.n_tok, (bq / a.n_tok) * 4 + wave, a.Hq + a.Hkv, threadIdx.x & 63);
 }
 
 constexpr int kBKV = 32;  // keys per tile
@@ -1314,11 +1423,27 @@ hipError_t launch_k_rebuild(int dtype, const void *vt, long long vt_hs, int vt_l
 
 hipError_t launch_norm_rope(const NormRopeArgs &a, int dtype, hipStream_t s) {
   if (a.n_tok <= 0) return hipSuccess;
-  if (!a.rope_tab) return hipErrorInvalidValue;
+  if (!a.rope_tab || !a.vt_dst) return hipErrorInvalidValue;
+  const bool fused = DG_NORM_ROPE_VT && dtype == DG_BF16 && (a.dh == 256 || a.dh == 512) && a.ld % 8 == 0 &&
+                     a.v_off % 8 == 0 && reinterpret_cast<uintptr_t>(a.qkv) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(a.vt_dst) % 16 == 0 && a.vt_col0 % 8 == 0 && a.vt_ld % 8 == 0 &&
+                     a.vt_hs % 8 == 0 && a.vt_ring % 8 == 0;
+  if (fused) {
+    const int tj = a.dh == 256 ? 64 : 32;   // V tile tokens (32 * RH)
+    const int n_vt = a.Hkv * ((a.n_tok + tj - 1) / tj);
+    const dim3 grid(n_vt + a.n_tok * ((a.Hq + a.Hkv + 3) / 4));
+    if (a.dh == 256) hipLaunchKernelGGL((norm_rope_vt_kernel<4, 2>), grid, dim3(256), 0, s, a, n_vt);
+    else hipLaunchKernelGGL((norm_rope_vt_kernel<8, 1>), grid, dim3(256), 0, s, a, n_vt);
+    return hipGetLastError();
+  }
+  if (!a.v_dst) return hipErrorInvalidValue;
   const dim3 grid(a.n_tok, (a.Hq + 2 * a.Hkv + 3) / 4);
   if (dtype == DG_BF16) hipLaunchKernelGGL(norm_rope_kernel<bf16_t>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(norm_rope_kernel<float>, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_v_transpose(dtype, a.v_dst, a.n_tok, a.Hkv, a.dh, a.vt_dst, a.vt_hs, a.vt_ld, a.vt_col0, s,
+                            a.vt_ring);
 }
 
 }  // namespace dg

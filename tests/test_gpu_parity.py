@@ -239,6 +239,32 @@ def test_attn_encode_bf16_ragged():
     assert torch.equal(kd.cpu()[:, :100], ck[:, :100]) and torch.equal(kd.cpu()[:, 400:], ck[:, 400:])
 
 
+@pytest.mark.parametrize("layer_type", [0, 1])
+def test_attn_encode_bf16_ragged_aligned_start(layer_type):
+    """Causal encode of 300 tokens after 96 committed ones: the cache
+    columns start on an 8-column boundary, so the V heads go from the
+    projection straight to the transposed cache (64-token tiles, the last
+    one ragged, 4 tokens in its last 8-token chunk); global layers add the
+    unit-RMS value norm at d_h = 512."""
+    cfg = synth.sliding_cfg() if layer_type == 0 else synth.global_cfg()
+    if layer_type == 0:
+        cfg = dict(cfg, window=128)
+    g = synth.generator(48 + layer_type)
+    w = synth.attn_weights(cfg, g)
+    Hkv, dh = cfg["n_kv_heads"], cfg["head_dim"]
+    ck, cv = synth.kv_cache_random(Hkv, 512, dh, g, "bf16")
+    x = synth.hidden_states(300, cfg["hidden"], g, "bf16")
+    xo, kd, vd, n1 = run_gpu_attn(cfg, w, ck, cv, 96, x, 1)
+    assert n1 == 396
+    ref, rk, rv = O.attn_layer(cfg, npw(w), np64(ck), np64(cv), 96, np64(x), 1, "bf16")
+    assert_delta_close(np64(xo), ref, np64(x), "bf16", "encode delta")
+    assert_close(np64(kd)[:, 96:396], rk, "bf16", "appended k")
+    assert_close(np64(vd)[:, 96:396], rv, "bf16", "appended v")
+    # value columns outside [96, 396) untouched
+    v = vd.cpu()
+    assert torch.equal(v[:, :96], cv[:, :96]) and torch.equal(v[:, 396:], cv[:, 396:])
+
+
 def test_attn_poisoned_out_of_window_rows_are_not_read():
     cfg = synth.sliding_cfg()
     g = synth.generator(49)
