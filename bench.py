@@ -102,6 +102,51 @@ def cpu_baseline(mcfg, P, budget_note):
             "seconds_measured": round(4 * times["sliding"] + 2 * times["global"] + times["head"], 2)}
 
 
+def attainable_roofs(reps=5):
+    """The device's attainable roofs, measured with the library's probes on
+    the stream they run on: a read-only stream over 4 GiB (16 times the
+    256 MB last-level cache) and a bf16 MFMA loop filling every CU.  Both
+    probes' outputs are checked exactly, so the rates count work that was
+    done.  Median of `reps` timed launches after one untimed launch."""
+    import numpy as np
+    import torch
+
+    from discrete_text_diffusion_step_amd import binding as B
+
+    def median_ms(fn):
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+
+    nbytes, groups = 4 << 30, 2048
+    buf = torch.full((nbytes,), 1, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(groups, dtype=torch.int32, device="cuda")
+    t_read = median_ms(lambda: B.dg_probe_hbm_read(buf, groups, sink))
+    got = int(sink.cpu().numpy().view(np.uint32).astype(np.uint64).sum()) % 2 ** 32
+    if got != (nbytes // 4) * 0x01010101 % 2 ** 32:
+        raise RuntimeError("read probe: the word sum does not match the buffer")
+    del buf
+    torch.cuda.empty_cache()
+    iters, mgroups = 2048, 1024
+    msink = torch.empty(4 * mgroups, dtype=torch.float32, device="cuda")
+    t_mfma = median_ms(lambda: B.dg_probe_mfma_bf16(iters, 1.0, 2.0 ** -10, mgroups, msink))
+    if not torch.equal(msink.cpu(), torch.full((4 * mgroups,), 16.0 * iters * 32 * 2.0 ** -10)):
+        raise RuntimeError("MFMA probe: accumulators do not hold the expected sum")
+    flops = B.dg_probe_mfma_flops(iters, mgroups)
+    return {"hbm_read_GBs": round(nbytes / (t_read * 1e-3) / 1e9, 1),
+            "mfma_bf16_TFLOPs": round(flops / (t_mfma * 1e-3) / 1e12, 1),
+            "read_probe": f"{nbytes} B read once by {groups} workgroups of 256 threads (16-byte non-temporal loads, "
+                          f"8 in flight per thread): {t_read * 1e3:.1f} us",
+            "mfma_probe": f"{mgroups} workgroups x 4 waves x {iters} rounds of 16 independent 16x16x32 bf16 MFMAs "
+                          f"({flops / 1e12:.2f} TFLOP): {t_mfma * 1e3:.1f} us",
+            "datasheet": {"hbm_GBs": HBM_PEAK_GBS, "mfma_bf16_TFLOPs": 2500.0}}
+
+
 def variants(args, mcfg, w, model, kv, P, cap, ws, K=20, warmup=2):
     """The default run's extra lines, timed like the main one (warmup, then K
     steps between synchronisations): the same step with 8 canvases per
@@ -209,6 +254,8 @@ def main():
                     help="temperature at the last step of the adaptive generation run")
     ap.add_argument("--v-only", action="store_true",
                     help="global layers keep only V (keys rebuilt from it every call; one shared key scratch)")
+    ap.add_argument("--no-roofs", action="store_true",
+                    help="skip the attainable-roof probes (read-only HBM stream, bf16 MFMA loop)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the extra measurements of the default run (8 canvases per forward; fp8 expert weights)")
     ap.add_argument("--ring", action="store_true",
@@ -378,8 +425,18 @@ def main():
         "roofline": roof,
         "generation": gen,
     }
+    if not args.no_roofs:
+        roofs = attainable_roofs()
+        log(f"attainable roofs: {roofs}")
+        result["attainable_roofs"] = roofs
+        roof["attainable"] = roofs["hbm_read_GBs"]
+        roof["frac_of_attainable"] = round(achieved / roofs["hbm_read_GBs"], 4)
     if not args.no_variants and NB == 1 and not fp8 and not args.ring and not args.v_only:
         result["variants"] = variants(args, mcfg, w, model, kv, P, cap, ws)
+        if "attainable_roofs" in result:
+            r8 = result["variants"]["fp8_experts"]["roofline"]
+            r8["attainable"] = result["attainable_roofs"]["hbm_read_GBs"]
+            r8["frac_of_attainable"] = round(r8["achieved"] / r8["attainable"], 4)
     if not args.no_cpu_baseline and not fp8:
         log("cpu baseline (oracle sample)...")
         result["cpu_baseline"] = cpu_baseline(mcfg, P, "about 10-30 s of CPU work")

@@ -145,6 +145,9 @@ def lib(path=None):
                                          c_void]),
             "dg_rmsnorm": (c_int, [c_int, c_int, c_float, c_int, c_void, c_void, c_void, c_void]),
             "dg_set_kernel_timer": (None, [P(KernelTimer)]),
+            "dg_probe_hbm_read": (c_int, [c_void, c_size, c_void, c_int, c_void]),
+            "dg_probe_mfma_bf16": (c_int, [c_int, c_float, c_float, c_void, c_int, c_void]),
+            "dg_probe_mfma_flops": (ctypes.c_longlong, [c_int, c_int]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -380,6 +383,28 @@ def dg_rmsnorm(x, w, eps, out=None, stream=None):
     dt = DG_BF16 if x.dtype == torch.bfloat16 else DG_F32
     check(lib().dg_rmsnorm(n, D, eps, dt, ptr(x), ptr(w), ptr(y), stream_handle(stream)), "dg_rmsnorm")
     return y
+
+
+def dg_probe_hbm_read(buf, n_groups=2048, sink=None, stream=None):
+    """Read-only stream over `buf` (a device tensor); returns the sink, one
+    wrapping uint32 sum per workgroup (int32 tensor holding the bits)."""
+    if sink is None:
+        sink = torch.empty(n_groups, dtype=torch.int32, device=buf.device)
+    check(lib().dg_probe_hbm_read(ptr(buf), buf.numel() * buf.element_size(), ptr(sink), n_groups,
+                                  stream_handle(stream)), "dg_probe_hbm_read")
+    return sink
+
+
+def dg_probe_mfma_bf16(iters, a=1.0, b=2.0 ** -10, n_groups=1024, sink=None, stream=None):
+    """MFMA loop; returns the per-wave sink (float32, 4 per workgroup)."""
+    if sink is None:
+        sink = torch.empty(4 * n_groups, dtype=torch.float32, device="cuda")
+    check(lib().dg_probe_mfma_bf16(iters, a, b, ptr(sink), n_groups, stream_handle(stream)), "dg_probe_mfma_bf16")
+    return sink
+
+
+def dg_probe_mfma_flops(iters, n_groups):
+    return lib().dg_probe_mfma_flops(iters, n_groups)
 
 
 class Model:

@@ -459,6 +459,33 @@ typedef struct {
 
 void dg_set_kernel_timer(dg_kernel_timer *timer);
 
+/* ----------------------------------------------------------- roof probes */
+
+/* Not operations of the pages: two probes of the device's attainable roofs,
+ * against which the kernels' roofline fractions are reported beside the
+ * datasheet figures.  Both are enqueued on `stream` and produce results the
+ * caller checks exactly.
+ *
+ * dg_probe_hbm_read: n_groups workgroups of 256 threads read `bytes` (a
+ * multiple of 16, buf 16-byte aligned) once with 16-byte non-temporal loads,
+ * eight in flight per thread, the grid striding over the buffer.
+ * sink[g] (uint32, n_groups of them, device) receives the wrapping sum of the
+ * 32-bit words workgroup g read; the sum over g is the wrapping sum of every
+ * word of the buffer.  A buffer well beyond the last-level cache measures
+ * HBM.  DG_ERR_NULL / DG_ERR_SHAPE (n_groups outside [1, 65536], bytes or buf
+ * misaligned) before any HIP call.
+ *
+ * dg_probe_mfma_bf16: n_groups workgroups of four waves; each wave runs
+ * `iters` rounds (a multiple of 16) of 16 independent 16x16x32 bf16 MFMAs
+ * with every A element a and every B element b (both rounded to bf16).
+ * sink[4g + w] (float, device) = 16 * iters * 32 * a * b for wave w of
+ * workgroup g, exact when every partial sum is representable.
+ * dg_probe_mfma_flops gives the launch's floating-point operations
+ * (2 * 16 * 16 * 32 per MFMA), 0 for invalid arguments. */
+int dg_probe_hbm_read(const void *buf, size_t bytes, uint32_t *sink, int n_groups, void *stream);
+int dg_probe_mfma_bf16(int iters, float a, float b, float *sink, int n_groups, void *stream);
+long long dg_probe_mfma_flops(int iters, int n_groups);
+
 /* ------------------------------------------------------------------ misc */
 
 /* RMSNorm rows (aitrends rms code): y = w * x * sqrt(D) / (||x|| + eps).

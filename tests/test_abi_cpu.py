@@ -232,3 +232,21 @@ def test_ring_cache_validation_codes():
     bad = ring(1280, 100)
     bad.ring = 2
     assert call(_attn_c(), bad) == -2
+
+
+def test_probe_validation_codes():
+    L = B.lib()
+    p = ctypes.c_void_p(256)
+    assert L.dg_probe_hbm_read(None, 1024, p, 8, None) == -1
+    assert L.dg_probe_hbm_read(p, 1024, None, 8, None) == -1
+    assert L.dg_probe_hbm_read(p, 1000, p, 8, None) == -2          # bytes not a multiple of 16
+    assert L.dg_probe_hbm_read(ctypes.c_void_p(264), 1024, p, 8, None) == -2   # buffer not 16-byte aligned
+    assert L.dg_probe_hbm_read(p, 1024, p, 0, None) == -2
+    assert L.dg_probe_hbm_read(p, 1024, p, 65537, None) == -2
+    assert L.dg_probe_hbm_read(p, 0, p, 8, None) == 0               # nothing to read: no launch
+    assert L.dg_probe_mfma_bf16(16, 1.0, 1.0, None, 8, None) == -1
+    assert L.dg_probe_mfma_bf16(24, 1.0, 1.0, p, 8, None) == -2     # rounds not a multiple of 16
+    assert L.dg_probe_mfma_bf16(-16, 1.0, 1.0, p, 8, None) == -2
+    assert L.dg_probe_mfma_bf16(16, 1.0, 1.0, p, 0, None) == -2
+    assert B.dg_probe_mfma_flops(32, 3) == 3 * 4 * 32 * 16 * (2 * 16 * 16 * 32)
+    assert B.dg_probe_mfma_flops(24, 3) == 0 and B.dg_probe_mfma_flops(32, 0) == 0
