@@ -123,7 +123,7 @@ def attainable_roofs(reps=5):
         torch.cuda.synchronize()
         return sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
 
-    nbytes, groups = 4 << 30, 2048
+    nbytes, groups = 4 << 30, 1024
     buf = torch.full((nbytes,), 1, dtype=torch.uint8, device="cuda")
     sink = torch.empty(groups, dtype=torch.int32, device="cuda")
     t_read = median_ms(lambda: B.dg_probe_hbm_read(buf, groups, sink))
@@ -140,8 +140,8 @@ def attainable_roofs(reps=5):
     flops = B.dg_probe_mfma_flops(iters, mgroups)
     return {"hbm_read_GBs": round(nbytes / (t_read * 1e-3) / 1e9, 1),
             "mfma_bf16_TFLOPs": round(flops / (t_mfma * 1e-3) / 1e12, 1),
-            "read_probe": f"{nbytes} B read once by {groups} workgroups of 256 threads (16-byte non-temporal loads, "
-                          f"8 in flight per thread): {t_read * 1e3:.1f} us",
+            "read_probe": f"{nbytes} B read once by {groups} workgroups of 256 threads, each its own contiguous "
+                          f"span (16-byte non-temporal loads, 16 in flight per thread): {t_read * 1e3:.1f} us",
             "mfma_probe": f"{mgroups} workgroups x 4 waves x {iters} rounds of 16 independent 16x16x32 bf16 MFMAs "
                           f"({flops / 1e12:.2f} TFLOP): {t_mfma * 1e3:.1f} us",
             "datasheet": {"hbm_GBs": HBM_PEAK_GBS, "mfma_bf16_TFLOPs": 2500.0}}

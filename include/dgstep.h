@@ -468,7 +468,7 @@ void dg_set_kernel_timer(dg_kernel_timer *timer);
  *
  * dg_probe_hbm_read: n_groups workgroups of 256 threads read `bytes` (a
  * multiple of 16, buf 16-byte aligned) once with 16-byte non-temporal loads,
- * eight in flight per thread, the grid striding over the buffer.
+ * sixteen in flight per thread, each workgroup its own contiguous span.
  * sink[g] (uint32, n_groups of them, device) receives the wrapping sum of the
  * 32-bit words workgroup g read; the sum over g is the wrapping sum of every
  * word of the buffer.  A buffer well beyond the last-level cache measures
