@@ -214,7 +214,7 @@ AttnWs attn_carve(const dg_attn_cfg *c, const AttnPlan &p, const AttnPlan &pa, C
   const size_t n = static_cast<size_t>(p.n);
   w.h = cv.bytes(n * c->hidden * es);
   w.qkv = cv.bytes(n * p.Ntot * es);
-  w.v_rows = cv.bytes(n * p.Nk * es);   // per canvas [Hkv][C][dh] from the norm pass
+  w.v_rows = cv.bytes(n * p.Nk * es);   // per canvas [Hkv][C][dh]: V rows of the two-launch norm/RoPE form
   w.o = cv.bytes(n * p.Nq * es);
   const size_t rows = static_cast<size_t>(c->n_kv_heads) * pa.R;
   if (pa.n_split_max > 1) {

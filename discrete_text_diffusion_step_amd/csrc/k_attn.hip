@@ -4,8 +4,9 @@
 //    shared-K/V layers, split-half RoPE (pair t with t + d/2) with angles
 //    computed in fp64 from the absolute position (aitrends notebook summary,
 //    QK-norm and RoPE paragraphs with their code; glossary "Partial RoPE").
-//    Writes q in place and the layer's k/v rows to their destination: the
-//    workspace in decode mode, the KV cache in encode (commit) mode.
+//    Writes q in place, the layer's k rows to the key cache and its v rows
+//    into the transposed value cache (cache rows / columns [kv_len,
+//    kv_len + n): scratch in decode mode, kept in encode (commit) mode).
 //  * attn_fwd: flash-style softmax(q K^T) V with scale 1 (scalar QK-norm
 //    fixes the temperature).  One workgroup takes one kv head, a block of
 //    query rows of all q heads that share it (GQA rows packed as
@@ -41,8 +42,9 @@ __global__ __launch_bounds__(256) void rope_table_kernel(int pos0, int n_tok, in
 
 // One wave per (token, head item): items are the q heads, then the k heads
 // (normed, rotated, written to the cache), then the v heads (unit-RMS in
-// global layers, written to the row buffer).  Angles come from the table.
-// Items at or past `items` are left alone.
+// global layers, written to the row buffer v_dst; the fused launch below
+// writes them to the cache itself and stops at the k heads).  Angles come
+// from the table.  Items at or past `items` are left alone.
 template <typename T>
 __device__ __forceinline__ void norm_rope_item(const NormRopeArgs &a, int j, int it, int items, int lane) {
   const int half = a.dh >> 1;
