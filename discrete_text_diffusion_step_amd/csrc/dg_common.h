@@ -372,6 +372,11 @@ enum WideCfg {
 #ifndef DG_WMOE_MT
 #define DG_WMOE_MT 2
 #endif
+// 1: the grouped wide-tile products number their (group, column tile) items
+// so that each XCD takes a contiguous run of them
+#ifndef DG_GROUPED_XCD
+#define DG_GROUPED_XCD 1
+#endif
 // expert groups averaging more rows than this use the 256-row configurations
 // router product: split-K partials, summed in split order by the top-k pass
 #ifndef DG_ROUTER_KS
