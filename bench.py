@@ -221,7 +221,7 @@ def variants(args, mcfg, w, model, kv, P, cap, ws, K=20, warmup=2):
     out["fp8_experts"] = {
         "steps_per_s": round(K / el, 3), "ms_per_step": round(el * 1e3 / K, 4), "steps": K, "warmup": warmup,
         "expert_weights": "fp8_e4m3 (row scales), widened to bf16 in registers",
-        "roofline": {"kernel": "moe expert gate/up (grouped MFMA GEMM + SwiGLU, fp8 e4m3 weights widened to bf16)",
+        "roofline": {"kernel": "moe expert gate/up (grouped wide-tile MFMA GEMM + SwiGLU, fp8 e4m3 weights widened to bf16)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiling.read_traffic(fp8=True),
                      "avg_launch_us": round(avg_ms * 1e3, 2), "bytes_per_launch": nbytes, "launches": len(durs)}}
@@ -394,7 +394,7 @@ def main():
     avg_ms = sum(durs) / len(durs)
     bytes_launch = gateup_bytes(mcfg, CANVAS * NB)
     achieved = bytes_launch / (avg_ms * 1e-3) / 1e9
-    kname = ("moe expert gate/up (grouped MFMA GEMM + SwiGLU, fp8 e4m3 weights widened to bf16)" if fp8 else
+    kname = ("moe expert gate/up (grouped wide-tile MFMA GEMM + SwiGLU, fp8 e4m3 weights widened to bf16)" if fp8 else
              "moe expert gate/up (grouped wide-tile MFMA GEMM + SwiGLU)")
     roof = {"kernel": kname, "bound": "hbm",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -593,7 +593,11 @@ int moe_impl(const dg_moe_cfg *c, const dg_moe_w *w, int n, void *x, const float
   const bool wide = !fp8 && DG_WIDE_EXPERTS && rows_per_expert <= 48;
   {
     TimedLaunch tl(DG_KT_MOE_GATEUP, s);
-    if (fp8) DG_HIP(launch_gemm_f8_grouped(gu, EPI_SWIGLU, mtile, s));
+    if (fp8) {
+      hipError_t e = (DG_WIDE_F8_GU && mtile == DG_WMOE_MT) ? launch_gemm_wide_f8_gu(gu, s) : hipErrorNotSupported;
+      if (e == hipErrorNotSupported) e = launch_gemm_f8_grouped(gu, EPI_SWIGLU, mtile, s);
+      DG_HIP(e);
+    }
     else if (wide_l && wide_ok(dt, gu, WIDE_EXPERT_GU_L, moe_rows))
       DG_HIP(launch_gemm_wide(gu, EPI_SWIGLU, WIDE_EXPERT_GU_L, s));
     else if (wide_gu) DG_HIP(launch_gemm_wide(gu, EPI_SWIGLU, WIDE_EXPERT_GU, s));

@@ -265,6 +265,15 @@ hipError_t launch_gemm(const GemmArgs &a, int mode, int bm, int bn, hipStream_t 
 // Grouped expert product with OCP E4M3 weights ([N][K] bytes per expert) and
 // bf16 activations; mode EPI_SWIGLU or EPI_ROWSCALE_F32, mt = 2 or 4.
 hipError_t launch_gemm_f8_grouped(const GemmArgs &a, int mode, int mt, hipStream_t s);
+// The expert gate/up product (SwiGLU epilogue) with fp8 weights in the
+// wide-tile form: 16*DG_WMOE_MT rows x 64 columns of both matrices, four
+// waves sharing each activation stage through LDS.  Returns
+// hipErrorNotSupported unless K and K_x are multiples of 128, the weight
+// rows 16-byte aligned and every scale pointer given.
+hipError_t launch_gemm_wide_f8_gu(const GemmArgs &a, hipStream_t s);
+#ifndef DG_WIDE_F8_GU
+#define DG_WIDE_F8_GU 1
+#endif
 #ifndef DG_F8_NT_GU
 #define DG_F8_NT_GU 2
 #endif

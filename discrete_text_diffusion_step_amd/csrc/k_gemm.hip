@@ -1232,6 +1232,206 @@ __global__ __launch_bounds__(64 * NW) void gemm_wide_kernel(const GemmArgs a) {
   }
 }
 
+// ----------------------------------------------------------------------------
+// Wide-tile expert gate/up with OCP E4M3 weights (one fp32 scale per weight
+// row).  The bf16 wide tile with two changes: a stage is 128 deep, so each
+// weight row still arrives as a 128-byte segment (the same loads and private
+// LDS layout as bf16), while an activation stage is two 64-deep halves (two
+// LDS sub-tiles in the bf16 layout); each fragment read takes the 8 bytes of
+// a 32-deep k slice from the private region and widens them to bf16 with the
+// hardware conversion.  The scales multiply the gate and up columns in the
+// epilogue, before the SwiGLU.  K must be a multiple of 128.
+template <int MT, int NTW, int NW, int P>
+__device__ __forceinline__ void wide_tile_f8(const GemmArgs &a, bf16_t *lds, uint8_t *ldsb, int row_begin, int rows,
+                                             const uint8_t *const *Bp, const float *const *Sp, int n0, int ncols,
+                                             int K) {
+  constexpr int NB = 2;
+  constexpr int BM = MT * 16;
+  constexpr int D = BM / 8 / NW;         // A load instructions per wave per 64-deep half
+  static_assert(D * 8 * NW == BM, "A rows must split evenly over the waves");
+  constexpr int DB = NTW * 2;            // B load instructions per weight matrix per stage
+  constexpr int R = P + 1;               // B ring slots (A: one stage ahead)
+  constexpr int HALF = BM * 64;          // bf16 elements of one 64-deep A sub-tile
+  constexpr int STAGE = 2 * HALF;
+  constexpr int WB = NB * NTW * 16 * 128; // bytes of one wave's B region
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int lr = lane >> 3, lc = lane & 7;
+
+  uint32_t ao[D];
+  int aw[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    const int r = (wave + NW * j) * 8 + lr;
+    int pr = row_begin + (r < rows ? r : 0);
+    if (a.a_rows) pr = a.a_rows[pr];
+    ao[j] = (static_cast<uint32_t>(pr) * static_cast<uint32_t>(a.lda) + lc * 8) * 2u;
+    aw[j] = r * 64 + ((lc ^ ((r >> 1) & 7)) * 8);
+  }
+  int fo[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) fo[ks] = l16 * 64 + (((4 * ks + lg) ^ (l16 >> 1)) * 8);
+  // B fragment of 32-deep slice ks: bytes [32 ks + 8 lg, +8) of row l16
+  int fbo[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int c16 = 2 * ks + (lg >> 1);
+    fbo[ks] = l16 * 128 + ((c16 ^ ((l16 >> 1) & 7)) * 16) + (lg & 1) * 8;
+  }
+  uint32_t bo[DB];
+  int bw[DB];
+#pragma unroll
+  for (int j = 0; j < DB; ++j) {
+    const int r = j * 8 + lr;
+    const int c = wave * (NTW * 16) + r;
+    bo[j] = static_cast<uint32_t>(c < ncols ? c : 0) * static_cast<uint32_t>(a.ldb) + lc * 16;
+    bw[j] = r * 128 + ((lc ^ ((r >> 1) & 7)) * 16);
+  }
+  uint8_t *myb = ldsb + wave * WB;
+  const char *Ab = static_cast<const char *>(a.A);
+
+  f32x4 acc[NB][MT][NTW];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) acc[nb][mi][nt] = zero4();
+
+  Frag<bf16_t> ra[2][D];                 // the next stage's activation halves
+  Frag<bf16_t> rb[R][NB][DB];
+  auto load_a = [&](int st, Frag<bf16_t>(&xa)[2][D]) {
+    const uint32_t kbyte = static_cast<uint32_t>(st) * 256u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < D; ++j) xa[h][j].load(reinterpret_cast<const bf16_t *>(Ab + (ao[j] + kbyte + h * 128u)));
+  };
+  auto load_b = [&](int st, Frag<bf16_t>(&xb)[NB][DB]) {
+    const uint32_t kbyte = static_cast<uint32_t>(st) * 128u;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < DB; ++j) xb[nb][j].v = ld_stream(reinterpret_cast<const char *>(Bp[nb]) + (bo[j] + kbyte));
+  };
+  auto stage_a = [&](int buf, const Frag<bf16_t>(&xa)[2][D]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < D; ++j) *reinterpret_cast<bf16x8 *>(lds + buf * STAGE + h * HALF + aw[j]) = xa[h][j].v;
+  };
+  auto compute = [&](int buf, const Frag<bf16_t>(&xb)[NB][DB]) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < DB; ++j) *reinterpret_cast<bf16x8 *>(myb + nb * (NTW * 16 * 128) + bw[j]) = xb[nb][j].v;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      Frag<bf16_t> fb[NB][NTW];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const uint2 q = *reinterpret_cast<const uint2 *>(myb + nb * (NTW * 16 * 128) + nt * 16 * 128 + fbo[ks]);
+          const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false);
+          const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true);
+          const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, false);
+          const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, true);
+          uint32_t o[4];
+          __builtin_memcpy(&o[0], &p0, 4);
+          __builtin_memcpy(&o[1], &p1, 4);
+          __builtin_memcpy(&o[2], &p2, 4);
+          __builtin_memcpy(&o[3], &p3, 4);
+          __builtin_memcpy(&fb[nb][nt].v, o, 16);
+        }
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+        Frag<bf16_t> fa;
+        fa.load(lds + buf * STAGE + (ks >> 1) * HALF + mi * 16 * 64 + fo[ks & 1]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) mma(acc[nb][mi][nt], fa, fb[nb][nt]);
+      }
+    }
+  };
+
+  // as in wide_tile: no memory operation of the loop body under a branch;
+  // stages past the last re-load the last one and skip their MFMAs
+  const int nst = K / 128;
+  const int lastst = nst > 0 ? nst - 1 : 0;
+  if (nst > 0) {
+    load_a(0, ra);
+#pragma unroll
+    for (int r = 0; r < P; ++r) load_b(r < lastst ? r : lastst, rb[r]);
+    stage_a(0, ra);
+  }
+  lds_barrier();
+  for (int i = 0; i < nst; i += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int it = i + r;
+      load_a(it + 1 < lastst ? it + 1 : lastst, ra);
+      load_b(it + P < lastst ? it + P : lastst, rb[(r + P) % R]);
+      if (it < nst) compute(it & 1, rb[r]);
+      stage_a((it + 1) & 1, ra);
+      lds_barrier();
+    }
+  }
+
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int c = wave * (NTW * 16) + nt * 16 + l16;
+    if (c >= ncols) continue;
+    const int col = n0 + c;
+    const float sg = Sp[0][c], su = Sp[1][c];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mi * 16 + lg * 4 + i;
+        if (r >= rows) continue;
+        const long long row = row_begin + r;
+        const float v = acc[0][mi][nt][i] * sg, u = acc[1][mi][nt][i] * su;
+        static_cast<bf16_t *>(a.C)[row * a.ldc + col] = f32_to_bf16(silu_f(v) * u);
+      }
+  }
+}
+
+template <int MT, int NTW, int NW, int P>
+__global__ __launch_bounds__(64 * NW) void gemm_wide_f8_kernel(const GemmArgs a) {
+  constexpr int BM = MT * 16, BN = NW * NTW * 16;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * BM * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t ldsb[NW * 2 * NTW * 16 * 128];
+  int g, n0;
+  grouped_item(g, n0, BN);
+  const bool sh = g < a.n_xgroups;
+  const int Ng = sh ? a.N_x : a.N;
+  if (n0 >= Ng) return;
+  GemmArgs ga = a;
+  const uint8_t *Bp[2];
+  const float *Sp[2];
+  if (sh) {
+    ga.K = a.K_x;
+    ga.ldb = a.ldb_x;
+    Bp[0] = static_cast<const uint8_t *>(a.Bx0) + static_cast<long long>(n0) * a.ldb_x;
+    Bp[1] = static_cast<const uint8_t *>(a.Bx1) + static_cast<long long>(n0) * a.ldb_x;
+    Sp[0] = a.bxs0 + n0;
+    Sp[1] = a.bxs1 + n0;
+  } else {
+    const int e = g - a.n_xgroups;
+    const long long off = static_cast<long long>(e) * a.b_gstride + static_cast<long long>(n0) * a.ldb;
+    Bp[0] = static_cast<const uint8_t *>(a.seg_B0[0]) + off;
+    Bp[1] = static_cast<const uint8_t *>(a.seg_B1[0]) + off;
+    Sp[0] = a.bs0 + static_cast<long long>(e) * a.N + n0;
+    Sp[1] = a.bs1 + static_cast<long long>(e) * a.N + n0;
+  }
+  const int r0 = a.g_off[g], r1 = a.g_off[g + 1];
+  for (int rb = r0; rb < r1; rb += BM)
+    wide_tile_f8<MT, NTW, NW, P>(ga, lds, ldsb, rb, min(BM, r1 - rb), Bp, Sp, n0, min(BN, Ng - n0), ga.K);
+}
+
 template <int MT, int NTW, int NB, int NW, int KSUB, int P, int MODE>
 hipError_t launch_wide_one(const GemmArgs &a, hipStream_t s) {
   constexpr int BM = MT * 16, BN = NW * NTW * 16;
@@ -1630,6 +1830,22 @@ hipError_t launch_gemm_f8_grouped(const GemmArgs &a, int mode, int mt, hipStream
   DG_F8_CASE(EPI_ROWSCALE_F32, 4, DG_F8_NT_DN, 1, DG_F8_S)
 #undef DG_F8_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_wide_f8_gu(const GemmArgs &a, hipStream_t s) {
+  constexpr int MT = DG_WMOE_MT, NTW = 1, NW = 4, BN = NW * NTW * 16;
+  if (!a.g_off || a.K % 128 || a.K_x % 128 || a.ldb % 16 || a.ldb_x % 16 || a.lda % 8 || !a.bs0 || !a.bs1 ||
+      !a.bxs0 || !a.bxs1)
+    return hipErrorNotSupported;
+  // 32-bit byte offsets: every activation row and every weight tile
+  if (static_cast<long long>(a.M) * a.lda * 2 >= (1ll << 31) ||
+      static_cast<long long>(a.N > a.N_x ? a.N : a.N_x) * (a.ldb > a.ldb_x ? a.ldb : a.ldb_x) >= (1ll << 31))
+    return hipErrorNotSupported;
+  const int nmax = a.N > a.N_x ? a.N : a.N_x;
+  const dim3 grid((nmax + BN - 1) / BN, a.n_groups);
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_wide_f8_kernel<MT, NTW, NW, DG_WMOE_P>), grid, dim3(64 * NW), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_wide(const GemmArgs &a, int mode, int cfg, hipStream_t s) {

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 COPY_BYTES = 1 << 30
 GATEUP_KERNEL = "gemm_wide_kernel<2, 1, 2, 4, 2, 3, 3>"                     # expert gate/up (SwiGLU)
-GATEUP_KERNEL_FP8 = "gemm_f8_grouped_kernel<2, 2, 2, 3, 2>"                  # the same with e4m3 weights
+GATEUP_KERNEL_FP8 = "gemm_wide_f8_kernel<2, 1, 4, 3>"                         # the same with e4m3 weights
 DOWN_KERNEL = "gemm_down_ring_kernel<2, 4, 3, 4, false>"                    # expert down (routing-weight row scale)
 DOWN_KERNEL_FP8 = "gemm_down_ring_kernel<2, 4, 2, 4, true>"                 # the same with e4m3 weights
 COPY_KERNEL = "copyBuffer"
