@@ -123,14 +123,19 @@ def summarize_stats(stats_csv, command, top=25, step_calls=None):
 
 
 def summarize_step(trace_csv, marker="sample_finalize_kernel"):
-    """Per-kernel time inside one denoising step: the launches between the
-    last two sampler finalisations of the trace."""
+    """Per-kernel time inside one denoising step: the launches after one
+    sampler finalisation up to the next.  Of the complete steps in the trace
+    (same launch count as the last one) the one with the median span is
+    shown, so a host stall under the profiler does not stand for the step."""
     rows = _rows(trace_csv)
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     idx = [i for i, r in enumerate(rows) if marker in r["Kernel_Name"]]
     if len(idx) < 2:
         return "no complete step in the trace\n"
-    seq = rows[idx[-2] + 1: idx[-1] + 1]
+    steps = [rows[i + 1: j + 1] for i, j in zip(idx[:-1], idx[1:])]
+    steps = [q for q in steps if len(q) == len(steps[-1])]
+    steps.sort(key=lambda q: int(q[-1]["End_Timestamp"]) - int(q[0]["Start_Timestamp"]))
+    seq = steps[len(steps) // 2]
     agg = {}
     for r in seq:
         d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
