@@ -381,8 +381,8 @@ enum WideCfg {
 #ifndef DG_WMOE_MT
 #define DG_WMOE_MT 2
 #endif
-// 1: the grouped wide-tile products number their (group, column tile) items
-// so that each XCD takes a contiguous run of them
+// 1: the grouped wide-tile products with 32-row tiles number their (group,
+// column tile) items so that each XCD takes a contiguous run of them
 #ifndef DG_GROUPED_XCD
 #define DG_GROUPED_XCD 1
 #endif

@@ -818,14 +818,16 @@ __device__ __forceinline__ void stream_tile_f8(const GemmArgs &a, float *red, in
 
 // (group, column tile) of a grouped launch over a grid of (column tiles,
 // groups).  Consecutive workgroups go to the eight XCDs in turn, so with
-// DG_GROUPED_XCD each XCD takes a contiguous run of items instead: the
-// column tiles of one group then share that XCD's L2 for the group's
-// activation rows (expert gate/up: HBM fetch 1.078x -> 1.040x of the
-// algorithmic bytes, 176.7-182.8 -> 174.3 us per launch).
-__device__ __forceinline__ void grouped_item(int &g, int &n0, int BN) {
+// `xcd` each XCD takes a contiguous run of items instead: the column tiles
+// of one group then share that XCD's L2 for the group's activation rows.
+// Measured on the 32-row expert tiles (gate/up: HBM fetch 1.078x -> 1.040x
+// of the algorithmic bytes, 176.7-182.8 -> 174.3 us per launch); the
+// 256-row tiles of long groups ran slower with it (8 canvases per forward:
+// 160.0 against 162.1 canvas-steps/s), so they keep the plain order.
+__device__ __forceinline__ void grouped_item(int &g, int &n0, int BN, bool xcd) {
   g = blockIdx.y;
   n0 = blockIdx.x * BN;
-  if (DG_GROUPED_XCD) {
+  if (xcd) {
     const int gx = gridDim.x, total = gx * gridDim.y;
     int L = blockIdx.y * gx + blockIdx.x;
     const int full = total & ~7;
@@ -844,7 +846,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 2 ? 2
   constexpr int BM = MT * 16, BN = NT * 16;
   __shared__ __attribute__((aligned(16))) float red[4 * NB * MT * NT * 4 * 64];
   int g, n0;
-  grouped_item(g, n0, BN);
+  grouped_item(g, n0, BN, false);
   const bool sh = g < a.n_xgroups;
   const int Ng = sh ? a.N_x : a.N;
   if (n0 >= Ng) return;
@@ -1210,7 +1212,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_wide_kernel(const GemmArgs a) {
                                               min(BN, a.seg_start[s + 1] - n0), kb, ke > kb ? ke : kb, split);
   } else {
     int g, n0;
-    grouped_item(g, n0, BN);
+    grouped_item(g, n0, BN, DG_GROUPED_XCD && MT <= 2);
     const int Ng = (g < a.n_xgroups) ? a.N_x : a.N;
     if (n0 >= Ng) return;
     const bf16_t *Bp[NB];
@@ -1405,7 +1407,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_wide_f8_kernel(const GemmArgs a)
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * BM * 128];
   __shared__ __attribute__((aligned(16))) uint8_t ldsb[NW * 2 * NTW * 16 * 128];
   int g, n0;
-  grouped_item(g, n0, BN);
+  grouped_item(g, n0, BN, DG_GROUPED_XCD && MT <= 2);
   const bool sh = g < a.n_xgroups;
   const int Ng = sh ? a.N_x : a.N;
   if (n0 >= Ng) return;
