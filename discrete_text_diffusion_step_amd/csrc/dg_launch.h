@@ -102,6 +102,31 @@ hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh
 #ifndef DG_ATTN_PAIR
 #define DG_ATTN_PAIR 1
 #endif
+// bf16 attention in the solo form (each wave owns whole 16-query tiles over
+// the full head dimension), by head dimension: bit 0 for d_h 256, bit 1 for
+// d_h 512 (the pair form otherwise); QT query tiles per wave, NW waves per
+// workgroup
+#ifndef DG_ATTN_SOLO
+#define DG_ATTN_SOLO 1
+#endif
+#ifndef DG_SOLO256_QT
+#define DG_SOLO256_QT 1
+#endif
+#ifndef DG_SOLO256_NW
+#define DG_SOLO256_NW 8
+#endif
+#ifndef DG_SOLO512_QT
+#define DG_SOLO512_QT 1
+#endif
+#ifndef DG_SOLO512_NW
+#define DG_SOLO512_NW 8
+#endif
+#ifndef DG_SOLO_VDEPTH
+#define DG_SOLO_VDEPTH 8
+#endif
+#ifndef DG_SOLO_NBUF
+#define DG_SOLO_NBUF 2
+#endif
 #ifndef DG_ATTN_TGT_SMALL
 #define DG_ATTN_TGT_SMALL 256
 #endif

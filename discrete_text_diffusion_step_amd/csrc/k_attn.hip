@@ -15,7 +15,11 @@
 //    (S^T = K Q^T) so that each lane owns one query column and the
 //    probabilities sit in registers in exactly the B-operand layout of the
 //    P V MFMA -- no LDS round trip for P.  Online softmax in fp32.
-//  * attn_combine: merges the per-slice (max, sum, O) partials.
+//    bf16 forms: attn_pair (d_h 512; two waves split the head dimension of
+//    each query tile) and attn_solo (d_h 256; each wave owns whole query
+//    tiles).
+//  * attn_combine: merges the per-slice (max, sum, O) partials (bf16 rows
+//    divided by their slice's sum for the bf16 forms, fp32 otherwise).
 #include "dg_launch.h"
 
 namespace dg {
@@ -646,6 +650,27 @@ __device__ __forceinline__ void p_to_bf16(Frag<bf16_t> &f, const float *s) {
   f.v = *reinterpret_cast<bf16x8 *>(w);
 }
 
+__device__ __forceinline__ void store4(bf16_t *p, const float *f) {
+  uint2 u;
+  u.x = static_cast<uint32_t>(f32_to_bf16(f[0])) | (static_cast<uint32_t>(f32_to_bf16(f[1])) << 16);
+  u.y = static_cast<uint32_t>(f32_to_bf16(f[2])) | (static_cast<uint32_t>(f32_to_bf16(f[3])) << 16);
+  *reinterpret_cast<uint2 *>(p) = u;
+}
+__device__ __forceinline__ void store4(float *p, const float *f) {
+  *reinterpret_cast<float4 *>(p) = make_float4(f[0], f[1], f[2], f[3]);
+}
+// four floats to bf16 by the packed conversion (round to nearest even, as
+// f32_to_bf16 on finite values), one 8-byte store
+__device__ __forceinline__ void store4_pk(bf16_t *p, const float *f) {
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  const f2_t a = {f[0], f[1]}, b = {f[2], f[3]};
+  uint2 u;
+  u.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf2_t));
+  u.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf2_t));
+  *reinterpret_cast<uint2 *>(p) = u;
+}
+
 // Raw buffer resource (gfx9 layout: 48-bit base, stride 0, byte extent,
 // word 3 = 32-bit data format), wave-uniform.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -1052,12 +1077,15 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) op[dt * 16 + lg * 4 + i] = f32_to_bf16(o[dt][qt][i] * inv);
     } else {
+      // split partials as in the solo form: rows divided by this split's l, bf16
       const long long prow = static_cast<long long>(split) * a.Hkv * R + static_cast<long long>(g) * R + rr;
-      float *op = a.o_part + prow * DH + hf * HALF;
+      T *op = reinterpret_cast<T *>(a.o_part) + prow * DH + hf * HALF;
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < DTH; ++dt)
-        *reinterpret_cast<float4 *>(op + dt * 16 + lg * 4) =
-            make_float4(o[dt][qt][0], o[dt][qt][1], o[dt][qt][2], o[dt][qt][3]);
+      for (int dt = 0; dt < DTH; ++dt) {
+        const float f[4] = {o[dt][qt][0] * inv, o[dt][qt][1] * inv, o[dt][qt][2] * inv, o[dt][qt][3] * inv};
+        store4_pk(op + dt * 16 + lg * 4, f);
+      }
       if (lg == 0 && hf == 0) {
         a.ml_part[prow * 2] = m_run[qt];
         a.ml_part[prow * 2 + 1] = l;
@@ -1066,21 +1094,389 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
   }
 }
 
-__device__ __forceinline__ void store4(bf16_t *p, const float *f) {
-  uint2 u;
-  u.x = static_cast<uint32_t>(f32_to_bf16(f[0])) | (static_cast<uint32_t>(f32_to_bf16(f[1])) << 16);
-  u.y = static_cast<uint32_t>(f32_to_bf16(f[2])) | (static_cast<uint32_t>(f32_to_bf16(f[3])) << 16);
-  *reinterpret_cast<uint2 *>(p) = u;
+
+// Solo form of the bf16 attention: each wave owns QT 16-query tiles over the
+// whole head dimension, so its scores need no exchange with another wave and
+// every softmax runs once.  NW waves share each K / V^T tile.  NBUF tile
+// buffers form a ring: the loads of tile i + NBUF - 1 are issued at the start
+// of tile i, into the buffers tile i - 1 used, and one workgroup barrier per
+// tile hands them over (after it every wave has finished tile i - 1).
+// Tile loads, key order, masking and the online softmax are those of the
+// pair form above.
+// Split partials: each split stores its rows divided by its own normaliser
+// (O_s / l_s, a convex combination of value rows) rounded to bf16, beside
+// fp32 (m_s, l_s); the merge weights split s by l_s exp(m_s - M) / sum.
+template <int DH, int QT, int NW, int NBUF>
+__global__ __launch_bounds__(NW * 64) void attn_solo_kernel(const AttnArgs a) {
+  using T = bf16_t;
+  using C = AttnCfg<T, DH>;
+  constexpr int BQ = NW * 16 * QT;
+  constexpr int DS = DH / 32, DT = DH / 16;
+  static_assert(C::KINS % NW == 0 && C::VINS % NW == 0, "the waves share each tile's loads equally");
+  constexpr int kNK = C::KINS / NW, kNV = C::VINS / NW;   // loads per wave per K / V^T tile
+  static_assert(NBUF >= 2 && NBUF <= 3, "two or three tile buffers");
+  __shared__ __attribute__((aligned(16))) T sK[NBUF][C::KCH * C::VEC];
+  __shared__ __attribute__((aligned(16))) T sV[NBUF][C::VCH * C::VEC];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int R = a.n_rep * a.n_tok;
+  const int qblocks = (R + BQ - 1) / BQ;
+  int L = blockIdx.y * gridDim.x + blockIdx.x;
+  const int total = gridDim.x * gridDim.y;
+  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  const int qb = L % qblocks;
+  const int split = (L / qblocks) % a.n_split;
+  const int g = L / (qblocks * a.n_split);
+  const int r0 = qb * BQ;
+  const int r1 = min(R, r0 + BQ);
+
+  int lo = a.key_lo, hi = a.kv_len + a.n_tok;
+  if (a.causal) {
+    int jmin = r0 % a.n_tok, jmax = (r1 - 1) % a.n_tok;
+    if (r0 / a.n_tok != (r1 - 1) / a.n_tok) {
+      jmin = 0;
+      jmax = a.n_tok - 1;
+    }
+    hi = a.kv_len + jmax + 1;
+    lo = a.sliding ? max(0, a.kv_len + jmin - a.window + 1) : 0;
+  }
+  const int span = max(0, hi - lo);
+  int chunk = (span + a.n_split - 1) / a.n_split;
+  chunk = (chunk + kBKV - 1) / kBKV * kBKV;
+  const int k_lo = lo + split * chunk;
+  const int k_hi = min(hi, k_lo + chunk);
+  const int t_first = (k_lo / kBKV) * kBKV;
+  const int n_tiles = k_hi > k_lo ? (k_hi - t_first + kBKV - 1) / kBKV : 0;
+
+  // This wave's queries: positions first (the tile masks need them), the
+  // fragments after the first tiles' loads are issued, so the two latencies
+  // overlap; they are consumed before the loop, so their wait (which also
+  // covers those tile loads) is not repeated on every tile.
+  int qrow[QT], qpos[QT];
+  bool qval[QT];
+  const T *qptr[QT];
+  Frag<T> qf[QT][DS];
+  const T *Q = static_cast<const T *>(a.q);
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int r = r0 + wave * 16 * QT + qt * 16 + l16;
+    qval[qt] = r < r1;
+    const int rr = qval[qt] ? r : r0;
+    const int h = g * a.n_rep + rr / a.n_tok;
+    const int j = rr % a.n_tok;
+    qrow[qt] = rr;
+    qpos[qt] = a.kv_len + j;
+    qptr[qt] = Q + static_cast<long long>(j) * a.q_ld + h * DH;
+  }
+  auto qload = [&]() {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        if (qval[qt]) qf[qt][s].load(qptr[qt] + s * 32 + lg * 8);
+        else qf[qt][s].zero();
+      }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int s = 0; s < DS; ++s) asm volatile("" ::"v"(qf[qt][s].v));
+  };
+
+  f32x4 o[DT][QT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) o[dt][qt] = zero4();
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -1e30f;
+    l_run[qt] = 0.f;
+  }
+
+  const T *Kg = static_cast<const T *>(a.k_cache) + g * a.cache_hs;
+  const T *Vg = static_cast<const T *>(a.v_cache) + g * a.vcache_hs;
+  const int vld = a.vcache_ld;
+  static_assert(C::VCPR == 4, "V^T chunk swizzle below assumes four 16-byte chunks per row");
+  constexpr bool kRowPerLoad = C::KCPR == 64;
+  uint32_t koff[kRowPerLoad ? 1 : kNK] = {};
+  if constexpr (!kRowPerLoad) {
+#pragma unroll
+    for (int j = 0; j < kNK; ++j) {
+      const int p = (wave + NW * j) * 64 + lane;
+      const int r = p / C::KCPR, c = (p % C::KCPR) ^ C::kswz(r);
+      koff[j] = static_cast<uint32_t>((r * DH + c * C::VEC) * sizeof(T));
+    }
+  }
+  // V^T chunk (wave + NW j)*64 + lane is row d = (wave + NW j)*16 + lane/4;
+  // its swizzle (d/4) % 4 = (lane/16) % 4 is the same for every j
+  const uint32_t voff = static_cast<uint32_t>(
+      ((lane >> 2) * vld + (((lane & 3) ^ ((lane >> 4) & 3)) * C::VEC)) * sizeof(T));
+  const i32x4_t k_rsrc = buffer_rsrc(Kg, static_cast<uint32_t>((a.ring ? a.ring : k_hi) * DH * sizeof(T)));
+  const i32x4_t v_rsrc = buffer_rsrc(Vg, static_cast<uint32_t>(DH * vld * sizeof(T)));
+
+  auto issue_k = [&](int t0, T *kb) {
+    if (t0 >= k_lo && t0 + kBKV <= k_hi) {
+      const int row0 = a.ring ? t0 % a.ring : t0;
+      const int soff = row0 * DH * static_cast<int>(sizeof(T));
+      if constexpr (kRowPerLoad) {
+        uint32_t ln;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        const uint32_t l16b = ln << 4;
+#pragma unroll
+        for (int j = 0; j < kNK; ++j) {
+          const int r = wave + NW * j;
+          dma16(k_rsrc, l16b ^ static_cast<uint32_t>(C::kswz(r) * 16), soff + r * DH * static_cast<int>(sizeof(T)),
+                kb + r * 64 * C::VEC);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kNK; ++j) dma16(k_rsrc, koff[j], soff, kb + (wave + NW * j) * 64 * C::VEC);
+      }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < kNK; ++j) {
+      const int blk = wave + NW * j;
+      const int p = blk * 64 + lane;
+      const int r = p / C::KCPR, c = (p % C::KCPR) ^ C::kswz(r);
+      int m = t0 + r;
+      m = m < k_lo ? k_lo : (m >= k_hi ? k_hi - 1 : m);
+      if (a.ring) m %= a.ring;
+      dma16(k_rsrc, static_cast<uint32_t>((m * DH + c * C::VEC) * sizeof(T)), 0, kb + blk * 64 * C::VEC);
+    }
+  };
+  auto issue_v = [&](int t0, T *vb) {
+    if (a.ring || t0 + kBKV <= vld) {
+      const int col0 = a.ring ? t0 % a.ring : t0;
+#pragma unroll
+      for (int j = 0; j < kNV; ++j)
+        dma16(v_rsrc, voff, (col0 + (wave + NW * j) * 16 * vld) * static_cast<int>(sizeof(T)),
+              vb + (wave + NW * j) * 64 * C::VEC);
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < kNV; ++j) {
+      const int blk = wave + NW * j;
+      const int p = blk * 64 + lane;
+      const int d = p / C::VCPR, c = (p % C::VCPR) ^ C::vswz(d);
+      int k0 = t0 + c * C::VEC;
+      k0 = a.ring ? k0 % a.ring : (k0 > vld - C::VEC ? vld - C::VEC : k0);
+      dma16(v_rsrc, static_cast<uint32_t>((d * vld + k0) * sizeof(T)), 0, vb + blk * 64 * C::VEC);
+    }
+  };
+
+  int pq_min = qpos[0], pq_max = qpos[0];
+#pragma unroll
+  for (int qt = 1; qt < QT; ++qt) {
+    pq_min = min(pq_min, qpos[qt]);
+    pq_max = max(pq_max, qpos[qt]);
+  }
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) {
+    pq_min = min(pq_min, __shfl_xor(pq_min, sh, 64));
+    pq_max = max(pq_max, __shfl_xor(pq_max, sh, 64));
+  }
+  pq_min = __builtin_amdgcn_readfirstlane(pq_min);
+  pq_max = __builtin_amdgcn_readfirstlane(pq_max);
+
+  // One 32-key tile.  This wave's loads in flight at its start are those of
+  // this tile and, with three buffers, of the next one if it exists (loads
+  // complete in issue order).
+  auto tile = [&](int ti, const T *kb, const T *vb, T *kb_next, T *vb_next) {
+    const int t0 = t_first + ti * kBKV;
+    const bool in_range = t0 >= k_lo && t0 + kBKV <= k_hi;
+    const bool unmasked = in_range && (!a.causal || (t0 + kBKV - 1 <= pq_min &&
+                                                     (!a.sliding || t0 > pq_max - a.window)));
+    if (NBUF == 3 && ti + 1 < n_tiles) wait_vm<kNK + kNV>();
+    else wait_vm<0>();
+    lds_sync();   // every wave's share of this tile has landed; tile ti - 1's buffers are free
+    if (ti + NBUF - 1 < n_tiles) {
+      issue_k(t0 + (NBUF - 1) * kBKV, kb_next);
+      issue_v(t0 + (NBUF - 1) * kBKV, vb_next);
+    }
+    // ---- S^T = K Q^T over the whole head dimension: every K fragment of
+    // the tile is read from LDS before the first product, so one LDS latency
+    // is exposed per tile rather than one per step
+    f32x4 st[2][QT];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) st[kt][qt] = zero4();
+    {
+      Frag<T> kf[DS][2];
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) load_k_frag<T, DH>(kf[s][kt], kb, key_row(l16, kt), s * 32 + lg * 8);
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) mma(st[kt][qt], kf[s][kt], qf[qt][s]);
+    }
+    // the first VD V^T fragments are read now, so their latency hides behind
+    // the softmax; the rest run VD steps ahead of their products
+    constexpr int VD = DT < DG_SOLO_VDEPTH ? DT : DG_SOLO_VDEPTH;
+    Frag<T> vf[VD];
+#pragma unroll
+    for (int dt = 0; dt < VD; ++dt) load_v_frag<T, DH>(vf[dt], vb, dt * 16 + l16, lg);
+    // ---- mask (tiles cut by the key range, the causal diagonal or the window)
+    if (!unmasked) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = t0 + lg * 8 + kt * 4 + i;
+            bool ok = m >= k_lo && m < k_hi;
+            if (a.causal) {
+              const int pq = qpos[qt];
+              ok = ok && (m <= pq) && (!a.sliding || m > pq - a.window);
+            }
+            if (!ok) st[kt][qt][i] = -INFINITY;
+          }
+    }
+    // ---- online softmax (reference maximum moved past kRescaleSlack only)
+    Frag<T> pf[QT];
+    float corr[QT];
+    bool grow = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mt = -1e30f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) mt = fmaxf(mt, fmaxf(fmaxf(st[kt][qt][0], st[kt][qt][1]),
+                                                          fmaxf(st[kt][qt][2], st[kt][qt][3])));
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      corr[qt] = mt;
+      grow = grow || mt > m_run[qt] + kRescaleSlack;
+    }
+    if (__ballot(grow) != 0ull) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float m_new = fmaxf(m_run[qt], corr[qt]);
+        const float c = __builtin_amdgcn_exp2f((m_run[qt] - m_new) * kLog2e);
+        m_run[qt] = m_new;
+        l_run[qt] *= c;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          o[dt][qt][0] *= c;
+          o[dt][qt][1] *= c;
+          o[dt][qt][2] *= c;
+          o[dt][qt][3] *= c;
+        }
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float nm = -m_run[qt] * kLog2e;
+      float sv[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(st[kt][qt][i], kLog2e, nm));
+          sv[kt * 4 + i] = e;
+          psum += e;
+        }
+      l_run[qt] += psum;
+      p_to_bf16(pf[qt], sv);
+    }
+    // ---- O^T += V^T P^T (tiles cut by the key range: values of keys
+    // outside it are zeroed, as the cache holds anything there)
+    if (in_range) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) mma(o[dt][qt], vf[dt % VD], pf[qt]);
+        if (dt + VD < DT) load_v_frag<T, DH>(vf[dt % VD], vb, (dt + VD) * 16 + l16, lg);
+      }
+    } else {
+      uint32_t vm[4];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int m = t0 + lg * 8 + e;
+        const bool ok = m >= k_lo && m < k_hi;
+        if ((e & 1) == 0) vm[e >> 1] = 0;
+        vm[e >> 1] |= ok ? ((e & 1) ? 0xffff0000u : 0x0000ffffu) : 0u;
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        mask_frag(vf[dt % VD], vm);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) mma(o[dt][qt], vf[dt % VD], pf[qt]);
+        if (dt + VD < DT) load_v_frag<T, DH>(vf[dt % VD], vb, (dt + VD) * 16 + l16, lg);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p) {
+    if (p < n_tiles) {
+      issue_k(t_first + p * kBKV, sK[p]);
+      issue_v(t_first + p * kBKV, sV[p]);
+    }
+  }
+  qload();
+  // unrolled over the ring, so every buffer address is a constant
+  for (int ti = 0; ti < n_tiles; ti += NBUF) {
+    tile(ti, sK[0], sV[0], sK[NBUF - 1], sV[NBUF - 1]);
+    if (ti + 1 >= n_tiles) break;
+    tile(ti + 1, sK[1], sV[1], sK[0], sV[0]);
+    if constexpr (NBUF == 3) {
+      if (ti + 2 >= n_tiles) break;
+      tile(ti + 2, sK[2], sV[2], sK[1], sV[1]);
+    }
+  }
+
+  // ---- finish: lanes sharing a query (same l16) hold partial sums of l
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float l = l_run[qt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (!qval[qt]) continue;
+    const int rr = qrow[qt];
+    if (a.n_split == 1) {
+      const int h = g * a.n_rep + rr / a.n_tok;
+      const int j = rr % a.n_tok;
+      T *op = static_cast<T *>(a.out) + static_cast<long long>(j) * a.out_ld + h * DH;
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) op[dt * 16 + lg * 4 + i] = f32_to_bf16(o[dt][qt][i] * inv);
+    } else {
+      const long long prow = static_cast<long long>(split) * a.Hkv * R + static_cast<long long>(g) * R + rr;
+      T *op = reinterpret_cast<T *>(a.o_part) + prow * DH;
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const float f[4] = {o[dt][qt][0] * inv, o[dt][qt][1] * inv, o[dt][qt][2] * inv, o[dt][qt][3] * inv};
+        store4_pk(op + dt * 16 + lg * 4, f);
+      }
+      if (lg == 0) {
+        a.ml_part[prow * 2] = m_run[qt];
+        a.ml_part[prow * 2 + 1] = l;
+      }
+    }
+  }
 }
-__device__ __forceinline__ void store4(float *p, const float *f) {
-  *reinterpret_cast<float4 *>(p) = make_float4(f[0], f[1], f[2], f[3]);
-}
+
 
 // Merge of the split-KV partials, one wave per (kv head, row): lane s reads
 // split s's (max, sum) and the wave forms w_s = exp(m_s - M) / sum_s l_s
 // exp(m_s - M) by reductions (no barrier); every lane then adds its four
 // columns over the splits in order.
-template <typename T>
+// BP: the partial rows are bf16 and already divided by their split's l
+// (the solo form), so split s is weighted by l_s exp(m_s - M) / L.
+template <typename T, bool BP>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a, int dh) {
   const int R = a.n_rep * a.n_tok;
   const long long rows = static_cast<long long>(a.Hkv) * R;
@@ -1097,7 +1493,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a, int
   const float M = wave_max(m);
   const float e = lane < ns ? __expf(m - M) : 0.f;
   const float L = wave_sum(l * e);
-  const float wl = L > 0.f ? e / L : 0.f;
+  const float wl = L > 0.f ? (BP ? l * e : e) / L : 0.f;
   const int g = static_cast<int>(idx / R), rr = static_cast<int>(idx % R);
   const int h = g * a.n_rep + rr / a.n_tok;
   const int j = rr % a.n_tok;
@@ -1107,7 +1503,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a, int
 #pragma unroll 4
     for (int s = 0; s < ns; ++s) {
       const float w = __shfl(wl, s, 64);
-      const float4 v = *reinterpret_cast<const float4 *>(a.o_part + (s * rows + idx) * dh + d);
+      float4 v;
+      if constexpr (BP) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(reinterpret_cast<const bf16_t *>(a.o_part) +
+                                                         (s * rows + idx) * dh + d);
+        v = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                        __uint_as_float(u.y & 0xffff0000u));
+      } else {
+        v = *reinterpret_cast<const float4 *>(a.o_part + (s * rows + idx) * dh + d);
+      }
       acc[0] += w * v.x;
       acc[1] += w * v.y;
       acc[2] += w * v.z;
@@ -1181,23 +1585,53 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const T *src, int n, i
   }
 }
 
+template <int DH>
+struct SoloCfg {
+  static constexpr bool on = (DG_ATTN_SOLO >> (DH == 512 ? 1 : 0)) & 1;
+  static constexpr int QT = DH == 512 ? DG_SOLO512_QT : DG_SOLO256_QT;
+  static constexpr int NW = DH == 512 ? DG_SOLO512_NW : DG_SOLO256_NW;
+  static constexpr int BQ = NW * 16 * QT;
+  // three tile buffers where they fit beside nothing else in 160 KB of LDS
+  static constexpr int tile_bytes = 2 * kBKV * DH * 2;
+  static constexpr int NBUF = (DG_SOLO_NBUF >= 3 && 3 * tile_bytes <= 160 * 1024) ? 3 : 2;
+};
+
 template <typename T, int DH>
 hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
   using C = AttnCfg<T, DH>;
   const int R = a.n_rep * a.n_tok;
   const int qblocks = (R + C::BQ - 1) / C::BQ;
+  bool bf16_parts = false;   // the solo and pair forms write bf16 split partials
   if constexpr (sizeof(T) == 2 && (DH == 256 || DH == 512)) {
-    // the pair form addresses a head's cache with 32-bit byte offsets
-    if (DG_ATTN_PAIR && static_cast<long long>(a.vcache_ld) * DH * static_cast<long long>(sizeof(T)) < (1ll << 31))
+    // the solo and pair forms address a head's cache with 32-bit byte offsets
+    const bool fits = static_cast<long long>(a.vcache_ld) * DH * static_cast<long long>(sizeof(T)) < (1ll << 31);
+    bool solo = false;
+    if constexpr (SoloCfg<DH>::on) {
+      using S = SoloCfg<DH>;
+      if (fits) {
+        const int qb = (R + S::BQ - 1) / S::BQ;
+        hipLaunchKernelGGL((attn_solo_kernel<DH, S::QT, S::NW, S::NBUF>), dim3(a.Hkv * qb, a.n_split),
+                           dim3(S::NW * 64), 0, s, a);
+        solo = true;
+      }
+    }
+    if (solo) {
+      bf16_parts = true;
+    } else if (DG_ATTN_PAIR && fits) {
       hipLaunchKernelGGL((attn_pair_kernel<DH>), dim3(a.Hkv * qblocks, a.n_split), dim3(512), 0, s, a);
-    else
+      bf16_parts = true;
+    } else {
       hipLaunchKernelGGL((attn_fwd_kernel<T, DH>), dim3(a.Hkv * qblocks, a.n_split), dim3(256), 0, s, a);
+    }
   } else {
     hipLaunchKernelGGL((attn_fwd_kernel<T, DH>), dim3(a.Hkv * qblocks, a.n_split), dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<T>, dim3((a.Hkv * R + 3) / 4), dim3(256), 0, s, a, DH);
+  if (bf16_parts)
+    hipLaunchKernelGGL((attn_combine_kernel<T, true>), dim3((a.Hkv * R + 3) / 4), dim3(256), 0, s, a, DH);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<T, false>), dim3((a.Hkv * R + 3) / 4), dim3(256), 0, s, a, DH);
   return hipGetLastError();
 }
 
@@ -1364,8 +1798,8 @@ int attn_block_rows(int dtype, int dh) {
     switch (dh) {
       case 64: return AttnCfg<bf16_t, 64>::BQ;
       case 128: return AttnCfg<bf16_t, 128>::BQ;
-      case 256: return AttnCfg<bf16_t, 256>::BQ;
-      case 512: return AttnCfg<bf16_t, 512>::BQ;
+      case 256: return SoloCfg<256>::on ? SoloCfg<256>::BQ : AttnCfg<bf16_t, 256>::BQ;
+      case 512: return SoloCfg<512>::on ? SoloCfg<512>::BQ : AttnCfg<bf16_t, 512>::BQ;
     }
   } else {
     switch (dh) {
