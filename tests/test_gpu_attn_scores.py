@@ -54,3 +54,27 @@ def test_wide_scores(kind, P, n_tok, causal):
     assert np.isfinite(np64(xo)).all()
     e = assert_delta_close(np64(xo), ref, np64(x), "bf16", f"{kind} P={P} causal={causal}")
     print(f"{kind} P={P} n={n_tok} causal={causal}: rel err of the update {e:.2e}")
+
+
+def test_scores_rising_along_the_keys():
+    """Committed keys scaled from 1x to 8x across the sliding window (QK-norm
+    gains of 2): within every key slice the later tiles' scores pass the
+    first tile's maximum by far more than 32 nats, which is where a kernel
+    whose softmax keeps a fixed reference must re-run the slice against the
+    exact maximum.  The layer output must match the oracle's plain softmax."""
+    cfg = synth.sliding_cfg()
+    P, n_tok = 2048, 256
+    g = synth.generator(97)
+    w = synth.attn_weights(cfg, g, gamma=(2.0, 2.0))
+    cap = P + n_tok
+    ck, cv = synth.kv_cache_random(cfg["n_kv_heads"], cap, cfg["head_dim"], g, "bf16")
+    lo = P - cfg["window"]
+    ramp = torch.ones(cap)
+    ramp[lo:P] = torch.linspace(1.0, 8.0, P - lo)
+    ck = (ck.float() * ramp[None, :, None]).to(torch.bfloat16)
+    x = synth.hidden_states(n_tok, cfg["hidden"], g, "bf16")
+    xo = run(cfg, w, ck, cv, P, x, 0)
+    ref, _, _ = O.attn_layer(cfg, npw(w), np64(ck), np64(cv), P, np64(x), 0, "bf16")
+    assert np.isfinite(np64(xo)).all()
+    e = assert_delta_close(np64(xo), ref, np64(x), "bf16", "rising scores")
+    print(f"rising key scale: rel err of the update {e:.2e}")
