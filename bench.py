@@ -238,6 +238,8 @@ def main():
     ap.add_argument("--canvases", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-generate", action="store_true", help="skip the adaptive-stop generation run")
+    ap.add_argument("--attn-workload", action="store_true",
+                    help="run only the sliding and global attention layers at the step's shape (for profiles)")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="only run the counter workload (copy calibration + MoE layer) for rocprofv3 --pmc")
     ap.add_argument("--experts", choices=("bf16", "fp8"), default="bf16",
@@ -273,6 +275,10 @@ def main():
     if args.pmc_workload:
         torch.cuda.set_device(0)
         profiling.pmc_workload(fp8=args.experts == "fp8")
+        return
+    if args.attn_workload:
+        torch.cuda.set_device(0)
+        profiling.attn_workload()
         return
     from discrete_text_diffusion_step_amd import binding as B
     from discrete_text_diffusion_step_amd import synth

@@ -60,6 +60,61 @@ def pmc_workload(n_reps=5, fp8=False):
     print("pmc workload done", flush=True)
 
 
+def attn_workload(n_reps=20):
+    """The attention layers of the canvas step at its shape (256 canvas rows
+    after 4,096 committed rows; the sliding layer's window of 1,024 and the
+    global layer's 4,352 keys), n_reps calls of each; run under rocprofv3
+    --kernel-trace --stats or --pmc."""
+    import torch
+
+    from . import binding as B
+    from . import synth
+    P, C = 4096, 256
+    for cfg in (synth.sliding_cfg(), synth.global_cfg()):
+        g = synth.generator(5)
+        w = {k: (v.cuda() if v is not None else None) for k, v in synth.attn_weights(cfg, g).items()}
+        cap = P + C
+        ck, cv = synth.kv_cache_random(cfg["n_kv_heads"], cap, cfg["head_dim"], g, "bf16")
+        kd, vtd = ck.cuda(), cv.transpose(1, 2).contiguous().cuda()
+        x = synth.hidden_states(C, cfg["hidden"], g, "bf16").cuda()
+        for _ in range(n_reps):
+            xd = x.clone()
+            B.dg_attn_layer(cfg, w, kd, vtd, P, xd, 0)
+        torch.cuda.synchronize()
+        print(f"attention workload: layer type {cfg['layer_type']} done", flush=True)
+
+
+def summarize_counters(counter_csvs, name_part="attn_"):
+    """Per kernel (name containing name_part): the mean over dispatches of
+    each counter, summed over its instances, from rocprofv3 --pmc runs."""
+    per = {}   # (kernel, counter) -> per-run means (dispatch ids restart in every run)
+    for path in counter_csvs:
+        run = {}
+        for r in _rows(path):
+            n = r["Kernel_Name"]
+            if name_part not in n:
+                continue
+            short = n.split("(anonymous namespace)::")[-1].split("(")[0]
+            d = run.setdefault((short, r["Counter_Name"]), {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        for key, d in run.items():
+            per.setdefault(key, []).append(sum(d.values()) / len(d))
+    kernels = sorted({k for k, _ in per})
+    out = []
+    for k in kernels:
+        vals = {c: sum(m) / len(m) for (kk, c), m in per.items() if kk == k}
+        out.append(k)
+        for c in sorted(vals):
+            out.append(f"  {c:28s} {vals[c]:16.0f}")
+        waves = vals.get("SQ_WAVES")
+        if waves:
+            for c, label in (("SQ_INSTS_VALU", "VALU instructions per wave"), ("SQ_INSTS_MFMA", "MFMA instructions per wave"),
+                             ("SQ_INSTS_LDS", "LDS instructions per wave")):
+                if c in vals:
+                    out.append(f"  {label:28s} {vals[c] / waves:16.1f}")
+    return "\n".join(out) + "\n"
+
+
 def _rows(path):
     with open(path) as f:
         return list(csv.DictReader(f))
@@ -183,9 +238,11 @@ if __name__ == "__main__":
         fp8 = len(sys.argv) > 6 and sys.argv[6] == "fp8"
         product = sys.argv[7] if len(sys.argv) > 7 else "gate/up"
         sys.stdout.write(summarize_traffic(fetch_csv, write_csv, command, alg, fp8=fp8, product=product))
+    elif what == "counters":
+        sys.stdout.write(summarize_counters(sys.argv[2:]))
     elif what == "stats":
         sys.stdout.write(summarize_stats(sys.argv[2], sys.argv[3]))
         if len(sys.argv) > 4:
             sys.stdout.write("\n" + summarize_step(sys.argv[4]))
     else:
-        raise SystemExit("usage: profiling.py traffic|stats ...")
+        raise SystemExit("usage: profiling.py traffic|stats|counters ...")
