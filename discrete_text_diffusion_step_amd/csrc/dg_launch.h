@@ -124,6 +124,10 @@ hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh
 #ifndef DG_SOLO_VDEPTH
 #define DG_SOLO_VDEPTH 8
 #endif
+// 1: the softmax's column maximum by VALU row swaps (0: by ds_bpermute)
+#ifndef DG_ATTN_PERMLANE
+#define DG_ATTN_PERMLANE 1
+#endif
 #ifndef DG_SOLO_NBUF
 #define DG_SOLO_NBUF 2
 #endif

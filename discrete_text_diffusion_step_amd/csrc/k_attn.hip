@@ -362,6 +362,22 @@ __device__ __forceinline__ void mask_frag(Frag<float> &f, const uint32_t *m) {
   for (int j = 0; j < 8; ++j) f.v[j] = __uint_as_float(__float_as_uint(f.v[j]) & m[j]);
 }
 
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one score column of
+// an MFMA tile).  gfx950's row swaps do it in the VALU: swapping a register
+// with itself by v_permlane16_swap leaves each lane holding its own value and
+// that of lane l ^ 16 in the two results (v_permlane32_swap: lane l ^ 32), so
+// no LDS round trip (ds_bpermute) sits in the softmax.
+__device__ __forceinline__ float col_max4(float v) {
+  if (DG_ATTN_PERMLANE) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+
 // One workgroup: kv head g, query rows [r0, r1) of the heads sharing it,
 // keys [k_lo, k_hi), all read from the cache (this call's rows sit at
 // [kv_len, kv_len + n_tok)).  32-key tiles start at multiples of 32; two
@@ -520,8 +536,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
           sv[kt * 4 + i] = v;
           mt = fmaxf(mt, v);
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = col_max4(mt);
       const float m_new = fmaxf(m_run[qt], mt);
       const float corr = __expf(m_run[qt] - m_new);
       float psum = 0.f;
@@ -635,6 +650,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnArgs a) {
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;   // nats a score may exceed the reference max by
+
 
 // P to bf16: gfx950 packs two floats with round-to-nearest-even in one
 // instruction (the same rounding as f32_to_bf16 on the finite values P holds)
@@ -972,8 +988,7 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) mt = fmaxf(mt, fmaxf(fmaxf(st[kt][qt][0], st[kt][qt][1]),
                                                           fmaxf(st[kt][qt][2], st[kt][qt][3])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = col_max4(mt);
       corr[qt] = mt;
       grow = grow || mt > m_run[qt] + kRescaleSlack;
     }
@@ -1351,8 +1366,7 @@ __global__ __launch_bounds__(NW * 64) void attn_solo_kernel(const AttnArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) mt = fmaxf(mt, fmaxf(fmaxf(st[kt][qt][0], st[kt][qt][1]),
                                                           fmaxf(st[kt][qt][2], st[kt][qt][3])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = col_max4(mt);
       corr[qt] = mt;
       grow = grow || mt > m_run[qt] + kRescaleSlack;
     }
