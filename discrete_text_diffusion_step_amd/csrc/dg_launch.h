@@ -4,6 +4,40 @@
 
 namespace dg {
 
+// Wave64 all-reductions in the VALU, no LDS round trips: DPP quad_perm
+// [1,0,3,2] and [2,3,0,1] pair lanes l ^ 1 and l ^ 2; row_half_mirror pairs
+// the two quads of each 8 lanes and row_mirror the two 8s of each 16 (all
+// lanes of a group hold the same value by then, so any pairing across the
+// halves will do); gfx950's row swaps (v_permlane16_swap /
+// v_permlane32_swap of a register with itself) pair lanes l ^ 16 and l ^ 32.
+// Every lane ends with the same value.  Callers run with the whole wave
+// active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <typename Op>
+__device__ __forceinline__ float wave_allreduce(float v, Op op) {
+  v = op(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = op(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = op(v, dpp_f32<0x141>(v));   // row_half_mirror
+  v = op(v, dpp_f32<0x140>(v));   // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float wave_allsum(float v) {
+  return wave_allreduce(v, [](float x, float y) { return x + y; });
+}
+__device__ __forceinline__ float wave_allmax(float v) {
+  return wave_allreduce(v, [](float x, float y) { return fmaxf(x, y); });
+}
+
+}  // namespace dg
+
+namespace dg {
+
 struct NormRopeArgs {
   void *qkv;                 // [n_tok][ld] raw projections (q | k | v)
   long long ld;

@@ -126,7 +126,7 @@ __device__ __forceinline__ void norm_rope_item(const NormRopeArgs &a, int j, int
     }
     float scale = 1.0f;
     if (norm) {
-      ss = wave_sum(ss);
+      ss = wave_allsum(ss);
       scale = a.sqrt_dh / (sqrtf(ss) + a.eps);
     }
 #pragma unroll
@@ -1504,9 +1504,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a, int
     m = a.ml_part[(lane * rows + idx) * 2];
     l = a.ml_part[(lane * rows + idx) * 2 + 1];
   }
-  const float M = wave_max(m);
+  const float M = wave_allmax(m);
   const float e = lane < ns ? __expf(m - M) : 0.f;
-  const float L = wave_sum(l * e);
+  const float L = wave_allsum(l * e);
   const float wl = L > 0.f ? (BP ? l * e : e) / L : 0.f;
   const int g = static_cast<int>(idx / R), rr = static_cast<int>(idx % R);
   const int h = g * a.n_rep + rr / a.n_tok;

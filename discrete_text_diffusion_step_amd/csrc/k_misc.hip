@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int n, int D, float eps, f
 #pragma unroll
     for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
   }
-  ss = wave_sum(ss);
+  ss = wave_allsum(ss);
   const float scale = sqrt_d / (sqrtf(ss) + eps);
   T *yr = y + static_cast<long long>(row) * D;
   for (int c = lane * 8; c < D; c += 64 * 8) {
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kResThreads) void residual_rmsnorm_kernel(const flo
     }
     store8(xr + c, v);
   }
-  ss = wave_sum(ss);
+  ss = wave_allsum(ss);
   if (lane == 0) red[wave] = ss;
   __syncthreads();
   ss = 0.f;
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const T *w, int cols,
   const T *wr = w + row * cols;
   float m = 0.f;
   for (int c = tid; c < cols; c += 256) m = fmaxf(m, fabsf(to_f32<T>(wr[c])));
-  m = wave_max(m);
+  m = wave_allmax(m);
   if (lane == 0) red[wave] = m;
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
