@@ -158,6 +158,11 @@ hipError_t launch_v_transpose(int dtype, const void *src, int n, int Hkv, int dh
 #ifndef DG_SOLO_VDEPTH
 #define DG_SOLO_VDEPTH 8
 #endif
+// 1: the pair form waits for the V^T tile before the score exchange's
+// barrier (two barriers per tile); 0: a third barrier before P V
+#ifndef DG_PAIR_V_AT_EXCHANGE
+#define DG_PAIR_V_AT_EXCHANGE 1
+#endif
 // 1: the softmax's column maximum by VALU row swaps (0: by ds_bpermute)
 #ifndef DG_ATTN_PERMLANE
 #define DG_ATTN_PERMLANE 1

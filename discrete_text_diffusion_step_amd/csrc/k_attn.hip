@@ -953,6 +953,13 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) xs[wave][(kt * QT + qt) * 4 + i][lane] = st[kt][qt][i];
+    if (DG_PAIR_V_AT_EXCHANGE) {
+      // V(i) was issued a tile and a half ago; waiting for it here lets the
+      // exchange barrier publish it too (loads in flight after it: K(i+1)
+      // and V(i+1), if that tile exists)
+      if (ti + 1 < n_tiles) wait_vm<kNK + kNV>();
+      else wait_vm<0>();
+    }
     lds_sync();
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -1030,10 +1037,12 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
     }
     // ---- O^T += V^T P^T over this wave's half (tiles cut by the key range:
     // values of keys outside it are zeroed, as the cache holds anything there)
-    if (ti + 2 < n_tiles) wait_vm<2 * kNK + kNV>();
-    else if (ti + 1 < n_tiles) wait_vm<kNK + kNV>();
-    else wait_vm<0>();
-    lds_sync();
+    if (!DG_PAIR_V_AT_EXCHANGE) {
+      if (ti + 2 < n_tiles) wait_vm<2 * kNK + kNV>();
+      else if (ti + 1 < n_tiles) wait_vm<kNK + kNV>();
+      else wait_vm<0>();
+      lds_sync();
+    }
     Frag<T> vf[2];
     load_v_frag<T, DH>(vf[0], vb, hf * HALF + l16, lg);
     if (in_range) {
