@@ -27,6 +27,18 @@ __device__ __forceinline__ float wave_allreduce(float v, Op op) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// the same on 32-bit integers (exact for any value)
+template <typename Op>
+__device__ __forceinline__ int wave_allreduce_i(int v, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));
+  const auto a = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(v), static_cast<unsigned>(v), false, false);
+  v = op(static_cast<int>(a[0]), static_cast<int>(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(v), static_cast<unsigned>(v), false, false);
+  return op(static_cast<int>(b[0]), static_cast<int>(b[1]));
+}
 __device__ __forceinline__ float wave_allsum(float v) {
   return wave_allreduce(v, [](float x, float y) { return x + y; });
 }

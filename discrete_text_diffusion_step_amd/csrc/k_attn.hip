@@ -902,10 +902,9 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
     pq_min = min(pq_min, qpos[qt]);
     pq_max = max(pq_max, qpos[qt]);
   }
-#pragma unroll
-  for (int sh = 1; sh < 64; sh <<= 1) {
-    pq_min = min(pq_min, __shfl_xor(pq_min, sh, 64));
-    pq_max = max(pq_max, __shfl_xor(pq_max, sh, 64));
+  if (a.causal) {   // the bounds serve only the causal masks
+    pq_min = wave_allreduce_i(pq_min, [](int x, int y) { return min(x, y); });
+    pq_max = wave_allreduce_i(pq_max, [](int x, int y) { return max(x, y); });
   }
   pq_min = __builtin_amdgcn_readfirstlane(pq_min);
   pq_max = __builtin_amdgcn_readfirstlane(pq_max);
@@ -1298,10 +1297,9 @@ __global__ __launch_bounds__(NW * 64) void attn_solo_kernel(const AttnArgs a) {
     pq_min = min(pq_min, qpos[qt]);
     pq_max = max(pq_max, qpos[qt]);
   }
-#pragma unroll
-  for (int sh = 1; sh < 64; sh <<= 1) {
-    pq_min = min(pq_min, __shfl_xor(pq_min, sh, 64));
-    pq_max = max(pq_max, __shfl_xor(pq_max, sh, 64));
+  if (a.causal) {   // the bounds serve only the causal masks
+    pq_min = wave_allreduce_i(pq_min, [](int x, int y) { return min(x, y); });
+    pq_max = wave_allreduce_i(pq_max, [](int x, int y) { return max(x, y); });
   }
   pq_min = __builtin_amdgcn_readfirstlane(pq_min);
   pq_max = __builtin_amdgcn_readfirstlane(pq_max);
