@@ -133,20 +133,6 @@ __device__ __forceinline__ void contig_to_frags(const bf16x8 &x0, const bf16x8 &
   __builtin_memcpy(&f1, o1, 16);
 }
 
-// ---------------------------------------------------------- wave reductions
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
 // 16-byte vector of T elements.
 template <typename T> struct Vec16 { static constexpr int n = 16 / sizeof(T); };
 
