@@ -914,7 +914,9 @@ __global__ __launch_bounds__(512) void attn_pair_kernel(const AttnArgs a) {
   // wave has finished P V on tile i-1 (after the barrier that opens tile i).
   // The DMA queue per wave is therefore K0 V0 K1 V1 K2 ..., and the waits
   // count loads issued after the one needed: K(i) is followed by V(i) and
-  // K(i+1); V(i) by K(i+1), V(i+1) and K(i+2), each present if that tile is.
+  // K(i+1); V(i), waited for before the exchange barrier, by K(i+1) and
+  // V(i+1) (and K(i+2) too where a third barrier before P V carries it),
+  // each present if that tile is.
   auto tile = [&](int ti, T *kb, const T *vb, T *vb_next) {
     const int t0 = t_first + ti * kBKV;
     const bool in_range = t0 >= k_lo && t0 + kBKV <= k_hi;
