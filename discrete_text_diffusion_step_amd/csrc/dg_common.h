@@ -133,6 +133,20 @@ __device__ __forceinline__ void contig_to_frags(const bf16x8 &x0, const bf16x8 &
   __builtin_memcpy(&f1, o1, 16);
 }
 
+// 1: the XCD-aware tile numbering for grids of any size (0: multiples of 8 only)
+#ifndef DG_XCD_ANY_GRID
+#define DG_XCD_ANY_GRID 1
+#endif
+// Workgroup b of a grid of `total` runs on XCD b % 8.  Logical tile numbers
+// that keep neighbours on one XCD (one L2): XCD x takes the contiguous block
+// [x*q + min(x, r), ...) of q + (x < r) numbers, q = total / 8, r = total % 8
+// (a permutation of [0, total) for any total).
+__device__ __forceinline__ int xcd_tile(int b, int total) {
+  if (!DG_XCD_ANY_GRID && (total & 7)) return b;
+  const int q = total >> 3, r = total & 7, x = b & 7;
+  return x * q + (x < r ? x : r) + (b >> 3);
+}
+
 // 16-byte vector of T elements.
 template <typename T> struct Vec16 { static constexpr int n = 16 / sizeof(T); };
 

@@ -192,12 +192,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const GemmArgs a) {
   if (a.g_off == nullptr) {
     // dense: one tile per workgroup; consecutive workgroup ids are spread
     // over the 8 XCDs, so renumber tiles to keep neighbours on one XCD (L2)
-    int L = blockIdx.x;
-    const int total = gridDim.x;
-    if ((total & 7) == 0) {
-      const int per = total >> 3;
-      L = (L & 7) * per + (L >> 3);
-    }
+    const int L = xcd_tile(blockIdx.x, gridDim.x);
     const int m_tiles = (a.M + BM - 1) / BM;
     const int n_tiles = (a.N + BN - 1) / BN;
     int m_tile, n_tile, split;
@@ -904,12 +899,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmArgs a) {
   constexpr int BM = MT * 16, BN = NT * 16;
   __shared__ __attribute__((aligned(16))) float red[4 * NB * MT * NT * 4 * 64];
   if (a.g_off == nullptr) {
-    int L = blockIdx.x;
-    const int total = gridDim.x;
-    if ((total & 7) == 0) {
-      const int per = total >> 3;
-      L = (L & 7) * per + (L >> 3);
-    }
+    const int L = xcd_tile(blockIdx.x, gridDim.x);
     const int m_tiles = (a.M + BM - 1) / BM;
     const int n_tiles = (a.N + BN - 1) / BN;
     int m_tile, n_tile, split;
@@ -1177,12 +1167,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_wide_kernel(const GemmArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * MT * 16 * 64];
   __shared__ __attribute__((aligned(16))) bf16_t ldsb[NW * NB * NTW * 16 * 64];
   if (a.g_off == nullptr) {
-    int L = blockIdx.x;
-    const int total = gridDim.x;
-    if ((total & 7) == 0) {
-      const int per = total >> 3;
-      L = (L & 7) * per + (L >> 3);
-    }
+    const int L = xcd_tile(blockIdx.x, gridDim.x);
     const int m_tiles = (a.M + BM - 1) / BM;
     const int n_tiles = (a.N + BN - 1) / BN;
     int m_tile, n_tile, split;
