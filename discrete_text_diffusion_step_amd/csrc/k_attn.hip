@@ -1525,7 +1525,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs a, int
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int s = 0; s < ns; ++s) {
-      const float w = __shfl(wl, s, 64);
+      // split s's weight from lane s (a wave-uniform index: a VALU read, no LDS)
+      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s));
       float4 v;
       if constexpr (BP) {
         const uint2 u = *reinterpret_cast<const uint2 *>(reinterpret_cast<const bf16_t *>(a.o_part) +
