@@ -343,6 +343,11 @@ enum WideCfg {
   WIDE_ROWS256_N128_OP = 6,  // the 256 x 128 form with DG_OPROJ_P weight stages ahead (output projection)
   // every configuration walks k in stages of 64
 };
+// 1: the wide-tile loops issue each stage's global loads ahead of its MFMAs
+// (a scheduling barrier after the loads)
+#ifndef DG_LOAD_FENCE
+#define DG_LOAD_FENCE 1
+#endif
 #ifndef DG_WIDE_P
 #define DG_WIDE_P 3
 #endif

@@ -1123,6 +1123,10 @@ __device__ __forceinline__ void wide_tile(const GemmArgs &a, bf16_t *lds, bf16_t
       if constexpr (PA == 2) load_a(it + 2 < lastst ? it + 2 : lastst, ra[r & 1]);
       else load_a(it + 1 < lastst ? it + 1 : lastst, ra[0]);
       load_b(it + P < lastst ? it + P : lastst, rb[(r + P) % R]);
+      // the loads go out before the stage's MFMAs: left to itself the
+      // scheduler sinks them to the end of the body, next to the LDS write
+      // that waits for A, and every stage then waits a whole memory round trip
+      if constexpr (DG_LOAD_FENCE) __builtin_amdgcn_sched_barrier(0);
       if (it < nst) compute(it & 1, rb[r]);
       stage_a((it + 1) & 1, ra[PA == 2 ? ((r + 1) & 1) : 0]);
       lds_barrier();
@@ -1361,6 +1365,7 @@ __device__ __forceinline__ void wide_tile_f8(const GemmArgs &a, bf16_t *lds, uin
       const int it = i + r;
       load_a(it + 1 < lastst ? it + 1 : lastst, ra);
       load_b(it + P < lastst ? it + P : lastst, rb[(r + P) % R]);
+      if constexpr (DG_LOAD_FENCE) __builtin_amdgcn_sched_barrier(0);   // as in wide_tile
       if (it < nst) compute(it & 1, rb[r]);
       stage_a((it + 1) & 1, ra);
       lds_barrier();
