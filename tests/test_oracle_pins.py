@@ -459,6 +459,20 @@ def test_moe_identical_experts_weights_sum_to_scale():
     np.testing.assert_allclose(out, x + y, rtol=1e-11, atol=1e-11)
 
 
+def test_route_scale_scales_only_the_routed_experts():
+    # O11: the scale multiplies the renormalised top-k weights, never the
+    # shared expert: the routed part of the update is linear in it
+    cfg, w, x, _ = tiny_moe()
+    h = O.rms(x, w["w_in_norm"], cfg["rms_eps"])
+    shared = O.swiglu_ffn(h, w["ws_gate"], w["ws_up"], w["ws_down"], "f32")
+    o1, i1, w1, _ = O.moe_block(dict(cfg, route_scale=1.0), w, x, "f32")
+    o3, i3, w3, _ = O.moe_block(dict(cfg, route_scale=0.3), w, x, "f32")
+    np.testing.assert_array_equal(i1, i3)
+    np.testing.assert_allclose(w1.sum(axis=1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(w3, 0.3 * w1, rtol=1e-14)
+    np.testing.assert_allclose(o3 - x - shared, 0.3 * (o1 - x - shared), rtol=1e-10, atol=1e-12)
+
+
 def test_swiglu_silu_closed_form():
     z = np.array([-3.0, -0.5, 0.0, 0.5, 3.0])
     np.testing.assert_allclose(O.silu(z), z * scipy.special.expit(z), rtol=1e-15)
